@@ -1,0 +1,115 @@
+"""Pins for the oracle's number-format tables and encoders (CPU only).
+
+The tables are built from the OCP FP8 / MX bit-field definitions; here they
+are checked exhaustively against PyTorch's independent float8 casts and
+against closed-form values of the formats."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import formats as F
+
+
+def test_e4m3_table_matches_torch_cast_exhaustively():
+    codes = torch.arange(256, dtype=torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    ours = F.E4M3_TABLE
+    nan = np.isnan(ref)
+    assert np.array_equal(nan, np.isnan(ours))
+    assert np.array_equal(ref[~nan], ours[~nan])
+    assert sorted(np.flatnonzero(nan).tolist()) == [0x7F, 0xFF]
+
+
+def test_e4m3_closed_form_landmarks():
+    assert F.E4M3_TABLE[0x7E] == 448.0            # largest finite
+    assert F.E4M3_TABLE[0x01] == 2.0 ** -9        # smallest subnormal
+    assert F.E4M3_TABLE[0x08] == 2.0 ** -6        # smallest normal
+    assert F.E4M3_TABLE[0x38] == 1.0
+    assert F.E4M3_TABLE[0xB8] == -1.0
+    assert F.E4M3_TABLE[0x80] == 0.0 and np.signbit(F.E4M3_TABLE[0x80])
+    pos = F.E4M3_TABLE[:0x7F]
+    assert np.all(np.diff(pos) > 0)               # strictly increasing in code order
+
+
+def test_e2m1_table_matches_mx_element_list():
+    # OCP MX v1.0 lists the E2M1 magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6.
+    mags = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    assert F.E2M1_TABLE[:8].tolist() == mags
+    assert F.E2M1_TABLE[8:].tolist() == [-m for m in mags]
+
+
+def test_e8m0_matches_torch_cast_exhaustively():
+    codes = torch.arange(256, dtype=torch.uint8)
+    ref = codes.view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    ours = F.e8m0_decode(np.arange(256))
+    assert np.isnan(ours[255]) and np.isnan(ref[255])
+    assert np.array_equal(ref[:255], ours[:255])
+    assert ours[127] == 1.0 and ours[0] == 2.0 ** -127
+
+
+def test_e2m1_nibble_order():
+    # byte 0x21: low nibble 1 (0.5) is element 0, high nibble 2 (1.0) element 1
+    out = F.e2m1_unpack(np.array([[0x21, 0xF9]], dtype=np.uint8))
+    assert out.tolist() == [[0.5, 1.0, -0.5, -6.0]]
+
+
+def test_bf16_decode_matches_torch():
+    rng = np.random.default_rng(0)
+    v = torch.tensor(rng.standard_normal(4096) * 100, dtype=torch.float32).to(torch.bfloat16)
+    bits = v.view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(F.bf16_decode(bits), v.to(torch.float64).numpy())
+
+
+def test_e4m3_encode_roundtrips_every_code():
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    vals = F.E4M3_TABLE[codes]
+    back = F.e4m3_encode(vals)
+    assert np.array_equal(back, codes)
+
+
+def test_e4m3_encode_midpoints_go_to_even_code():
+    pos = F.E4M3_TABLE[:0x7F]
+    mids = (pos[1:] + pos[:-1]) / 2          # between code c and c+1
+    got = F.e4m3_encode(mids)
+    lower = np.arange(0x7E)
+    want = np.where(lower % 2 == 0, lower, lower + 1)
+    assert np.array_equal(got, want.astype(np.uint8))
+    # just off the midpoint goes to the nearer code
+    eps = 1e-9
+    assert np.array_equal(F.e4m3_encode(mids - eps * pos[1:]), lower.astype(np.uint8))
+    assert np.array_equal(F.e4m3_encode(mids + eps * pos[1:]), (lower + 1).astype(np.uint8))
+
+
+def test_e4m3_encode_saturates():
+    got = F.e4m3_encode(np.array([448.0, 463.9, 464.0, 500.0, 1e30, -449.0, -1e9]))
+    assert got.tolist() == [0x7E, 0x7E, 0x7E, 0x7E, 0x7E, 0xFE, 0xFE]
+    with pytest.raises(ValueError):
+        F.e4m3_encode(np.array([np.nan]))
+
+
+def test_e4m3_encode_agrees_with_torch_cast():
+    rng = np.random.default_rng(1)
+    v = np.concatenate([rng.standard_normal(20000) * 50,
+                        rng.standard_normal(20000) * 2.0 ** -7]).astype(np.float32)
+    ref = torch.tensor(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    ours = F.e4m3_encode(v.astype(np.float64))
+    # torch keeps the sign of values that round to zero as well
+    assert np.array_equal(ours, ref)
+
+
+def test_bf16_round_matches_torch_rne():
+    rng = np.random.default_rng(2)
+    v = (rng.standard_normal(50000) * 10).astype(np.float32)
+    ref = torch.tensor(v).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(F.bf16_round(v.astype(np.float64)), ref)
+    # an exact tie between two BF16 values rounds to the even mantissa
+    one = 1.0
+    ulp = 2.0 ** -7
+    assert F.bf16_round(np.array([one + ulp / 2]))[0] == one
+    assert F.bf16_round(np.array([one + 1.5 * ulp]))[0] == one + 2 * ulp
+
+
+def test_f32_round():
+    assert F.f32_round(np.array([1.0 + 2.0 ** -30]))[0] == 1.0
+    assert F.f32_round(np.array([1.0 + 2.0 ** -23]))[0] == 1.0 + 2.0 ** -23
