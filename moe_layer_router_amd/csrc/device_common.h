@@ -1,0 +1,161 @@
+// Device helpers shared by the MoE layer kernels (gfx950 / CDNA4 only).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define DEV __device__ __forceinline__
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+// ------------------------------------------------------------ conversions
+// OCP E4M3 ("fn") byte -> fp32, exact.  Normals: rebias the exponent field
+// (7 -> 127) by placing the 7 magnitude bits at bit 20 and adding 120 << 23.
+// Subnormals (exponent field 0) are m * 2^-9.
+DEV float e4m3_to_f32(uint32_t b) {
+  const uint32_t mag = b & 0x7Fu;
+  const float normal = __uint_as_float((mag << 20) + (120u << 23));
+  const float sub = (float)(mag & 7u) * 0x1p-9f;
+  const float v = (mag >= 8u) ? normal : sub;
+  return (b & 0x80u) ? -v : v;
+}
+
+// BF16 bit pattern of an fp32 whose significand fits in 8 bits (exact).
+DEV uint32_t f32_to_bf16_exact(float f) { return __float_as_uint(f) >> 16; }
+
+// fp32 -> BF16 bits, round to nearest even (finite inputs).
+DEV uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+DEV float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// Four E4M3 bytes (one dword) -> four BF16 values packed in two dwords.
+DEV void e4m3x4_to_bf16x4(uint32_t q, uint32_t& lo, uint32_t& hi) {
+  const uint32_t b0 = f32_to_bf16_exact(e4m3_to_f32(q & 0xFFu));
+  const uint32_t b1 = f32_to_bf16_exact(e4m3_to_f32((q >> 8) & 0xFFu));
+  const uint32_t b2 = f32_to_bf16_exact(e4m3_to_f32((q >> 16) & 0xFFu));
+  const uint32_t b3 = f32_to_bf16_exact(e4m3_to_f32(q >> 24));
+  lo = b0 | (b1 << 16);
+  hi = b2 | (b3 << 16);
+}
+
+// fp32 -> E4M3 byte with the hardware converter (round to nearest even);
+// the input is clamped to +-448 first, so the result saturates.
+DEV uint32_t f32_to_e4m3(float v) {
+  v = fminf(fmaxf(v, -448.0f), 448.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v, 0.0f, 0, false) & 0xFFu;
+}
+DEV uint32_t f32x2_to_e4m3x2(float v0, float v1) {
+  v0 = fminf(fmaxf(v0, -448.0f), 448.0f);
+  v1 = fminf(fmaxf(v1, -448.0f), 448.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false) & 0xFFFFu;
+}
+
+// Monotone map of fp32 onto uint32 (larger float -> larger key); -0 and +0
+// map to the same key.
+DEV uint32_t f32_order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+DEV float f32_from_order_key(uint32_t k) {
+  const uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+  return __uint_as_float(u);
+}
+
+// ------------------------------------------------------------------- MFMA
+// 16x16x128 block-scaled MFMA (gfx950).  Lane l holds row (A) / column (B)
+// l%16.  8-bit operands: lane group g = l/16 holds K 16g..16g+15 (bytes
+// 0..15) and K 64+16g..64+16g+15 (bytes 16..31).  4-bit operands: lane group
+// g holds K 32g..32g+31, two per byte, even K in the low nibble, in the low
+// 16 bytes.  The E8M0 scale supplied by lane l applies to row/column l%16 and
+// K 32g..32g+31.  Result: lane l, element v is row 4g+v, column l%16.
+DEV v4f mfma_fp8_fp8(const v8i& a, const v8i& b, const v4f& c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+DEV v4f mfma_fp8_fp4(const v8i& a, const v8i& b, const v4f& c, int bscale) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 4, 0, 127, 0, bscale);
+}
+// 16x16x32 BF16 MFMA: lane l holds row/column l%16, 8 K of group l/16.
+DEV v4f mfma_bf16(const v8bf& a, const v8bf& b, const v4f& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+DEV v8bf as_v8bf(const v4i& v) { return __builtin_bit_cast(v8bf, v); }
+
+// -------------------------------------------------------- wave reductions
+DEV float wave_max_xor16(float v) {           // max over the 16 lanes sharing l/16
+  v = fmaxf(v, __shfl_xor(v, 1));
+  v = fmaxf(v, __shfl_xor(v, 2));
+  v = fmaxf(v, __shfl_xor(v, 4));
+  v = fmaxf(v, __shfl_xor(v, 8));
+  return v;
+}
+
+DEV uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) {
+    const uint32_t lo = __shfl_xor((uint32_t)v, m);
+    const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), m);
+    const uint64_t o = ((uint64_t)hi << 32) | lo;
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+// Inclusive prefix sum over a workgroup of `nthreads` (multiple of 64) ints.
+// `scratch` needs nthreads/64 ints of LDS.  Returns the inclusive sum of the
+// thread's value; *total receives the workgroup total.
+DEV int block_inclusive_scan(int v, int* scratch, int* total) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int o = __shfl_up(v, d);
+    if (lane >= d) v += o;
+  }
+  if (lane == 63) scratch[wv] = v;
+  __syncthreads();
+  int pre = 0, tot = 0;
+  for (int i = 0; i < nw; ++i) {
+    const int s = scratch[i];
+    if (i < wv) pre += s;
+    tot += s;
+  }
+  __syncthreads();
+  *total = tot;
+  return v + pre;
+}
+
+// ----------------------------------------------------- memory helpers
+// Hide the known bits of a per-lane offset from the optimiser.  LDS
+// addresses are then formed as (opaque base + compile-time constant), which
+// folds into the DS instruction's immediate offset instead of being
+// materialised (and kept live) as one register per constant.
+DEV uint32_t opaque(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+// Make v depend on dep (no instruction is emitted): v cannot be computed
+// before dep is available, which bounds how far the scheduler hoists loads.
+DEV uint32_t after(uint32_t v, float dep) {
+  asm volatile("" : "+v"(v) : "v"(dep));
+  return v;
+}
+template <typename T>
+DEV T lds_ld(const char* lds, uint32_t off) { return *reinterpret_cast<const T*>(lds + off); }
+template <typename T>
+DEV void lds_st(char* lds, uint32_t off, const T& v) { *reinterpret_cast<T*>(lds + off) = v; }
+
+DEV v4i ld16(const void* p) { return *reinterpret_cast<const v4i*>(p); }
+DEV void st16(void* p, const v4i& v) { *reinterpret_cast<v4i*>(p) = v; }
+
+}  // namespace moe

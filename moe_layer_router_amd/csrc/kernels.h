@@ -1,0 +1,59 @@
+// Kernel entry points and the workspace plan shared by the host code.
+#pragma once
+#include "device_common.h"
+#include "expert_gemm.h"
+#include "permute.h"
+#include "router.h"
+
+namespace moe {
+
+// Counters at the start of the zeroed workspace region.
+enum {
+  CTR_QUEUE = 0,      // persistent-kernel work queue head
+  CTR_COUNT_DONE,     // histogram items finished
+  CTR_SCAN_FLAG,      // 1 once offsets / base / tiles are written
+  CTR_SCATTER_DONE,   // scatter items finished
+  CTR_G1_DONE,        // gate|up items finished
+  CTR_NUM = 16
+};
+
+// Everything a kernel needs: shapes, caller buffers and workspace regions.
+struct Plan {
+  int T, H, E, I, k;
+  int act_fp8, wdt;            // ACT_*, W_*
+  int routing_given;
+  int nblk;                    // 256-token blocks
+  int nT64, nE64;              // router tiles
+  int max_tiles;
+  int nnb1, nnb2;              // N blocks of gate|up (128 channels) and down (256 columns)
+  int slab_group;              // down-GEMM N blocks processed per tile before moving on
+  int nCT;                     // combine token chunks per N block
+  // caller buffers
+  const uint8_t* x; const float* x_scales; const uint16_t* wr; const float* bias;
+  const uint8_t* w_gu; const void* w_gu_scales; const uint8_t* w_d; const void* w_d_scales;
+  uint16_t* y; int32_t* ids; float* wts; int32_t* offsets; int32_t* perm;
+  // workspace
+  int32_t* err;                // device error word (byte offset 0)
+  int32_t* ctr;                // [CTR_NUM]
+  int32_t* rdone;              // [nT64]   router items finished per token tile
+  int32_t* tkdone;             // [nblk]   top-k items finished per 256-token block
+  int32_t* done1;              // [max_tiles] gate|up items finished per tile
+  int32_t* done2;              // [nnb2]   down items finished per N block
+  size_t zero_bytes;           // bytes to clear from ctr up to the end of done2
+  float* logits; int32_t* blockcnt; int32_t* base; int32_t* row_of;
+  Tile* tiles; int32_t* meta;
+  uint8_t* aq; float* sa; uint16_t* staging;
+};
+
+constexpr int kCombineTokens = 256;
+
+__host__ __device__ inline GemmArgs gemm_args(const Plan& p) {
+  GemmArgs g;
+  g.x = p.x; g.x_scales = p.x_scales; g.perm = p.perm; g.topk_w = p.wts;
+  g.w_gu = p.w_gu; g.w_gu_scales = p.w_gu_scales; g.w_d = p.w_d; g.w_d_scales = p.w_d_scales;
+  g.aq = p.aq; g.sa = p.sa; g.staging = p.staging;
+  g.T = p.T; g.H = p.H; g.E = p.E; g.I = p.I; g.k = p.k;
+  return g;
+}
+
+}  // namespace moe

@@ -1,0 +1,634 @@
+// Kernels of the fused MoE layer: the separate-kernel pipeline and the
+// persistent work-queue kernel that runs the whole layer in one launch.
+//
+// The single-launch form is the Mega MoE idea (机器之心, "DeepSeek悄悄更新：Mega
+// MoE、FP4 Indexer来了", section "Mega MoE 是什么？"): dispatch, both linear
+// maps, SwiGLU and combine fused into one kernel so that the GPU does not
+// alternate between computing and waiting.  On one GPU the dispatch and
+// combine are local permutations, and the overlap is between HBM weight
+// streaming and MFMA work of different work items running side by side.
+#include "kernels.h"
+
+namespace moe {
+
+// ----------------------------------------------------------- separate mode
+__global__ void k_zero(int32_t* p, size_t n) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = 0;
+}
+
+__global__ void __launch_bounds__(256) k_router(RouterArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  router_tile(a, blockIdx.y * kRouterTokens, blockIdx.x * kRouterExperts, lds);
+}
+
+__global__ void __launch_bounds__(256) k_topk(const float* logits, int T, int E, int k, int32_t* ids, float* wts) {
+  const int t0 = blockIdx.x * 64;
+  topk_tokens(logits, E, k, t0, min(64, T - t0), ids, wts);
+}
+
+__global__ void __launch_bounds__(256) k_count(const int32_t* ids, int T, int k, int E, int32_t* blockcnt) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  perm_count_block(ids, T, k, E, blockIdx.x, blockcnt, reinterpret_cast<int*>(lds));
+}
+
+__global__ void __launch_bounds__(256) k_scan(const int32_t* blockcnt, int nblk, int E, int32_t* base,
+                                              int32_t* offsets, Tile* tiles, int32_t* meta) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  perm_scan(blockcnt, nblk, E, base, offsets, tiles, meta, reinterpret_cast<int*>(lds));
+}
+
+__global__ void __launch_bounds__(256) k_scatter(const int32_t* ids, int T, int k, int E, const int32_t* base,
+                                                 int32_t* perm, int32_t* row_of) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  perm_scatter_block(ids, T, k, E, blockIdx.x, base, perm, row_of, reinterpret_cast<uint64_t*>(lds));
+}
+
+// Persistent grid over (tile, N block) items.  Workgroup b runs on XCD b % 8
+// (round-robin dispatch); each XCD takes a contiguous run of items per round,
+// so the N blocks of one row tile share that XCD's L2 for their A rows.
+template <int AF, int WF, int STAGE>
+__global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
+k_gemm(GemmArgs g, const Tile* tiles, const int32_t* meta, int nnb) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int nitems = meta[0] * nnb;
+  const int G = gridDim.x, b = blockIdx.x;
+  const int slot = (b & 7) * (G >> 3) + (b >> 3);
+  for (int base = 0; base + slot < nitems; base += G) {
+    const int i = base + slot;
+    const Tile t = tiles[i / nnb];
+    expert_gemm_tile<AF, WF, STAGE>(g, t.e, t.r0, t.rows, i % nnb, lds);
+  }
+}
+
+__global__ void __launch_bounds__(256) k_combine(const uint16_t* staging, uint16_t* y, int T, int H, int k) {
+  const int t0 = blockIdx.x * 16;
+  combine_rows(staging, y, H, k, t0, min(T, t0 + 16), 0, H);
+}
+
+// ------------------------------------------------------- persistent kernel
+constexpr unsigned kSpinLimit = 1u << 22;
+
+// Thread 0 waits (bounded) until *c >= target, with acquire ordering at
+// device scope; the workgroup then proceeds together.  Returns false if the
+// wait timed out or another workgroup reported a failure.
+DEV bool wait_counter(const int32_t* c, int target, int32_t* err, int* s_ok) {
+  if (threadIdx.x == 0) {
+    int ok = 1;
+    unsigned spins = 0;
+    while (__hip_atomic_load(c, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      if (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) { ok = 0; break; }
+      __builtin_amdgcn_s_sleep(8);
+      if (++spins > kSpinLimit) {
+        __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ok = 0;
+        break;
+      }
+    }
+    *s_ok = ok;
+  }
+  __syncthreads();
+  const int ok = *s_ok;
+  __syncthreads();
+  return ok != 0;
+}
+
+// Publish this workgroup's global writes, then add 1 to each counter.
+DEV void signal_add(int32_t* c0, int32_t* c1 = nullptr) {
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __hip_atomic_fetch_add(c0, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    if (c1) __hip_atomic_fetch_add(c1, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Work queue, in dependency order (an item only ever waits for items with a
+// smaller queue index, all of which were taken by running workgroups, so the
+// queue cannot deadlock whatever the grid size):
+//   router tiles (64 tokens x 64 experts)       -> rdone[token tile]
+//   top-k of 64 tokens                          -> tkdone[256-token block]
+//   expert histogram of 256 tokens              -> COUNT_DONE
+//   scan (offsets, block bases, tile list)      -> SCAN_FLAG
+//   stable scatter of 256 tokens                -> SCATTER_DONE
+//   gate|up items (tile, 128 channels)          -> done1[tile]
+//   per group of down N blocks: down items (tile, N block), tile-major,
+//   then combine items (N block, 256 tokens)    <- done2[N block]
+// Each phase of the persistent kernel is its own (non-inlined) function, so
+// that register allocation sees one phase at a time.  Each declares the
+// dynamic LDS array itself so that its accesses compile to LDS instructions.
+#define MEGA_LDS extern __shared__ __attribute__((aligned(16))) char lds[]
+template <int AF, int WF, int STAGE>
+__device__ __noinline__ void mega_gemm_item(const Plan& p, Tile tl, int nb) {
+  MEGA_LDS;
+  expert_gemm_tile<AF, WF, STAGE>(gemm_args(p), tl.e, tl.r0, tl.rows, nb, lds);
+}
+__device__ __noinline__ void mega_router_item(const Plan& p, int tt, int et) {
+  MEGA_LDS;
+  RouterArgs ra{p.x, p.x_scales, p.wr, p.bias, p.logits, p.T, p.H, p.E, p.act_fp8};
+  router_tile(ra, tt * kRouterTokens, et * kRouterExperts, lds);
+}
+__device__ __noinline__ void mega_topk_item(const Plan& p, int tt) {
+  const int t0 = tt * 64;
+  topk_tokens(p.logits, p.E, p.k, t0, min(64, p.T - t0), p.ids, p.wts);
+}
+__device__ __noinline__ void mega_count_item(const Plan& p, int b) {
+  MEGA_LDS;
+  perm_count_block(p.ids, p.T, p.k, p.E, b, p.blockcnt, reinterpret_cast<int*>(lds));
+}
+__device__ __noinline__ void mega_scan_item(const Plan& p) {
+  MEGA_LDS;
+  perm_scan(p.blockcnt, p.nblk, p.E, p.base, p.offsets, p.tiles, p.meta, reinterpret_cast<int*>(lds));
+}
+__device__ __noinline__ void mega_scatter_item(const Plan& p, int b) {
+  MEGA_LDS;
+  perm_scatter_block(p.ids, p.T, p.k, p.E, b, p.base, p.perm, p.row_of, reinterpret_cast<uint64_t*>(lds));
+}
+__device__ __noinline__ void mega_combine_item(const Plan& p, int nb, int c) {
+  const int t0 = c * kCombineTokens;
+  combine_rows(p.staging, p.y, p.H, p.k, t0, min(p.T, t0 + kCombineTokens), nb * 256, min(p.H, nb * 256 + 256));
+}
+
+template <int AF, int WF>
+__global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
+k_mega(Plan p) {
+  __shared__ int s_q, s_ok, s_ntiles;
+  const int tid = threadIdx.x;
+  const int nR = p.routing_given ? 0 : p.nT64 * p.nE64;
+  const int nK = p.routing_given ? 0 : p.nT64;
+  const int q_topk = nR, q_count = nR + nK, q_scan = q_count + p.nblk;
+  const int q_scat = q_scan + 1, q_dyn = q_scat + p.nblk;
+  bool seen_scatter = false;
+  int ntiles = -1;
+
+  for (;;) {
+    if (tid == 0) s_q = __hip_atomic_fetch_add(&p.ctr[CTR_QUEUE], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int q = s_q;
+    __syncthreads();
+
+    if (q < q_topk) {
+      const int tt = q / p.nE64, et = q % p.nE64;
+      mega_router_item(p, tt, et);
+      signal_add(&p.rdone[tt]);
+    } else if (q < q_count) {
+      const int tt = q - q_topk;
+      if (!wait_counter(&p.rdone[tt], p.nE64, p.err, &s_ok)) break;
+      mega_topk_item(p, tt);
+      signal_add(&p.tkdone[tt >> 2]);
+    } else if (q < q_scan) {
+      const int b = q - q_count;
+      if (!p.routing_given) {
+        const int tiles_in_block = min(4, p.nT64 - 4 * b);
+        if (!wait_counter(&p.tkdone[b], tiles_in_block, p.err, &s_ok)) break;
+      }
+      mega_count_item(p, b);
+      signal_add(&p.ctr[CTR_COUNT_DONE]);
+    } else if (q == q_scan) {
+      if (!wait_counter(&p.ctr[CTR_COUNT_DONE], p.nblk, p.err, &s_ok)) break;
+      mega_scan_item(p);
+      signal_add(&p.ctr[CTR_SCAN_FLAG]);
+    } else if (q < q_dyn) {
+      if (!wait_counter(&p.ctr[CTR_SCAN_FLAG], 1, p.err, &s_ok)) break;
+      mega_scatter_item(p, q - q_scat);
+      signal_add(&p.ctr[CTR_SCATTER_DONE]);
+    } else {
+      if (ntiles < 0) {
+        if (!wait_counter(&p.ctr[CTR_SCAN_FLAG], 1, p.err, &s_ok)) break;
+        if (tid == 0) s_ntiles = __hip_atomic_load(&p.meta[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        ntiles = s_ntiles;
+        __syncthreads();
+      }
+      int i = q - q_dyn;
+      const int n1 = ntiles * p.nnb1;
+      if (i < n1) {
+        if (!seen_scatter) {
+          if (!wait_counter(&p.ctr[CTR_SCATTER_DONE], p.nblk, p.err, &s_ok)) break;
+          seen_scatter = true;
+        }
+        const int t = i / p.nnb1;
+        mega_gemm_item<AF, WF, 1>(p, p.tiles[t], i % p.nnb1);
+        signal_add(&p.done1[t], &p.ctr[CTR_G1_DONE]);
+        continue;
+      }
+      i -= n1;
+      bool found = false, failed = false;
+      for (int g0 = 0; g0 < p.nnb2; g0 += p.slab_group) {
+        const int ns = min(p.slab_group, p.nnb2 - g0);
+        const int n2 = ntiles * ns, nc = ns * p.nCT;
+        if (i < n2) {
+          const int t = i / ns, nb = g0 + i % ns;
+          if (!wait_counter(&p.done1[t], p.nnb1, p.err, &s_ok)) { failed = true; break; }
+          mega_gemm_item<AF, WF, 2>(p, p.tiles[t], nb);
+          signal_add(&p.done2[nb]);
+          found = true;
+          break;
+        }
+        i -= n2;
+        if (i < nc) {
+          const int nb = g0 + i / p.nCT, c = i % p.nCT;
+          if (!wait_counter(&p.done2[nb], ntiles, p.err, &s_ok)) { failed = true; break; }
+          mega_combine_item(p, nb, c);
+          found = true;
+          break;
+        }
+        i -= nc;
+      }
+      if (failed || !found) break;
+    }
+  }
+}
+
+}  // namespace moe
+
+// ===================================================================== host
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "../../include/moe_layer.h"
+
+using namespace moe;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+moe_status fail(moe_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+struct Layout {
+  size_t err, zero_begin, ctr, rdone, tkdone, done1, done2, zero_end;
+  size_t logits, blockcnt, base, offsets, perm, row_of, tiles, meta, aq, sa, staging, total;
+  int nblk, nT64, nE64, max_tiles, nnb1, nnb2;
+};
+
+Layout make_layout(const moe_desc* d) {
+  Layout L{};
+  const size_t T = d->T, E = d->E, k = d->top_k, H = d->H, I = d->I;
+  L.nblk = (int)((T + kPermBlock - 1) / kPermBlock);
+  L.nT64 = (int)((T + 63) / 64);
+  L.nE64 = (int)((E + 63) / 64);
+  L.max_tiles = (int)(E + (T * k + kTileRows - 1) / kTileRows);
+  L.nnb1 = (int)(I / 128);
+  L.nnb2 = (int)((H + 255) / 256);
+  size_t o = 0;
+  L.err = o; o += 256;
+  L.zero_begin = o;
+  L.ctr = o; o += CTR_NUM * 4;
+  L.rdone = o; o += (size_t)L.nT64 * 4;
+  L.tkdone = o; o += (size_t)L.nblk * 4;
+  L.done1 = o; o += (size_t)L.max_tiles * 4;
+  L.done2 = o; o += (size_t)L.nnb2 * 4;
+  L.zero_end = o;
+  o = align256(o);
+  L.logits = o; o = align256(o + T * E * 4);
+  L.blockcnt = o; o = align256(o + (size_t)L.nblk * E * 4);
+  L.base = o; o = align256(o + (size_t)L.nblk * E * 4);
+  L.offsets = o; o = align256(o + (E + 1) * 4);
+  L.perm = o; o = align256(o + T * k * 4);
+  L.row_of = o; o = align256(o + T * k * 4);
+  L.tiles = o; o = align256(o + (size_t)L.max_tiles * sizeof(Tile));
+  L.meta = o; o = align256(o + 64);
+  L.aq = o; o = align256(o + T * k * I * (d->act_dtype == MOE_DTYPE_FP8_E4M3 ? 1 : 2));
+  L.sa = o; o = align256(o + T * k * (I / 128) * 4);
+  L.staging = o; o = align256(o + T * k * H * 2);
+  L.total = o;
+  return L;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+moe_status check_desc(const moe_desc* d) {
+  if (!d) return fail(MOE_ERR_INVALID_ARGUMENT, "descriptor is NULL");
+  if (d->T < 1) return fail(MOE_ERR_INVALID_ARGUMENT, "T must be >= 1 (got %d)", d->T);
+  if (d->H < 128 || d->H % 128) return fail(MOE_ERR_INVALID_ARGUMENT, "H must be a positive multiple of 128 (got %d)", d->H);
+  if (d->I < 128 || d->I % 128) return fail(MOE_ERR_INVALID_ARGUMENT, "I must be a positive multiple of 128 (got %d)", d->I);
+  if (d->E < 1) return fail(MOE_ERR_INVALID_ARGUMENT, "E must be >= 1 (got %d)", d->E);
+  if (d->top_k < 1 || d->top_k > d->E) return fail(MOE_ERR_INVALID_ARGUMENT, "top_k must be in [1, E] (got %d)", d->top_k);
+  if (d->E > 1024) return fail(MOE_ERR_UNSUPPORTED, "E > 1024 is not supported (got %d)", d->E);
+  if (d->top_k > 16) return fail(MOE_ERR_UNSUPPORTED, "top_k > 16 is not supported (got %d)", d->top_k);
+  if (d->H > 16384) return fail(MOE_ERR_UNSUPPORTED, "H > 16384 is not supported (got %d)", d->H);
+  if (d->I > 16384) return fail(MOE_ERR_UNSUPPORTED, "I > 16384 is not supported (got %d)", d->I);
+  if ((long long)d->T * d->top_k > (1LL << 30)) return fail(MOE_ERR_UNSUPPORTED, "T * top_k too large");
+  const bool pair_ok = (d->act_dtype == MOE_DTYPE_BF16 && d->weight_dtype == MOE_DTYPE_BF16) ||
+                       (d->act_dtype == MOE_DTYPE_FP8_E4M3 && d->weight_dtype == MOE_DTYPE_FP8_E4M3) ||
+                       (d->act_dtype == MOE_DTYPE_FP8_E4M3 && d->weight_dtype == MOE_DTYPE_FP4_E2M1);
+  if (!pair_ok)
+    return fail(MOE_ERR_UNSUPPORTED, "unsupported dtype pair act=%d weight=%d (supported: bf16xbf16, fp8xfp8, fp8xfp4)",
+                d->act_dtype, d->weight_dtype);
+  if (d->mode != MOE_MODE_MEGA && d->mode != MOE_MODE_SEPARATE)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "unknown mode %d", d->mode);
+  if (d->flags & ~MOE_FLAG_ROUTING_GIVEN) return fail(MOE_ERR_INVALID_ARGUMENT, "unknown flags 0x%x", d->flags);
+  return MOE_OK;
+}
+
+moe_status check_ptr(const void* p, const char* name, bool required = true) {
+  if (!p) return required ? fail(MOE_ERR_INVALID_ARGUMENT, "%s is NULL", name) : MOE_OK;
+  if (!aligned16(p)) return fail(MOE_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", name);
+  return MOE_OK;
+}
+
+#define TRY(expr)                       \
+  do {                                  \
+    moe_status _s = (expr);             \
+    if (_s != MOE_OK) return _s;        \
+  } while (0)
+
+#define HIP_TRY(expr)                                                                    \
+  do {                                                                                   \
+    hipError_t _e = (expr);                                                              \
+    if (_e != hipSuccess) return fail(MOE_ERR_HIP, "%s: %s", #expr, hipGetErrorString(_e)); \
+  } while (0)
+
+struct DevInfo {
+  int checked = 0, ok = 0, cus = 0;
+};
+std::mutex g_dev_mu;
+DevInfo g_dev[64];
+
+moe_status device_info(DevInfo* out) {
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  if (dev < 0 || dev >= 64) return fail(MOE_ERR_UNSUPPORTED, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  DevInfo& di = g_dev[dev];
+  if (!di.checked) {
+    hipDeviceProp_t prop;
+    HIP_TRY(hipGetDeviceProperties(&prop, dev));
+    di.ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    di.cus = prop.multiProcessorCount;
+    di.checked = 1;
+  }
+  if (!di.ok) return fail(MOE_ERR_UNSUPPORTED, "this library is built for gfx950 (MI355X) only");
+  *out = di;
+  return MOE_OK;
+}
+
+moe_status fill_plan(const moe_desc* d, const Layout& L, char* ws, Plan* P) {
+  Plan& p = *P;
+  memset(&p, 0, sizeof p);
+  p.T = d->T; p.H = d->H; p.E = d->E; p.I = d->I; p.k = d->top_k;
+  p.act_fp8 = d->act_dtype == MOE_DTYPE_FP8_E4M3;
+  p.wdt = d->weight_dtype == MOE_DTYPE_FP8_E4M3 ? W_FP8 : d->weight_dtype == MOE_DTYPE_FP4_E2M1 ? W_FP4 : W_BF16;
+  p.routing_given = (d->flags & MOE_FLAG_ROUTING_GIVEN) != 0;
+  p.nblk = L.nblk; p.nT64 = L.nT64; p.nE64 = L.nE64; p.max_tiles = L.max_tiles;
+  p.nnb1 = L.nnb1; p.nnb2 = L.nnb2;
+  p.slab_group = 4;
+  p.nCT = (d->T + kCombineTokens - 1) / kCombineTokens;
+  p.err = reinterpret_cast<int32_t*>(ws + L.err);
+  p.ctr = reinterpret_cast<int32_t*>(ws + L.ctr);
+  p.rdone = reinterpret_cast<int32_t*>(ws + L.rdone);
+  p.tkdone = reinterpret_cast<int32_t*>(ws + L.tkdone);
+  p.done1 = reinterpret_cast<int32_t*>(ws + L.done1);
+  p.done2 = reinterpret_cast<int32_t*>(ws + L.done2);
+  p.zero_bytes = L.zero_end - L.zero_begin;
+  p.logits = reinterpret_cast<float*>(ws + L.logits);
+  p.blockcnt = reinterpret_cast<int32_t*>(ws + L.blockcnt);
+  p.base = reinterpret_cast<int32_t*>(ws + L.base);
+  p.offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
+  p.perm = reinterpret_cast<int32_t*>(ws + L.perm);
+  p.row_of = reinterpret_cast<int32_t*>(ws + L.row_of);
+  p.tiles = reinterpret_cast<Tile*>(ws + L.tiles);
+  p.meta = reinterpret_cast<int32_t*>(ws + L.meta);
+  p.aq = reinterpret_cast<uint8_t*>(ws + L.aq);
+  p.sa = reinterpret_cast<float*>(ws + L.sa);
+  p.staging = reinterpret_cast<uint16_t*>(ws + L.staging);
+  return MOE_OK;
+}
+
+enum { WS_LAYER, WS_ROUTE, WS_PERMUTE };
+
+size_t workspace_need(const moe_desc* d, int what) {
+  const Layout L = make_layout(d);
+  return what == WS_ROUTE ? L.blockcnt : what == WS_PERMUTE ? L.aq : L.total;
+}
+
+moe_status check_workspace(const moe_desc* d, const void* ws, size_t bytes, int what = WS_LAYER) {
+  TRY(check_ptr(ws, "workspace"));
+  const size_t need = workspace_need(d, what);
+  if (bytes < need)
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", bytes, need);
+  return MOE_OK;
+}
+
+template <typename K>
+moe_status set_lds_limit(K kernel, int bytes) {
+  if (bytes > 64 * 1024) HIP_TRY(hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes));
+  return MOE_OK;
+}
+
+int gemm_lds(int act_fp8) { return act_fp8 ? GemmLds<ACT_FP8>::kBytes : GemmLds<ACT_BF16>::kBytes; }
+
+int mega_lds(const Plan& p) {
+  int b = gemm_lds(p.act_fp8);
+  b = b > kRouterLds ? b : kRouterLds;
+  b = b > 4 * p.E * 8 ? b : 4 * p.E * 8;
+  b = b > (2 * p.E + 64) * 4 ? b : (2 * p.E + 64) * 4;
+  return b;
+}
+
+moe_status launch_route(const Plan& p, float* logits, hipStream_t st) {
+  RouterArgs ra{p.x, p.x_scales, p.wr, p.bias, logits, p.T, p.H, p.E, p.act_fp8};
+  hipLaunchKernelGGL(k_router, dim3(p.nE64, p.nT64), dim3(256), kRouterLds, st, ra);
+  HIP_TRY(hipGetLastError());
+  hipLaunchKernelGGL(k_topk, dim3(p.nT64), dim3(256), 0, st, logits, p.T, p.E, p.k, p.ids, p.wts);
+  HIP_TRY(hipGetLastError());
+  return MOE_OK;
+}
+
+moe_status launch_permute(const Plan& p, int32_t* row_of, hipStream_t st) {
+  hipLaunchKernelGGL(k_count, dim3(p.nblk), dim3(256), p.E * 4, st, p.ids, p.T, p.k, p.E, p.blockcnt);
+  HIP_TRY(hipGetLastError());
+  hipLaunchKernelGGL(k_scan, dim3(1), dim3(256), (2 * p.E + 64) * 4, st, p.blockcnt, p.nblk, p.E, p.base, p.offsets,
+                     p.tiles, p.meta);
+  HIP_TRY(hipGetLastError());
+  hipLaunchKernelGGL(k_scatter, dim3(p.nblk), dim3(256), 4 * p.E * 8, st, p.ids, p.T, p.k, p.E, p.base, p.perm, row_of);
+  HIP_TRY(hipGetLastError());
+  return MOE_OK;
+}
+
+template <int AF, int WF>
+moe_status launch_layer(const Plan& p, const DevInfo& di, int mode, hipStream_t st) {
+  const size_t zero_ints = (p.zero_bytes + 256) / 4;   // error word region + counters
+  hipLaunchKernelGGL(k_zero, dim3(16), dim3(256), 0, st, p.err, zero_ints);
+  HIP_TRY(hipGetLastError());
+  if (mode == MOE_MODE_SEPARATE) {
+    if (!p.routing_given) TRY(launch_route(p, p.logits, st));
+    TRY(launch_permute(p, p.row_of, st));
+    const GemmArgs g = gemm_args(p);
+    const int lds = gemm_lds(AF == ACT_FP8);
+    TRY(set_lds_limit(k_gemm<AF, WF, 1>, lds));
+    TRY(set_lds_limit(k_gemm<AF, WF, 2>, lds));
+    const int grid = di.cus * 2;
+    hipLaunchKernelGGL((k_gemm<AF, WF, 1>), dim3(grid), dim3(256), lds, st, g, p.tiles, p.meta, p.nnb1);
+    HIP_TRY(hipGetLastError());
+    hipLaunchKernelGGL((k_gemm<AF, WF, 2>), dim3(grid), dim3(256), lds, st, g, p.tiles, p.meta, p.nnb2);
+    HIP_TRY(hipGetLastError());
+    hipLaunchKernelGGL(k_combine, dim3((p.T + 15) / 16), dim3(256), 0, st, p.staging, p.y, p.T, p.H, p.k);
+    HIP_TRY(hipGetLastError());
+  } else {
+    const int lds = mega_lds(p);
+    TRY(set_lds_limit(k_mega<AF, WF>, lds));
+    int occ = 0;
+    HIP_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_mega<AF, WF>, 256, lds));
+    if (occ < 1) occ = 1;
+    hipLaunchKernelGGL((k_mega<AF, WF>), dim3(di.cus * occ), dim3(256), lds, st, p);
+    HIP_TRY(hipGetLastError());
+  }
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+size_t moe_workspace_size(const moe_desc* d) {
+  if (check_desc(d) != MOE_OK) return 0;
+  return workspace_need(d, WS_LAYER);
+}
+
+size_t moe_route_workspace_size(const moe_desc* d) {
+  if (check_desc(d) != MOE_OK) return 0;
+  return workspace_need(d, WS_ROUTE);
+}
+
+size_t moe_permute_workspace_size(const moe_desc* d) {
+  if (check_desc(d) != MOE_OK) return 0;
+  return workspace_need(d, WS_PERMUTE);
+}
+
+moe_status moe_get_workspace_regions(const moe_desc* d, moe_workspace_regions* out) {
+  TRY(check_desc(d));
+  if (!out) return fail(MOE_ERR_INVALID_ARGUMENT, "out is NULL");
+  const Layout L = make_layout(d);
+  out->logits = L.logits;
+  out->perm = L.perm;
+  out->row_of = L.row_of;
+  out->offsets = L.offsets;
+  out->inter = L.aq;
+  out->inter_scales = L.sa;
+  out->staging = L.staging;
+  out->total = L.total;
+  return MOE_OK;
+}
+
+moe_status moe_validate(const moe_desc* d, const void* x, const float* x_scales, const void* router_w,
+                        const float* router_bias, const void* w_gate_up, const void* w_gate_up_scales,
+                        const void* w_down, const void* w_down_scales, const void* y, const int32_t* topk_ids,
+                        const float* topk_weights, const void* workspace, size_t workspace_bytes) {
+  TRY(check_desc(d));
+  const bool given = (d->flags & MOE_FLAG_ROUTING_GIVEN) != 0;
+  TRY(check_ptr(x, "x", !given));
+  TRY(check_ptr(x_scales, "x_scales", d->act_dtype == MOE_DTYPE_FP8_E4M3 && !given));
+  TRY(check_ptr(router_w, "router_w", !given));
+  TRY(check_ptr(router_bias, "router_bias", false));
+  TRY(check_ptr(w_gate_up, "w_gate_up"));
+  TRY(check_ptr(w_gate_up_scales, "w_gate_up_scales", d->weight_dtype != MOE_DTYPE_BF16));
+  TRY(check_ptr(w_down, "w_down"));
+  TRY(check_ptr(w_down_scales, "w_down_scales", d->weight_dtype != MOE_DTYPE_BF16));
+  TRY(check_ptr(y, "y"));
+  TRY(check_ptr(topk_ids, "topk_ids"));
+  TRY(check_ptr(topk_weights, "topk_weights"));
+  if (given && !x) return fail(MOE_ERR_INVALID_ARGUMENT, "x is NULL");
+  if (given && d->act_dtype == MOE_DTYPE_FP8_E4M3 && !x_scales) return fail(MOE_ERR_INVALID_ARGUMENT, "x_scales is NULL");
+  TRY(check_workspace(d, workspace, workspace_bytes));
+  return MOE_OK;
+}
+
+moe_status moe_forward(const moe_desc* d, const void* x, const float* x_scales, const void* router_w,
+                       const float* router_bias, const void* w_gate_up, const void* w_gate_up_scales,
+                       const void* w_down, const void* w_down_scales, void* y, int32_t* topk_ids,
+                       float* topk_weights, int32_t* expert_offsets, int32_t* perm, void* workspace,
+                       size_t workspace_bytes, moe_stream_t stream) {
+  TRY(moe_validate(d, x, x_scales, router_w, router_bias, w_gate_up, w_gate_up_scales, w_down, w_down_scales, y,
+                   topk_ids, topk_weights, workspace, workspace_bytes));
+  TRY(check_ptr(expert_offsets, "expert_offsets", false));
+  TRY(check_ptr(perm, "perm", false));
+  DevInfo di;
+  TRY(device_info(&di));
+  const Layout L = make_layout(d);
+  Plan p;
+  TRY(fill_plan(d, L, static_cast<char*>(workspace), &p));
+  p.x = static_cast<const uint8_t*>(x); p.x_scales = x_scales;
+  p.wr = static_cast<const uint16_t*>(router_w); p.bias = router_bias;
+  p.w_gu = static_cast<const uint8_t*>(w_gate_up); p.w_gu_scales = w_gate_up_scales;
+  p.w_d = static_cast<const uint8_t*>(w_down); p.w_d_scales = w_down_scales;
+  p.y = static_cast<uint16_t*>(y); p.ids = topk_ids; p.wts = topk_weights;
+  if (expert_offsets) p.offsets = expert_offsets;
+  if (perm) p.perm = perm;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (p.act_fp8 && p.wdt == W_FP8) return launch_layer<ACT_FP8, W_FP8>(p, di, d->mode, st);
+  if (p.act_fp8 && p.wdt == W_FP4) return launch_layer<ACT_FP8, W_FP4>(p, di, d->mode, st);
+  return launch_layer<ACT_BF16, W_BF16>(p, di, d->mode, st);
+}
+
+moe_status moe_route(const moe_desc* d, const void* x, const float* x_scales, const void* router_w,
+                     const float* router_bias, float* logits, int32_t* topk_ids, float* topk_weights,
+                     void* workspace, size_t workspace_bytes, moe_stream_t stream) {
+  TRY(check_desc(d));
+  TRY(check_ptr(x, "x"));
+  TRY(check_ptr(x_scales, "x_scales", d->act_dtype == MOE_DTYPE_FP8_E4M3));
+  TRY(check_ptr(router_w, "router_w"));
+  TRY(check_ptr(router_bias, "router_bias", false));
+  TRY(check_ptr(logits, "logits", false));
+  TRY(check_ptr(topk_ids, "topk_ids"));
+  TRY(check_ptr(topk_weights, "topk_weights"));
+  TRY(check_workspace(d, workspace, workspace_bytes, WS_ROUTE));
+  DevInfo di;
+  TRY(device_info(&di));
+  const Layout L = make_layout(d);
+  Plan p;
+  TRY(fill_plan(d, L, static_cast<char*>(workspace), &p));
+  p.x = static_cast<const uint8_t*>(x); p.x_scales = x_scales;
+  p.wr = static_cast<const uint16_t*>(router_w); p.bias = router_bias;
+  p.ids = topk_ids; p.wts = topk_weights;
+  return launch_route(p, logits ? logits : p.logits, static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_permute(const moe_desc* d, const int32_t* topk_ids, int32_t* expert_offsets, int32_t* perm,
+                       int32_t* row_of, void* workspace, size_t workspace_bytes, moe_stream_t stream) {
+  TRY(check_desc(d));
+  TRY(check_ptr(topk_ids, "topk_ids"));
+  TRY(check_ptr(expert_offsets, "expert_offsets"));
+  TRY(check_ptr(perm, "perm"));
+  TRY(check_ptr(row_of, "row_of", false));
+  TRY(check_workspace(d, workspace, workspace_bytes, WS_PERMUTE));
+  DevInfo di;
+  TRY(device_info(&di));
+  const Layout L = make_layout(d);
+  Plan p;
+  TRY(fill_plan(d, L, static_cast<char*>(workspace), &p));
+  p.ids = const_cast<int32_t*>(topk_ids);
+  p.offsets = expert_offsets;
+  p.perm = perm;
+  return launch_permute(p, row_of, static_cast<hipStream_t>(stream));
+}
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARGUMENT: return "MOE_ERR_INVALID_ARGUMENT";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+  }
+  return "unknown moe_status";
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

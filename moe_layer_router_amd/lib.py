@@ -1,0 +1,188 @@
+"""Python binding of the C ABI in include/moe_layer.h (ctypes).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels of
+libmoe_layer.so.  Tensors are torch tensors (device memory and streams come
+from PyTorch); each function has the name of the C entry point it calls and
+raises MoeError when that entry point returns a non-OK status.  There is no
+fallback: if the library is not built, importing this module fails.
+"""
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmoe_layer.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m moe_layer_router_amd.build` "
+                      "(or __graft_entry__.build())")
+
+# PyTorch ships its own HIP runtime with the same soname (libamdhip64.so.7).
+# Importing torch first makes the dynamic loader bind this library to that
+# already-loaded runtime, so device pointers and streams from torch are valid
+# here; loading the library first would put two HIP runtimes in the process.
+import torch  # noqa: E402,F401
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+# moe_status
+MOE_OK = 0
+MOE_ERR_INVALID_ARGUMENT = 1
+MOE_ERR_UNSUPPORTED = 2
+MOE_ERR_WORKSPACE_TOO_SMALL = 3
+MOE_ERR_HIP = 4
+# moe_dtype
+MOE_DTYPE_BF16 = 0
+MOE_DTYPE_FP8_E4M3 = 1
+MOE_DTYPE_FP4_E2M1 = 2
+# moe_mode
+MOE_MODE_MEGA = 0
+MOE_MODE_SEPARATE = 1
+# flags
+MOE_FLAG_ROUTING_GIVEN = 1
+
+DTYPES = {"bf16": MOE_DTYPE_BF16, "fp8": MOE_DTYPE_FP8_E4M3, "fp4": MOE_DTYPE_FP4_E2M1}
+MODES = {"mega": MOE_MODE_MEGA, "separate": MOE_MODE_SEPARATE}
+
+
+class MoeDesc(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("E", ctypes.c_int32),
+                ("I", ctypes.c_int32), ("top_k", ctypes.c_int32), ("act_dtype", ctypes.c_int32),
+                ("weight_dtype", ctypes.c_int32), ("mode", ctypes.c_int32), ("flags", ctypes.c_int32)]
+
+
+class MoeWorkspaceRegions(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in
+                ("logits", "perm", "row_of", "offsets", "inter", "inter_scales", "staging", "total")]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status, func):
+        self.status = status
+        super().__init__(f"{func}: {moe_status_string(status)}: {moe_last_error()}")
+
+
+_P = ctypes.c_void_p
+_lib.moe_abi_version.restype = ctypes.c_int32
+_lib.moe_abi_version.argtypes = []
+_lib.moe_workspace_size.restype = ctypes.c_size_t
+_lib.moe_workspace_size.argtypes = [ctypes.POINTER(MoeDesc)]
+_lib.moe_route_workspace_size.restype = ctypes.c_size_t
+_lib.moe_route_workspace_size.argtypes = [ctypes.POINTER(MoeDesc)]
+_lib.moe_permute_workspace_size.restype = ctypes.c_size_t
+_lib.moe_permute_workspace_size.argtypes = [ctypes.POINTER(MoeDesc)]
+_lib.moe_get_workspace_regions.restype = ctypes.c_int
+_lib.moe_get_workspace_regions.argtypes = [ctypes.POINTER(MoeDesc), ctypes.POINTER(MoeWorkspaceRegions)]
+_lib.moe_validate.restype = ctypes.c_int
+_lib.moe_validate.argtypes = [ctypes.POINTER(MoeDesc)] + [_P] * 11 + [_P, ctypes.c_size_t]
+_lib.moe_forward.restype = ctypes.c_int
+_lib.moe_forward.argtypes = [ctypes.POINTER(MoeDesc)] + [_P] * 13 + [_P, ctypes.c_size_t, _P]
+_lib.moe_route.restype = ctypes.c_int
+_lib.moe_route.argtypes = [ctypes.POINTER(MoeDesc)] + [_P] * 7 + [_P, ctypes.c_size_t, _P]
+_lib.moe_permute.restype = ctypes.c_int
+_lib.moe_permute.argtypes = [ctypes.POINTER(MoeDesc)] + [_P] * 4 + [_P, ctypes.c_size_t, _P]
+_lib.moe_status_string.restype = ctypes.c_char_p
+_lib.moe_status_string.argtypes = [ctypes.c_int]
+_lib.moe_last_error.restype = ctypes.c_char_p
+_lib.moe_last_error.argtypes = []
+
+
+def make_desc(T, H, E, I, top_k, act="fp8", weight="fp8", mode="mega", flags=0) -> MoeDesc:
+    return MoeDesc(T, H, E, I, top_k, DTYPES[act], DTYPES[weight], MODES.get(mode, mode), flags)
+
+
+def _ptr(t):
+    """Device (or host) address of a tensor, an int address, or None."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status, func):
+    if status != MOE_OK:
+        raise MoeError(status, func)
+
+
+def moe_abi_version() -> int:
+    return _lib.moe_abi_version()
+
+
+def moe_status_string(status: int) -> str:
+    return _lib.moe_status_string(status).decode()
+
+
+def moe_last_error() -> str:
+    return _lib.moe_last_error().decode()
+
+
+def moe_workspace_size(desc: MoeDesc) -> int:
+    return _lib.moe_workspace_size(ctypes.byref(desc))
+
+
+def moe_route_workspace_size(desc: MoeDesc) -> int:
+    return _lib.moe_route_workspace_size(ctypes.byref(desc))
+
+
+def moe_permute_workspace_size(desc: MoeDesc) -> int:
+    return _lib.moe_permute_workspace_size(ctypes.byref(desc))
+
+
+def moe_get_workspace_regions(desc: MoeDesc) -> dict:
+    r = MoeWorkspaceRegions()
+    _check(_lib.moe_get_workspace_regions(ctypes.byref(desc), ctypes.byref(r)), "moe_get_workspace_regions")
+    return {n: getattr(r, n) for n, _ in MoeWorkspaceRegions._fields_}
+
+
+def moe_validate(desc, x, x_scales, router_w, router_bias, w_gate_up, w_gate_up_scales,
+                 w_down, w_down_scales, y, topk_ids, topk_weights, workspace, workspace_bytes=None) -> int:
+    """Returns the status (does not raise); pointers may be tensors or ints."""
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None or isinstance(workspace, int) else _nbytes(workspace)
+    return _lib.moe_validate(ctypes.byref(desc), _ptr(x), _ptr(x_scales), _ptr(router_w), _ptr(router_bias),
+                             _ptr(w_gate_up), _ptr(w_gate_up_scales), _ptr(w_down), _ptr(w_down_scales),
+                             _ptr(y), _ptr(topk_ids), _ptr(topk_weights), _ptr(workspace), workspace_bytes)
+
+
+def moe_forward(desc, x, x_scales, router_w, router_bias, w_gate_up, w_gate_up_scales, w_down,
+                w_down_scales, y, topk_ids, topk_weights, expert_offsets, perm, workspace, stream=None):
+    st = _lib.moe_forward(ctypes.byref(desc), _ptr(x), _ptr(x_scales), _ptr(router_w), _ptr(router_bias),
+                          _ptr(w_gate_up), _ptr(w_gate_up_scales), _ptr(w_down), _ptr(w_down_scales),
+                          _ptr(y), _ptr(topk_ids), _ptr(topk_weights), _ptr(expert_offsets), _ptr(perm),
+                          _ptr(workspace), _nbytes(workspace), _stream(stream))
+    _check(st, "moe_forward")
+
+
+def moe_route(desc, x, x_scales, router_w, router_bias, logits, topk_ids, topk_weights, workspace,
+              stream=None):
+    st = _lib.moe_route(ctypes.byref(desc), _ptr(x), _ptr(x_scales), _ptr(router_w), _ptr(router_bias),
+                        _ptr(logits), _ptr(topk_ids), _ptr(topk_weights), _ptr(workspace), _nbytes(workspace),
+                        _stream(stream))
+    _check(st, "moe_route")
+
+
+def moe_permute(desc, topk_ids, expert_offsets, perm, row_of, workspace, stream=None):
+    st = _lib.moe_permute(ctypes.byref(desc), _ptr(topk_ids), _ptr(expert_offsets), _ptr(perm), _ptr(row_of),
+                          _ptr(workspace), _nbytes(workspace), _stream(stream))
+    _check(st, "moe_permute")
+
+
+def exported_symbols():
+    """Names of the C entry points this binding wraps (for ABI checks)."""
+    return ["moe_abi_version", "moe_workspace_size", "moe_route_workspace_size",
+            "moe_permute_workspace_size", "moe_get_workspace_regions", "moe_validate", "moe_forward", "moe_route",
+            "moe_permute", "moe_status_string", "moe_last_error"]

@@ -42,6 +42,13 @@ R7  FP8 weights carry one fp32 scale per 128 x 128 block of the stored [N, K]
 R8  The permuted (expert-contiguous) row order sorts the flat index
     p = t*k + j by expert, stably, so rows of one expert are in ascending token
     order.
+R10 FP8 re-quantisation near-ties: the device forms a with fp32 (and
+    MFMA-internal) accumulation, so its a / s differs from the fp64 value
+    by up to a small amount relative to the row's largest element.  Where
+    the window a / s +- TIE_EPS straddles an E4M3 rounding boundary, every
+    value the window rounds to is a correct result of the method.  The
+    oracle then accepts a code supplied by the caller, but only at such
+    positions and only inside the window.
 R9  The combine is the weighted sum over j of w[t, j] * expert_output.  The
     reference result is the unrounded fp64 sum; the device sums in fp32 in
     ascending j and rounds the result to BF16.
@@ -159,9 +166,30 @@ def swiglu(g: np.ndarray, u: np.ndarray) -> np.ndarray:
     return silu(g) * u
 
 
-def requant_fp8(a: np.ndarray):
+# Half-width of the window around a / s (whose largest magnitude is 448)
+# within which the device's own pre-quantisation value may lie (reading
+# R10): 448 * 2**-13, about five times the largest device-versus-fp64
+# difference of a / s observed with fp32 accumulation.
+TIE_EPS = F.E4M3_MAX * 2.0 ** -13
+
+
+def tie_window(v: np.ndarray):
+    """For each value of a / s, the smallest and largest E4M3 value that the
+    round-to-nearest-even encoding of any value within TIE_EPS of it can
+    give.  Where they differ, every E4M3 value between them (inclusive) is a
+    correct re-quantisation result (reading R10)."""
+    lo = F.E4M3_TABLE[F.e4m3_encode(v - TIE_EPS)]
+    hi = F.E4M3_TABLE[F.e4m3_encode(v + TIE_EPS)]
+    return lo != hi, lo, hi
+
+
+def requant_fp8(a: np.ndarray, resolve=None):
     """Per-row, per-128-channel FP8 re-quantisation of the intermediate
     (Tile Kernels section, quantisation bullet, fused with SwiGLU; reading R6).
+
+    resolve: optional uint8 [m, C] codes chosen by another implementation;
+    they replace the oracle's code only where the tie window of a / s holds
+    more than one value (reading R10), and must there lie in the window.
 
     Returns (codes uint8 [m, C], scales fp32-valued float64 [m, C/128],
     dequantised float64 [m, C])."""
@@ -170,28 +198,41 @@ def requant_fp8(a: np.ndarray):
     amax = np.abs(blocks).max(axis=2)
     s = F.f32_round(amax / F.E4M3_MAX)
     s = np.where(amax == 0.0, 1.0, s)
-    codes = F.e4m3_encode(blocks / s[:, :, None])
+    v = blocks / s[:, :, None]
+    codes = F.e4m3_encode(v)
+    if resolve is not None:
+        amb, lo, hi = tie_window(v)
+        r = np.asarray(resolve, dtype=np.uint8).reshape(m, C // 128, 128)
+        rv = F.E4M3_TABLE[r]
+        valid = (rv >= lo) & (rv <= hi)
+        if not np.all(valid[amb]):
+            raise ValueError("a supplied code at a re-quantisation near-tie lies outside its tie window")
+        codes = np.where(amb, r, codes)
     deq = F.E4M3_TABLE[codes] * s[:, :, None]
     return codes.reshape(m, C), s, deq.reshape(m, C)
 
 
-def quantise_intermediate(spec: Spec, a: np.ndarray) -> np.ndarray:
-    """The value GEMM2 consumes: FP8 re-quantised (R6), or BF16-rounded for
-    all-BF16 layers."""
+def quantise_intermediate(spec: Spec, a: np.ndarray, resolve=None) -> np.ndarray:
+    """The value GEMM2 consumes: FP8 re-quantised (R6, R10), or BF16-rounded
+    for all-BF16 layers."""
     if spec.act == "bf16":
         return F.bf16_round(a)
-    return requant_fp8(a)[2]
+    return requant_fp8(a, resolve)[2]
 
 
-def expert_ffn(spec: Spec, xrows: np.ndarray, w_gu: np.ndarray, w_d: np.ndarray) -> np.ndarray:
+def expert_intermediate(spec: Spec, xrows: np.ndarray, w_gu: np.ndarray) -> np.ndarray:
+    """Linear 1 (gate|up) and SwiGLU of one expert's rows, before requant."""
+    G = xrows @ w_gu.T                        # [m, 2I]
+    return swiglu(G[:, : spec.I], G[:, spec.I:])
+
+
+def expert_ffn(spec: Spec, xrows: np.ndarray, w_gu: np.ndarray, w_d: np.ndarray, resolve=None) -> np.ndarray:
     """One expert on its gathered rows: linear 1 (gate|up), SwiGLU, requant,
     linear 2 (Mega MoE section: 线性变换 -> SwiGLU -> 线性变换).
 
     xrows [m, H] fp64; w_gu [2I, H] and w_d [H, I] dequantised fp64."""
-    G = xrows @ w_gu.T                        # [m, 2I]
-    g, u = G[:, : spec.I], G[:, spec.I:]
-    a = swiglu(g, u)
-    ahat = quantise_intermediate(spec, a)
+    a = expert_intermediate(spec, xrows, w_gu)
+    ahat = quantise_intermediate(spec, a, resolve)
     return ahat @ w_d.T                       # [m, H]
 
 
@@ -205,7 +246,7 @@ def route(spec: Spec, inputs: dict):
     return xhat, logits, ids, w
 
 
-def layer(spec: Spec, inputs: dict, ids=None, tokens=None) -> dict:
+def layer(spec: Spec, inputs: dict, ids=None, tokens=None, inter_codes=None) -> dict:
     """The whole layer in fp64.
 
     inputs: dict with x, x_scales, router_w, router_bias, w_gate_up,
@@ -241,11 +282,14 @@ def layer(spec: Spec, inputs: dict, ids=None, tokens=None) -> dict:
         if not np.any(keep):
             continue
         rows, toks = rows[keep], toks[keep]
+        resolve = None
+        if inter_codes is not None:
+            resolve = np.asarray(inter_codes[np.arange(offsets[e], offsets[e + 1])[keep]])
         wgu_s = None if inputs.get("w_gate_up_scales") is None else np.asarray(inputs["w_gate_up_scales"][e])
         wd_s = None if inputs.get("w_down_scales") is None else np.asarray(inputs["w_down_scales"][e])
         w_gu = decode_weight(spec, np.asarray(inputs["w_gate_up"][e]), wgu_s)
         w_d = decode_weight(spec, np.asarray(inputs["w_down"][e]), wd_s)
-        O = expert_ffn(spec, xhat[toks], w_gu, w_d)
+        O = expert_ffn(spec, xhat[toks], w_gu, w_d, resolve)
         wt = w.reshape(-1)[rows]
         # Tokens are distinct within one expert, so these row updates never
         # collide; the sum over j is formed across the expert loop.

@@ -1,0 +1,112 @@
+"""The C ABI on the host (no GPU): the library loads, exports every entry
+point the header declares, sizes workspaces, and rejects bad arguments with
+the documented status codes."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from moe_layer_router_amd import lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = []
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", fn)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names += re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(moe_[a-z_0-9]+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_symbol():
+    declared = _declared_functions()
+    assert "moe_forward" in declared and "moe_validate" in declared
+    so = ctypes.CDLL(lib.LIB_PATH)
+    for name in declared:
+        assert hasattr(so, name), f"{name} declared in include/ but not exported"
+    assert sorted(lib.exported_symbols()) == declared
+
+
+def test_abi_version_and_status_strings():
+    assert lib.moe_abi_version() == 1
+    assert lib.moe_status_string(lib.MOE_OK) == "MOE_OK"
+    assert lib.moe_status_string(lib.MOE_ERR_WORKSPACE_TOO_SMALL) == "MOE_ERR_WORKSPACE_TOO_SMALL"
+
+
+def test_workspace_sizes():
+    d = lib.make_desc(8192, 7168, 256, 2048, 8)
+    full = lib.moe_workspace_size(d)
+    # staging (T*k*H bf16) + intermediate (T*k*I) dominate
+    assert full >= 8192 * 8 * (7168 * 2 + 2048)
+    assert 0 < lib.moe_route_workspace_size(d) <= lib.moe_permute_workspace_size(d) <= full
+    assert lib.moe_workspace_size(lib.make_desc(0, 7168, 256, 2048, 8)) == 0
+    bf = lib.moe_workspace_size(lib.make_desc(64, 256, 8, 128, 2, "bf16", "bf16"))
+    f8 = lib.moe_workspace_size(lib.make_desc(64, 256, 8, 128, 2, "fp8", "fp8"))
+    assert bf > f8  # BF16 intermediate is twice the bytes
+
+
+A = 0x100000  # a fake, 16-byte-aligned address: validation never dereferences
+
+
+def _validate(d, **over):
+    args = dict(x=A, x_scales=A, router_w=A, router_bias=None, w_gate_up=A, w_gate_up_scales=A,
+                w_down=A, w_down_scales=A, y=A, topk_ids=A, topk_weights=A, workspace=A,
+                workspace_bytes=lib.moe_workspace_size(d) if lib.moe_workspace_size(d) else 1 << 40)
+    args.update(over)
+    return lib.moe_validate(d, **args)
+
+
+def test_validate_accepts_good_arguments():
+    assert _validate(lib.make_desc(100, 512, 16, 256, 4)) == lib.MOE_OK
+    assert _validate(lib.make_desc(100, 512, 16, 256, 4, "fp8", "fp4")) == lib.MOE_OK
+    assert _validate(lib.make_desc(64, 256, 8, 128, 2, "bf16", "bf16"), x_scales=None,
+                     w_gate_up_scales=None, w_down_scales=None) == lib.MOE_OK
+
+
+@pytest.mark.parametrize("shape,status", [
+    ((0, 512, 16, 256, 4), lib.MOE_ERR_INVALID_ARGUMENT),       # T < 1
+    ((10, 500, 16, 256, 4), lib.MOE_ERR_INVALID_ARGUMENT),      # H % 128
+    ((10, 512, 16, 200, 4), lib.MOE_ERR_INVALID_ARGUMENT),      # I % 128
+    ((10, 512, 4, 256, 5), lib.MOE_ERR_INVALID_ARGUMENT),       # k > E
+    ((10, 512, 4, 256, 0), lib.MOE_ERR_INVALID_ARGUMENT),       # k < 1
+    ((10, 512, 2048, 256, 4), lib.MOE_ERR_UNSUPPORTED),         # E > 1024
+    ((10, 512, 64, 256, 17), lib.MOE_ERR_UNSUPPORTED),          # k > 16
+    ((10, 32768, 16, 256, 4), lib.MOE_ERR_UNSUPPORTED),         # H > 16384
+])
+def test_validate_rejects_bad_shapes(shape, status):
+    assert _validate(lib.make_desc(*shape)) == status
+    assert lib.moe_last_error() != ""
+
+
+def test_validate_rejects_bad_dtype_pairs_and_modes():
+    assert _validate(lib.make_desc(10, 512, 16, 256, 4, "bf16", "fp8")) == lib.MOE_ERR_UNSUPPORTED
+    assert _validate(lib.make_desc(10, 512, 16, 256, 4, "fp8", "bf16")) == lib.MOE_ERR_UNSUPPORTED
+    assert _validate(lib.make_desc(10, 512, 16, 256, 4, mode=7)) == lib.MOE_ERR_INVALID_ARGUMENT
+    assert _validate(lib.make_desc(10, 512, 16, 256, 4, flags=8)) == lib.MOE_ERR_INVALID_ARGUMENT
+
+
+def test_validate_rejects_bad_pointers_and_workspace():
+    d = lib.make_desc(100, 512, 16, 256, 4)
+    assert _validate(d, x=None) == lib.MOE_ERR_INVALID_ARGUMENT
+    assert _validate(d, x_scales=None) == lib.MOE_ERR_INVALID_ARGUMENT
+    assert _validate(d, w_down_scales=None) == lib.MOE_ERR_INVALID_ARGUMENT
+    assert _validate(d, y=A + 8) == lib.MOE_ERR_INVALID_ARGUMENT            # misaligned
+    assert "aligned" in lib.moe_last_error()
+    assert _validate(d, workspace_bytes=lib.moe_workspace_size(d) - 1) == lib.MOE_ERR_WORKSPACE_TOO_SMALL
+    assert _validate(d, workspace=None) == lib.MOE_ERR_INVALID_ARGUMENT
+    # with given routing the router inputs are optional
+    g = lib.make_desc(100, 512, 16, 256, 4, flags=lib.MOE_FLAG_ROUTING_GIVEN)
+    assert _validate(g, router_w=None) == lib.MOE_OK
+
+
+def test_single_hip_runtime_in_process():
+    """The library binds to PyTorch's HIP runtime: torch's device pointers and
+    streams are only valid in that runtime."""
+    maps = open("/proc/self/maps").read().splitlines()
+    hip = sorted(set(l.split()[-1] for l in maps if "libamdhip64" in l))
+    assert len(hip) == 1, hip
