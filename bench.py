@@ -1,0 +1,206 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused MoE layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--mode mega|separate]
+
+A step is one full layer forward (router, top-k, permutation, gate|up GEMM +
+SwiGLU + FP8 requant, down GEMM, weighted combine) over one batch of
+synthetic tokens whose inputs are already resident in HBM.  Prints one JSON
+line: tokens/s, effective TFLOP/s, the roofline of the dominant kernel (the
+persistent layer kernel in mega mode) and the oracle's throughput on a
+bounded sample of the same workload timed on the host cores.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# MI355X published peaks
+PEAK_HBM_GBS = 8000.0
+PEAK_TFLOPS = {"fp8": 5000.0, "fp4": 10100.0, "bf16": 2500.0}
+
+
+def algorithmic_cost(cfg, inputs, counts):
+    """Algorithmic FLOPs and HBM bytes of one layer forward.
+
+    FLOPs: 6*T*k*H*I for the two expert GEMMs (2 flop per multiply-add,
+    gate|up is 2I wide) plus 2*T*H*E for the router.  Bytes: weights and
+    scales of every expert that receives a token (each read once), plus
+    x, its scales, the router weights and bias, y, top-k ids and weights."""
+    T, H, E, k, I = cfg.T, cfg.H, cfg.E, cfg.k, cfg.I
+    f_exp = 6.0 * T * k * H * I
+    f_router = 2.0 * T * H * E
+    active = int((counts > 0).sum())
+
+    def per_expert(name):
+        t = inputs[name]
+        return 0 if t is None else t[0].numel() * t.element_size()
+    w_bytes = active * sum(per_expert(n) for n in ("w_gate_up", "w_gate_up_scales", "w_down", "w_down_scales"))
+    io = 0
+    for n in ("x", "x_scales", "router_w", "router_bias"):
+        t = inputs[n]
+        io += 0 if t is None else t.numel() * t.element_size()
+    io += T * H * 2 + T * k * 4 * 2
+    return f_exp, f_router, w_bytes + io, active
+
+
+def roofline(cfg, f_exp, f_router, nbytes, t_s):
+    exp_fmt = cfg.weight if cfg.weight == "bf16" else "fp8"     # FP8 x FP4 issues at the FP8 rate
+    t_mfma = f_exp / (PEAK_TFLOPS[exp_fmt] * 1e12) + f_router / (PEAK_TFLOPS["bf16"] * 1e12)
+    t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
+    if t_hbm >= t_mfma:
+        ach = nbytes / t_s / 1e9
+        return {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBS, 4)}, t_mfma, t_hbm
+    ach = (f_exp + f_router) / t_s / 1e12
+    peak = PEAK_TFLOPS[exp_fmt]
+    return {"bound": "mfma", "achieved": round(ach, 1), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(ach / peak, 4)}, t_mfma, t_hbm
+
+
+def cpu_baseline(cfg, inputs, n_experts=4):
+    """The oracle as it stands, on a bounded sample of the same workload:
+    routing and the permutation for all T tokens, then the complete expert
+    work (decode, gate|up, SwiGLU, requant, down, combine) of `n_experts`
+    experts.  The full-layer time is extrapolated as
+    t_route + E * (mean time per expert)."""
+    from threadpoolctl import threadpool_info
+    from oracle import moe_oracle as O
+    from workloads import gen
+
+    spec = gen.spec_of(cfg)
+    ov = gen.oracle_view(inputs, lazy_weights=True)
+    t0 = time.perf_counter()
+    xhat, logits, ids, w = O.route(spec, ov)
+    counts, offsets, perm, row_of = O.permutation(ids, cfg.E)
+    t_route = time.perf_counter() - t0
+    busy = np.argsort(-counts, kind="stable")
+    sample = [int(e) for e in busy[np.linspace(0, min(cfg.E, int((counts > 0).sum())) - 1, n_experts).astype(int)]]
+    y = np.zeros((cfg.T, cfg.H))
+    t1 = time.perf_counter()
+    for e in sample:
+        rows = perm[offsets[e]: offsets[e + 1]]
+        toks = rows // cfg.k
+        s1 = None if ov["w_gate_up_scales"] is None else ov["w_gate_up_scales"][e]
+        s2 = None if ov["w_down_scales"] is None else ov["w_down_scales"][e]
+        wgu = O.decode_weight(spec, ov["w_gate_up"][e], s1)
+        wd = O.decode_weight(spec, ov["w_down"][e], s2)
+        y[toks] += w.reshape(-1)[rows][:, None] * O.expert_ffn(spec, xhat[toks], wgu, wd)
+    t_exp = (time.perf_counter() - t1) / len(sample)
+    active = int((counts > 0).sum())
+    t_full = t_route + active * t_exp
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": round(cfg.T / t_full, 3), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"fp64 numpy oracle: routing + permutation of all {cfg.T} tokens ({t_route:.2f} s) and the "
+                       f"full expert work of {len(sample)} of {active} active experts ({t_exp:.2f} s each, "
+                       f"experts {sample}); layer time extrapolated as t_route + {active} * t_expert = {t_full:.1f} s"),
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="dsv3_fp8")
+    ap.add_argument("--mode", default="mega", choices=["mega", "separate"])
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-experts", type=int, default=4)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): the layer is measured on a "
+              "single MI355X; expert parallelism across GPUs is not part of this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from moe_layer_router_amd import layer
+    from workloads import gen
+
+    cfg = gen.CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] generating {cfg.name} inputs on {dev}", file=sys.stderr, flush=True)
+    raw = gen.make_inputs(cfg, seed=args.seed, device=dev)
+    # weights go into the MFMA-tiled layout once, as at model load time
+    inputs = layer.pack_weights(raw)
+    torch.cuda.synchronize()
+    ws = layer.Workspace(dev)
+    stream = torch.cuda.current_stream()
+    out = layer.forward(inputs, cfg.k, mode=args.mode, workspace=ws)
+    torch.cuda.synchronize()
+    if int(out["workspace"][:4].view(torch.int32).item()) != 0:
+        raise RuntimeError("device watchdog fired")
+    counts = np.diff(out["expert_offsets"].cpu().numpy())
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        layer.forward(inputs, cfg.k, mode=args.mode, workspace=ws, out=out)
+    torch.cuda.synchronize()
+
+    # timed region: K back-to-back layer calls on the current stream; one
+    # event pair per call gives the persistent kernel's duration as well
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t_begin = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_begin.record(stream)
+    for i in range(args.steps):
+        starts[i].record(stream)
+        layer.forward(inputs, cfg.k, mode=args.mode, workspace=ws, out=out)
+        ends[i].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_begin.elapsed_time(t_end)
+    per = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+    ms = total_ms / args.steps
+    if not torch.isfinite(out["y"].float()).all():
+        raise RuntimeError("non-finite output")
+
+    f_exp, f_router, nbytes, active = algorithmic_cost(cfg, inputs, counts)
+    t_launch = float(per.mean()) / 1e3
+    roof, t_mfma, t_hbm = roofline(cfg, f_exp, f_router, nbytes, t_launch)
+    roof["traffic"] = None
+    tflops = (f_exp + f_router) / (ms / 1e3) / 1e12
+    exp_fmt = cfg.weight if cfg.weight == "bf16" else "fp8"
+    result = {
+        "metric": "MoE-layer tokens/s & TFLOP/s (% MFMA peak), T=8192 H=7168 E=256 top-8 FP8",
+        "value": round(cfg.T / (ms / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"fp8": "fp8 e4m3 x fp8 e4m3", "fp4": "fp8 e4m3 x fp4 e2m1", "bf16": "bf16"}[cfg.weight],
+        "data": "synthetic (seeded N(0,1) activations, N(0,1/fan_in) weights, quantised; no real weights)",
+        "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "E": cfg.E, "top_k": cfg.k, "I": cfg.I,
+                   "act": cfg.act, "weight": cfg.weight, "zipf": cfg.zipf, "mode": args.mode,
+                   "active_experts": active},
+        "tflops": round(tflops, 1),
+        "mfma_peak_frac": round(tflops / PEAK_TFLOPS[exp_fmt], 4),
+        "hbm_gbs": round(nbytes / (ms / 1e3) / 1e9, 1),
+        "roofline": roof,
+        "roofline_model": {"algorithmic_tflop": round((f_exp + f_router) / 1e12, 4),
+                           "algorithmic_gb": round(nbytes / 1e9, 4),
+                           "t_mfma_ms": round(t_mfma * 1e3, 4), "t_hbm_ms": round(t_hbm * 1e3, 4),
+                           "kernel_ms": round(t_launch * 1e3, 4),
+                           "roofline_frac": round(max(t_mfma, t_hbm) / t_launch, 4)},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on a bounded sample (host cores)", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(cfg, raw, args.cpu_experts)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

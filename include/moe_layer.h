@@ -22,24 +22,42 @@
  *   o_j      = ahat @ W_down[e]^T
  *   y[t,:]   = BF16( sum_j w[j] * o_j )     (fp32 sum in ascending j)
  *
- * Layouts (all row-major, contiguous, caller-owned device memory):
+ * Layouts (row-major unless stated, contiguous, caller-owned device memory):
  *   x                 [T][H]    BF16, or FP8 E4M3 bytes with
  *   x_scales          [T][H/128] fp32 (one scale per token per 128 channels)
  *   router_w          [E][H]    BF16
  *   router_bias       [E]       fp32, optional (NULL = no bias)
  *   w_gate_up         [E][2I][H]   BF16 or FP8 E4M3 bytes;
  *                     [E][2I][H/2] FP4 E2M1, two per byte, even K in the low nibble
+ *                     -- passed to moe_forward in the MFMA-tiled layout below
  *   w_gate_up_scales  [E][2I/128][H/128] fp32 (FP8, one per 128x128 block)
- *                     [E][2I][H/32]      E8M0 bytes (FP4, one per 32 along K)
+ *                     [E][2I][H/32]      E8M0 bytes (FP4, one per 32 along K;
+ *                                        MFMA-tiled for moe_forward)
  *                     NULL for BF16
- *   w_down            [E][H][I] (BF16 / FP8) or [E][H][I/2] (FP4)
- *   w_down_scales     [E][H/128][I/128] fp32 (FP8) or [E][H][I/32] E8M0 (FP4)
+ *   w_down            [E][H][I] (BF16 / FP8) or [E][H][I/2] (FP4), MFMA-tiled
+ *   w_down_scales     [E][H/128][I/128] fp32 (FP8) or [E][H][I/32] E8M0 (FP4,
+ *                     MFMA-tiled)
  *   y                 [T][H]    BF16 (output)
  *   topk_ids          [T][top_k] int32 (output; input with MOE_FLAG_ROUTING_GIVEN)
  *   topk_weights      [T][top_k] fp32  (output; input with MOE_FLAG_ROUTING_GIVEN)
  *   expert_offsets    [E+1] int32, optional output: first permuted row of each expert
  *   perm              [T*top_k] int32, optional output: flat index t*top_k+j held by
  *                     each permuted row (rows grouped by expert, ascending token)
+ *
+ * MFMA-tiled weight layout.  The expert GEMMs stream weights straight from
+ * HBM into matrix-core operand registers; a wave's operand load is 1 KB, and
+ * it is contiguous only if the weights are stored in operand order.  For an
+ * expert matrix with N rows and K columns (N = 2I, K = H for w_gate_up;
+ * N = H, K = I for w_down), let BS be the bytes of one row per 128 columns
+ * (BF16 256, FP8 128, FP4 64) and nsteps = K/128.  The tiled matrix of
+ * expert e (same size and position as the row-major one) is the sequence of
+ * blocks (t, s), t = 0 .. N/16-1, s = 0 .. nsteps-1, block (t, s) at byte
+ * (t*nsteps + s)*16*BS, each made of BS/64 pieces of 1024 bytes: byte
+ * 16*l + j of piece p (l = 0..63, j = 0..15) is byte BS*s + 64*p + 16*(l/16)
+ * + j of row 16*t + l%16 of the row-major matrix.  FP4 E8M0 scales: block
+ * (t, s) is 64 bytes at (t*nsteps + s)*64, byte l holding the scale of row
+ * 16*t + l%16 for K group 4*s + l/16.  FP8 fp32 block scales stay row-major.
+ * moe_pack_weights converts row-major weights into this layout.
  *
  * Supported dtype pairs (act x weight): BF16 x BF16, FP8 x FP8, FP8 x FP4.
  * Limits: T >= 1; H and I multiples of 128 (H <= 16384, I <= 16384);
@@ -176,6 +194,21 @@ moe_status moe_route(const moe_desc* d,
 moe_status moe_permute(const moe_desc* d, const int32_t* topk_ids,
                        int32_t* expert_offsets, int32_t* perm, int32_t* row_of,
                        void* workspace, size_t workspace_bytes, moe_stream_t stream);
+
+/* moe_pack_weights `which` */
+#define MOE_WEIGHTS_GATE_UP 0     /* N = 2I rows, K = H columns per expert */
+#define MOE_WEIGHTS_DOWN 1        /* N = H rows,  K = I columns per expert */
+
+/* Convert one expert weight tensor from the row-major layout to the
+ * MFMA-tiled layout that moe_forward reads (see the top of this file):
+ * src -> dst, both [E] experts of N x K elements of d->weight_dtype.  For
+ * FP4 weights the E8M0 scales are converted too (src_scales -> dst_scales,
+ * both required); for BF16 / FP8 weights the scale pointers must be NULL
+ * (FP8 block scales are used as they are).  Out of place: dst must not
+ * overlap src.  A pure byte permutation, enqueued on `stream`; run it once
+ * when the weights are loaded. */
+moe_status moe_pack_weights(const moe_desc* d, int32_t which, const void* src, const void* src_scales,
+                            void* dst, void* dst_scales, moe_stream_t stream);
 
 /* Human-readable name of a status, and the calling thread's last error text. */
 const char* moe_status_string(moe_status s);

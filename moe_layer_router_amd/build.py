@@ -2,7 +2,7 @@
 
     python -m moe_layer_router_amd.build
 
-produces moe_layer_router_amd/lib/libmoe_layer.so from csrc/kernels.hip.
+produces moe_layer_router_amd/libmoe_layer.so from csrc/kernels.hip.
 """
 
 import os
@@ -17,9 +17,12 @@ SOURCES = [os.path.join(PKG, "csrc", "kernels.hip")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-# Packed fp32 VALU instructions are disabled for all device code.
+# Packed fp32 VALU instructions are disabled for all device code.  MFMA
+# results go to ordinary VGPRs (the GEMM promotes every MFMA result with
+# VALU FMAs; results in AGPRs would need a copy each).
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-mfma-vgpr-form",
          "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-function"]
 
 

@@ -101,6 +101,12 @@ DEV float wave_max_xor16(float v) {           // max over the 16 lanes sharing l
   return v;
 }
 
+// Value of lane (l & ~3) | V for every lane l (a DPP quad broadcast).
+template <int V>
+DEV float quad_bcast(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), V * 0x55, 0xF, 0xF, true));
+}
+
 DEV uint64_t wave_max_u64(uint64_t v) {
 #pragma unroll
   for (int m = 1; m < kWave; m <<= 1) {
@@ -154,6 +160,51 @@ template <typename T>
 DEV T lds_ld(const char* lds, uint32_t off) { return *reinterpret_cast<const T*>(lds + off); }
 template <typename T>
 DEV void lds_st(char* lds, uint32_t off, const T& v) { *reinterpret_cast<T*>(lds + off) = v; }
+
+// ------------------------------------------------------- buffer loads
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef __attribute__((address_space(3))) void lds_void;
+// Raw buffer over [base, base + bytes): 32-bit offsets, and loads past the
+// end return zero instead of faulting.  Word 3 = 0x00020000 (CDNA raw
+// buffer, 32-bit data format).
+DEV rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+DEV v4i buf_ld16(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+DEV float buf_ldf(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0));
+}
+DEV uint32_t buf_ldu8(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, (int)voff, (int)soff, 0);
+}
+// 16 bytes per lane from the buffer straight into LDS: lane l's bytes land
+// at lds_base + 16*l (lds_base is wave-uniform).
+DEV void buf_ld16_lds(rsrc_t r, void* lds_base, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 16, (int)voff, (int)soff, 0, 0);
+}
+// Wait until at most n vector-memory operations of this wave are in flight
+// (other counters untouched).
+template <int n>
+DEV void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
+}
+
+// Workgroup barrier that first waits for this wave's LDS operations and for
+// all but its n most recent vector-memory operations.  Unlike
+// __syncthreads() it does not wait for every direct-to-LDS load in flight,
+// so loads issued for later pipeline stages stay outstanding.  The memory
+// clobber keeps the compiler from moving memory accesses across it.  (It
+// is inline asm on purpose: the compiler does not know that other waves
+// read the LDS that direct loads write, and may relax an s_waitcnt builtin
+// that it considers unneeded.)
+template <int n>
+DEV void barrier_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(n) : "memory");
+}
 
 DEV v4i ld16(const void* p) { return *reinterpret_cast<const v4i*>(p); }
 DEV void st16(void* p, const v4i& v) { *reinterpret_cast<v4i*>(p) = v; }

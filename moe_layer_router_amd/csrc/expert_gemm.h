@@ -7,8 +7,8 @@
 // bullet of the "Tile Kernels" section of youleyou, "DeepSeek 模型更新解读 Tile
 // Kernels 与 DeepEP V2 新特性".
 //
-// One work item is a row tile of one expert (up to 128 permuted rows) times
-// one N block:
+// One work item is a row tile of one expert (up to 256 permuted rows for FP8
+// activations, 128 for BF16) times one N block:
 //   stage 1: 128 intermediate channels c0..c0+127, i.e. gate rows c0.. and up
 //            rows I+c0.. of W_gate_up (256 B-columns), K = H.  Epilogue:
 //            a = SiLU(g) * u, then per row an FP8 E4M3 re-quantisation of the
@@ -18,12 +18,15 @@
 //            multiply by the token's routing weight, round to BF16 and store
 //            into the staging row of flat index p = t*k + j.
 //
-// Tiling: 256 threads = 4 waves.  A (activation rows) goes through LDS,
-// double-buffered, 128 K per step; wave w reads all 128 rows.  B (weights)
+// Tiling: 256 threads = 4 waves, one per SIMD (512 VGPRs each).  A
+// (activation rows, gathered by token for stage 1) is copied HBM -> LDS by
+// direct buffer loads into two stages, one step ahead, 128 K per step; wave
+// w reads all rows.  B (weights)
 // is streamed from HBM straight into registers: wave w owns 64 B-columns
 // (four 16-column MFMA tiles) and no other wave reads them, so weights are
-// fetched exactly once per item and never touch LDS.  The next step's B is
-// loaded while the current step's MFMAs run.
+// fetched exactly once per item and never touch LDS.  B is loaded two steps
+// ahead of the MFMAs that use it.  All loads use buffer
+// resources with 32-bit offsets (loads past a buffer's end read zero).
 //
 // Accumulation: one 16x16x128 scaled MFMA covers a whole 128-wide K step of a
 // 16x16 tile.  FP8 scales (per token per 128 channels for activations, per
@@ -59,17 +62,30 @@ struct GemmArgs {
 
 constexpr int kGemmThreads = 256;
 
+// Full tiles: 128 rows for FP8 activations, 64 for BF16.  With one wave per
+// SIMD a wave holds 16*RS x 64 fp32 accumulators (4*RS*4 VGPRs), which must
+// stay in VALU-addressable registers for the per-128-K promotion, next to
+// three (FP8) or two (BF16) steps of B fragments.
+constexpr int kGemmMaxRsFp8 = 8;
+constexpr int kGemmMaxRsBf16 = 4;
+
 template <int AF>
 struct GemmLds {
   static constexpr int kABytes = (AF == ACT_FP8) ? 128 : 256;   // A bytes per row per step
-  static constexpr int kA = 0;
-  static constexpr int kSC = kA + 2 * kTileRows * kABytes;       // [2][2][128] fp32
-  static constexpr int kRowI = kSC + 2 * 2 * kTileRows * 4;      // [128] int
-  static constexpr int kRowW = kRowI + kTileRows * 4;            // [128] fp32
-  static constexpr int kAmax = kRowW + kTileRows * 4;            // [4][128] fp32
-  static constexpr int kRsc = kAmax + 4 * kTileRows * 4;         // [128] fp32 scale
-  static constexpr int kRinv = kRsc + kTileRows * 4;             // [128] fp32 1/scale
-  static constexpr int kBytes = kRinv + kTileRows * 4;
+  static constexpr int kMaxRs = (AF == ACT_FP8) ? kGemmMaxRsFp8 : kGemmMaxRsBf16;
+  static constexpr int kRows = kMaxRs * 16;                      // rows of a full tile
+  static constexpr int kASlot = kRows * kABytes;                 // one A stage
+  static constexpr int kA = 0;                                   // [2] A stages
+  static constexpr int kScRows = kGemmThreads;                   // every thread writes a scale
+  static constexpr int kAStages = 3;
+  static constexpr int kSC = kA + kAStages * kASlot;             // [2][2][kScRows] fp32 row scales
+  static constexpr int kRowI = kSC + 2 * 2 * kScRows * 4;        // [kRows] int
+  static constexpr int kRowW = kRowI + kRows * 4;                // [kRows] fp32
+  static constexpr int kAmax = kRowW + kRows * 4;                // [4][kRows] fp32
+  static constexpr int kRsc = kAmax + 4 * kRows * 4;             // [kRows] fp32 scale
+  static constexpr int kRinv = kRsc + kRows * 4;                 // [kRows] fp32 1/scale
+  static constexpr int kScw = kRinv + kRows * 4;                 // [2][128] fp32 weight block scales
+  static constexpr int kBytes = kScw + 2 * 128 * 4;
 };
 
 // One step's B fragments: d[cs][i] are 16-byte pieces of column tile cs
@@ -79,14 +95,31 @@ struct BFrag {
   int sc[4];
 };
 
-template <int AF, int WF, int STAGE>
+// 16-byte chunk position of logical chunk c of A row `row` in LDS.  FP8 rows
+// (8 chunks): c ^ (row & 7) ^ ((row >> 3) & 1), so that the 16 rows read by
+// one MFMA operand fetch fall in distinct banks whether LDS serves 8 or 16
+// lanes per cycle, and the swizzle of row rs*16 + r depends on r only.
+// BF16 rows (16 chunks): c ^ (row & 15).
+template <int CPR>
+DEV int a_swz(int row, int c) {
+  if (CPR == 8) return c ^ (row & 7) ^ ((row >> 3) & 1);
+  return c ^ (row & 15);
+}
+
+// One work item: `RS` 16-row subtiles (rows [r0, r0+m), m <= 16*RS) of
+// expert e times one N block nb.  256 threads, one wave per SIMD.
+template <int AF, int WF, int STAGE, int RS>
 DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char* lds) {
   using L = GemmLds<AF>;
+  static_assert(RS >= 1 && RS <= L::kMaxRs, "row subtiles");
   constexpr int AB = L::kABytes;                  // A bytes per row per step
   constexpr int CPR = AB / 16;                    // 16-byte chunks per A row per step
-  constexpr int AJ = kTileRows * CPR / kGemmThreads;
-  constexpr int ASTAGE = kTileRows * AB;          // bytes of one A stage
+  constexpr int RPD = 1024 / AB;                  // rows per wave-wide 1 KB DMA
+  constexpr int R = RS * 16;                      // rows computed
+  constexpr int NDMA = (R * AB + 4095) / 4096;    // DMA instructions per thread per step
   constexpr int ESZ = (AF == ACT_FP8) ? 1 : 2;    // activation element size
+  constexpr int NB = (WF == W_BF16) ? 16 : 8;     // B load instructions per lane per step
+  constexpr int NBUF = (WF == W_BF16) ? 2 : 3;     // B register buffers (prefetch distance + 1)
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int gq = lane >> 4, c16 = lane & 15;
   const int K = (STAGE == 1) ? g.H : g.I;
@@ -94,31 +127,37 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
   const int ksb = K / 128;                        // fp32 scale blocks along K
 
   float* SC = reinterpret_cast<float*>(lds + L::kSC);
+  float* SCW = reinterpret_cast<float*>(lds + L::kScw);
   int* ROWI = reinterpret_cast<int*>(lds + L::kRowI);
   float* ROWW = reinterpret_cast<float*>(lds + L::kRowW);
 
-  // ---- N block and weight pointers
+  // ---- N block and weights
   const int c0 = (STAGE == 1) ? nb * 128 : 0;
   const int n0 = (STAGE == 2) ? nb * 256 : 0;
-  // Whether this wave's B columns exist.  Always true for stage 1; kept as a
-  // runtime test in both stages because the branch it creates also stops the
-  // scheduler from interleaving the two halves of the software pipeline
-  // (which would raise register pressure past the budget).
-  const bool wave_ok = (STAGE == 1) ? (c0 + 32 * w < g.I) : (n0 + 64 * w < g.H);
+  // Whether this wave's B columns exist (only the last down-projection block
+  // can be half empty).  Waves without columns still run the main loop on a
+  // clamped row so that it stays branch-free; their results are not stored.
+  const bool wave_ok = (STAGE == 1) || (n0 + 64 * w < g.H);
   const int N = (STAGE == 1) ? 2 * g.I : g.H;
-  const size_t wrow = (WF == W_FP8) ? (size_t)K : (WF == W_BF16) ? (size_t)K * 2 : (size_t)K / 2;
-  const uint8_t* Wbase = ((STAGE == 1) ? g.w_gu : g.w_d) + (size_t)e * N * wrow;
+  const uint32_t wrow = (WF == W_FP8) ? K : (WF == W_BF16) ? K * 2 : K / 2;
+  const uint8_t* Wexp = ((STAGE == 1) ? g.w_gu : g.w_d) + (size_t)e * N * wrow;
+  const rsrc_t wrs = make_rsrc(Wexp, (uint32_t)N * wrow);
   const void* Sbase = (STAGE == 1) ? g.w_gu_scales : g.w_d_scales;
-  const uint8_t* bptr[4];                         // this lane's weight row, at its K group
-  const uint8_t* bscp[4];                         // FP4: this lane's E8M0 scale row
+  const rsrc_t srs = make_rsrc(reinterpret_cast<const uint8_t*>(Sbase) + (size_t)e * N * (K / 32),
+                               (WF == W_FP4) ? (uint32_t)N * (K / 32) : 0u);
+  // Weights are in the MFMA-tiled layout (see moe_pack_weights): for each
+  // 16-row tile and 128-K step, a block of 16*BS bytes made of 1 KB pieces,
+  // piece p holding in its 16 bytes at 16*l the row 16t + l%16, bytes
+  // BS*s + 64p + 16*(l/16) .. +15 of the row-major matrix.  One piece is
+  // exactly one B operand load of a wave: 1 KB contiguous.
+  constexpr uint32_t BS = (WF == W_FP8) ? 128 : (WF == W_BF16) ? 256 : 64;   // bytes per row per K step
+  uint32_t boff[4], bsoff[4];                      // this lane's piece offsets (and E8M0 offsets)
 #pragma unroll
   for (int cs = 0; cs < 4; ++cs) {
-    const int n = (STAGE == 1) ? ((cs < 2) ? c0 : g.I + c0) + 32 * w + 16 * (cs & 1) + c16
-                               : n0 + 64 * w + 16 * cs + c16;
-    const int ncl = wave_ok ? n : 0;
-    const int goff = (WF == W_FP8) ? gq * 32 : (WF == W_FP4) ? gq * 16 : gq * 64;
-    bptr[cs] = Wbase + (size_t)ncl * wrow + goff;
-    bscp[cs] = reinterpret_cast<const uint8_t*>(Sbase) + ((size_t)e * N + ncl) * (K / 32) + gq;
+    const int nt = ((STAGE == 1) ? ((cs < 2) ? c0 : g.I + c0) + 32 * w + 16 * (cs & 1) : n0 + 64 * w + 16 * cs) / 16;
+    const int ntc = wave_ok ? nt : 0;
+    boff[cs] = (uint32_t)ntc * (uint32_t)nsteps * 16u * BS + 16u * lane;
+    bsoff[cs] = (uint32_t)ntc * (uint32_t)nsteps * 64u + lane;
   }
   // fp32 weight-scale rows (FP8): two 128-blocks of N per item
   const int sb0 = (STAGE == 1) ? c0 / 128 : n0 / 128;
@@ -126,7 +165,7 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
   const float* wsc = (WF == W_FP8) ? reinterpret_cast<const float*>(Sbase) + (size_t)e * (N / 128) * ksb : nullptr;
 
   __syncthreads();                                 // LDS of the previous item is free
-  if (tid < kTileRows) {
+  if (tid < R) {
     // clamped so that a malformed permutation can never index out of bounds
     const int p = (tid < m) ? min(max(g.perm[r0 + tid], 0), g.T * g.k - 1) : 0;
     if (STAGE == 1) {
@@ -136,184 +175,291 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
       ROWW[tid] = (tid < m) ? g.topk_w[p] : 0.f;
     }
   }
+  // the item's two rows of FP8 weight block scales (K <= 16384: <= 128 blocks)
+  if (WF == W_FP8 && AF == ACT_FP8) {
+    const int set = tid >> 7, kb = tid & 127;
+    if (kb < nsteps) SCW[tid] = wsc[(size_t)(set ? sb1 : sb0) * ksb + kb];
+  }
   __syncthreads();
 
-  // ---- per-lane LDS offsets (constants are added at each access)
-  // A stores: chunk q = tid + 256*j holds row q / CPR, chunk q % CPR; since
-  // 256 is a multiple of CPR the swizzle (chunk ^ row % CPR) is the same for
-  // every j and row q / CPR = tid / CPR + j * 256 / CPR.
-  const int wr_row = tid / CPR, wr_c = tid % CPR;
-  const uint32_t a_wr = opaque(L::kA + wr_row * AB + ((wr_c ^ (wr_row & (CPR - 1))) << 4));
-  // A operand reads: row rs*16 + c16; rs*16 is a multiple of CPR's period.
-  // 16x16x128 f8f6f4 operand layout (gfx950): an 8-bit operand's lane group g
-  // holds K 16g..16g+15 in its first 16 bytes and K 64+16g..64+16g+15 in the
-  // next 16; a 4-bit operand's lane group g holds K 32g..32g+31 (even K in the
-  // low nibble); the E8M0 scale of lane group g covers K 32g..32g+31.  With
-  // FP8 weights both operands use the same (arbitrary) K order, chunks 2g and
-  // 2g+1; against FP4 weights the FP8 A operand must follow the 8-bit layout,
-  // chunks g and g+4.
+  // ---- A rows: direct-to-LDS loads.  Wave w's DMA j fills rows
+  // RPD*(4j+w) .. +RPD of a stage; lane l writes row + l / CPR, physical
+  // chunk l % CPR, i.e. logical chunk a_swz(row, l % CPR).  Rows past the
+  // tile's valid count repeat row 0 (their results are never stored).
+  const rsrc_t ars = (STAGE == 1) ? make_rsrc(g.x, (uint32_t)((size_t)g.T * g.H * ESZ))
+                                  : make_rsrc(g.aq, (uint32_t)((size_t)g.T * g.k * g.I * ESZ));
+  uint32_t aoff[NDMA];
+#pragma unroll
+  for (int j = 0; j < NDMA; ++j) {
+    const int row = RPD * (4 * j + w) + lane / CPR;
+    const int c = a_swz<CPR>(row, lane % CPR);
+    const int rowc = (row < m) ? row : 0;
+    const uint32_t rbase = (STAGE == 1) ? (uint32_t)ROWI[rowc] * g.H : (uint32_t)(r0 + rowc) * g.I;
+    aoff[j] = rbase * ESZ + c * 16;
+  }
+  // stage `slot` (= s % kAStages) receives A(s)
+  auto dma_a = [&](int s, int slot, int j) __attribute__((always_inline)) {
+    char* dst = lds + L::kA + slot * L::kASlot + w * 1024;
+    buf_ld16_lds(ars, dst + j * 4096, aoff[j], (uint32_t)s * 128 * ESZ);
+  };
+
+  // ---- per-row scales (FP8 activations): SC[slot][set] holds sA[row] *
+  // sB[set] for the tile's rows, stored subtile-minor (row rs*16 + i at
+  // position i*kMaxRs + rs), so that a lane reads the scales of its row i for
+  // every subtile with one or two 16-byte LDS reads.
+  const int srow = (tid < m) ? tid : 0;
+  const rsrc_t sars = (AF != ACT_FP8) ? make_rsrc(nullptr, 0)
+                      : (STAGE == 1) ? make_rsrc(g.x_scales, (uint32_t)g.T * (g.H / 128) * 4)
+                                     : make_rsrc(g.sa, (uint32_t)(g.T * g.k) * (g.I / 128) * 4);
+  const uint32_t saoff = (STAGE == 1) ? (uint32_t)ROWI[srow < R ? srow : 0] * (g.H / 128) * 4
+                                      : (uint32_t)(r0 + srow) * (g.I / 128) * 4;
+  auto load_scale = [&](int s) __attribute__((always_inline)) -> float {
+    return (AF == ACT_FP8) ? buf_ldf(sars, saoff, (uint32_t)s * 4) : 1.f;
+  };
+  auto store_scale = [&](int s, int par, float sa) __attribute__((always_inline)) {   // par = s & 1
+    if (AF != ACT_FP8) return;
+    const int sc = min(s, nsteps - 1);             // steps past the end are never used
+    const float w0 = (WF == W_FP8) ? SCW[sc] : 1.f;
+    const float w1 = (WF == W_FP8) ? SCW[128 + sc] : 1.f;
+    // no branch here: a conditional block would let the compiler sink the
+    // step's MFMAs below the step's closing barrier
+    const int pos = (tid < L::kRows) ? (tid & 15) * L::kMaxRs + (tid >> 4) : tid;   // spare threads: unused slots
+    SC[(par * 2 + 0) * L::kScRows + pos] = sa * w0;
+    SC[(par * 2 + 1) * L::kScRows + pos] = sa * w1;
+  };
+
+  // ---- B loads (HBM straight to registers), one instruction per piece q
+  auto load_b_piece = [&](int s, BFrag& b, int q) __attribute__((always_inline)) {
+    if (WF == W_FP8) {
+      b.d[q >> 1][q & 1] = buf_ld16(wrs, boff[q >> 1] + 1024 * (q & 1), (uint32_t)s * 16 * BS);
+    } else if (WF == W_FP4) {
+      if ((q & 1) == 0) b.d[q >> 1][0] = buf_ld16(wrs, boff[q >> 1], (uint32_t)s * 16 * BS);
+      else b.sc[q >> 1] = (int)buf_ldu8(srs, bsoff[q >> 1], (uint32_t)s * 64);
+    } else {
+      b.d[q >> 2][q & 3] = buf_ld16(wrs, boff[q >> 2] + 1024 * (q & 3), (uint32_t)s * 16 * BS);
+    }
+  };
+
+  // ---- MFMA operand offsets.  16x16x128 f8f6f4 operand layout (gfx950): an
+  // 8-bit operand's lane group g holds K 16g..16g+15 in its first 16 bytes
+  // and K 64+16g..64+16g+15 in the next 16; a 4-bit operand's lane group g
+  // holds K 32g..32g+31 (even K in the low nibble); the E8M0 scale of lane
+  // group g covers K 32g..32g+31.  So an FP8 operand of lane group g is
+  // 16-byte chunks g and g+4 of the 128-byte K step, an FP4 operand is chunk
+  // g of the 64-byte step.  16x16x32 BF16: lane group g holds K 8g..8g+7 of
+  // each 32-K MFMA i, i.e. chunk 4i+g of the 256-byte step.  Each B load
+  // instruction thereby reads 64 contiguous bytes of every weight row it
+  // touches (one L1 request per row instead of four scattered pieces).
   uint32_t a_rd[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     int chunk;
     if (AF == ACT_FP8)
-      chunk = (i >= 2) ? 0 : (WF == W_FP4) ? gq + 4 * i : 2 * gq + i;
+      chunk = (i >= 2) ? 0 : gq + 4 * i;
     else
-      chunk = 4 * gq + i;
-    a_rd[i] = opaque(L::kA + c16 * AB + ((chunk ^ (c16 & (CPR - 1))) << 4));
+      chunk = 4 * i + gq;
+    a_rd[i] = opaque(L::kA + c16 * AB + (a_swz<CPR>(c16, chunk) << 4));
   }
-  const uint32_t sc_rd = opaque(L::kSC + 16 * gq);
+  // this lane's row within a subtile for the DPP scale broadcast (MFMA output
+  // lane l holds rows 4*(l/16) + v; lane v of each quad fetches row 4*(l/16)+v)
+  constexpr int NSET = (STAGE == 1 && WF == W_FP8) ? 2 : 1;
+  const uint32_t sc_rd = opaque(L::kSC + (4 * gq + (c16 & 3)) * L::kMaxRs * 4 +
+                                ((STAGE == 2 && WF == W_FP8 && w >= 2) ? L::kScRows * 4 : 0));
 
-  // A source rows (hoisted): token rows of x for stage 1, intermediate rows for stage 2
-  // Rows past the tile's valid count load a valid row instead (row 0 of the
-  // tile): their results are never stored, so no branch is needed.
-  const uint8_t* asrc[AJ];
+  v4f acc[RS][4];
 #pragma unroll
-  for (int j = 0; j < AJ; ++j) {
-    int row = wr_row + j * (kGemmThreads / CPR);
-    row = (row < m) ? row : 0;
-    if (STAGE == 1)
-      asrc[j] = g.x + (size_t)ROWI[row] * g.H * ESZ + wr_c * 16;
-    else
-      asrc[j] = g.aq + (size_t)(r0 + row) * g.I * ESZ + wr_c * 16;
-  }
-  const int srow = ((tid & 127) < m) ? (tid & 127) : 0;
-  const float* sAp = (AF == ACT_FP8)
-      ? ((STAGE == 1) ? g.x_scales + (size_t)ROWI[srow] * (g.H / 128)
-                      : g.sa + (size_t)(r0 + srow) * (g.I / 128))
-      : nullptr;
-
-  // ---- A loads (global -> registers -> LDS)
-  v4i areg[AJ];
-  float sA_next = 0.f, sw0_next = 0.f, sw1_next = 0.f;
-  auto load_a = [&](int s) __attribute__((always_inline)) {
-#pragma unroll
-    for (int j = 0; j < AJ; ++j) areg[j] = ld16(asrc[j] + (size_t)s * 128 * ESZ);
-    if (AF == ACT_FP8) {
-      sA_next = sAp[s];
-      if (WF == W_FP8) {
-        sw0_next = wsc[(size_t)sb0 * ksb + s];
-        sw1_next = wsc[(size_t)sb1 * ksb + s];
-      }
-    }
-  };
-  auto store_a = [&](int stage) __attribute__((always_inline)) {
-#pragma unroll
-    for (int j = 0; j < AJ; ++j) lds_st(lds, a_wr + stage * ASTAGE + j * (kGemmThreads / CPR) * AB, areg[j]);
-    if (AF == ACT_FP8) {
-      float v = sA_next;
-      if (WF == W_FP8) v *= (tid < 128) ? sw0_next : sw1_next;
-      SC[stage * 2 * kTileRows + tid] = v;        // [stage][set = tid / 128][row = tid % 128]
-    }
-  };
-
-  // ---- B loads (straight to registers)
-  auto load_b = [&](int s, BFrag& b) __attribute__((always_inline)) {
-    if (!wave_ok) return;
-#pragma unroll
-    for (int cs = 0; cs < 4; ++cs) {
-      if (WF == W_FP8) {
-        const uint8_t* p = bptr[cs] + (size_t)s * 128;
-        b.d[cs][0] = ld16(p);
-        b.d[cs][1] = ld16(p + 16);
-      } else if (WF == W_FP4) {
-        b.d[cs][0] = ld16(bptr[cs] + (size_t)s * 64);
-        b.sc[cs] = bscp[cs][s * 4];
-      } else {
-        const uint8_t* p = bptr[cs] + (size_t)s * 256;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) b.d[cs][i] = ld16(p + 16 * i);
-      }
-    }
-  };
-
-  v4f acc[8][4];
-#pragma unroll
-  for (int rs = 0; rs < 8; ++rs)
+  for (int rs = 0; rs < RS; ++rs)
 #pragma unroll
     for (int cs = 0; cs < 4; ++cs) acc[rs][cs] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int stage, const BFrag& b) __attribute__((always_inline)) {
-    if (!wave_ok) return;
+  // The step's MFMAs and FMAs have no memory side effects, so the compiler
+  // may sink them below the step's closing barrier (an asm statement), which
+  // would serialise the loads behind it with the math.  An empty volatile asm
+  // that "modifies" every accumulator keeps them above it.
+  auto pin_acc = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int rs = 0; rs < RS; ++rs)
+#pragma unroll
+      for (int cs = 0; cs < 4; ++cs) {
+        float x0 = acc[rs][cs][0], x1 = acc[rs][cs][1], x2 = acc[rs][cs][2], x3 = acc[rs][cs][3];
+        asm volatile("" : "+v"(x0), "+v"(x1), "+v"(x2), "+v"(x3));
+        acc[rs][cs] = v4f{x0, x1, x2, x3};
+      }
+  };
+
+  // Software pipeline over row subtiles, one scheduling region per subtile
+  // (sched_barrier keeps the compiler from hoisting every LDS read to the
+  // top, which would need registers for all subtiles at once): region rs
+  // issues a share of the step's global loads, the LDS reads of subtile
+  // rs+1, the MFMAs of rs and the fp32 promotion of rs-1, so the vector ALU
+  // scales and the memory pipeline accepts new loads while the matrix core
+  // works.  `issue(j)` issues global load j of the step (0 <= j < nload).
+  auto compute = [&](int slot, int par, const BFrag& b, int nload, auto&& issue) __attribute__((always_inline)) {
     const v4f zero = {0.f, 0.f, 0.f, 0.f};
+    const uint32_t so = (uint32_t)slot * L::kASlot;
+    const uint32_t sco = (uint32_t)par * 2 * L::kScRows * 4;
+    constexpr int NREG = (AF == ACT_FP8) ? RS + 1 : RS;
+    auto issue_share = [&](int r) __attribute__((always_inline)) {
 #pragma unroll
-    for (int rs = 0; rs < 8; ++rs) {
-      const uint32_t ao = stage * ASTAGE + rs * 16 * AB;
-      // operands of row tile rs are read only once row tile rs-2 is finished
-      const float dep = (rs >= 2) ? acc[rs - 2][3][3] : 0.f;
-      if (AF == ACT_FP8) {
-        const v4i a0 = lds_ld<v4i>(lds, after(a_rd[0], dep) + ao);
-        const v4i a1 = lds_ld<v4i>(lds, after(a_rd[1], dep) + ao);
-        const v8i av = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-        const uint32_t so = after(sc_rd, dep);
-        const v4f s0 = lds_ld<v4f>(lds, so + (stage * 2) * kTileRows * 4 + rs * 64);
-        const v4f s1 = lds_ld<v4f>(lds, so + (stage * 2 + 1) * kTileRows * 4 + rs * 64);
+      for (int j = r * nload / NREG; j < (r + 1) * nload / NREG; ++j) issue(j);
+    };
+    if (AF == ACT_FP8) {
+      constexpr int NC = (RS + 3) / 4;
+      v4i a0[2], a1[2];
+      v4f p[2][4], scv[NSET][NC];
 #pragma unroll
-        for (int cs = 0; cs < 4; ++cs) {
-          v4f p;
-          if (WF == W_FP8) {
-            const v8i bv = {b.d[cs][0][0], b.d[cs][0][1], b.d[cs][0][2], b.d[cs][0][3],
-                            b.d[cs][1][0], b.d[cs][1][1], b.d[cs][1][2], b.d[cs][1][3]};
-            p = mfma_fp8_fp8(av, bv, zero);
-          } else {
-            const v8i bv = {b.d[cs][0][0], b.d[cs][0][1], b.d[cs][0][2], b.d[cs][0][3], 0, 0, 0, 0};
-            p = mfma_fp8_fp4(av, bv, zero, b.sc[cs]);
+      for (int st = 0; st < NSET; ++st)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) scv[st][c] = lds_ld<v4f>(lds, sc_rd + sco + st * L::kScRows * 4 + c * 16);
+      auto lda = [&](int rs) __attribute__((always_inline)) {
+        const uint32_t ao = so + rs * 16 * AB;
+        a0[rs & 1] = lds_ld<v4i>(lds, a_rd[0] + ao);
+        a1[rs & 1] = lds_ld<v4i>(lds, a_rd[1] + ao);
+      };
+      lda(0);
+#pragma unroll
+      for (int rs = 0; rs <= RS; ++rs) {
+        __builtin_amdgcn_sched_barrier(0);
+        issue_share(rs);
+        if (rs + 1 < RS) lda(rs + 1);
+        if (rs < RS) {
+          const v4i x0 = a0[rs & 1], x1 = a1[rs & 1];
+          const v8i av = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+#pragma unroll
+          for (int cs = 0; cs < 4; ++cs) {
+            if (WF == W_FP8) {
+              const v8i bv = {b.d[cs][0][0], b.d[cs][0][1], b.d[cs][0][2], b.d[cs][0][3],
+                              b.d[cs][1][0], b.d[cs][1][1], b.d[cs][1][2], b.d[cs][1][3]};
+              p[rs & 1][cs] = mfma_fp8_fp8(av, bv, zero);
+            } else {
+              const v8i bv = {b.d[cs][0][0], b.d[cs][0][1], b.d[cs][0][2], b.d[cs][0][3], 0, 0, 0, 0};
+              p[rs & 1][cs] = mfma_fp8_fp4(av, bv, zero, b.sc[cs]);
+            }
           }
-          bool set1;
-          if (WF == W_FP4) set1 = false;
-          else if (STAGE == 1) set1 = cs >= 2;
-          else set1 = (w >= 2);
-          const v4f sc = set1 ? s1 : s0;
-#pragma unroll
-          for (int v = 0; v < 4; ++v) acc[rs][cs][v] = __builtin_fmaf(p[v], sc[v], acc[rs][cs][v]);
         }
-      } else {
+        if (rs > 0) {
+          const int q = rs - 1;
+          float bc[NSET][4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const v4i a = lds_ld<v4i>(lds, after(a_rd[i], dep) + ao);
+          for (int st = 0; st < NSET; ++st) {
+            const float x = scv[st][q >> 2][q & 3];
+            bc[st][0] = quad_bcast<0>(x);
+            bc[st][1] = quad_bcast<1>(x);
+            bc[st][2] = quad_bcast<2>(x);
+            bc[st][3] = quad_bcast<3>(x);
+          }
 #pragma unroll
-          for (int cs = 0; cs < 4; ++cs) acc[rs][cs] = mfma_bf16(as_v8bf(a), as_v8bf(b.d[cs][i]), acc[rs][cs]);
+          for (int cs = 0; cs < 4; ++cs) {
+            const int st = (NSET == 2 && cs >= 2) ? 1 : 0;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[q][cs][v] = __builtin_fmaf(p[q & 1][cs][v], bc[st][v], acc[q][cs][v]);
+          }
+        }
+        // One wave per SIMD: the matrix core only overlaps vector ALU work
+        // that sits between MFMAs in the instruction stream, so interleave
+        // each MFMA with a share of the promotion FMAs, LDS reads and loads.
+        if (rs < RS) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);   // VALU
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // global load
+          }
         }
       }
-      __builtin_amdgcn_sched_barrier(0);          // keep one row tile's operands live at a time
+      __builtin_amdgcn_sched_barrier(0);
+      pin_acc();
+    } else {
+      v4i a[2][4];
+      auto lda = [&](int rs) __attribute__((always_inline)) {
+        const uint32_t ao = so + rs * 16 * AB;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[rs & 1][i] = lds_ld<v4i>(lds, a_rd[i] + ao);
+      };
+      lda(0);
+#pragma unroll
+      for (int rs = 0; rs < RS; ++rs) {
+        __builtin_amdgcn_sched_barrier(0);
+        issue_share(rs);
+        if (rs + 1 < RS) lda(rs + 1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int cs = 0; cs < 4; ++cs)
+            acc[rs][cs] = mfma_bf16(as_v8bf(a[rs & 1][i]), as_v8bf(b.d[cs][i]), acc[rs][cs]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      pin_acc();
     }
   };
 
-  // ---- main loop: A double-buffered in LDS, B double-buffered in registers
-  // (BF16 weights are 4x the bytes per step and stay single-buffered)
-  BFrag b0, b1;
-  load_a(0);
-  store_a(0);
-  if (WF == W_BF16) {
-    __syncthreads();
-    for (int s = 0; s < nsteps; ++s) {
-      load_b(s, b0);
-      if (s + 1 < nsteps) load_a(s + 1);
-      compute(s & 1, b0);
-      if (s + 1 < nsteps) store_a((s + 1) & 1);
-      __syncthreads();
+  // ---- main loop.  A (three LDS stages, direct loads) and the activation
+  // scales are loaded two steps ahead, B NBUF-1 steps ahead (NBUF register
+  // buffers).  Step s: compute s while issuing scale(s+2), A(s+2) and
+  // B(s+NBUF-1), spread over the compute; publish the row scales of s+1;
+  // then a barrier that first waits until only this step's loads may still
+  // be in flight, so A(s+1) (issued a step earlier) has landed in LDS for
+  // every wave.  The vector memory counter
+  // completes in order, so every load gets about two steps of latency.
+  // Loads for steps past the end are issued anyway (buffer loads past a
+  // buffer's end read zero, and those stages are never computed): the step
+  // stays straight-line, which keeps the compiler's wait counts exact.  The
+  // prologue issues its loads in the steady state's order, so that the
+  // compiler's wait counts at the loop head are as exact as inside the loop.
+  constexpr int NSA = (AF == ACT_FP8) ? 1 : 0;
+  constexpr int NLOAD = NSA + NDMA + NB;           // global loads issued per step
+  BFrag bb[NBUF];
+  auto issue_a = [&](int s) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < NDMA; ++j) dma_a(s, s, j);
+  };
+  auto load_b = [&](int s, BFrag& b) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < NB; ++q) load_b_piece(s, b, q);
+  };
+  const float sa0 = load_scale(0);
+  issue_a(0);
+  if (NBUF == 3) load_b(0, bb[0]);
+  const float sa1 = load_scale(1);
+  issue_a(1);
+  load_b(NBUF - 2, bb[NBUF - 2]);
+  store_scale(0, 0, sa0);
+  barrier_vmcnt<NLOAD>();
+  // The loop body is UNR steps, a multiple of NBUF (B buffer rotation), of
+  // 2 (scale parity) and of kAStages (A stage rotation), so every buffer
+  // and LDS stage index in it is a compile-time constant; UNR > NBUF also
+  // makes the loop head, where the compiler's wait counts are merged from
+  // two paths and come out conservative, rarer.
+  constexpr int UNR = 6;
+  static_assert(UNR % NBUF == 0 && UNR % 2 == 0 && UNR % L::kAStages == 0, "loop unroll");
+  auto step = [&](int s, int u, float sa_next) __attribute__((always_inline)) -> float {
+    float sa2 = 1.f;
+    compute(u % L::kAStages, u & 1, bb[u % NBUF], NLOAD, [&](int j) __attribute__((always_inline)) {
+      if (j < NSA) sa2 = load_scale(s + 2);
+      else if (j < NSA + NDMA) dma_a(s + 2, (u + 2) % L::kAStages, j - NSA);
+      else load_b_piece(s + NBUF - 1, bb[(u + NBUF - 1) % NBUF], j - NSA - NDMA);
+    });
+    store_scale(s + 1, (u + 1) & 1, sa_next);
+    barrier_vmcnt<NLOAD>();
+    return sa2;
+  };
+  float sa_next = sa1;
+  for (int s = 0; s < nsteps; s += UNR) {
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      if (u > 0 && s + u >= nsteps) break;
+      sa_next = step(s + u, u, sa_next);
     }
-  } else {
-  load_b(0, b0);
+  }
+  wait_vmcnt<0>();                                 // the last steps' overrun loads
   __syncthreads();
-  for (int s = 0; s < nsteps; s += 2) {
-    if (s + 1 < nsteps) { load_a(s + 1); load_b(s + 1, b1); }
-    compute(0, b0);
-    if (s + 1 < nsteps) store_a(1);
-    __syncthreads();
-    if (s + 1 >= nsteps) break;
-    if (s + 2 < nsteps) { load_a(s + 2); load_b(s + 2, b0); }
-    compute(1, b1);
-    if (s + 2 < nsteps) store_a(0);
-    __syncthreads();
-  }
-  }
 
-  // ---- epilogues (the A region is reused as the output staging tile)
+  // ---- epilogues (the A stages are reused as the output staging tile)
   if (STAGE == 1) {
     // a = SiLU(g) * u, written over the gate accumulators: av[rs][q] = acc[rs][q]
 #pragma unroll
-    for (int rs = 0; rs < 8; ++rs) {
+    for (int rs = 0; rs < RS; ++rs) {
 #pragma unroll
       for (int q = 0; q < 2; ++q)
 #pragma unroll
@@ -321,14 +467,13 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
           const float gv = acc[rs][q][v], uv = acc[rs][2 + q][v];
           acc[rs][q][v] = gv / (1.0f + __expf(-gv)) * uv;
         }
-      __builtin_amdgcn_sched_barrier(0);
     }
     auto av = [&](int rs, int q, int v) __attribute__((always_inline)) { return acc[rs][q][v]; };
     if (AF == ACT_FP8) {
       float* RSC = reinterpret_cast<float*>(lds + L::kRsc);
-      const uint32_t amax_wr = opaque(L::kAmax + w * kTileRows * 4 + 16 * gq);
+      const uint32_t amax_wr = opaque(L::kAmax + w * L::kRows * 4 + 16 * gq);
 #pragma unroll
-      for (int rs = 0; rs < 8; ++rs)
+      for (int rs = 0; rs < RS; ++rs)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           float mx = fmaxf(fabsf(av(rs, 0, v)), fabsf(av(rs, 1, v)));
@@ -336,10 +481,10 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
           if (c16 == 0) lds_st(lds, amax_wr + (rs * 16 + v) * 4, mx);
         }
       __syncthreads();
-      if (tid < kTileRows) {
+      if (tid < R) {
         const float* AMAX = reinterpret_cast<const float*>(lds + L::kAmax);
-        const float mx = fmaxf(fmaxf(AMAX[tid], AMAX[kTileRows + tid]),
-                               fmaxf(AMAX[2 * kTileRows + tid], AMAX[3 * kTileRows + tid]));
+        const float mx = fmaxf(fmaxf(AMAX[tid], AMAX[L::kRows + tid]),
+                               fmaxf(AMAX[2 * L::kRows + tid], AMAX[3 * L::kRows + tid]));
         const float sc = (mx > 0.f) ? mx / 448.0f : 1.0f;
         RSC[tid] = sc;
         reinterpret_cast<float*>(lds + L::kRinv)[tid] = 1.0f / sc;
@@ -348,7 +493,7 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
       const uint32_t rinv_rd = opaque(L::kRinv + 16 * gq);
       const uint32_t out_wr = opaque(L::kA + 4 * gq * 128 + 32 * w + c16);
 #pragma unroll
-      for (int rs = 0; rs < 8; ++rs)
+      for (int rs = 0; rs < RS; ++rs)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const float inv = lds_ld<float>(lds, rinv_rd + (rs * 16 + v) * 4);
@@ -357,9 +502,7 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
           lds_st(lds, o + 16, (uint8_t)f32_to_e4m3(av(rs, 1, v) * inv));
         }
       __syncthreads();
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int q = tid + kGemmThreads * j;
+      for (int q = tid; q < R * 8; q += kGemmThreads) {
         const int row = q >> 3, c = q & 7;
         if (row < m) st16(g.aq + (size_t)(r0 + row) * g.I + c0 + c * 16, ld16(lds + L::kA + row * 128 + c * 16));
       }
@@ -367,7 +510,7 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
     } else {
       const uint32_t out_wr = opaque(L::kA + (4 * gq * 128 + 32 * w + c16) * 2);
 #pragma unroll
-      for (int rs = 0; rs < 8; ++rs)
+      for (int rs = 0; rs < RS; ++rs)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const uint32_t o = out_wr + (rs * 16 + v) * 256;
@@ -375,44 +518,52 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
           lds_st(lds, o + 32, (uint16_t)f32_to_bf16_rne(av(rs, 1, v)));
         }
       __syncthreads();
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int q = tid + kGemmThreads * j;
+      for (int q = tid; q < R * 16; q += kGemmThreads) {
         const int row = q >> 4, c = q & 15;
         if (row < m)
           st16(g.aq + ((size_t)(r0 + row) * g.I + c0) * 2 + c * 16, ld16(lds + L::kA + row * 256 + c * 16));
       }
     }
   } else {
+    // chunks of CH row subtiles (at most 64 rows x 256 columns of BF16 = 32 KB)
+    constexpr int CH = (RS < 4) ? RS : 4;
     const uint32_t out_wr = opaque(L::kA + (4 * gq * 256 + 64 * w + c16) * 2);
     const uint32_t roww_rd = opaque(L::kRowW + 16 * gq);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      if (h == 1) __syncthreads();                 // first half's copy-out is done
-      if (wave_ok) {
+    for (int h = 0; h < RS / CH; ++h) {
+      if (h > 0) __syncthreads();                  // previous chunk's copy-out is done
 #pragma unroll
-        for (int rs = 4 * h; rs < 4 * h + 4; ++rs)
+      for (int rs = CH * h; rs < CH * h + CH; ++rs)
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const float rw = lds_ld<float>(lds, roww_rd + (rs * 16 + v) * 4);
+        for (int v = 0; v < 4; ++v) {
+          const float rw = lds_ld<float>(lds, roww_rd + (rs * 16 + v) * 4);
 #pragma unroll
-            for (int cs = 0; cs < 4; ++cs)
-              lds_st(lds, out_wr + ((rs - 4 * h) * 16 + v) * 512 + cs * 32,
-                     (uint16_t)f32_to_bf16_rne(acc[rs][cs][v] * rw));
-          }
-      }
+          for (int cs = 0; cs < 4; ++cs)
+            lds_st(lds, out_wr + ((rs - CH * h) * 16 + v) * 512 + cs * 32,
+                   (uint16_t)f32_to_bf16_rne(acc[rs][cs][v] * rw));
+        }
       __syncthreads();
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int q = tid + kGemmThreads * j;
+      for (int q = tid; q < CH * 16 * 32; q += kGemmThreads) {
         const int rl = q >> 5, c = q & 31;
-        const int row = 64 * h + rl, col = n0 + c * 8;
+        const int row = CH * 16 * h + rl, col = n0 + c * 8;
         if (row < m && col < g.H)
           st16(reinterpret_cast<uint8_t*>(g.staging) + ((size_t)ROWI[row] * g.H + col) * 2,
                ld16(lds + L::kA + rl * 512 + c * 16));
       }
     }
   }
+}
+
+// Dispatch a tile to the GEMM variant with the tile's number of row subtiles.
+template <int AF, int WF, int STAGE>
+DEV void expert_gemm_item(const GemmArgs& g, const Tile& t, int nb, char* lds) {
+  constexpr int FULL = GemmLds<AF>::kMaxRs;
+  if (t.rs <= 1)
+    expert_gemm_tile<AF, WF, STAGE, 1>(g, t.e, t.r0, t.rows, nb, lds);
+  else if (t.rs <= 4)
+    expert_gemm_tile<AF, WF, STAGE, 4>(g, t.e, t.r0, t.rows, nb, lds);
+  else
+    expert_gemm_tile<AF, WF, STAGE, FULL>(g, t.e, t.r0, t.rows, nb, lds);
 }
 
 // y[t, n0:n1] = BF16( sum_j staging[t*k + j, n0:n1] ) for tokens [t0, t1),

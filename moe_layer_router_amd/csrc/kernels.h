@@ -14,7 +14,10 @@ enum {
   CTR_SCAN_FLAG,      // 1 once offsets / base / tiles are written
   CTR_SCATTER_DONE,   // scatter items finished
   CTR_G1_DONE,        // gate|up items finished
-  CTR_NUM = 16
+  CTR_QUEUE2,         // persistent kernel: queue head after the gate|up items
+  CTR_Q1 = 8,         // [kXcds] gate|up item queues, one per expert class
+  CTR_Q2 = 16,        // [kXcds] down item queues (separate kernels)
+  CTR_NUM = 32
 };
 
 // Everything a kernel needs: shapes, caller buffers and workspace regions.
@@ -25,6 +28,7 @@ struct Plan {
   int nblk;                    // 256-token blocks
   int nT64, nE64;              // router tiles
   int max_tiles;
+  int tile_rows;               // rows of a full GEMM tile
   int nnb1, nnb2;              // N blocks of gate|up (128 channels) and down (256 columns)
   int slab_group;              // down-GEMM N blocks processed per tile before moving on
   int nCT;                     // combine token chunks per N block
@@ -46,6 +50,25 @@ struct Plan {
 };
 
 constexpr int kCombineTokens = 256;
+
+// Per-class work queues over (tile, N block) items.  A workgroup on XCD x
+// takes items of class x (tiles first[x] .. first[x+1], a copy of meta[1..]
+// in LDS) and, once those are all claimed, moves on to the following
+// classes.  Returns the global item index, or -1 when every class is
+// exhausted.  `cls` is the workgroup's current class (start: its XCD),
+// advanced as classes run dry.  Called by one thread.
+DEV int pop_class_item(int32_t* queues, const int* first, int nnb, int* cls) {
+  for (int n = 0; n < kXcds; ++n) {
+    const int x = *cls;
+    const int lo = first[x] * nnb, cnt = first[x + 1] * nnb - lo;
+    if (cnt > 0) {
+      const int j = __hip_atomic_fetch_add(&queues[x], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (j < cnt) return lo + j;
+    }
+    *cls = (x + 1) % kXcds;
+  }
+  return -1;
+}
 
 __host__ __device__ inline GemmArgs gemm_args(const Plan& p) {
   GemmArgs g;

@@ -31,10 +31,10 @@ __global__ void __launch_bounds__(256) k_count(const int32_t* ids, int T, int k,
   perm_count_block(ids, T, k, E, blockIdx.x, blockcnt, reinterpret_cast<int*>(lds));
 }
 
-__global__ void __launch_bounds__(256) k_scan(const int32_t* blockcnt, int nblk, int E, int32_t* base,
+__global__ void __launch_bounds__(256) k_scan(const int32_t* blockcnt, int nblk, int E, int tile_rows, int32_t* base,
                                               int32_t* offsets, Tile* tiles, int32_t* meta) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
-  perm_scan(blockcnt, nblk, E, base, offsets, tiles, meta, reinterpret_cast<int*>(lds));
+  perm_scan(blockcnt, nblk, E, tile_rows, base, offsets, tiles, meta, reinterpret_cast<int*>(lds));
 }
 
 __global__ void __launch_bounds__(256) k_scatter(const int32_t* ids, int T, int k, int E, const int32_t* base,
@@ -43,20 +43,57 @@ __global__ void __launch_bounds__(256) k_scatter(const int32_t* ids, int T, int 
   perm_scatter_block(ids, T, k, E, blockIdx.x, base, perm, row_of, reinterpret_cast<uint64_t*>(lds));
 }
 
-// Persistent grid over (tile, N block) items.  Workgroup b runs on XCD b % 8
-// (round-robin dispatch); each XCD takes a contiguous run of items per round,
-// so the N blocks of one row tile share that XCD's L2 for their A rows.
+// Persistent grid (one workgroup per CU) over (tile, N block) items taken
+// from the per-class queues.  Workgroup b runs on XCD b % 8 (round-robin
+// dispatch) and starts on that class.  Thread 0 claims the next item while
+// the current one runs, so the atomic's latency is hidden.
 template <int AF, int WF, int STAGE>
-__global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
-k_gemm(GemmArgs g, const Tile* tiles, const int32_t* meta, int nnb) {
+__global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+k_gemm(GemmArgs g, const Tile* tiles, const int32_t* meta, int nnb, int32_t* queues) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
-  const int nitems = meta[0] * nnb;
-  const int G = gridDim.x, b = blockIdx.x;
-  const int slot = (b & 7) * (G >> 3) + (b >> 3);
-  for (int base = 0; base + slot < nitems; base += G) {
-    const int i = base + slot;
-    const Tile t = tiles[i / nnb];
-    expert_gemm_tile<AF, WF, STAGE>(g, t.e, t.r0, t.rows, i % nnb, lds);
+  __shared__ int s_item, s_first[kXcds + 1];
+  int cls = blockIdx.x % kXcds;
+  if (threadIdx.x <= kXcds) s_first[threadIdx.x] = meta[1 + threadIdx.x];
+  __syncthreads();
+  if (threadIdx.x == 0) s_item = pop_class_item(queues, s_first, nnb, &cls);
+  __syncthreads();
+  for (int i = s_item; i >= 0;) {
+    __syncthreads();                                          // everyone has read s_item
+    if (threadIdx.x == 0) s_item = pop_class_item(queues, s_first, nnb, &cls);
+    int t, nb;
+    gemm_item_of(tiles, nnb, i, &t, &nb);
+    expert_gemm_item<AF, WF, STAGE>(g, tiles[t], nb, lds);   // starts with a barrier
+    i = s_item;
+  }
+}
+
+// Row-major [E*N][K] weights -> MFMA-tiled blocks (a byte permutation; the
+// layout is defined in moe_layer.h).  One thread per 16-byte unit of the
+// destination, in destination order, so that the writes are contiguous.
+__global__ void __launch_bounds__(256) k_pack_weights(const uint8_t* src, uint8_t* dst, size_t rows, int nsteps,
+                                                      int bs) {
+  const int np = bs / 64;
+  const size_t units = rows * (size_t)nsteps * bs / 16;
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < units; i += (size_t)gridDim.x * blockDim.x) {
+    const int l = (int)(i & 63);
+    size_t r = i >> 6;
+    const int p = (int)(r % np);
+    r /= np;
+    const int s = (int)(r % nsteps);
+    const size_t row = (r / nsteps) * 16 + (l & 15);
+    st16(dst + i * 16, ld16(src + row * ((size_t)nsteps * bs) + (size_t)bs * s + 64 * p + 16 * (l >> 4)));
+  }
+}
+
+// E8M0 scales [E*N][K/32] -> 64-byte blocks per (16-row tile, K step).
+__global__ void __launch_bounds__(256) k_pack_e8m0(const uint8_t* src, uint8_t* dst, size_t rows, int nsteps) {
+  const size_t n = rows * (size_t)nsteps * 4;
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
+    const int l = (int)(i & 63);
+    const size_t r = i >> 6;
+    const int s = (int)(r % nsteps);
+    const size_t row = (r / nsteps) * 16 + (l & 15);
+    dst[i] = src[row * ((size_t)nsteps * 4) + 4 * s + (l >> 4)];
   }
 }
 
@@ -68,14 +105,16 @@ __global__ void __launch_bounds__(256) k_combine(const uint16_t* staging, uint16
 // ------------------------------------------------------- persistent kernel
 constexpr unsigned kSpinLimit = 1u << 22;
 
-// Thread 0 waits (bounded) until *c >= target, with acquire ordering at
-// device scope; the workgroup then proceeds together.  Returns false if the
-// wait timed out or another workgroup reported a failure.
+// Thread 0 waits (bounded) until *c >= target; the workgroup then proceeds
+// together.  The spin uses relaxed loads and a single device-scope acquire
+// fence follows it: an acquire on every poll would invalidate the caches
+// each time, taking cached weights away from every workgroup on the XCD.
+// Returns false if the wait timed out or another workgroup reported a failure.
 DEV bool wait_counter(const int32_t* c, int target, int32_t* err, int* s_ok) {
   if (threadIdx.x == 0) {
     int ok = 1;
     unsigned spins = 0;
-    while (__hip_atomic_load(c, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < target) {
+    while (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
       if (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) { ok = 0; break; }
       __builtin_amdgcn_s_sleep(8);
       if (++spins > kSpinLimit) {
@@ -84,6 +123,7 @@ DEV bool wait_counter(const int32_t* c, int target, int32_t* err, int* s_ok) {
         break;
       }
     }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     *s_ok = ok;
   }
   __syncthreads();
@@ -102,17 +142,19 @@ DEV void signal_add(int32_t* c0, int32_t* c1 = nullptr) {
   }
 }
 
-// Work queue, in dependency order (an item only ever waits for items with a
-// smaller queue index, all of which were taken by running workgroups, so the
-// queue cannot deadlock whatever the grid size):
-//   router tiles (64 tokens x 64 experts)       -> rdone[token tile]
-//   top-k of 64 tokens                          -> tkdone[256-token block]
-//   expert histogram of 256 tokens              -> COUNT_DONE
-//   scan (offsets, block bases, tile list)      -> SCAN_FLAG
-//   stable scatter of 256 tokens                -> SCATTER_DONE
-//   gate|up items (tile, 128 channels)          -> done1[tile]
-//   per group of down N blocks: down items (tile, N block), tile-major,
-//   then combine items (N block, 256 tokens)    <- done2[N block]
+// Three queues, each in dependency order.  An item only ever waits for items
+// that precede it in its own queue or belong to an earlier queue, and a
+// workgroup moves to the next queue only once every item of the current one
+// has been claimed by a running workgroup, so no wait can deadlock whatever
+// the grid size:
+//   head queue:   router tiles (64 tokens x 64 experts) -> rdone[token tile]
+//                 top-k of 64 tokens                    -> tkdone[256-token block]
+//                 expert histogram of 256 tokens        -> COUNT_DONE
+//                 scan (offsets, block bases, tiles)    -> SCAN_FLAG
+//                 stable scatter of 256 tokens          -> SCATTER_DONE
+//   class queues: gate|up items (tile, 128 channels)    -> done1[tile]
+//   tail queue:   per group of down N blocks: down items (tile, N block)
+//                 -> done2[N block], then combine items (N block, 256 tokens)
 // Each phase of the persistent kernel is its own (non-inlined) function, so
 // that register allocation sees one phase at a time.  Each declares the
 // dynamic LDS array itself so that its accesses compile to LDS instructions.
@@ -120,7 +162,7 @@ DEV void signal_add(int32_t* c0, int32_t* c1 = nullptr) {
 template <int AF, int WF, int STAGE>
 __device__ __noinline__ void mega_gemm_item(const Plan& p, Tile tl, int nb) {
   MEGA_LDS;
-  expert_gemm_tile<AF, WF, STAGE>(gemm_args(p), tl.e, tl.r0, tl.rows, nb, lds);
+  expert_gemm_item<AF, WF, STAGE>(gemm_args(p), tl, nb, lds);
 }
 __device__ __noinline__ void mega_router_item(const Plan& p, int tt, int et) {
   MEGA_LDS;
@@ -137,7 +179,7 @@ __device__ __noinline__ void mega_count_item(const Plan& p, int b) {
 }
 __device__ __noinline__ void mega_scan_item(const Plan& p) {
   MEGA_LDS;
-  perm_scan(p.blockcnt, p.nblk, p.E, p.base, p.offsets, p.tiles, p.meta, reinterpret_cast<int*>(lds));
+  perm_scan(p.blockcnt, p.nblk, p.E, p.tile_rows, p.base, p.offsets, p.tiles, p.meta, reinterpret_cast<int*>(lds));
 }
 __device__ __noinline__ void mega_scatter_item(const Plan& p, int b) {
   MEGA_LDS;
@@ -149,93 +191,101 @@ __device__ __noinline__ void mega_combine_item(const Plan& p, int nb, int c) {
 }
 
 template <int AF, int WF>
-__global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
+__global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 k_mega(Plan p) {
-  __shared__ int s_q, s_ok, s_ntiles;
+  __shared__ int s_q, s_ok, s_first[kXcds + 1];
   const int tid = threadIdx.x;
   const int nR = p.routing_given ? 0 : p.nT64 * p.nE64;
   const int nK = p.routing_given ? 0 : p.nT64;
   const int q_topk = nR, q_count = nR + nK, q_scan = q_count + p.nblk;
-  const int q_scat = q_scan + 1, q_dyn = q_scat + p.nblk;
-  bool seen_scatter = false;
-  int ntiles = -1;
+  const int q_scat = q_scan + 1, q_end = q_scat + p.nblk;
 
+  // 1. routing and permutation items from the head queue
   for (;;) {
     if (tid == 0) s_q = __hip_atomic_fetch_add(&p.ctr[CTR_QUEUE], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     const int q = s_q;
     __syncthreads();
-
+    if (q >= q_end) break;
     if (q < q_topk) {
       const int tt = q / p.nE64, et = q % p.nE64;
       mega_router_item(p, tt, et);
       signal_add(&p.rdone[tt]);
     } else if (q < q_count) {
       const int tt = q - q_topk;
-      if (!wait_counter(&p.rdone[tt], p.nE64, p.err, &s_ok)) break;
+      if (!wait_counter(&p.rdone[tt], p.nE64, p.err, &s_ok)) return;
       mega_topk_item(p, tt);
       signal_add(&p.tkdone[tt >> 2]);
     } else if (q < q_scan) {
       const int b = q - q_count;
       if (!p.routing_given) {
         const int tiles_in_block = min(4, p.nT64 - 4 * b);
-        if (!wait_counter(&p.tkdone[b], tiles_in_block, p.err, &s_ok)) break;
+        if (!wait_counter(&p.tkdone[b], tiles_in_block, p.err, &s_ok)) return;
       }
       mega_count_item(p, b);
       signal_add(&p.ctr[CTR_COUNT_DONE]);
     } else if (q == q_scan) {
-      if (!wait_counter(&p.ctr[CTR_COUNT_DONE], p.nblk, p.err, &s_ok)) break;
+      if (!wait_counter(&p.ctr[CTR_COUNT_DONE], p.nblk, p.err, &s_ok)) return;
       mega_scan_item(p);
       signal_add(&p.ctr[CTR_SCAN_FLAG]);
-    } else if (q < q_dyn) {
-      if (!wait_counter(&p.ctr[CTR_SCAN_FLAG], 1, p.err, &s_ok)) break;
+    } else {
+      if (!wait_counter(&p.ctr[CTR_SCAN_FLAG], 1, p.err, &s_ok)) return;
       mega_scatter_item(p, q - q_scat);
       signal_add(&p.ctr[CTR_SCATTER_DONE]);
-    } else {
-      if (ntiles < 0) {
-        if (!wait_counter(&p.ctr[CTR_SCAN_FLAG], 1, p.err, &s_ok)) break;
-        if (tid == 0) s_ntiles = __hip_atomic_load(&p.meta[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __syncthreads();
-        ntiles = s_ntiles;
-        __syncthreads();
-      }
-      int i = q - q_dyn;
-      const int n1 = ntiles * p.nnb1;
-      if (i < n1) {
-        if (!seen_scatter) {
-          if (!wait_counter(&p.ctr[CTR_SCATTER_DONE], p.nblk, p.err, &s_ok)) break;
-          seen_scatter = true;
-        }
-        const int t = i / p.nnb1;
-        mega_gemm_item<AF, WF, 1>(p, p.tiles[t], i % p.nnb1);
-        signal_add(&p.done1[t], &p.ctr[CTR_G1_DONE]);
-        continue;
-      }
-      i -= n1;
-      bool found = false, failed = false;
-      for (int g0 = 0; g0 < p.nnb2; g0 += p.slab_group) {
-        const int ns = min(p.slab_group, p.nnb2 - g0);
-        const int n2 = ntiles * ns, nc = ns * p.nCT;
-        if (i < n2) {
-          const int t = i / ns, nb = g0 + i % ns;
-          if (!wait_counter(&p.done1[t], p.nnb1, p.err, &s_ok)) { failed = true; break; }
-          mega_gemm_item<AF, WF, 2>(p, p.tiles[t], nb);
-          signal_add(&p.done2[nb]);
-          found = true;
-          break;
-        }
-        i -= n2;
-        if (i < nc) {
-          const int nb = g0 + i / p.nCT, c = i % p.nCT;
-          if (!wait_counter(&p.done2[nb], ntiles, p.err, &s_ok)) { failed = true; break; }
-          mega_combine_item(p, nb, c);
-          found = true;
-          break;
-        }
-        i -= nc;
-      }
-      if (failed || !found) break;
     }
+  }
+
+  // 2. gate|up items from the per-class queues (every head item has been
+  // claimed by a running workgroup, so these waits end)
+  if (!wait_counter(&p.ctr[CTR_SCATTER_DONE], p.nblk, p.err, &s_ok)) return;
+  if (tid <= kXcds) s_first[tid] = __hip_atomic_load(&p.meta[1 + tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const int ntiles = s_first[kXcds];
+  int cls = blockIdx.x % kXcds;
+  if (tid == 0) s_q = pop_class_item(p.ctr + CTR_Q1, s_first, p.nnb1, &cls);
+  __syncthreads();
+  for (int i = s_q; i >= 0;) {
+    __syncthreads();
+    if (tid == 0) s_q = pop_class_item(p.ctr + CTR_Q1, s_first, p.nnb1, &cls);
+    int t, nb;
+    gemm_item_of(p.tiles, p.nnb1, i, &t, &nb);
+    mega_gemm_item<AF, WF, 1>(p, p.tiles[t], nb);
+    signal_add(&p.done1[t], &p.ctr[CTR_G1_DONE]);
+    i = s_q;
+  }
+
+  // 3. down items and combine items, per group of N blocks, from the tail
+  // queue (all gate|up items have been claimed before any of these)
+  for (;;) {
+    __syncthreads();
+    if (tid == 0) s_q = __hip_atomic_fetch_add(&p.ctr[CTR_QUEUE2], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    int i = s_q;
+    bool found = false;
+    for (int g0 = 0; g0 < p.nnb2; g0 += p.slab_group) {
+      const int ns = min(p.slab_group, p.nnb2 - g0);
+      const int n2 = ntiles * ns, nc = ns * p.nCT;
+      if (i < n2) {
+        int t, nbl;
+        gemm_item_of(p.tiles, ns, i, &t, &nbl);
+        const int nb = g0 + nbl;
+        if (!wait_counter(&p.done1[t], p.nnb1, p.err, &s_ok)) return;
+        mega_gemm_item<AF, WF, 2>(p, p.tiles[t], nb);
+        signal_add(&p.done2[nb]);
+        found = true;
+        break;
+      }
+      i -= n2;
+      if (i < nc) {
+        const int nb = g0 + i / p.nCT, c = i % p.nCT;
+        if (!wait_counter(&p.done2[nb], ntiles, p.err, &s_ok)) return;
+        mega_combine_item(p, nb, c);
+        found = true;
+        break;
+      }
+      i -= nc;
+    }
+    if (!found) break;
   }
 }
 
@@ -248,7 +298,7 @@ k_mega(Plan p) {
 #include <mutex>
 #include <string>
 
-#include "../../include/moe_layer.h"
+#include "moe_layer.h"
 
 using namespace moe;
 
@@ -280,7 +330,7 @@ Layout make_layout(const moe_desc* d) {
   L.nblk = (int)((T + kPermBlock - 1) / kPermBlock);
   L.nT64 = (int)((T + 63) / 64);
   L.nE64 = (int)((E + 63) / 64);
-  L.max_tiles = (int)(E + (T * k + kTileRows - 1) / kTileRows);
+  L.max_tiles = (int)(E + (T * k + kMinTileRows - 1) / kMinTileRows);
   L.nnb1 = (int)(I / 128);
   L.nnb2 = (int)((H + 255) / 256);
   size_t o = 0;
@@ -384,6 +434,7 @@ moe_status fill_plan(const moe_desc* d, const Layout& L, char* ws, Plan* P) {
   p.wdt = d->weight_dtype == MOE_DTYPE_FP8_E4M3 ? W_FP8 : d->weight_dtype == MOE_DTYPE_FP4_E2M1 ? W_FP4 : W_BF16;
   p.routing_given = (d->flags & MOE_FLAG_ROUTING_GIVEN) != 0;
   p.nblk = L.nblk; p.nT64 = L.nT64; p.nE64 = L.nE64; p.max_tiles = L.max_tiles;
+  p.tile_rows = p.act_fp8 ? GemmLds<ACT_FP8>::kRows : GemmLds<ACT_BF16>::kRows;
   p.nnb1 = L.nnb1; p.nnb2 = L.nnb2;
   p.slab_group = 4;
   p.nCT = (d->T + kCombineTokens - 1) / kCombineTokens;
@@ -435,7 +486,7 @@ int mega_lds(const Plan& p) {
   int b = gemm_lds(p.act_fp8);
   b = b > kRouterLds ? b : kRouterLds;
   b = b > 4 * p.E * 8 ? b : 4 * p.E * 8;
-  b = b > (2 * p.E + 64) * 4 ? b : (2 * p.E + 64) * 4;
+  b = b > (2 * p.E + 72) * 4 ? b : (2 * p.E + 72) * 4;
   return b;
 }
 
@@ -451,8 +502,8 @@ moe_status launch_route(const Plan& p, float* logits, hipStream_t st) {
 moe_status launch_permute(const Plan& p, int32_t* row_of, hipStream_t st) {
   hipLaunchKernelGGL(k_count, dim3(p.nblk), dim3(256), p.E * 4, st, p.ids, p.T, p.k, p.E, p.blockcnt);
   HIP_TRY(hipGetLastError());
-  hipLaunchKernelGGL(k_scan, dim3(1), dim3(256), (2 * p.E + 64) * 4, st, p.blockcnt, p.nblk, p.E, p.base, p.offsets,
-                     p.tiles, p.meta);
+  hipLaunchKernelGGL(k_scan, dim3(1), dim3(256), (2 * p.E + 72) * 4, st, p.blockcnt, p.nblk, p.E, p.tile_rows, p.base,
+                     p.offsets, p.tiles, p.meta);
   HIP_TRY(hipGetLastError());
   hipLaunchKernelGGL(k_scatter, dim3(p.nblk), dim3(256), 4 * p.E * 8, st, p.ids, p.T, p.k, p.E, p.base, p.perm, row_of);
   HIP_TRY(hipGetLastError());
@@ -471,10 +522,12 @@ moe_status launch_layer(const Plan& p, const DevInfo& di, int mode, hipStream_t 
     const int lds = gemm_lds(AF == ACT_FP8);
     TRY(set_lds_limit(k_gemm<AF, WF, 1>, lds));
     TRY(set_lds_limit(k_gemm<AF, WF, 2>, lds));
-    const int grid = di.cus * 2;
-    hipLaunchKernelGGL((k_gemm<AF, WF, 1>), dim3(grid), dim3(256), lds, st, g, p.tiles, p.meta, p.nnb1);
+    const int grid = di.cus;
+    hipLaunchKernelGGL((k_gemm<AF, WF, 1>), dim3(grid), dim3(256), lds, st, g, p.tiles, p.meta, p.nnb1,
+                       p.ctr + CTR_Q1);
     HIP_TRY(hipGetLastError());
-    hipLaunchKernelGGL((k_gemm<AF, WF, 2>), dim3(grid), dim3(256), lds, st, g, p.tiles, p.meta, p.nnb2);
+    hipLaunchKernelGGL((k_gemm<AF, WF, 2>), dim3(grid), dim3(256), lds, st, g, p.tiles, p.meta, p.nnb2,
+                       p.ctr + CTR_Q2);
     HIP_TRY(hipGetLastError());
     hipLaunchKernelGGL(k_combine, dim3((p.T + 15) / 16), dim3(256), 0, st, p.staging, p.y, p.T, p.H, p.k);
     HIP_TRY(hipGetLastError());
@@ -616,6 +669,41 @@ moe_status moe_permute(const moe_desc* d, const int32_t* topk_ids, int32_t* expe
   p.offsets = expert_offsets;
   p.perm = perm;
   return launch_permute(p, row_of, static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_pack_weights(const moe_desc* d, int32_t which, const void* src, const void* src_scales, void* dst,
+                            void* dst_scales, moe_stream_t stream) {
+  TRY(check_desc(d));
+  if (which != MOE_WEIGHTS_GATE_UP && which != MOE_WEIGHTS_DOWN)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "which must be MOE_WEIGHTS_GATE_UP or MOE_WEIGHTS_DOWN (got %d)", which);
+  TRY(check_ptr(src, "src"));
+  TRY(check_ptr(dst, "dst"));
+  const bool fp4 = d->weight_dtype == MOE_DTYPE_FP4_E2M1;
+  if (fp4) {
+    TRY(check_ptr(src_scales, "src_scales"));
+    TRY(check_ptr(dst_scales, "dst_scales"));
+  } else if (src_scales || dst_scales) {
+    return fail(MOE_ERR_INVALID_ARGUMENT, "scale pointers must be NULL unless the weights are FP4");
+  }
+  const size_t N = which == MOE_WEIGHTS_GATE_UP ? 2 * (size_t)d->I : (size_t)d->H;
+  const int K = which == MOE_WEIGHTS_GATE_UP ? d->H : d->I;
+  const int bs = d->weight_dtype == MOE_DTYPE_BF16 ? 256 : fp4 ? 64 : 128;
+  const size_t rows = (size_t)d->E * N, bytes = rows * (size_t)(K / 128) * bs;
+  const uintptr_t s0 = (uintptr_t)src, d0 = (uintptr_t)dst;
+  if (s0 < d0 + bytes && d0 < s0 + bytes) return fail(MOE_ERR_INVALID_ARGUMENT, "dst overlaps src");
+  DevInfo di;
+  TRY(device_info(&di));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int grid = di.cus * 8;
+  hipLaunchKernelGGL(k_pack_weights, dim3(grid), dim3(256), 0, st, static_cast<const uint8_t*>(src),
+                     static_cast<uint8_t*>(dst), rows, K / 128, bs);
+  HIP_TRY(hipGetLastError());
+  if (fp4) {
+    hipLaunchKernelGGL(k_pack_e8m0, dim3(grid), dim3(256), 0, st, static_cast<const uint8_t*>(src_scales),
+                       static_cast<uint8_t*>(dst_scales), rows, K / 128);
+    HIP_TRY(hipGetLastError());
+  }
+  return MOE_OK;
 }
 
 const char* moe_status_string(moe_status s) {

@@ -15,11 +15,27 @@
 namespace moe {
 
 constexpr int kPermBlock = 256;      // tokens per histogram / scatter block
-constexpr int kTileRows = 128;       // rows per GEMM tile
+constexpr int kMinTileRows = 64;     // smallest full GEMM row tile (bounds the tile count)
 
-struct Tile {                        // one GEMM row tile: rows [r0, r0 + rows) of expert e
-  int e, r0, rows, pad;
+// One GEMM row tile: rows [r0, r0 + rows) of expert e, computed by the GEMM
+// variant with `rs` 16-row subtiles (the smallest of 1, 4 or the full tile
+// that covers `rows`).  The tiles of one expert are g0 .. g0 + gn - 1.
+struct Tile {
+  int e, r0, rows, rs, g0, gn;
 };
+
+// Work item i of a GEMM over (tile, N block) pairs with nnb N blocks.  Items
+// are ordered expert by expert, then by N block, then by the expert's tiles,
+// so that the items reading the same weight slab are adjacent in the queue
+// and run at the same time (the later reads hit the caches).
+DEV void gemm_item_of(const Tile* tiles, int nnb, int i, int* t, int* nb) {
+  const Tile& x = tiles[i / nnb];
+  const int local = i - x.g0 * nnb;
+  *nb = local / x.gn;
+  *t = x.g0 + local % x.gn;
+}
+
+DEV int tile_variant(int rows, int full_rs) { return rows <= 16 ? 1 : rows <= 64 ? 4 : full_rs; }
 
 // Expert id of entry i, clamped into [0, E): ids produced by the router are
 // always in range; given ids outside it are treated as E-1 so that every
@@ -39,17 +55,46 @@ DEV void perm_count_block(const int32_t* ids, int T, int k, int E, int b, int32_
   __syncthreads();
 }
 
+// Number of expert classes: expert e belongs to class e % kXcds, and the
+// tiles of class x are worked on first by the workgroups of XCD x, so that
+// sibling tiles of one expert (which read the same weights) share an L2.
+constexpr int kXcds = 8;
+
+DEV int class_pos(int e, int E8) { return (e % kXcds) * E8 + e / kXcds; }
+
+// In-place exclusive scan of a[0..n) in LDS by the whole workgroup; returns
+// the total.  Ends with a barrier.
+DEV int lds_exclusive_scan(int* a, int n, int* scratch) {
+  const int per = (n + blockDim.x - 1) / blockDim.x;
+  const int lo = min(n, (int)threadIdx.x * per), hi = min(n, lo + per);
+  int sum = 0;
+  for (int i = lo; i < hi; ++i) sum += a[i];
+  int tot;
+  int run = block_inclusive_scan(sum, scratch, &tot) - sum;
+  for (int i = lo; i < hi; ++i) {
+    const int c = a[i];
+    a[i] = run;
+    run += c;
+  }
+  __syncthreads();
+  return tot;
+}
+
 // Exclusive scans over blocks and experts, and the GEMM tile list.
 //   base[b][e]   = first permuted row of expert e's rows from block b
 //   offsets[e]   = first permuted row of expert e (offsets[E] = T*k)
-//   tiles        = ceil(count_e / 128) tiles per expert, in expert order
-//   meta[0]      = number of tiles
-// LDS: 2*E + 64 ints.  Any workgroup size that is a multiple of 64.
-DEV void perm_scan(const int32_t* blockcnt, int nblk, int E, int32_t* base, int32_t* offsets,
+//   tiles        = ceil(count_e / tile_rows) tiles per expert, ordered by
+//                  expert class, then expert (each expert's tiles adjacent)
+//   meta[0]      = number of tiles; meta[1 + x] = first tile of class x
+//                  (x = 0 .. kXcds, the last entry equal to meta[0])
+// LDS: (2*E + 8 + 64) ints.  Any workgroup size that is a multiple of 64.
+DEV void perm_scan(const int32_t* blockcnt, int nblk, int E, int tile_rows, int32_t* base, int32_t* offsets,
                    Tile* tiles, int32_t* meta, int* lds) {
-  int* cnt = lds;
-  int* toff = lds + E;
-  int* scratch = lds + 2 * E;
+  const int E8 = (E + kXcds - 1) / kXcds;
+  int* cnt = lds;                   // [E] rows per expert, then expert offsets
+  int* tcl = lds + E;               // [kXcds * E8] tiles per expert in class order, then first tiles
+  int* scratch = tcl + kXcds * E8;  // [64]
+  for (int i = threadIdx.x; i < kXcds * E8; i += blockDim.x) tcl[i] = 0;
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
     int run = 0;
     for (int b = 0; b < nblk; ++b) {
@@ -60,37 +105,26 @@ DEV void perm_scan(const int32_t* blockcnt, int nblk, int E, int32_t* base, int3
     cnt[e] = run;
   }
   __syncthreads();
-  // each thread scans a contiguous run of experts, then a workgroup scan
-  const int per = (E + blockDim.x - 1) / blockDim.x;
-  const int e_lo = min(E, (int)threadIdx.x * per), e_hi = min(E, e_lo + per);
-  int rows = 0, ntile = 0;
-  for (int e = e_lo; e < e_hi; ++e) {
-    rows += cnt[e];
-    ntile += (cnt[e] + kTileRows - 1) / kTileRows;
-  }
-  int tot_rows, tot_tiles;
-  int rows_incl = block_inclusive_scan(rows, scratch, &tot_rows);
-  int tiles_incl = block_inclusive_scan(ntile, scratch, &tot_tiles);
-  int r = rows_incl - rows, tl = tiles_incl - ntile;
-  for (int e = e_lo; e < e_hi; ++e) {
-    const int c = cnt[e];
-    cnt[e] = r;              // now the expert offset
-    toff[e] = tl;
-    r += c;
-    tl += (c + kTileRows - 1) / kTileRows;
-  }
+  for (int e = threadIdx.x; e < E; e += blockDim.x) tcl[class_pos(e, E8)] = (cnt[e] + tile_rows - 1) / tile_rows;
   __syncthreads();
+  const int tot_rows = lds_exclusive_scan(cnt, E, scratch);
+  const int tot_tiles = lds_exclusive_scan(tcl, kXcds * E8, scratch);
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
     const int off = cnt[e];
     const int c = ((e + 1 < E) ? cnt[e + 1] : tot_rows) - off;
     offsets[e] = off;
     for (int b = 0; b < nblk; ++b) base[(size_t)b * E + e] += off;
-    int t = toff[e];
-    for (int r0 = 0; r0 < c; r0 += kTileRows, ++t) tiles[t] = Tile{e, off + r0, min(kTileRows, c - r0), 0};
+    const int g0 = tcl[class_pos(e, E8)], gn = (c + tile_rows - 1) / tile_rows;
+    for (int i = 0; i < gn; ++i) {
+      const int rows = min(tile_rows, c - i * tile_rows);
+      tiles[g0 + i] = Tile{e, off + i * tile_rows, rows, tile_variant(rows, tile_rows / 16), g0, gn};
+    }
   }
   if (threadIdx.x == 0) {
     offsets[E] = tot_rows;
     meta[0] = tot_tiles;
+    for (int x = 0; x < kXcds; ++x) meta[1 + x] = tcl[x * E8];
+    meta[1 + kXcds] = tot_tiles;
   }
   __syncthreads();
 }

@@ -6,6 +6,28 @@ import torch
 from . import lib
 
 
+def pack_weights(inputs: dict, top_k: int = 1, stream=None) -> dict:
+    """Copy of `inputs` whose expert weights (and FP4 scales) are in the
+    MFMA-tiled layout moe_forward reads (moe_pack_weights).  The input dict
+    is not modified; the result carries "weights_packed": True."""
+    if inputs.get("weights_packed"):
+        return inputs
+    desc = desc_from_inputs(inputs, top_k)
+    fp4 = desc.weight_dtype == lib.MOE_DTYPE_FP4_E2M1
+    out = dict(inputs)
+    for which, w, sc in ((lib.MOE_WEIGHTS_GATE_UP, "w_gate_up", "w_gate_up_scales"),
+                         (lib.MOE_WEIGHTS_DOWN, "w_down", "w_down_scales")):
+        dst = torch.empty_like(inputs[w])
+        dst_sc = torch.empty_like(inputs[sc]) if fp4 else None
+        lib.moe_pack_weights(desc, which, inputs[w].contiguous(), inputs[sc].contiguous() if fp4 else None,
+                             dst, dst_sc, stream)
+        out[w] = dst
+        if fp4:
+            out[sc] = dst_sc
+    out["weights_packed"] = True
+    return out
+
+
 def desc_from_inputs(inputs: dict, top_k: int, mode: str = "mega", flags: int = 0, I=None) -> lib.MoeDesc:
     x = inputs["x"]
     T, H = x.shape
@@ -38,9 +60,12 @@ class Workspace:
 
 def forward(inputs: dict, top_k: int, mode: str = "mega", workspace: Workspace = None,
             routing=None, want_perm: bool = True, stream=None, out=None) -> dict:
-    """Run the layer.  routing=(topk_ids, topk_weights) feeds given routing
+    """Run the layer on inputs whose weights went through pack_weights().
+    routing=(topk_ids, topk_weights) feeds given routing
     (MOE_FLAG_ROUTING_GIVEN).  Returns dict(y, topk_ids, topk_weights,
     expert_offsets, perm)."""
+    if not inputs.get("weights_packed"):
+        raise ValueError("forward() needs MFMA-tiled weights: pass the inputs through pack_weights() first")
     flags = lib.MOE_FLAG_ROUTING_GIVEN if routing is not None else 0
     desc = desc_from_inputs(inputs, top_k, mode, flags)
     dev = inputs["x"].device

@@ -40,6 +40,9 @@ MOE_MODE_MEGA = 0
 MOE_MODE_SEPARATE = 1
 # flags
 MOE_FLAG_ROUTING_GIVEN = 1
+# moe_pack_weights `which`
+MOE_WEIGHTS_GATE_UP = 0
+MOE_WEIGHTS_DOWN = 1
 
 DTYPES = {"bf16": MOE_DTYPE_BF16, "fp8": MOE_DTYPE_FP8_E4M3, "fp4": MOE_DTYPE_FP4_E2M1}
 MODES = {"mega": MOE_MODE_MEGA, "separate": MOE_MODE_SEPARATE}
@@ -81,6 +84,8 @@ _lib.moe_route.restype = ctypes.c_int
 _lib.moe_route.argtypes = [ctypes.POINTER(MoeDesc)] + [_P] * 7 + [_P, ctypes.c_size_t, _P]
 _lib.moe_permute.restype = ctypes.c_int
 _lib.moe_permute.argtypes = [ctypes.POINTER(MoeDesc)] + [_P] * 4 + [_P, ctypes.c_size_t, _P]
+_lib.moe_pack_weights.restype = ctypes.c_int
+_lib.moe_pack_weights.argtypes = [ctypes.POINTER(MoeDesc), ctypes.c_int32] + [_P] * 4 + [_P]
 _lib.moe_status_string.restype = ctypes.c_char_p
 _lib.moe_status_string.argtypes = [ctypes.c_int]
 _lib.moe_last_error.restype = ctypes.c_char_p
@@ -181,8 +186,14 @@ def moe_permute(desc, topk_ids, expert_offsets, perm, row_of, workspace, stream=
     _check(st, "moe_permute")
 
 
+def moe_pack_weights(desc, which, src, src_scales, dst, dst_scales, stream=None):
+    st = _lib.moe_pack_weights(ctypes.byref(desc), which, _ptr(src), _ptr(src_scales), _ptr(dst), _ptr(dst_scales),
+                               _stream(stream))
+    _check(st, "moe_pack_weights")
+
+
 def exported_symbols():
     """Names of the C entry points this binding wraps (for ABI checks)."""
     return ["moe_abi_version", "moe_workspace_size", "moe_route_workspace_size",
             "moe_permute_workspace_size", "moe_get_workspace_regions", "moe_validate", "moe_forward", "moe_route",
-            "moe_permute", "moe_status_string", "moe_last_error"]
+            "moe_permute", "moe_pack_weights", "moe_status_string", "moe_last_error"]

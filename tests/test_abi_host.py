@@ -110,3 +110,21 @@ def test_single_hip_runtime_in_process():
     maps = open("/proc/self/maps").read().splitlines()
     hip = sorted(set(l.split()[-1] for l in maps if "libamdhip64" in l))
     assert len(hip) == 1, hip
+
+
+def test_pack_weights_rejects_bad_arguments_without_device():
+    """Argument checks of moe_pack_weights run on the host before any device
+    call: bad `which`, NULL pointers, scale pointers for non-FP4 weights,
+    overlapping buffers."""
+    d = lib.make_desc(64, 256, 4, 256, 2, "fp8", "fp8")
+    st = lib._lib.moe_pack_weights
+    import ctypes
+    ok_src, ok_dst = 0x10000, 0x8000000
+    assert st(ctypes.byref(d), 7, ok_src, None, ok_dst, None, None) == lib.MOE_ERR_INVALID_ARGUMENT
+    assert st(ctypes.byref(d), lib.MOE_WEIGHTS_DOWN, None, None, ok_dst, None, None) == lib.MOE_ERR_INVALID_ARGUMENT
+    assert st(ctypes.byref(d), lib.MOE_WEIGHTS_DOWN, ok_src, ok_src, ok_dst, ok_dst, None) == lib.MOE_ERR_INVALID_ARGUMENT
+    assert st(ctypes.byref(d), lib.MOE_WEIGHTS_DOWN, ok_src, None, ok_src + 16, None, None) == lib.MOE_ERR_INVALID_ARGUMENT
+    d4 = lib.make_desc(64, 256, 4, 256, 2, "fp8", "fp4")
+    assert st(ctypes.byref(d4), lib.MOE_WEIGHTS_GATE_UP, ok_src, None, ok_dst, None, None) == lib.MOE_ERR_INVALID_ARGUMENT
+    assert st(ctypes.byref(d4), lib.MOE_WEIGHTS_GATE_UP, ok_src + 8, 0x20000, ok_dst, 0x9000000, None) == \
+        lib.MOE_ERR_INVALID_ARGUMENT   # misaligned

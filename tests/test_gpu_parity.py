@@ -121,7 +121,7 @@ SMALL = [
 def _layer_check(L, cfg, mode, inp=None, routing=None, seed=0):
     if inp is None:
         inp = gen.make_inputs(cfg, seed=seed)
-    out = L.forward(to_dev(inp), cfg.k, mode=mode,
+    out = L.forward(L.pack_weights(to_dev(inp)), cfg.k, mode=mode,
                     routing=None if routing is None else tuple(torch.as_tensor(r).cuda() for r in routing))
     torch.cuda.synchronize()
     assert int(out["workspace"][:4].view(torch.int32).item()) == 0, "device watchdog fired"
@@ -150,7 +150,7 @@ def test_layer_matches_oracle(L, cfg, mode):
 
 @pytest.mark.parametrize("cfg", SMALL[:3], ids=lambda c: c.name)
 def test_mega_equals_separate_bitwise_and_deterministic(L, cfg):
-    inp = to_dev(gen.make_inputs(cfg, seed=4))
+    inp = L.pack_weights(to_dev(gen.make_inputs(cfg, seed=4)))
     a = L.forward(inp, cfg.k, mode="separate")
     b = L.forward(inp, cfg.k, mode="mega")
     c = L.forward(inp, cfg.k, mode="mega")
@@ -168,7 +168,7 @@ def test_given_routing_skew_and_empty_experts(L, mode):
     inp = gen.make_inputs(cfg, seed=5)
     ids = np.tile(np.array([[5, 0]], dtype=np.int32), (333, 1))
     w = np.tile(np.array([[0.75, 0.25]], dtype=np.float32), (333, 1))
-    out = L.forward(to_dev(inp), 2, mode=mode, routing=(torch.tensor(ids), torch.tensor(w)))
+    out = L.forward(L.pack_weights(to_dev(inp)), 2, mode=mode, routing=(torch.tensor(ids), torch.tensor(w)))
     torch.cuda.synchronize()
     spec = gen.spec_of(cfg)
     ov = gen.oracle_view(inp)
@@ -192,7 +192,7 @@ def test_intermediate_matches_oracle(L, cfg):
     the device's code must be one of the two neighbours); scales agree to
     1e-5.  BF16 layers: within one BF16 rounding of the oracle."""
     inp = gen.make_inputs(cfg, seed=6)
-    out = L.forward(to_dev(inp), cfg.k, mode="separate")
+    out = L.forward(L.pack_weights(to_dev(inp)), cfg.k, mode="separate")
     torch.cuda.synchronize()
     spec = gen.spec_of(cfg)
     ov = gen.oracle_view(inp)
@@ -228,3 +228,43 @@ def test_intermediate_matches_oracle(L, cfg):
         n_tot += mis.size
     if cfg.act == "fp8":
         assert n_mis <= 0.01 * n_tot
+
+
+# ------------------------------------------------------------ weight layout
+def _tiled_reference(w: np.ndarray, bs: int) -> np.ndarray:
+    """The MFMA-tiled layout of moe_layer.h written out with numpy: w is the
+    row-major [E][N][K-bytes] byte matrix; block (t, s) of BS/64 pieces of
+    1 KB, byte 16*l + j of piece p = row 16t + l%16, byte BS*s + 64p +
+    16*(l//16) + j."""
+    E, N, KB = w.shape
+    nsteps, npieces = KB // bs, bs // 64
+    v = w.reshape(E, N // 16, 16, nsteps, npieces, 4, 16)      # e, t, row%16, s, p, l//16, j
+    v = v.transpose(0, 1, 3, 4, 5, 2, 6)                        # e, t, s, p, l//16, row%16, j
+    return np.ascontiguousarray(v).reshape(E, N, KB)
+
+
+def _tiled_scales_reference(sc: np.ndarray) -> np.ndarray:
+    """E8M0 scales [E][N][K/32] -> per (t, s) 64 bytes, byte l = row 16t +
+    l%16, group 4s + l//16."""
+    E, N, G = sc.shape
+    v = sc.reshape(E, N // 16, 16, G // 4, 4).transpose(0, 1, 3, 4, 2)
+    return np.ascontiguousarray(v).reshape(E, N, G)
+
+
+@pytest.mark.parametrize("weight", ["fp8", "fp4", "bf16"])
+def test_pack_weights_layout_bit_exact(L, weight):
+    act = "bf16" if weight == "bf16" else "fp8"
+    cfg = gen.LayerConfig("pack_" + weight, 8, 384, 3, 2, 256, act, weight)
+    inp = to_dev(gen.make_inputs(cfg, seed=9))
+    packed = L.pack_weights(inp)
+    torch.cuda.synchronize()
+    bs = {"fp8": 128, "fp4": 64, "bf16": 256}[weight]
+    for w, sc in (("w_gate_up", "w_gate_up_scales"), ("w_down", "w_down_scales")):
+        src = inp[w].cpu().contiguous().view(torch.uint8).numpy().reshape(cfg.E, inp[w].shape[1], -1)
+        got = packed[w].cpu().contiguous().view(torch.uint8).numpy().reshape(src.shape)
+        assert np.array_equal(got, _tiled_reference(src, bs)), w
+        if weight == "fp4":
+            s_src = inp[sc].cpu().numpy()
+            assert np.array_equal(packed[sc].cpu().numpy(), _tiled_scales_reference(s_src)), sc
+        elif weight == "fp8":
+            assert packed[sc] is inp[sc]
