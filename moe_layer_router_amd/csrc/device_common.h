@@ -170,19 +170,39 @@ typedef __attribute__((address_space(3))) void lds_void;
 DEV rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
 }
+// Cache policy of a buffer access (the instruction's cache-coherence bits):
+// 0 = default; kCoherent (sc1) = device-scope coherent.  The L2 of each XCD
+// is not coherent with the others: data that one workgroup writes and a
+// workgroup on another XCD reads inside the same kernel is written and read
+// with kCoherent (stores write through, loads do not use stale L2 lines), so
+// that no device-wide fence (which would write back or invalidate the whole
+// L2) is needed between them.
+constexpr int kCoherent = 16;
+
+template <int AUX = 0>
 DEV v4i buf_ld16(rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+  return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, AUX));
 }
+template <int AUX = 0>
 DEV float buf_ldf(rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0));
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, AUX));
+}
+template <int AUX = 0>
+DEV void buf_st16(rsrc_t r, uint32_t voff, const v4i& v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)voff, 0, AUX);
+}
+template <int AUX = 0>
+DEV void buf_stf(rsrc_t r, uint32_t voff, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, v), r, (int)voff, 0, AUX);
 }
 DEV uint32_t buf_ldu8(rsrc_t r, uint32_t voff, uint32_t soff) {
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, (int)voff, (int)soff, 0);
 }
 // 16 bytes per lane from the buffer straight into LDS: lane l's bytes land
 // at lds_base + 16*l (lds_base is wave-uniform).
+template <int AUX = 0>
 DEV void buf_ld16_lds(rsrc_t r, void* lds_base, uint32_t voff, uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 16, (int)voff, (int)soff, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 16, (int)voff, (int)soff, 0, AUX);
 }
 // Wait until at most n vector-memory operations of this wave are in flight
 // (other counters untouched).

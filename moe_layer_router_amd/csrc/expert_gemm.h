@@ -107,9 +107,17 @@ DEV int a_swz(int row, int c) {
 }
 
 // One work item: `RS` 16-row subtiles (rows [r0, r0+m), m <= 16*RS) of
-// expert e times one N block nb.  256 threads, one wave per SIMD.
-template <int AF, int WF, int STAGE, int RS>
-DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char* lds) {
+// expert e times one N block nb.  256 threads, one wave per SIMD.  With COH
+// the intermediate (written by stage 1, read by stage 2) and the staging
+// rows (written by stage 2) are accessed device-coherently (kCoherent), for
+// use inside the persistent kernel where producer and consumer items may run
+// on different XCDs.  `signal_prev` (may be NULL) is a counter to increment
+// once the stores of this workgroup's previous item have completed: the
+// prologue's barrier below waits for every older memory operation of each
+// wave, so the previous item is signalled without a wait of its own.
+template <int AF, int WF, int STAGE, int RS, int COH>
+DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char* lds, int32_t* signal_prev) {
+  constexpr int CP = COH ? kCoherent : 0;            // cache policy of cross-item data
   using L = GemmLds<AF>;
   static_assert(RS >= 1 && RS <= L::kMaxRs, "row subtiles");
   constexpr int AB = L::kABytes;                  // A bytes per row per step
@@ -200,7 +208,7 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
   // stage `slot` (= s % kAStages) receives A(s)
   auto dma_a = [&](int s, int slot, int j) __attribute__((always_inline)) {
     char* dst = lds + L::kA + slot * L::kASlot + w * 1024;
-    buf_ld16_lds(ars, dst + j * 4096, aoff[j], (uint32_t)s * 128 * ESZ);
+    buf_ld16_lds<STAGE == 2 ? CP : 0>(ars, dst + j * 4096, aoff[j], (uint32_t)s * 128 * ESZ);
   };
 
   // ---- per-row scales (FP8 activations): SC[slot][set] holds sA[row] *
@@ -214,7 +222,7 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
   const uint32_t saoff = (STAGE == 1) ? (uint32_t)ROWI[srow < R ? srow : 0] * (g.H / 128) * 4
                                       : (uint32_t)(r0 + srow) * (g.I / 128) * 4;
   auto load_scale = [&](int s) __attribute__((always_inline)) -> float {
-    return (AF == ACT_FP8) ? buf_ldf(sars, saoff, (uint32_t)s * 4) : 1.f;
+    return (AF == ACT_FP8) ? buf_ldf<STAGE == 2 ? CP : 0>(sars, saoff, (uint32_t)s * 4) : 1.f;
   };
   auto store_scale = [&](int s, int par, float sa) __attribute__((always_inline)) {   // par = s & 1
     if (AF != ACT_FP8) return;
@@ -426,6 +434,7 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
   load_b(NBUF - 2, bb[NBUF - 2]);
   store_scale(0, 0, sa0);
   barrier_vmcnt<NLOAD>();
+  if (signal_prev && tid == 0) __hip_atomic_fetch_add(signal_prev, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   // The loop body is UNR steps, a multiple of NBUF (B buffer rotation), of
   // 2 (scale parity) and of kAStages (A stage rotation), so every buffer
   // and LDS stage index in it is a compile-time constant; UNR > NBUF also
@@ -456,6 +465,10 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
   __syncthreads();
 
   // ---- epilogues (the A stages are reused as the output staging tile)
+  const uint32_t nrows = (uint32_t)(g.T * g.k);
+  const rsrc_t aqw = make_rsrc(g.aq, nrows * (uint32_t)g.I * ESZ);
+  const rsrc_t saw = make_rsrc(g.sa, nrows * (uint32_t)(g.I / 128) * 4);
+  const rsrc_t stw = make_rsrc(g.staging, nrows * (uint32_t)g.H * 2);
   if (STAGE == 1) {
     // a = SiLU(g) * u, written over the gate accumulators: av[rs][q] = acc[rs][q]
 #pragma unroll
@@ -504,9 +517,9 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
       __syncthreads();
       for (int q = tid; q < R * 8; q += kGemmThreads) {
         const int row = q >> 3, c = q & 7;
-        if (row < m) st16(g.aq + (size_t)(r0 + row) * g.I + c0 + c * 16, ld16(lds + L::kA + row * 128 + c * 16));
+        if (row < m) buf_st16<CP>(aqw, (uint32_t)(r0 + row) * g.I + c0 + c * 16, ld16(lds + L::kA + row * 128 + c * 16));
       }
-      if (tid < m) g.sa[(size_t)(r0 + tid) * (g.I / 128) + c0 / 128] = RSC[tid];
+      if (tid < m) buf_stf<CP>(saw, ((uint32_t)(r0 + tid) * (g.I / 128) + c0 / 128) * 4, RSC[tid]);
     } else {
       const uint32_t out_wr = opaque(L::kA + (4 * gq * 128 + 32 * w + c16) * 2);
 #pragma unroll
@@ -521,7 +534,7 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
       for (int q = tid; q < R * 16; q += kGemmThreads) {
         const int row = q >> 4, c = q & 15;
         if (row < m)
-          st16(g.aq + ((size_t)(r0 + row) * g.I + c0) * 2 + c * 16, ld16(lds + L::kA + row * 256 + c * 16));
+          buf_st16<CP>(aqw, ((uint32_t)(r0 + row) * g.I + c0) * 2 + c * 16, ld16(lds + L::kA + row * 256 + c * 16));
       }
     }
   } else {
@@ -547,35 +560,36 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
         const int rl = q >> 5, c = q & 31;
         const int row = CH * 16 * h + rl, col = n0 + c * 8;
         if (row < m && col < g.H)
-          st16(reinterpret_cast<uint8_t*>(g.staging) + ((size_t)ROWI[row] * g.H + col) * 2,
-               ld16(lds + L::kA + rl * 512 + c * 16));
+          buf_st16<CP>(stw, ((uint32_t)ROWI[row] * g.H + col) * 2, ld16(lds + L::kA + rl * 512 + c * 16));
       }
     }
   }
 }
 
 // Dispatch a tile to the GEMM variant with the tile's number of row subtiles.
-template <int AF, int WF, int STAGE>
-DEV void expert_gemm_item(const GemmArgs& g, const Tile& t, int nb, char* lds) {
+template <int AF, int WF, int STAGE, int COH>
+DEV void expert_gemm_item(const GemmArgs& g, const Tile& t, int nb, char* lds, int32_t* signal_prev = nullptr) {
   constexpr int FULL = GemmLds<AF>::kMaxRs;
   if (t.rs <= 1)
-    expert_gemm_tile<AF, WF, STAGE, 1>(g, t.e, t.r0, t.rows, nb, lds);
+    expert_gemm_tile<AF, WF, STAGE, 1, COH>(g, t.e, t.r0, t.rows, nb, lds, signal_prev);
   else if (t.rs <= 4)
-    expert_gemm_tile<AF, WF, STAGE, 4>(g, t.e, t.r0, t.rows, nb, lds);
+    expert_gemm_tile<AF, WF, STAGE, 4, COH>(g, t.e, t.r0, t.rows, nb, lds, signal_prev);
   else
-    expert_gemm_tile<AF, WF, STAGE, FULL>(g, t.e, t.r0, t.rows, nb, lds);
+    expert_gemm_tile<AF, WF, STAGE, FULL, COH>(g, t.e, t.r0, t.rows, nb, lds, signal_prev);
 }
 
 // y[t, n0:n1] = BF16( sum_j staging[t*k + j, n0:n1] ) for tokens [t0, t1),
 // fp32 sums in ascending j; 8 channels (16 bytes) per thread and step.
-DEV void combine_rows(const uint16_t* staging, uint16_t* y, int H, int k, int t0, int t1, int n0, int n1) {
+template <int COH>
+DEV void combine_rows(const uint16_t* staging, uint16_t* y, int T, int H, int k, int t0, int t1, int n0, int n1) {
+  const rsrc_t srs = make_rsrc(staging, (uint32_t)T * (uint32_t)k * (uint32_t)H * 2);
   const int cpt = (n1 - n0) / 8;
   const int total = (t1 - t0) * cpt;
   for (int idx = threadIdx.x; idx < total; idx += blockDim.x) {
     const int t = t0 + idx / cpt, c = n0 + (idx % cpt) * 8;
     float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int j = 0; j < k; ++j) {
-      const v4i v = ld16(reinterpret_cast<const uint8_t*>(staging) + ((size_t)(t * k + j) * H + c) * 2);
+      const v4i v = buf_ld16<COH ? kCoherent : 0>(srs, ((uint32_t)(t * k + j) * H + c) * 2, 0);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         s[2 * i] += bf16_to_f32((uint32_t)v[i] & 0xFFFFu);

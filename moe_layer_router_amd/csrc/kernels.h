@@ -30,7 +30,6 @@ struct Plan {
   int max_tiles;
   int tile_rows;               // rows of a full GEMM tile
   int nnb1, nnb2;              // N blocks of gate|up (128 channels) and down (256 columns)
-  int slab_group;              // down-GEMM N blocks processed per tile before moving on
   int nCT;                     // combine token chunks per N block
   // caller buffers
   const uint8_t* x; const float* x_scales; const uint16_t* wr; const float* bias;

@@ -62,7 +62,7 @@ k_gemm(GemmArgs g, const Tile* tiles, const int32_t* meta, int nnb, int32_t* que
     if (threadIdx.x == 0) s_item = pop_class_item(queues, s_first, nnb, &cls);
     int t, nb;
     gemm_item_of(tiles, nnb, i, &t, &nb);
-    expert_gemm_item<AF, WF, STAGE>(g, tiles[t], nb, lds);   // starts with a barrier
+    expert_gemm_item<AF, WF, STAGE, 0>(g, tiles[t], nb, lds, nullptr);   // starts with a barrier
     i = s_item;
   }
 }
@@ -99,7 +99,7 @@ __global__ void __launch_bounds__(256) k_pack_e8m0(const uint8_t* src, uint8_t* 
 
 __global__ void __launch_bounds__(256) k_combine(const uint16_t* staging, uint16_t* y, int T, int H, int k) {
   const int t0 = blockIdx.x * 16;
-  combine_rows(staging, y, H, k, t0, min(T, t0 + 16), 0, H);
+  combine_rows<0>(staging, y, T, H, k, t0, min(T, t0 + 16), 0, H);
 }
 
 // ------------------------------------------------------- persistent kernel
@@ -110,7 +110,7 @@ constexpr unsigned kSpinLimit = 1u << 22;
 // fence follows it: an acquire on every poll would invalidate the caches
 // each time, taking cached weights away from every workgroup on the XCD.
 // Returns false if the wait timed out or another workgroup reported a failure.
-DEV bool wait_counter(const int32_t* c, int target, int32_t* err, int* s_ok) {
+DEV bool wait_counter(const int32_t* c, int target, int32_t* err, int* s_ok, bool acquire = true) {
   if (threadIdx.x == 0) {
     int ok = 1;
     unsigned spins = 0;
@@ -123,13 +123,28 @@ DEV bool wait_counter(const int32_t* c, int target, int32_t* err, int* s_ok) {
         break;
       }
     }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    if (acquire) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     *s_ok = ok;
   }
   __syncthreads();
   const int ok = *s_ok;
   __syncthreads();
   return ok != 0;
+}
+
+// Publish this workgroup's coherent (kCoherent, write-through) stores, then
+// add 1 to each counter: each wave waits until its stores have completed,
+// the workgroup synchronises, and one thread increments.  No device-wide
+// fence: the data was written past the L2, and readers load it coherently,
+// so the relaxed counter is the only ordering needed.  (Used by the gate|up
+// and down items, whose outputs are read only through kCoherent accesses.)
+DEV void signal_coherent(int32_t* c0, int32_t* c1 = nullptr) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __hip_atomic_fetch_add(c0, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (c1) __hip_atomic_fetch_add(c1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 // Publish this workgroup's global writes, then add 1 to each counter.
@@ -153,16 +168,18 @@ DEV void signal_add(int32_t* c0, int32_t* c1 = nullptr) {
 //                 scan (offsets, block bases, tiles)    -> SCAN_FLAG
 //                 stable scatter of 256 tokens          -> SCATTER_DONE
 //   class queues: gate|up items (tile, 128 channels)    -> done1[tile]
-//   tail queue:   per group of down N blocks: down items (tile, N block)
-//                 -> done2[N block], then combine items (N block, 256 tokens)
-// Each phase of the persistent kernel is its own (non-inlined) function, so
+//   class queues: down items (tile, 256 columns)        -> done2[N block]
+//   tail queue:   combine items (N block, 256 tokens)
+// The short phases of the persistent kernel are non-inlined functions, so
 // that register allocation sees one phase at a time.  Each declares the
 // dynamic LDS array itself so that its accesses compile to LDS instructions.
 #define MEGA_LDS extern __shared__ __attribute__((aligned(16))) char lds[]
+// The GEMM items are inlined into the kernel: as a called function they
+// would save and restore the callee-saved VGPRs they use on every item.
 template <int AF, int WF, int STAGE>
-__device__ __noinline__ void mega_gemm_item(const Plan& p, Tile tl, int nb) {
+__device__ __forceinline__ void mega_gemm_item(const Plan& p, Tile tl, int nb, int32_t* signal_prev) {
   MEGA_LDS;
-  expert_gemm_item<AF, WF, STAGE>(gemm_args(p), tl, nb, lds);
+  expert_gemm_item<AF, WF, STAGE, 1>(gemm_args(p), tl, nb, lds, signal_prev);
 }
 __device__ __noinline__ void mega_router_item(const Plan& p, int tt, int et) {
   MEGA_LDS;
@@ -187,7 +204,8 @@ __device__ __noinline__ void mega_scatter_item(const Plan& p, int b) {
 }
 __device__ __noinline__ void mega_combine_item(const Plan& p, int nb, int c) {
   const int t0 = c * kCombineTokens;
-  combine_rows(p.staging, p.y, p.H, p.k, t0, min(p.T, t0 + kCombineTokens), nb * 256, min(p.H, nb * 256 + 256));
+  combine_rows<1>(p.staging, p.y, p.T, p.H, p.k, t0, min(p.T, t0 + kCombineTokens), nb * 256,
+                  min(p.H, nb * 256 + 256));
 }
 
 template <int AF, int WF>
@@ -242,6 +260,7 @@ k_mega(Plan p) {
   __syncthreads();
   const int ntiles = s_first[kXcds];
   int cls = blockIdx.x % kXcds;
+  int32_t* pending = nullptr;              // counter of the previous item, not yet signalled
   if (tid == 0) s_q = pop_class_item(p.ctr + CTR_Q1, s_first, p.nnb1, &cls);
   __syncthreads();
   for (int i = s_q; i >= 0;) {
@@ -249,43 +268,43 @@ k_mega(Plan p) {
     if (tid == 0) s_q = pop_class_item(p.ctr + CTR_Q1, s_first, p.nnb1, &cls);
     int t, nb;
     gemm_item_of(p.tiles, p.nnb1, i, &t, &nb);
-    mega_gemm_item<AF, WF, 1>(p, p.tiles[t], nb);
-    signal_add(&p.done1[t], &p.ctr[CTR_G1_DONE]);
+    mega_gemm_item<AF, WF, 1>(p, p.tiles[t], nb, pending);
+    pending = &p.done1[t];                 // signalled once its stores have completed
     i = s_q;
   }
+  if (pending) signal_coherent(pending);
+  pending = nullptr;
 
-  // 3. down items and combine items, per group of N blocks, from the tail
-  // queue (all gate|up items have been claimed before any of these)
+  // 3. down items from the per-class queues (all gate|up items have been
+  // claimed); an item waits for the gate|up items of its tile.  Relaxed
+  // waits suffice: the intermediate is read with coherent loads.
+  cls = blockIdx.x % kXcds;
+  __syncthreads();
+  if (tid == 0) s_q = pop_class_item(p.ctr + CTR_Q2, s_first, p.nnb2, &cls);
+  __syncthreads();
+  for (int i = s_q; i >= 0;) {
+    __syncthreads();
+    if (tid == 0) s_q = pop_class_item(p.ctr + CTR_Q2, s_first, p.nnb2, &cls);
+    int t, nb;
+    gemm_item_of(p.tiles, p.nnb2, i, &t, &nb);
+    if (!wait_counter(&p.done1[t], p.nnb1, p.err, &s_ok, false)) return;
+    mega_gemm_item<AF, WF, 2>(p, p.tiles[t], nb, pending);
+    pending = &p.done2[nb];
+    i = s_q;
+  }
+  if (pending) signal_coherent(pending);
+
+  // 4. combine items (N block, 256 tokens) once every down item of the N
+  // block is done (all down items have been claimed)
   for (;;) {
     __syncthreads();
     if (tid == 0) s_q = __hip_atomic_fetch_add(&p.ctr[CTR_QUEUE2], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
-    int i = s_q;
-    bool found = false;
-    for (int g0 = 0; g0 < p.nnb2; g0 += p.slab_group) {
-      const int ns = min(p.slab_group, p.nnb2 - g0);
-      const int n2 = ntiles * ns, nc = ns * p.nCT;
-      if (i < n2) {
-        int t, nbl;
-        gemm_item_of(p.tiles, ns, i, &t, &nbl);
-        const int nb = g0 + nbl;
-        if (!wait_counter(&p.done1[t], p.nnb1, p.err, &s_ok)) return;
-        mega_gemm_item<AF, WF, 2>(p, p.tiles[t], nb);
-        signal_add(&p.done2[nb]);
-        found = true;
-        break;
-      }
-      i -= n2;
-      if (i < nc) {
-        const int nb = g0 + i / p.nCT, c = i % p.nCT;
-        if (!wait_counter(&p.done2[nb], ntiles, p.err, &s_ok)) return;
-        mega_combine_item(p, nb, c);
-        found = true;
-        break;
-      }
-      i -= nc;
-    }
-    if (!found) break;
+    const int i = s_q;
+    if (i >= p.nnb2 * p.nCT) break;
+    const int nb = i / p.nCT, c = i % p.nCT;
+    if (!wait_counter(&p.done2[nb], ntiles, p.err, &s_ok, false)) return;
+    mega_combine_item(p, nb, c);
   }
 }
 
@@ -436,7 +455,6 @@ moe_status fill_plan(const moe_desc* d, const Layout& L, char* ws, Plan* P) {
   p.nblk = L.nblk; p.nT64 = L.nT64; p.nE64 = L.nE64; p.max_tiles = L.max_tiles;
   p.tile_rows = p.act_fp8 ? GemmLds<ACT_FP8>::kRows : GemmLds<ACT_BF16>::kRows;
   p.nnb1 = L.nnb1; p.nnb2 = L.nnb2;
-  p.slab_group = 4;
   p.nCT = (d->T + kCombineTokens - 1) / kCombineTokens;
   p.err = reinterpret_cast<int32_t*>(ws + L.err);
   p.ctr = reinterpret_cast<int32_t*>(ws + L.ctr);
