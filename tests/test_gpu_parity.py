@@ -115,6 +115,10 @@ SMALL = [
     gen.CONFIGS["tiny_bf16"],
     gen.LayerConfig("s_multitile", 600, 384, 4, 2, 384, "fp8", "fp8"),     # >128 rows per expert, H % 256 != 0
     gen.LayerConfig("s_zipf_fp4", 256, 1024, 64, 8, 256, "fp8", "fp4", zipf=1.1),
+    gen.LayerConfig("s_one_token", 1, 256, 4, 2, 128, "fp8", "fp8"),          # T = 1
+    gen.LayerConfig("s_max_h", 40, 16384, 2, 1, 128, "fp8", "fp8"),           # largest H
+    gen.LayerConfig("s_max_i", 40, 128, 2, 2, 16384, "fp8", "fp4"),           # largest I
+    gen.LayerConfig("s_k_eq_e", 50, 256, 4, 4, 128, "bf16", "bf16"),          # every expert for every token
 ]
 
 
