@@ -12,8 +12,10 @@ bounded sample of the same workload timed on the host cores.
 """
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -21,6 +23,39 @@ import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def source_digest() -> str:
+    """sha256 over the HIP sources, the C header and the build flags: a
+    traffic figure taken from hardware counters is valid only for the kernel
+    built from exactly these."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "moe_layer_router_amd", "csrc")
+    files = sorted(os.path.join(csrc, f) for f in os.listdir(csrc) if f.endswith((".h", ".hip")))
+    files += [os.path.join(ROOT, "include", "moe_layer.h"), os.path.join(ROOT, "moe_layer_router_amd", "build.py")]
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` on `workload` from the committed
+    counter summary (FETCH_SIZE and WRITE_SIZE, calibrated against a copy of
+    known size), or None when there is none or it was taken on other
+    sources."""
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"```json\n(.*?)\n```", open(path).read(), re.S)
+    if not m:
+        return None
+    d = json.loads(m.group(1))
+    if d.get("source_sha256") != source_digest():
+        return None
+    return d.get("traffic_bytes")
 
 # MI355X published peaks
 PEAK_HBM_GBS = 8000.0
@@ -113,7 +148,10 @@ def main():
     ap.add_argument("--mode", default="mega", choices=["mega", "separate"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-experts", type=int, default=4)
+    ap.add_argument("--cpu-experts", type=int, default=48)
+    ap.add_argument("--no-ablation", action="store_true", help="skip timing the other mode")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run one device copy of 1 GiB (a counter calibration point for profiling runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): the layer is measured on a "
@@ -132,42 +170,58 @@ def main():
     # weights go into the MFMA-tiled layout once, as at model load time
     inputs = layer.pack_weights(raw)
     torch.cuda.synchronize()
+    if args.calib_copy:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
     ws = layer.Workspace(dev)
     stream = torch.cuda.current_stream()
-    out = layer.forward(inputs, cfg.k, mode=args.mode, workspace=ws)
-    torch.cuda.synchronize()
-    if int(out["workspace"][:4].view(torch.int32).item()) != 0:
-        raise RuntimeError("device watchdog fired")
-    counts = np.diff(out["expert_offsets"].cpu().numpy())
-    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        layer.forward(inputs, cfg.k, mode=args.mode, workspace=ws, out=out)
-    torch.cuda.synchronize()
 
-    # timed region: K back-to-back layer calls on the current stream; one
-    # event pair per call gives the persistent kernel's duration as well
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    t_begin = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_begin.record(stream)
-    for i in range(args.steps):
-        starts[i].record(stream)
-        layer.forward(inputs, cfg.k, mode=args.mode, workspace=ws, out=out)
-        ends[i].record(stream)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t_begin.elapsed_time(t_end)
-    per = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
-    ms = total_ms / args.steps
-    if not torch.isfinite(out["y"].float()).all():
-        raise RuntimeError("non-finite output")
+    def timed(mode):
+        """Warm-up, then K back-to-back layer calls on the current stream,
+        timed as a whole and per call (one event pair per call: the counter
+        clearing kernel (a few microseconds) and the layer's kernels)."""
+        out = layer.forward(inputs, cfg.k, mode=mode, workspace=ws)
+        torch.cuda.synchronize()
+        if int(out["workspace"][:4].view(torch.int32).item()) != 0:
+            raise RuntimeError("device watchdog fired")
+        print(f"[bench] {mode}: warmup {args.warmup}", file=sys.stderr, flush=True)
+        for _ in range(args.warmup):
+            layer.forward(inputs, cfg.k, mode=mode, workspace=ws, out=out)
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        t_begin = torch.cuda.Event(enable_timing=True)
+        t_end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t_begin.record(stream)
+        for i in range(args.steps):
+            starts[i].record(stream)
+            layer.forward(inputs, cfg.k, mode=mode, workspace=ws, out=out)
+            ends[i].record(stream)
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        print(f"[bench] {mode}: timed {args.steps} steps", file=sys.stderr, flush=True)
+        if not torch.isfinite(out["y"].float()).all():
+            raise RuntimeError("non-finite output")
+        per = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+        return out, t_begin.elapsed_time(t_end) / args.steps, per
+
+    out, ms, per = timed(args.mode)
+    counts = np.diff(out["expert_offsets"].cpu().numpy())
+    other = "separate" if args.mode == "mega" else "mega"
+    ablation = None
+    if not args.no_ablation:
+        _, ms_other, _ = timed(other)
+        ablation = {"mode": other, "ms_per_step": round(ms_other, 4), "tokens_per_s": round(cfg.T / (ms_other / 1e3), 1)}
 
     f_exp, f_router, nbytes, active = algorithmic_cost(cfg, inputs, counts)
     t_launch = float(per.mean()) / 1e3
     roof, t_mfma, t_hbm = roofline(cfg, f_exp, f_router, nbytes, t_launch)
-    roof["traffic"] = None
+    kernel = "k_mega" if args.mode == "mega" else "layer_separate"
+    roof["kernel"] = kernel
+    roof["traffic"] = measured_traffic(kernel, cfg.name)
     tflops = (f_exp + f_router) / (ms / 1e3) / 1e12
     exp_fmt = cfg.weight if cfg.weight == "bf16" else "fp8"
     result = {
@@ -195,6 +249,7 @@ def main():
                            "t_mfma_ms": round(t_mfma * 1e3, 4), "t_hbm_ms": round(t_hbm * 1e3, 4),
                            "kernel_ms": round(t_launch * 1e3, 4),
                            "roofline_frac": round(max(t_mfma, t_hbm) / t_launch, 4)},
+        "ablation": ablation,
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on a bounded sample (host cores)", file=sys.stderr, flush=True)
