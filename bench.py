@@ -148,7 +148,7 @@ def main():
     ap.add_argument("--mode", default="mega", choices=["mega", "separate"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-experts", type=int, default=48)
+    ap.add_argument("--cpu-experts", type=int, default=64, choices=range(1, 1 << 16), metavar="N")
     ap.add_argument("--no-ablation", action="store_true", help="skip timing the other mode")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one device copy of 1 GiB (a counter calibration point for profiling runs)")

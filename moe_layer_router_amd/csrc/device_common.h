@@ -93,11 +93,18 @@ DEV v4f mfma_bf16(const v8bf& a, const v8bf& b, const v4f& c) {
 DEV v8bf as_v8bf(const v4i& v) { return __builtin_bit_cast(v8bf, v); }
 
 // -------------------------------------------------------- wave reductions
-DEV float wave_max_xor16(float v) {           // max over the 16 lanes sharing l/16
-  v = fmaxf(v, __shfl_xor(v, 1));
-  v = fmaxf(v, __shfl_xor(v, 2));
-  v = fmaxf(v, __shfl_xor(v, 4));
-  v = fmaxf(v, __shfl_xor(v, 8));
+// Max over the 16 lanes of a DPP row (the lanes sharing l/16), returned to
+// every lane of the row.  Four DPP moves (swap neighbours, swap pairs, mirror
+// halves of 8, mirror the row) instead of cross-lane LDS permutes.
+template <int CTRL>
+DEV float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+DEV float row_max16(float v) {
+  v = fmaxf(v, dpp_mov<0xB1>(v));    // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_mov<0x4E>(v));    // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_mov<0x141>(v));   // row_half_mirror
+  v = fmaxf(v, dpp_mov<0x140>(v));   // row_mirror
   return v;
 }
 

@@ -478,7 +478,7 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const float gv = acc[rs][q][v], uv = acc[rs][2 + q][v];
-          acc[rs][q][v] = gv / (1.0f + __expf(-gv)) * uv;
+          acc[rs][q][v] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
         }
     }
     auto av = [&](int rs, int q, int v) __attribute__((always_inline)) { return acc[rs][q][v]; };
@@ -490,7 +490,7 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           float mx = fmaxf(fabsf(av(rs, 0, v)), fabsf(av(rs, 1, v)));
-          mx = wave_max_xor16(mx);
+          mx = row_max16(mx);
           if (c16 == 0) lds_st(lds, amax_wr + (rs * 16 + v) * 4, mx);
         }
       __syncthreads();
@@ -504,43 +504,55 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
       }
       __syncthreads();
       const uint32_t rinv_rd = opaque(L::kRinv + 16 * gq);
-      const uint32_t out_wr = opaque(L::kA + 4 * gq * 128 + 32 * w + c16);
+      // Staging rows hold their 16-byte chunks permuted: chunk c of row r at
+      // c ^ ((r >> 2) & 3), so that the four row groups of one byte write
+      // (rows 4g + v, g = l/16) fall in different LDS banks.
+      const uint32_t wr0 = opaque(L::kA + 4 * gq * 128 + 16 * ((2 * w) ^ gq) + c16);
+      const uint32_t wr1 = opaque(L::kA + 4 * gq * 128 + 16 * ((2 * w + 1) ^ gq) + c16);
 #pragma unroll
       for (int rs = 0; rs < RS; ++rs)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const float inv = lds_ld<float>(lds, rinv_rd + (rs * 16 + v) * 4);
-          const uint32_t o = out_wr + (rs * 16 + v) * 128;
-          lds_st(lds, o, (uint8_t)f32_to_e4m3(av(rs, 0, v) * inv));
-          lds_st(lds, o + 16, (uint8_t)f32_to_e4m3(av(rs, 1, v) * inv));
+          lds_st(lds, wr0 + (rs * 16 + v) * 128, (uint8_t)f32_to_e4m3(av(rs, 0, v) * inv));
+          lds_st(lds, wr1 + (rs * 16 + v) * 128, (uint8_t)f32_to_e4m3(av(rs, 1, v) * inv));
         }
       __syncthreads();
       for (int q = tid; q < R * 8; q += kGemmThreads) {
         const int row = q >> 3, c = q & 7;
-        if (row < m) buf_st16<CP>(aqw, (uint32_t)(r0 + row) * g.I + c0 + c * 16, ld16(lds + L::kA + row * 128 + c * 16));
+        if (row < m)
+          buf_st16<CP>(aqw, (uint32_t)(r0 + row) * g.I + c0 + c * 16,
+                       ld16(lds + L::kA + row * 128 + (c ^ ((row >> 2) & 3)) * 16));
       }
       if (tid < m) buf_stf<CP>(saw, ((uint32_t)(r0 + tid) * (g.I / 128) + c0 / 128) * 4, RSC[tid]);
     } else {
-      const uint32_t out_wr = opaque(L::kA + (4 * gq * 128 + 32 * w + c16) * 2);
+      // chunk c of staging row r at c ^ (((r >> 2) & 3) << 1) (bank spread)
+      const uint32_t lo = 2 * (c16 & 7), hc = c16 >> 3;
+      const uint32_t wr0 = opaque(L::kA + 4 * gq * 256 + 16 * ((4 * w + hc) ^ (2 * gq)) + lo);
+      const uint32_t wr1 = opaque(L::kA + 4 * gq * 256 + 16 * ((4 * w + 2 + hc) ^ (2 * gq)) + lo);
 #pragma unroll
       for (int rs = 0; rs < RS; ++rs)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const uint32_t o = out_wr + (rs * 16 + v) * 256;
-          lds_st(lds, o, (uint16_t)f32_to_bf16_rne(av(rs, 0, v)));
-          lds_st(lds, o + 32, (uint16_t)f32_to_bf16_rne(av(rs, 1, v)));
+          lds_st(lds, wr0 + (rs * 16 + v) * 256, (uint16_t)f32_to_bf16_rne(av(rs, 0, v)));
+          lds_st(lds, wr1 + (rs * 16 + v) * 256, (uint16_t)f32_to_bf16_rne(av(rs, 1, v)));
         }
       __syncthreads();
       for (int q = tid; q < R * 16; q += kGemmThreads) {
         const int row = q >> 4, c = q & 15;
         if (row < m)
-          buf_st16<CP>(aqw, ((uint32_t)(r0 + row) * g.I + c0) * 2 + c * 16, ld16(lds + L::kA + row * 256 + c * 16));
+          buf_st16<CP>(aqw, ((uint32_t)(r0 + row) * g.I + c0) * 2 + c * 16,
+                       ld16(lds + L::kA + row * 256 + (c ^ (((row >> 2) & 3) << 1)) * 16));
       }
     }
   } else {
     // chunks of CH row subtiles (at most 64 rows x 256 columns of BF16 = 32 KB)
     constexpr int CH = (RS < 4) ? RS : 4;
-    const uint32_t out_wr = opaque(L::kA + (4 * gq * 256 + 64 * w + c16) * 2);
+    // chunk c of staging row r at c ^ (((r >> 2) & 3) << 1) (bank spread)
+    uint32_t wrc[4];
+#pragma unroll
+    for (int cs = 0; cs < 4; ++cs)
+      wrc[cs] = opaque(L::kA + 4 * gq * 512 + 16 * ((8 * w + 2 * cs + (c16 >> 3)) ^ (2 * gq)) + 2 * (c16 & 7));
     const uint32_t roww_rd = opaque(L::kRowW + 16 * gq);
 #pragma unroll
     for (int h = 0; h < RS / CH; ++h) {
@@ -552,7 +564,7 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
           const float rw = lds_ld<float>(lds, roww_rd + (rs * 16 + v) * 4);
 #pragma unroll
           for (int cs = 0; cs < 4; ++cs)
-            lds_st(lds, out_wr + ((rs - CH * h) * 16 + v) * 512 + cs * 32,
+            lds_st(lds, wrc[cs] + ((rs - CH * h) * 16 + v) * 512,
                    (uint16_t)f32_to_bf16_rne(acc[rs][cs][v] * rw));
         }
       __syncthreads();
@@ -560,7 +572,8 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
         const int rl = q >> 5, c = q & 31;
         const int row = CH * 16 * h + rl, col = n0 + c * 8;
         if (row < m && col < g.H)
-          buf_st16<CP>(stw, ((uint32_t)ROWI[row] * g.H + col) * 2, ld16(lds + L::kA + rl * 512 + c * 16));
+          buf_st16<CP>(stw, ((uint32_t)ROWI[row] * g.H + col) * 2,
+                       ld16(lds + L::kA + rl * 512 + (c ^ (((rl >> 2) & 3) << 1)) * 16));
       }
     }
   }

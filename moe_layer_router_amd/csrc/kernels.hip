@@ -181,28 +181,28 @@ __device__ __forceinline__ void mega_gemm_item(const Plan& p, Tile tl, int nb, i
   MEGA_LDS;
   expert_gemm_item<AF, WF, STAGE, 1>(gemm_args(p), tl, nb, lds, signal_prev);
 }
-__device__ __noinline__ void mega_router_item(const Plan& p, int tt, int et) {
+__device__ __noinline__ void mega_router_item(Plan p, int tt, int et) {
   MEGA_LDS;
   RouterArgs ra{p.x, p.x_scales, p.wr, p.bias, p.logits, p.T, p.H, p.E, p.act_fp8};
   router_tile(ra, tt * kRouterTokens, et * kRouterExperts, lds);
 }
-__device__ __noinline__ void mega_topk_item(const Plan& p, int tt) {
+__device__ __noinline__ void mega_topk_item(Plan p, int tt) {
   const int t0 = tt * 64;
   topk_tokens(p.logits, p.E, p.k, t0, min(64, p.T - t0), p.ids, p.wts);
 }
-__device__ __noinline__ void mega_count_item(const Plan& p, int b) {
+__device__ __noinline__ void mega_count_item(Plan p, int b) {
   MEGA_LDS;
   perm_count_block(p.ids, p.T, p.k, p.E, b, p.blockcnt, reinterpret_cast<int*>(lds));
 }
-__device__ __noinline__ void mega_scan_item(const Plan& p) {
+__device__ __noinline__ void mega_scan_item(Plan p) {
   MEGA_LDS;
   perm_scan(p.blockcnt, p.nblk, p.E, p.tile_rows, p.base, p.offsets, p.tiles, p.meta, reinterpret_cast<int*>(lds));
 }
-__device__ __noinline__ void mega_scatter_item(const Plan& p, int b) {
+__device__ __noinline__ void mega_scatter_item(Plan p, int b) {
   MEGA_LDS;
   perm_scatter_block(p.ids, p.T, p.k, p.E, b, p.base, p.perm, p.row_of, reinterpret_cast<uint64_t*>(lds));
 }
-__device__ __noinline__ void mega_combine_item(const Plan& p, int nb, int c) {
+__device__ __noinline__ void mega_combine_item(Plan p, int nb, int c) {
   const int t0 = c * kCombineTokens;
   combine_rows<1>(p.staging, p.y, p.T, p.H, p.k, t0, min(p.T, t0 + kCombineTokens), nb * 256,
                   min(p.H, nb * 256 + 256));
