@@ -9,6 +9,7 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
 namespace moe {
 
@@ -180,10 +181,11 @@ DEV rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 // Cache policy of a buffer access (the instruction's cache-coherence bits):
 // 0 = default; kCoherent (sc1) = device-scope coherent.  The L2 of each XCD
 // is not coherent with the others: data that one workgroup writes and a
-// workgroup on another XCD reads inside the same kernel is written and read
-// with kCoherent (stores write through, loads do not use stale L2 lines), so
-// that no device-wide fence (which would write back or invalidate the whole
-// L2) is needed between them.
+// workgroup on another XCD reads inside the same kernel is written with
+// kCoherent (stores write through) and read with kCoherent (loads do not use
+// L2 lines) unless no L2 can hold an older copy of it, so that no
+// device-wide fence (which would write back or invalidate the whole L2) is
+// needed between them.
 constexpr int kCoherent = 16;
 
 template <int AUX = 0>
@@ -211,12 +213,19 @@ template <int AUX = 0>
 DEV void buf_ld16_lds(rsrc_t r, void* lds_base, uint32_t voff, uint32_t soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 16, (int)voff, (int)soff, 0, AUX);
 }
+// 4 bytes per lane from the buffer straight into LDS: lane l's word lands
+// at lds_base + 4*l (lds_base is wave-uniform).
+template <int AUX = 0>
+DEV void buf_ld4_lds(rsrc_t r, void* lds_base, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 4, (int)voff, (int)soff, 0, AUX);
+}
 // Wait until at most n vector-memory operations of this wave are in flight
-// (other counters untouched).
+// (other counters untouched).  Inline asm, like barrier_vmcnt below, so that
+// the compiler cannot drop it when the loads it waits for write LDS.
 template <int n>
 DEV void wait_vmcnt() {
   static_assert(n >= 0 && n < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(n) : "memory");
 }
 
 // Workgroup barrier that first waits for this wave's LDS operations and for

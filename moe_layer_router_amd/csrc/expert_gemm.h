@@ -85,7 +85,9 @@ struct GemmLds {
   static constexpr int kRsc = kAmax + 4 * kRows * 4;             // [kRows] fp32 scale
   static constexpr int kRinv = kRsc + kRows * 4;                 // [kRows] fp32 1/scale
   static constexpr int kScw = kRinv + kRows * 4;                 // [2][128] fp32 weight block scales
-  static constexpr int kBytes = kScw + 2 * 128 * 4;
+  static constexpr int kSaSlots = 6;
+  static constexpr int kSA = kScw + 2 * 128 * 4;                 // [kSaSlots][128] fp32 activation scales
+  static constexpr int kBytes = kSA + kSaSlots * 128 * 4;
 };
 
 // One step's B fragments: d[cs][i] are 16-byte pieces of column tile cs
@@ -108,10 +110,15 @@ DEV int a_swz(int row, int c) {
 
 // One work item: `RS` 16-row subtiles (rows [r0, r0+m), m <= 16*RS) of
 // expert e times one N block nb.  256 threads, one wave per SIMD.  With COH
-// the intermediate (written by stage 1, read by stage 2) and the staging
-// rows (written by stage 2) are accessed device-coherently (kCoherent), for
-// use inside the persistent kernel where producer and consumer items may run
-// on different XCDs.  `signal_prev` (may be NULL) is a counter to increment
+// (inside the persistent kernel, where producer and consumer items may run
+// on different XCDs) the outputs are stored write-through (kCoherent), so
+// that they are in memory once the producer's counter is signalled.  The
+// consumer reads the intermediate codes with ordinary, cached loads: each
+// 128-byte line of them belongs to one (row, N block), is written once per
+// launch and is read only after its writer's counter is complete, so no L2
+// can hold an older copy of it.  The intermediate's row scales (64 bytes per
+// row at I = 2048, so a line can hold rows of two tiles) are read
+// coherently.  `signal_prev` (may be NULL) is a counter to increment
 // once the stores of this workgroup's previous item have completed: the
 // prologue's barrier below waits for every older memory operation of each
 // wave, so the previous item is signalled without a wait of its own.
@@ -208,21 +215,30 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
   // stage `slot` (= s % kAStages) receives A(s)
   auto dma_a = [&](int s, int slot, int j) __attribute__((always_inline)) {
     char* dst = lds + L::kA + slot * L::kASlot + w * 1024;
-    buf_ld16_lds<STAGE == 2 ? CP : 0>(ars, dst + j * 4096, aoff[j], (uint32_t)s * 128 * ESZ);
+    buf_ld16_lds<0>(ars, dst + j * 4096, aoff[j], (uint32_t)s * 128 * ESZ);
   };
 
-  // ---- per-row scales (FP8 activations): SC[slot][set] holds sA[row] *
-  // sB[set] for the tile's rows, stored subtile-minor (row rs*16 + i at
-  // position i*kMaxRs + rs), so that a lane reads the scales of its row i for
-  // every subtile with one or two 16-byte LDS reads.
-  const int srow = (tid < m) ? tid : 0;
+  // ---- per-row scales (FP8 activations).  The activation scales of step s
+  // are loaded straight into LDS slot s % kSaSlots, three steps ahead: wave w
+  // loads rows 64*(w&1) + lane (waves 2 and 3 write the same values as 0 and
+  // 1), so that thread tid < 128 finds the scale of row tid where its own
+  // wave's load put it.  SC[par][set] holds sA[row] * sB[set] for the
+  // tile's rows, stored subtile-minor (row rs*16 + i at position
+  // i*kMaxRs + rs), so that a lane reads the scales of its row i for every
+  // subtile with one or two 16-byte LDS reads.
+  const int arow = 64 * (w & 1) + lane;
+  const int srow = (arow < m) ? arow : 0;
   const rsrc_t sars = (AF != ACT_FP8) ? make_rsrc(nullptr, 0)
                       : (STAGE == 1) ? make_rsrc(g.x_scales, (uint32_t)g.T * (g.H / 128) * 4)
                                      : make_rsrc(g.sa, (uint32_t)(g.T * g.k) * (g.I / 128) * 4);
   const uint32_t saoff = (STAGE == 1) ? (uint32_t)ROWI[srow < R ? srow : 0] * (g.H / 128) * 4
                                       : (uint32_t)(r0 + srow) * (g.I / 128) * 4;
-  auto load_scale = [&](int s) __attribute__((always_inline)) -> float {
-    return (AF == ACT_FP8) ? buf_ldf<STAGE == 2 ? CP : 0>(sars, saoff, (uint32_t)s * 4) : 1.f;
+  auto dma_sa = [&](int s, int slot) __attribute__((always_inline)) {   // slot = s % kSaSlots
+    buf_ld4_lds<STAGE == 2 ? CP : 0>(sars, lds + L::kSA + slot * 512 + (w & 1) * 256, saoff,
+                                     (uint32_t)min(s, nsteps - 1) * 4);
+  };
+  auto read_sa = [&](int slot) __attribute__((always_inline)) -> float {
+    return (AF == ACT_FP8) ? lds_ld<float>(lds, L::kSA + slot * 512 + (tid & 127) * 4) : 1.f;
   };
   auto store_scale = [&](int s, int par, float sa) __attribute__((always_inline)) {   // par = s & 1
     if (AF != ACT_FP8) return;
@@ -426,13 +442,25 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
 #pragma unroll
     for (int q = 0; q < NB; ++q) load_b_piece(s, b, q);
   };
-  const float sa0 = load_scale(0);
+  // The prologue issues its loads in the steady state's order: scale(0),
+  // then A(0) and B(0) with scale(1), then A(1) and B(1) with scale(2).
+  // (sched_barrier keeps the compiler from reordering the groups, which
+  // would make its wait counts for B at the loop head nearly a full drain)
+  if (NSA) dma_sa(0, 0);
+  if (NSA) dma_sa(1, 1);
   issue_a(0);
+  __builtin_amdgcn_sched_barrier(0);
   if (NBUF == 3) load_b(0, bb[0]);
-  const float sa1 = load_scale(1);
+  __builtin_amdgcn_sched_barrier(0);
+  if (NSA) dma_sa(2, 2);
   issue_a(1);
+  __builtin_amdgcn_sched_barrier(0);
   load_b(NBUF - 2, bb[NBUF - 2]);
-  store_scale(0, 0, sa0);
+  __builtin_amdgcn_sched_barrier(0);
+  if (NSA) {
+    wait_vmcnt<NSA + NDMA + (NBUF == 3 ? NB : 0) + NLOAD>();   // scale(0) is in LDS
+    store_scale(0, 0, read_sa(0));
+  }
   barrier_vmcnt<NLOAD>();
   if (signal_prev && tid == 0) __hip_atomic_fetch_add(signal_prev, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   // The loop body is UNR steps, a multiple of NBUF (B buffer rotation), of
@@ -442,23 +470,26 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
   // two paths and come out conservative, rarer.
   constexpr int UNR = 6;
   static_assert(UNR % NBUF == 0 && UNR % 2 == 0 && UNR % L::kAStages == 0, "loop unroll");
-  auto step = [&](int s, int u, float sa_next) __attribute__((always_inline)) -> float {
-    float sa2 = 1.f;
+  // Step s reads the scales of step s+1 (loaded two steps earlier, so they
+  // are in LDS since the previous step's barrier) into a register within
+  // the step: no loaded value is carried across the loop's back edge, where
+  // the compiler would drain every load in flight.
+  static_assert(UNR % L::kSaSlots == 0, "scale slot rotation");
+  auto step = [&](int s, int u) __attribute__((always_inline)) {
+    const float sa_next = read_sa((u + 1) % L::kSaSlots);
     compute(u % L::kAStages, u & 1, bb[u % NBUF], NLOAD, [&](int j) __attribute__((always_inline)) {
-      if (j < NSA) sa2 = load_scale(s + 2);
+      if (j < NSA) dma_sa(s + 3, (u + 3) % L::kSaSlots);
       else if (j < NSA + NDMA) dma_a(s + 2, (u + 2) % L::kAStages, j - NSA);
       else load_b_piece(s + NBUF - 1, bb[(u + NBUF - 1) % NBUF], j - NSA - NDMA);
     });
     store_scale(s + 1, (u + 1) & 1, sa_next);
     barrier_vmcnt<NLOAD>();
-    return sa2;
   };
-  float sa_next = sa1;
   for (int s = 0; s < nsteps; s += UNR) {
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       if (u > 0 && s + u >= nsteps) break;
-      sa_next = step(s + u, u, sa_next);
+      step(s + u, u);
     }
   }
   wait_vmcnt<0>();                                 // the last steps' overrun loads
@@ -593,7 +624,9 @@ DEV void expert_gemm_item(const GemmArgs& g, const Tile& t, int nb, char* lds, i
 
 // y[t, n0:n1] = BF16( sum_j staging[t*k + j, n0:n1] ) for tokens [t0, t1),
 // fp32 sums in ascending j; 8 channels (16 bytes) per thread and step.
-template <int COH>
+// Ordinary loads also in the persistent kernel: a 128-byte line of staging
+// lies in one (row, 256-column block), written once per launch, write-through,
+// before the block's counter that the caller waits for.
 DEV void combine_rows(const uint16_t* staging, uint16_t* y, int T, int H, int k, int t0, int t1, int n0, int n1) {
   const rsrc_t srs = make_rsrc(staging, (uint32_t)T * (uint32_t)k * (uint32_t)H * 2);
   const int cpt = (n1 - n0) / 8;
@@ -602,7 +635,7 @@ DEV void combine_rows(const uint16_t* staging, uint16_t* y, int T, int H, int k,
     const int t = t0 + idx / cpt, c = n0 + (idx % cpt) * 8;
     float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int j = 0; j < k; ++j) {
-      const v4i v = buf_ld16<COH ? kCoherent : 0>(srs, ((uint32_t)(t * k + j) * H + c) * 2, 0);
+      const v4i v = buf_ld16(srs, ((uint32_t)(t * k + j) * H + c) * 2, 0);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         s[2 * i] += bf16_to_f32((uint32_t)v[i] & 0xFFFFu);

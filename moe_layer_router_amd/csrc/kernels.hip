@@ -16,14 +16,16 @@ __global__ void k_zero(int32_t* p, size_t n) {
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = 0;
 }
 
+template <int AF>
 __global__ void __launch_bounds__(256) k_router(RouterArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
-  router_tile(a, blockIdx.y * kRouterTokens, blockIdx.x * kRouterExperts, lds);
+  router_tile<AF>(a, blockIdx.y * kRouterTokens, blockIdx.x * kRouterExperts, lds);
 }
 
+constexpr int kTopkTokens = 32;   // tokens per top-k workgroup (separate mode)
 __global__ void __launch_bounds__(256) k_topk(const float* logits, int T, int E, int k, int32_t* ids, float* wts) {
-  const int t0 = blockIdx.x * 64;
-  topk_tokens(logits, E, k, t0, min(64, T - t0), ids, wts);
+  const int t0 = blockIdx.x * kTopkTokens;
+  topk_tokens(logits, E, k, t0, min(kTopkTokens, T - t0), ids, wts);
 }
 
 __global__ void __launch_bounds__(256) k_count(const int32_t* ids, int T, int k, int E, int32_t* blockcnt) {
@@ -99,7 +101,7 @@ __global__ void __launch_bounds__(256) k_pack_e8m0(const uint8_t* src, uint8_t* 
 
 __global__ void __launch_bounds__(256) k_combine(const uint16_t* staging, uint16_t* y, int T, int H, int k) {
   const int t0 = blockIdx.x * 16;
-  combine_rows<0>(staging, y, T, H, k, t0, min(T, t0 + 16), 0, H);
+  combine_rows(staging, y, T, H, k, t0, min(T, t0 + 16), 0, H);
 }
 
 // ------------------------------------------------------- persistent kernel
@@ -135,9 +137,9 @@ DEV bool wait_counter(const int32_t* c, int target, int32_t* err, int* s_ok, boo
 // Publish this workgroup's coherent (kCoherent, write-through) stores, then
 // add 1 to each counter: each wave waits until its stores have completed,
 // the workgroup synchronises, and one thread increments.  No device-wide
-// fence: the data was written past the L2, and readers load it coherently,
-// so the relaxed counter is the only ordering needed.  (Used by the gate|up
-// and down items, whose outputs are read only through kCoherent accesses.)
+// fence: the data was written past the L2, and no cache holds an older copy
+// of it (see expert_gemm_tile), so the relaxed counter is the only ordering
+// needed.  (Used by the gate|up and down items.)
 DEV void signal_coherent(int32_t* c0, int32_t* c1 = nullptr) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
@@ -162,8 +164,8 @@ DEV void signal_add(int32_t* c0, int32_t* c1 = nullptr) {
 // workgroup moves to the next queue only once every item of the current one
 // has been claimed by a running workgroup, so no wait can deadlock whatever
 // the grid size:
-//   head queue:   router tiles (64 tokens x 64 experts) -> rdone[token tile]
-//                 top-k of 64 tokens                    -> tkdone[256-token block]
+//   head queue:   router tiles (128 tokens x 64 experts) -> rdone[token tile]
+//                 top-k of 128 tokens                    -> tkdone[256-token block]
 //                 expert histogram of 256 tokens        -> COUNT_DONE
 //                 scan (offsets, block bases, tiles)    -> SCAN_FLAG
 //                 stable scatter of 256 tokens          -> SCATTER_DONE
@@ -181,14 +183,15 @@ __device__ __forceinline__ void mega_gemm_item(const Plan& p, Tile tl, int nb, i
   MEGA_LDS;
   expert_gemm_item<AF, WF, STAGE, 1>(gemm_args(p), tl, nb, lds, signal_prev);
 }
+template <int AF>
 __device__ __noinline__ void mega_router_item(Plan p, int tt, int et) {
   MEGA_LDS;
   RouterArgs ra{p.x, p.x_scales, p.wr, p.bias, p.logits, p.T, p.H, p.E, p.act_fp8};
-  router_tile(ra, tt * kRouterTokens, et * kRouterExperts, lds);
+  router_tile<AF>(ra, tt * kRouterTokens, et * kRouterExperts, lds);
 }
 __device__ __noinline__ void mega_topk_item(Plan p, int tt) {
-  const int t0 = tt * 64;
-  topk_tokens(p.logits, p.E, p.k, t0, min(64, p.T - t0), p.ids, p.wts);
+  const int t0 = tt * kRouterTokens;
+  topk_tokens(p.logits, p.E, p.k, t0, min(kRouterTokens, p.T - t0), p.ids, p.wts);
 }
 __device__ __noinline__ void mega_count_item(Plan p, int b) {
   MEGA_LDS;
@@ -204,7 +207,7 @@ __device__ __noinline__ void mega_scatter_item(Plan p, int b) {
 }
 __device__ __noinline__ void mega_combine_item(Plan p, int nb, int c) {
   const int t0 = c * kCombineTokens;
-  combine_rows<1>(p.staging, p.y, p.T, p.H, p.k, t0, min(p.T, t0 + kCombineTokens), nb * 256,
+  combine_rows(p.staging, p.y, p.T, p.H, p.k, t0, min(p.T, t0 + kCombineTokens), nb * 256,
                   min(p.H, nb * 256 + 256));
 }
 
@@ -213,8 +216,8 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_wav
 k_mega(Plan p) {
   __shared__ int s_q, s_ok, s_first[kXcds + 1];
   const int tid = threadIdx.x;
-  const int nR = p.routing_given ? 0 : p.nT64 * p.nE64;
-  const int nK = p.routing_given ? 0 : p.nT64;
+  const int nR = p.routing_given ? 0 : p.nTR * p.nER;
+  const int nK = p.routing_given ? 0 : p.nTR;
   const int q_topk = nR, q_count = nR + nK, q_scan = q_count + p.nblk;
   const int q_scat = q_scan + 1, q_end = q_scat + p.nblk;
 
@@ -226,18 +229,19 @@ k_mega(Plan p) {
     __syncthreads();
     if (q >= q_end) break;
     if (q < q_topk) {
-      const int tt = q / p.nE64, et = q % p.nE64;
-      mega_router_item(p, tt, et);
+      const int tt = q / p.nER, et = q % p.nER;
+      mega_router_item<AF>(p, tt, et);
       signal_add(&p.rdone[tt]);
     } else if (q < q_count) {
       const int tt = q - q_topk;
-      if (!wait_counter(&p.rdone[tt], p.nE64, p.err, &s_ok)) return;
+      if (!wait_counter(&p.rdone[tt], p.nER, p.err, &s_ok)) return;
       mega_topk_item(p, tt);
-      signal_add(&p.tkdone[tt >> 2]);
+      signal_add(&p.tkdone[tt / (kPermBlock / kRouterTokens)]);
     } else if (q < q_scan) {
       const int b = q - q_count;
       if (!p.routing_given) {
-        const int tiles_in_block = min(4, p.nT64 - 4 * b);
+        constexpr int kPer = kPermBlock / kRouterTokens;   // router token tiles per block
+        const int tiles_in_block = min(kPer, p.nTR - kPer * b);
         if (!wait_counter(&p.tkdone[b], tiles_in_block, p.err, &s_ok)) return;
       }
       mega_count_item(p, b);
@@ -277,7 +281,7 @@ k_mega(Plan p) {
 
   // 3. down items from the per-class queues (all gate|up items have been
   // claimed); an item waits for the gate|up items of its tile.  Relaxed
-  // waits suffice: the intermediate is read with coherent loads.
+  // waits suffice (see signal_coherent).
   cls = blockIdx.x % kXcds;
   __syncthreads();
   if (tid == 0) s_q = pop_class_item(p.ctr + CTR_Q2, s_first, p.nnb2, &cls);
@@ -340,15 +344,15 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 struct Layout {
   size_t err, zero_begin, ctr, rdone, tkdone, done1, done2, zero_end;
   size_t logits, blockcnt, base, offsets, perm, row_of, tiles, meta, aq, sa, staging, total;
-  int nblk, nT64, nE64, max_tiles, nnb1, nnb2;
+  int nblk, nTR, nER, max_tiles, nnb1, nnb2;
 };
 
 Layout make_layout(const moe_desc* d) {
   Layout L{};
   const size_t T = d->T, E = d->E, k = d->top_k, H = d->H, I = d->I;
   L.nblk = (int)((T + kPermBlock - 1) / kPermBlock);
-  L.nT64 = (int)((T + 63) / 64);
-  L.nE64 = (int)((E + 63) / 64);
+  L.nTR = (int)((T + kRouterTokens - 1) / kRouterTokens);
+  L.nER = (int)((E + kRouterExperts - 1) / kRouterExperts);
   L.max_tiles = (int)(E + (T * k + kMinTileRows - 1) / kMinTileRows);
   L.nnb1 = (int)(I / 128);
   L.nnb2 = (int)((H + 255) / 256);
@@ -356,7 +360,7 @@ Layout make_layout(const moe_desc* d) {
   L.err = o; o += 256;
   L.zero_begin = o;
   L.ctr = o; o += CTR_NUM * 4;
-  L.rdone = o; o += (size_t)L.nT64 * 4;
+  L.rdone = o; o += (size_t)L.nTR * 4;
   L.tkdone = o; o += (size_t)L.nblk * 4;
   L.done1 = o; o += (size_t)L.max_tiles * 4;
   L.done2 = o; o += (size_t)L.nnb2 * 4;
@@ -452,7 +456,7 @@ moe_status fill_plan(const moe_desc* d, const Layout& L, char* ws, Plan* P) {
   p.act_fp8 = d->act_dtype == MOE_DTYPE_FP8_E4M3;
   p.wdt = d->weight_dtype == MOE_DTYPE_FP8_E4M3 ? W_FP8 : d->weight_dtype == MOE_DTYPE_FP4_E2M1 ? W_FP4 : W_BF16;
   p.routing_given = (d->flags & MOE_FLAG_ROUTING_GIVEN) != 0;
-  p.nblk = L.nblk; p.nT64 = L.nT64; p.nE64 = L.nE64; p.max_tiles = L.max_tiles;
+  p.nblk = L.nblk; p.nTR = L.nTR; p.nER = L.nER; p.max_tiles = L.max_tiles;
   p.tile_rows = p.act_fp8 ? GemmLds<ACT_FP8>::kRows : GemmLds<ACT_BF16>::kRows;
   p.nnb1 = L.nnb1; p.nnb2 = L.nnb2;
   p.nCT = (d->T + kCombineTokens - 1) / kCombineTokens;
@@ -510,9 +514,16 @@ int mega_lds(const Plan& p) {
 
 moe_status launch_route(const Plan& p, float* logits, hipStream_t st) {
   RouterArgs ra{p.x, p.x_scales, p.wr, p.bias, logits, p.T, p.H, p.E, p.act_fp8};
-  hipLaunchKernelGGL(k_router, dim3(p.nE64, p.nT64), dim3(256), kRouterLds, st, ra);
+  if (p.act_fp8) {
+    TRY(set_lds_limit(k_router<ACT_FP8>, kRouterLds));
+    hipLaunchKernelGGL(k_router<ACT_FP8>, dim3(p.nER, p.nTR), dim3(256), kRouterLds, st, ra);
+  } else {
+    TRY(set_lds_limit(k_router<ACT_BF16>, kRouterLds));
+    hipLaunchKernelGGL(k_router<ACT_BF16>, dim3(p.nER, p.nTR), dim3(256), kRouterLds, st, ra);
+  }
   HIP_TRY(hipGetLastError());
-  hipLaunchKernelGGL(k_topk, dim3(p.nT64), dim3(256), 0, st, logits, p.T, p.E, p.k, p.ids, p.wts);
+  hipLaunchKernelGGL(k_topk, dim3((p.T + kTopkTokens - 1) / kTopkTokens), dim3(256), 0, st, logits, p.T, p.E, p.k,
+                     p.ids, p.wts);
   HIP_TRY(hipGetLastError());
   return MOE_OK;
 }

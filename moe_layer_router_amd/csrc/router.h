@@ -21,120 +21,163 @@ struct RouterArgs {
   int act_fp8;
 };
 
-constexpr int kRouterTokens = 64;    // tokens per router tile
+constexpr int kRouterTokens = 128;   // tokens per router tile
 constexpr int kRouterExperts = 64;   // experts per router tile
-constexpr int kRouterLds = 2 * 64 * 256;
+constexpr int kRouterStages = 3;     // LDS stages (loads run two steps ahead)
+// One LDS stage (128 K): router weights [64 experts][256 B], activations
+// [128 tokens][128 B (E4M3) or 256 B (BF16)], activation scales [4 waves][64].
+constexpr int kRouterW = 0;
+constexpr int kRouterX = kRouterW + 64 * 256;
+constexpr int kRouterSc = kRouterX + 128 * 256;
+constexpr int kRouterStage = kRouterSc + 4 * 256;
+constexpr int kRouterLds = kRouterStages * kRouterStage;
 
-// Logits of tokens [t0, t0+64) x experts [e0, e0+64) on 256 threads.
+// Logits of tokens [t0, t0+128) x experts [e0, e0+64) on 256 threads.
 //
-// Both operands go through LDS as BF16 (E4M3 -> BF16 is exact), 128 K per
-// step.  Each 256-byte LDS row holds 16 chunks of 8 BF16; chunk c of row r
-// sits at position c ^ (r & 15) so that the 16 rows read by one MFMA operand
-// fetch hit distinct banks.  Wave w owns tokens 16w..16w+15 and all 64
-// experts (four 16x16 accumulators).  MFMA i of a step takes K elements
-// 32*g + 8*i .. +7 in lane group g for both operands, so each lane reads
-// whole 16-byte chunks.  For FP8 activations the per-128 scale multiplies
-// each step's partial sum (fp32), as the scale changes every 128 channels.
+// The logits are a dense [T, H] x [H, E] product, so the tile runs on 16x16x32
+// BF16 MFMAs: E4M3 activations convert exactly to BF16 with the gfx950
+// conversion instruction.  Router weights, activations and (E4M3) the per-128
+// activation scales are loaded straight into LDS, 128 K per step, two steps
+// ahead; each row of 16-byte chunks is stored with chunk c at c ^ (row & 15)
+// (c ^ (row & 7) for 128-byte activation rows) so that the 16 rows read by one
+// operand fetch fall in distinct banks.  Wave w owns tokens 32w..32w+31 (it
+// loads exactly those activation rows and scales itself) and all 64 experts:
+// 2 x 4 accumulator tiles.  Within a step, lane group g holds K elements
+// 32g + 8i .. +7 in MFMA i (the same permutation of K for both operands), so a
+// lane reads contiguous bytes.  E4M3: each step's partial sum is scaled by the
+// token's scale of that 128-channel block and added to the fp32 logits.
+template <int AF>
 DEV void router_tile(const RouterArgs& a, int t0, int e0, char* lds) {
+  constexpr int XB = (AF == ACT_FP8) ? 128 : 256;          // activation bytes per token per step
+  constexpr int NW = 4;                                      // weight loads per wave per step (1 KB each)
+  constexpr int NX = XB * 128 / 1024 / 4;                    // activation loads per wave per step
+  constexpr int NS = (AF == ACT_FP8) ? 1 : 0;                // scale loads per wave per step
+  constexpr int NLOAD = NW + NX + NS;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
-  char* xs = lds;
-  char* ws = lds + 64 * 256;
   const int nsteps = a.H / 128;
 
-  const int lrow = tid >> 2, lpart = tid & 3;
-  const int ltok = t0 + lrow, lexp = e0 + lrow;
-  const bool tok_ok = ltok < a.T, exp_ok = lexp < a.E;
-
-  v4i xr[4], wrr[4];
-  auto load = [&](int s) __attribute__((always_inline)) {
-    if (a.act_fp8) {
-      const uint8_t* p = a.x + (size_t)ltok * a.H + s * 128 + lpart * 32;
-      xr[0] = tok_ok ? ld16(p) : v4i{0, 0, 0, 0};
-      xr[1] = tok_ok ? ld16(p + 16) : v4i{0, 0, 0, 0};
+  const rsrc_t wrs = make_rsrc(a.wr, (uint32_t)a.E * (uint32_t)a.H * 2);
+  const rsrc_t xrs = make_rsrc(a.x, (uint32_t)a.T * (uint32_t)a.H * (XB / 128));
+  const rsrc_t srs = make_rsrc(a.x_scales, (AF == ACT_FP8) ? (uint32_t)a.T * (uint32_t)(a.H / 128) * 4 : 0u);
+  // per-lane global offsets (step 0) of this wave's loads
+  uint32_t woff[NW], xoff[NX];
+#pragma unroll
+  for (int j = 0; j < NW; ++j) {
+    const int r = 16 * w + 4 * j + lane / 16;                 // expert row of the tile
+    const int c = (lane & 15) ^ (r & 15);                     // logical chunk of physical chunk lane & 15
+    woff[j] = (uint32_t)(e0 + r) * (uint32_t)a.H * 2 + c * 16;
+  }
+#pragma unroll
+  for (int j = 0; j < NX; ++j) {
+    if (AF == ACT_FP8) {
+      const int r = 32 * w + 8 * j + lane / 8;
+      const int c = (lane & 7) ^ (r & 7);
+      xoff[j] = (uint32_t)(t0 + r) * (uint32_t)a.H + c * 16;
     } else {
-      const uint8_t* p = a.x + ((size_t)ltok * a.H + s * 128 + lpart * 32) * 2;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) xr[i] = tok_ok ? ld16(p + 16 * i) : v4i{0, 0, 0, 0};
-    }
-    const uint8_t* q = reinterpret_cast<const uint8_t*>(a.wr) + ((size_t)lexp * a.H + s * 128 + lpart * 32) * 2;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) wrr[i] = exp_ok ? ld16(q + 16 * i) : v4i{0, 0, 0, 0};
-  };
-  auto store = [&]() __attribute__((always_inline)) {
-    const int sw = lrow & 15;
-    if (a.act_fp8) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        uint32_t l0, h0, l1, h1;
-        e4m3x4_to_bf16x4((uint32_t)xr[i][0], l0, h0);
-        e4m3x4_to_bf16x4((uint32_t)xr[i][1], l1, h1);
-        st16(xs + lrow * 256 + (((lpart * 4 + 2 * i) ^ sw) << 4), v4i{(int)l0, (int)h0, (int)l1, (int)h1});
-        e4m3x4_to_bf16x4((uint32_t)xr[i][2], l0, h0);
-        e4m3x4_to_bf16x4((uint32_t)xr[i][3], l1, h1);
-        st16(xs + lrow * 256 + (((lpart * 4 + 2 * i + 1) ^ sw) << 4), v4i{(int)l0, (int)h0, (int)l1, (int)h1});
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) st16(xs + lrow * 256 + (((lpart * 4 + i) ^ sw) << 4), xr[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) st16(ws + lrow * 256 + (((lpart * 4 + i) ^ sw) << 4), wrr[i]);
-  };
-
-  v4f acc[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) acc[c] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  load(0);
-  for (int s = 0; s < nsteps; ++s) {
-    __syncthreads();          // previous step's LDS reads are done
-    store();
-    __syncthreads();
-    if (s + 1 < nsteps) load(s + 1);
-    float sc[4] = {1.f, 1.f, 1.f, 1.f};
-    if (a.act_fp8) {
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int t = t0 + 16 * w + 4 * g + v;
-        sc[v] = (t < a.T) ? a.x_scales[(size_t)t * (a.H / 128) + s] : 0.f;
-      }
-    }
-    v4f part[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) part[c] = a.act_fp8 ? v4f{0.f, 0.f, 0.f, 0.f} : acc[c];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int chunk = (g * 4 + i) ^ c16;
-      const v8bf av = as_v8bf(*reinterpret_cast<const v4i*>(xs + (16 * w + c16) * 256 + (chunk << 4)));
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const v8bf bv = as_v8bf(*reinterpret_cast<const v4i*>(ws + (16 * c + c16) * 256 + (chunk << 4)));
-        part[c] = mfma_bf16(av, bv, part[c]);
-      }
-    }
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      if (a.act_fp8) {
-#pragma unroll
-        for (int v = 0; v < 4; ++v) acc[c][v] += part[c][v] * sc[v];
-      } else {
-        acc[c] = part[c];
-      }
+      const int r = 32 * w + 4 * j + lane / 16;
+      const int c = (lane & 15) ^ (r & 15);
+      xoff[j] = (uint32_t)(t0 + r) * (uint32_t)a.H * 2 + c * 16;
     }
   }
+  const uint32_t soff = (uint32_t)(t0 + 32 * w + (lane & 31)) * (uint32_t)(a.H / 128) * 4;
+  auto issue = [&](int s, int j) __attribute__((always_inline)) {   // load j of step s
+    char* st = lds + (s % kRouterStages) * kRouterStage;
+    if (j < NW) {
+      buf_ld16_lds(wrs, st + kRouterW + (16 * w + 4 * j) * 256, woff[j], (uint32_t)s * 256);
+    } else if (j < NW + NX) {
+      const int jx = j - NW;
+      const int rows = (AF == ACT_FP8) ? 8 : 4;
+      buf_ld16_lds(xrs, st + kRouterX + (32 * w + rows * jx) * XB, xoff[jx], (uint32_t)s * 128 * (XB / 128));
+    } else {
+      buf_ld4_lds(srs, st + kRouterSc + w * 256, soff, (uint32_t)s * 4);
+    }
+  };
 
-  // accumulator element v of tile c: token row 4g+v, expert column c16
+  v4f acc[2][4];
+#pragma unroll
+  for (int st = 0; st < 2; ++st)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[st][c] = v4f{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int j = 0; j < NLOAD; ++j) issue(0, j);
+#pragma unroll
+  for (int j = 0; j < NLOAD; ++j) issue(1, j);
+  barrier_vmcnt<NLOAD>();
+
+  for (int s = 0; s < nsteps; ++s) {
+    const char* st = lds + (s % kRouterStages) * kRouterStage;
+    // A operands of both token subtiles
+    v8bf av[2][4];
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const int row = 32 * w + 16 * sub + c16;
+      if (AF == ACT_FP8) {
+        const v4i q0 = ld16(st + kRouterX + row * 128 + (((2 * g) ^ (row & 7)) << 4));
+        const v4i q1 = ld16(st + kRouterX + row * 128 + (((2 * g + 1) ^ (row & 7)) << 4));
+        const int qs[8] = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const v2bf p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(qs[2 * i], 1.0f, false);
+          const v2bf p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(qs[2 * i], 1.0f, true);
+          const v2bf p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(qs[2 * i + 1], 1.0f, false);
+          const v2bf p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(qs[2 * i + 1], 1.0f, true);
+          av[sub][i] = v8bf{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          av[sub][i] = as_v8bf(ld16(st + kRouterX + row * 256 + (((4 * g + i) ^ (row & 15)) << 4)));
+      }
+    }
+    v4f part[2][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      issue(s + 2, i);                                        // weights of step s+2
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int row = 16 * c + c16;
+        const v8bf bv = as_v8bf(ld16(st + kRouterW + row * 256 + (((4 * g + i) ^ (row & 15)) << 4)));
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+          if (AF == ACT_FP8)
+            part[sub][c] = mfma_bf16(av[sub][i], bv, i == 0 ? v4f{0.f, 0.f, 0.f, 0.f} : part[sub][c]);
+          else
+            acc[sub][c] = mfma_bf16(av[sub][i], bv, acc[sub][c]);
+        }
+      }
+    }
+#pragma unroll
+    for (int j = NW; j < NLOAD; ++j) issue(s + 2, j);          // activations (and scales) of step s+2
+    if (AF == ACT_FP8) {
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        const v4f sc = *reinterpret_cast<const v4f*>(st + kRouterSc + w * 256 + (16 * sub + 4 * g) * 4);
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[sub][c][v] = __builtin_fmaf(part[sub][c][v], sc[v], acc[sub][c][v]);
+      }
+    }
+    barrier_vmcnt<NLOAD>();
+  }
+  wait_vmcnt<0>();                                 // loads issued for steps past the end
+  __syncthreads();
+
+  // accumulator element v of tile (sub, c): token 32w + 16sub + 4g + v, expert 16c + c16
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     const int e = e0 + 16 * c + c16;
     if (e >= a.E) continue;
     const float b = a.bias ? a.bias[e] : 0.f;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int t = t0 + 16 * w + 4 * g + v;
-      if (t < a.T) a.logits[(size_t)t * a.E + e] = acc[c][v] + b;
-    }
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int t = t0 + 32 * w + 16 * sub + 4 * g + v;
+        if (t < a.T) a.logits[(size_t)t * a.E + e] = acc[sub][c][v] + b;
+      }
   }
 }
 
@@ -178,8 +221,79 @@ DEV void topk_token(const float* lrow, int E, int k, int32_t* ids, float* wts) {
   }
 }
 
-// Top-k for `count` consecutive tokens starting at t0, one wave per token in turn.
+// Max of a 64-bit key over the 16 lanes of a DPP row (the same four moves as
+// row_max16), returned to every lane of the row.
+template <int CTRL>
+DEV uint64_t dpp_mov64(uint64_t x) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)x, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(x >> 32), CTRL, 0xF, 0xF, false);
+  return ((uint64_t)hi << 32) | lo;
+}
+DEV uint64_t row_max16_u64(uint64_t v) {
+  uint64_t o;
+  o = dpp_mov64<0xB1>(v); v = o > v ? o : v;
+  o = dpp_mov64<0x4E>(v); v = o > v ? o : v;
+  o = dpp_mov64<0x141>(v); v = o > v ? o : v;
+  o = dpp_mov64<0x140>(v); v = o > v ? o : v;
+  return v;
+}
+DEV float row_sum16(float v) {
+  v += dpp_mov<0xB1>(v);
+  v += dpp_mov<0x4E>(v);
+  v += dpp_mov<0x141>(v);
+  v += dpp_mov<0x140>(v);
+  return v;
+}
+
+// Top-k of one token per DPP row (16 lanes), E <= 256, k <= 16: lane i of
+// the row holds experts i + 16j.  Same keys and order as topk_token.
+DEV void topk_token16(const float* lrow, bool valid, int E, int k, int32_t* ids, float* wts) {
+  const int li = threadIdx.x & 15;
+  uint64_t key[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int e = li + 16 * j;
+    key[j] = (valid && e < E) ? (((uint64_t)f32_order_key(lrow[e]) << 32) | (uint32_t)(E - 1 - e)) : 0ull;
+  }
+  int my_id = 0;
+  float my_val = 0.f, top = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    if (r < k) {
+      uint64_t best = key[0];
+#pragma unroll
+      for (int j = 1; j < 16; ++j) best = key[j] > best ? key[j] : best;
+      best = row_max16_u64(best);
+      const int e = E - 1 - (int)(uint32_t)best;
+      const float val = f32_from_order_key((uint32_t)(best >> 32));
+      if (r == 0) top = val;
+      if (li == r) { my_id = e; my_val = val; }
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (li + 16 * j == e) key[j] = 0ull;
+    }
+  }
+  const float ex = (li < k) ? expf(my_val - top) : 0.f;
+  const float sum = row_sum16(ex);
+  if (valid && li < k) {
+    ids[li] = my_id;
+    wts[li] = ex / sum;
+  }
+}
+
+// Top-k for `count` consecutive tokens starting at t0: one token per DPP row
+// (16 per workgroup pass) when E <= 256, else one wave per token.
 DEV void topk_tokens(const float* logits, int E, int k, int t0, int count, int32_t* ids, float* wts) {
+  if (E <= 256) {
+    const int rowid = threadIdx.x >> 4, nrows = blockDim.x >> 4;
+    for (int i0 = 0; i0 < count; i0 += nrows) {
+      const int i = i0 + rowid;
+      const bool valid = i < count;
+      const int t = t0 + (valid ? i : 0);
+      topk_token16(logits + (size_t)t * E, valid, E, k, ids + (size_t)t * k, wts + (size_t)t * k);
+    }
+    return;
+  }
   const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
   for (int i = w; i < count; i += nw) {
     const int t = t0 + i;
