@@ -631,21 +631,61 @@ DEV void combine_rows(const uint16_t* staging, uint16_t* y, int T, int H, int k,
   const rsrc_t srs = make_rsrc(staging, (uint32_t)T * (uint32_t)k * (uint32_t)H * 2);
   const int cpt = (n1 - n0) / 8;
   const int total = (t1 - t0) * cpt;
-  for (int idx = threadIdx.x; idx < total; idx += blockDim.x) {
-    const int t = t0 + idx / cpt, c = n0 + (idx % cpt) * 8;
-    float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
-      const v4i v = buf_ld16(srs, ((uint32_t)(t * k + j) * H + c) * 2, 0);
+  // U (token, 8-channel) pairs per thread and pass, rows read four j at a
+  // time: up to 16 loads in flight per thread
+  constexpr int U = 4;
+  const int nthr = blockDim.x;
+  for (int i0 = threadIdx.x; i0 < total; i0 += U * nthr) {
+    uint32_t off[U];
+    int tt[U], cc[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int idx = min(i0 + u * nthr, total - 1);
+      tt[u] = t0 + idx / cpt;
+      cc[u] = n0 + (idx % cpt) * 8;
+      off[u] = ((uint32_t)tt[u] * (uint32_t)k * (uint32_t)H + (uint32_t)cc[u]) * 2;
+    }
+    float s[U][8];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s[u][i] = 0.f;
+    auto add = [&](int u, const v4i& v) __attribute__((always_inline)) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        s[2 * i] += bf16_to_f32((uint32_t)v[i] & 0xFFFFu);
-        s[2 * i + 1] += bf16_to_f32((uint32_t)v[i] >> 16);
+        s[u][2 * i] += bf16_to_f32((uint32_t)v[i] & 0xFFFFu);
+        s[u][2 * i + 1] += bf16_to_f32((uint32_t)v[i] >> 16);
       }
-    }
-    v4i o;
+    };
+    const uint32_t row = (uint32_t)H * 2;
+    int j = 0;
+    for (; j + 4 <= k; j += 4) {
+      v4i v[4][U];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = (int)(f32_to_bf16_rne(s[2 * i]) | (f32_to_bf16_rne(s[2 * i + 1]) << 16));
-    st16(reinterpret_cast<uint8_t*>(y) + ((size_t)t * H + c) * 2, o);
+      for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[jj][u] = buf_ld16(srs, off[u] + (uint32_t)(j + jj) * row, 0);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+        for (int u = 0; u < U; ++u) add(u, v[jj][u]);
+    }
+    for (; j < k; ++j) {
+      v4i v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = buf_ld16(srs, off[u] + (uint32_t)j * row, 0);
+#pragma unroll
+      for (int u = 0; u < U; ++u) add(u, v[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (i0 + u * nthr >= total) continue;
+      v4i o;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        o[i] = (int)(f32_to_bf16_rne(s[u][2 * i]) | (f32_to_bf16_rne(s[u][2 * i + 1]) << 16));
+      st16(reinterpret_cast<uint8_t*>(y) + ((size_t)tt[u] * H + cc[u]) * 2, o);
+    }
   }
 }
 
