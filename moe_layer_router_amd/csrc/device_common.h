@@ -16,20 +16,6 @@ namespace moe {
 constexpr int kWave = 64;
 
 // ------------------------------------------------------------ conversions
-// OCP E4M3 ("fn") byte -> fp32, exact.  Normals: rebias the exponent field
-// (7 -> 127) by placing the 7 magnitude bits at bit 20 and adding 120 << 23.
-// Subnormals (exponent field 0) are m * 2^-9.
-DEV float e4m3_to_f32(uint32_t b) {
-  const uint32_t mag = b & 0x7Fu;
-  const float normal = __uint_as_float((mag << 20) + (120u << 23));
-  const float sub = (float)(mag & 7u) * 0x1p-9f;
-  const float v = (mag >= 8u) ? normal : sub;
-  return (b & 0x80u) ? -v : v;
-}
-
-// BF16 bit pattern of an fp32 whose significand fits in 8 bits (exact).
-DEV uint32_t f32_to_bf16_exact(float f) { return __float_as_uint(f) >> 16; }
-
 // fp32 -> BF16 bits, round to nearest even (finite inputs).
 DEV uint32_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
@@ -38,16 +24,6 @@ DEV uint32_t f32_to_bf16_rne(float f) {
 }
 
 DEV float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
-
-// Four E4M3 bytes (one dword) -> four BF16 values packed in two dwords.
-DEV void e4m3x4_to_bf16x4(uint32_t q, uint32_t& lo, uint32_t& hi) {
-  const uint32_t b0 = f32_to_bf16_exact(e4m3_to_f32(q & 0xFFu));
-  const uint32_t b1 = f32_to_bf16_exact(e4m3_to_f32((q >> 8) & 0xFFu));
-  const uint32_t b2 = f32_to_bf16_exact(e4m3_to_f32((q >> 16) & 0xFFu));
-  const uint32_t b3 = f32_to_bf16_exact(e4m3_to_f32(q >> 24));
-  lo = b0 | (b1 << 16);
-  hi = b2 | (b3 << 16);
-}
 
 // fp32 -> E4M3 byte with the hardware converter (round to nearest even);
 // the input is clamped to +-448 first, so the result saturates.
@@ -115,17 +91,6 @@ DEV float quad_bcast(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), V * 0x55, 0xF, 0xF, true));
 }
 
-DEV uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int m = 1; m < kWave; m <<= 1) {
-    const uint32_t lo = __shfl_xor((uint32_t)v, m);
-    const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), m);
-    const uint64_t o = ((uint64_t)hi << 32) | lo;
-    v = o > v ? o : v;
-  }
-  return v;
-}
-
 // Inclusive prefix sum over a workgroup of `nthreads` (multiple of 64) ints.
 // `scratch` needs nthreads/64 ints of LDS.  Returns the inclusive sum of the
 // thread's value; *total receives the workgroup total.
@@ -156,12 +121,6 @@ DEV int block_inclusive_scan(int v, int* scratch, int* total) {
 // materialised (and kept live) as one register per constant.
 DEV uint32_t opaque(uint32_t v) {
   asm volatile("" : "+v"(v));
-  return v;
-}
-// Make v depend on dep (no instruction is emitted): v cannot be computed
-// before dep is available, which bounds how far the scheduler hoists loads.
-DEV uint32_t after(uint32_t v, float dep) {
-  asm volatile("" : "+v"(v) : "v"(dep));
   return v;
 }
 template <typename T>

@@ -77,7 +77,8 @@ struct GemmLds {
   static constexpr int kASlot = kRows * kABytes;                 // one A stage
   static constexpr int kA = 0;                                   // [2] A stages
   static constexpr int kScRows = kGemmThreads;                   // every thread writes a scale
-  static constexpr int kAStages = 3;
+  static constexpr int kPd = (AF == ACT_FP8) ? 3 : 2;            // prefetch distance (steps)
+  static constexpr int kAStages = kPd + 1;
   static constexpr int kSC = kA + kAStages * kASlot;             // [2][2][kScRows] fp32 row scales
   static constexpr int kRowI = kSC + 2 * 2 * kScRows * 4;        // [kRows] int
   static constexpr int kRowW = kRowI + kRows * 4;                // [kRows] fp32
@@ -85,7 +86,7 @@ struct GemmLds {
   static constexpr int kRsc = kAmax + 4 * kRows * 4;             // [kRows] fp32 scale
   static constexpr int kRinv = kRsc + kRows * 4;                 // [kRows] fp32 1/scale
   static constexpr int kScw = kRinv + kRows * 4;                 // [2][128] fp32 weight block scales
-  static constexpr int kSaSlots = 6;
+  static constexpr int kSaSlots = kPd + 1;
   static constexpr int kSA = kScw + 2 * 128 * 4;                 // [kSaSlots][128] fp32 activation scales
   static constexpr int kBytes = kSA + kSaSlots * 128 * 4;
 };
@@ -134,7 +135,8 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
   constexpr int NDMA = (R * AB + 4095) / 4096;    // DMA instructions per thread per step
   constexpr int ESZ = (AF == ACT_FP8) ? 1 : 2;    // activation element size
   constexpr int NB = (WF == W_BF16) ? 16 : 8;     // B load instructions per lane per step
-  constexpr int NBUF = (WF == W_BF16) ? 2 : 3;     // B register buffers (prefetch distance + 1)
+  constexpr int PD = L::kPd;                       // A and scales: loaded PD (+1) steps ahead
+  constexpr int NBUF = (WF == W_BF16) ? 2 : PD + 1; // B register buffers (B distance NBUF - 1)
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int gq = lane >> 4, c16 = lane & 15;
   const int K = (STAGE == 1) ? g.H : g.I;
@@ -219,7 +221,7 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
   };
 
   // ---- per-row scales (FP8 activations).  The activation scales of step s
-  // are loaded straight into LDS slot s % kSaSlots, three steps ahead: wave w
+  // are loaded straight into LDS slot s % kSaSlots, PD + 1 steps ahead: wave w
   // loads rows 64*(w&1) + lane (waves 2 and 3 write the same values as 0 and
   // 1), so that thread tid < 128 finds the scale of row tid where its own
   // wave's load put it.  SC[par][set] holds sA[row] * sB[set] for the
@@ -329,7 +331,7 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
     };
     if (AF == ACT_FP8) {
       constexpr int NC = (RS + 3) / 4;
-      v4i a0[2], a1[2];
+      v4i a0[3], a1[3];
       v4f p[2][4], scv[NSET][NC];
 #pragma unroll
       for (int st = 0; st < NSET; ++st)
@@ -337,17 +339,20 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
         for (int c = 0; c < NC; ++c) scv[st][c] = lds_ld<v4f>(lds, sc_rd + sco + st * L::kScRows * 4 + c * 16);
       auto lda = [&](int rs) __attribute__((always_inline)) {
         const uint32_t ao = so + rs * 16 * AB;
-        a0[rs & 1] = lds_ld<v4i>(lds, a_rd[0] + ao);
-        a1[rs & 1] = lds_ld<v4i>(lds, a_rd[1] + ao);
+        a0[rs % 3] = lds_ld<v4i>(lds, a_rd[0] + ao);
+        a1[rs % 3] = lds_ld<v4i>(lds, a_rd[1] + ao);
       };
+      // A operands are read two subtiles ahead (three register sets), which
+      // gives each LDS read about two subtiles of MFMA time to land
       lda(0);
+      if (RS > 1) lda(1);
 #pragma unroll
       for (int rs = 0; rs <= RS; ++rs) {
         __builtin_amdgcn_sched_barrier(0);
         issue_share(rs);
-        if (rs + 1 < RS) lda(rs + 1);
+        if (rs + 2 < RS) lda(rs + 2);
         if (rs < RS) {
-          const v4i x0 = a0[rs & 1], x1 = a1[rs & 1];
+          const v4i x0 = a0[rs % 3], x1 = a1[rs % 3];
           const v8i av = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
 #pragma unroll
           for (int cs = 0; cs < 4; ++cs) {
@@ -418,72 +423,75 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
     }
   };
 
-  // ---- main loop.  A (three LDS stages, direct loads) and the activation
-  // scales are loaded two steps ahead, B NBUF-1 steps ahead (NBUF register
-  // buffers).  Step s: compute s while issuing scale(s+2), A(s+2) and
-  // B(s+NBUF-1), spread over the compute; publish the row scales of s+1;
-  // then a barrier that first waits until only this step's loads may still
-  // be in flight, so A(s+1) (issued a step earlier) has landed in LDS for
-  // every wave.  The vector memory counter
-  // completes in order, so every load gets about two steps of latency.
-  // Loads for steps past the end are issued anyway (buffer loads past a
-  // buffer's end read zero, and those stages are never computed): the step
-  // stays straight-line, which keeps the compiler's wait counts exact.  The
-  // prologue issues its loads in the steady state's order, so that the
-  // compiler's wait counts at the loop head are as exact as inside the loop.
+  // ---- main loop.  A (PD + 1 LDS stages, direct loads) is loaded PD steps
+  // ahead, the activation scales PD + 1 steps ahead, B NBUF - 1 steps ahead
+  // (NBUF register buffers).  Step s: read the scales of s+1, compute s while
+  // issuing scale(s+PD+1), A(s+PD) and B(s+NBUF-1), spread over the compute,
+  // publish the row scales of s+1, then a barrier that first waits until
+  // only the loads of the last PD-1 steps may still be in flight: A(s+1) has
+  // then landed in LDS for every wave, and so has scale(s+2).  The vector
+  // memory counter completes in order, so every load gets about PD-1 steps
+  // of latency.  Loads for steps past the end are issued anyway (buffer
+  // loads past a buffer's end read zero, and those stages are never
+  // computed): the step stays straight-line, which keeps the compiler's wait
+  // counts exact.  The prologue issues its loads in the steady state's order
+  // and group sizes, so the barrier's count means the same from step 0 on.
   constexpr int NSA = (AF == ACT_FP8) ? 1 : 0;
   constexpr int NLOAD = NSA + NDMA + NB;           // global loads issued per step
+  static_assert((PD - 1) * NLOAD < 64 && PD * NLOAD < 64, "vmcnt range");
+  static_assert(NBUF - 1 == PD || NSA == 0, "with activation scales, B runs PD steps ahead");
   BFrag bb[NBUF];
   auto issue_a = [&](int s) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < NDMA; ++j) dma_a(s, s, j);
+    for (int j = 0; j < NDMA; ++j) dma_a(s, s % L::kAStages, j);
   };
   auto load_b = [&](int s, BFrag& b) __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < NB; ++q) load_b_piece(s, b, q);
   };
-  // The prologue issues its loads in the steady state's order: scale(0),
-  // then A(0) and B(0) with scale(1), then A(1) and B(1) with scale(2).
-  // (sched_barrier keeps the compiler from reordering the groups, which
-  // would make its wait counts for B at the loop head nearly a full drain)
+  // Prologue: scale(0), then groups v = 0..PD-1 of {scale(v+1), A(v), B(v)
+  // if v < NBUF-1}.  (sched_barrier keeps the compiler from reordering the
+  // groups, which would make its wait counts for B at the loop head nearly a
+  // full drain.)
   if (NSA) dma_sa(0, 0);
-  if (NSA) dma_sa(1, 1);
-  issue_a(0);
-  __builtin_amdgcn_sched_barrier(0);
-  if (NBUF == 3) load_b(0, bb[0]);
-  __builtin_amdgcn_sched_barrier(0);
-  if (NSA) dma_sa(2, 2);
-  issue_a(1);
-  __builtin_amdgcn_sched_barrier(0);
-  load_b(NBUF - 2, bb[NBUF - 2]);
-  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int v = 0; v < PD; ++v) {
+    if (NSA) dma_sa(v + 1, (v + 1) % L::kSaSlots);
+    issue_a(v);
+    __builtin_amdgcn_sched_barrier(0);
+    if (v < NBUF - 1) load_b(v, bb[v]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // loads issued after scale(0), and after the last load of A(0)
+  constexpr int AFTER_SA0 = PD * (NSA + NDMA) + (NBUF - 1 < PD ? NBUF - 1 : PD) * NB;
+  constexpr int AFTER_A0 = AFTER_SA0 - NSA - NDMA;
+  static_assert(AFTER_SA0 < 64, "vmcnt range");
   if (NSA) {
-    wait_vmcnt<NSA + NDMA + (NBUF == 3 ? NB : 0) + NLOAD>();   // scale(0) is in LDS
+    wait_vmcnt<AFTER_SA0>();                       // scale(0) is in LDS
     store_scale(0, 0, read_sa(0));
   }
-  barrier_vmcnt<NLOAD>();
+  barrier_vmcnt<AFTER_A0>();                       // A(0) is in LDS for every wave
   if (signal_prev && tid == 0) __hip_atomic_fetch_add(signal_prev, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   // The loop body is UNR steps, a multiple of NBUF (B buffer rotation), of
-  // 2 (scale parity) and of kAStages (A stage rotation), so every buffer
-  // and LDS stage index in it is a compile-time constant; UNR > NBUF also
-  // makes the loop head, where the compiler's wait counts are merged from
-  // two paths and come out conservative, rarer.
-  constexpr int UNR = 6;
-  static_assert(UNR % NBUF == 0 && UNR % 2 == 0 && UNR % L::kAStages == 0, "loop unroll");
-  // Step s reads the scales of step s+1 (loaded two steps earlier, so they
-  // are in LDS since the previous step's barrier) into a register within
-  // the step: no loaded value is carried across the loop's back edge, where
-  // the compiler would drain every load in flight.
-  static_assert(UNR % L::kSaSlots == 0, "scale slot rotation");
+  // 2 (scale parity), of kAStages (A stage rotation) and of kSaSlots, so
+  // every buffer and LDS slot index in it is a compile-time constant; a long
+  // body also makes the loop head, where the compiler's wait counts are
+  // merged from two paths and come out conservative, rarer.  Step s reads
+  // the scales of step s+1 into a register within the step: no loaded value
+  // is carried across the loop's back edge, where the compiler would drain
+  // every load in flight.
+  constexpr int UNR = (AF == ACT_FP8) ? 8 : 6;
+  static_assert(UNR % NBUF == 0 && UNR % 2 == 0 && UNR % L::kAStages == 0 && UNR % L::kSaSlots == 0,
+                "loop unroll");
   auto step = [&](int s, int u) __attribute__((always_inline)) {
     const float sa_next = read_sa((u + 1) % L::kSaSlots);
     compute(u % L::kAStages, u & 1, bb[u % NBUF], NLOAD, [&](int j) __attribute__((always_inline)) {
-      if (j < NSA) dma_sa(s + 3, (u + 3) % L::kSaSlots);
-      else if (j < NSA + NDMA) dma_a(s + 2, (u + 2) % L::kAStages, j - NSA);
+      if (j < NSA) dma_sa(s + PD + 1, (u + PD + 1) % L::kSaSlots);
+      else if (j < NSA + NDMA) dma_a(s + PD, (u + PD) % L::kAStages, j - NSA);
       else load_b_piece(s + NBUF - 1, bb[(u + NBUF - 1) % NBUF], j - NSA - NDMA);
     });
     store_scale(s + 1, (u + 1) & 1, sa_next);
-    barrier_vmcnt<NLOAD>();
+    barrier_vmcnt<(PD - 1) * NLOAD>();
   };
   for (int s = 0; s < nsteps; s += UNR) {
 #pragma unroll

@@ -94,13 +94,19 @@ DEV void perm_scan(const int32_t* blockcnt, int nblk, int E, int tile_rows, int3
   int* cnt = lds;                   // [E] rows per expert, then expert offsets
   int* tcl = lds + E;               // [kXcds * E8] tiles per expert in class order, then first tiles
   int* scratch = tcl + kXcds * E8;  // [64]
+  // Blocks are read in batches of kBatch independent loads, so that the
+  // per-expert walk over blocks is not a chain of dependent memory round
+  // trips.  Pass 1: rows per expert.
+  constexpr int kBatch = 16;
   for (int i = threadIdx.x; i < kXcds * E8; i += blockDim.x) tcl[i] = 0;
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
     int run = 0;
-    for (int b = 0; b < nblk; ++b) {
-      const int c = blockcnt[(size_t)b * E + e];
-      base[(size_t)b * E + e] = run;
-      run += c;
+    for (int b0 = 0; b0 < nblk; b0 += kBatch) {
+      int c[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) c[i] = (b0 + i < nblk) ? blockcnt[(size_t)(b0 + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) run += c[i];
     }
     cnt[e] = run;
   }
@@ -113,7 +119,18 @@ DEV void perm_scan(const int32_t* blockcnt, int nblk, int E, int tile_rows, int3
     const int off = cnt[e];
     const int c = ((e + 1 < E) ? cnt[e + 1] : tot_rows) - off;
     offsets[e] = off;
-    for (int b = 0; b < nblk; ++b) base[(size_t)b * E + e] += off;
+    // pass 2: base[b][e] = off + rows of e in blocks before b
+    int run = off;
+    for (int b0 = 0; b0 < nblk; b0 += kBatch) {
+      int cb[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) cb[i] = (b0 + i < nblk) ? blockcnt[(size_t)(b0 + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        if (b0 + i < nblk) base[(size_t)(b0 + i) * E + e] = run;
+        run += cb[i];
+      }
+    }
     const int g0 = tcl[class_pos(e, E8)], gn = (c + tile_rows - 1) / tile_rows;
     for (int i = 0; i < gn; ++i) {
       const int rows = min(tile_rows, c - i * tile_rows);

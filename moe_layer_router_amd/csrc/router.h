@@ -181,46 +181,6 @@ DEV void router_tile(const RouterArgs& a, int t0, int e0, char* lds) {
   }
 }
 
-// Top-k of one token's logits by one wave.  Keys pack the order-preserving
-// image of the logit in the high word and (E-1-e) in the low word, so the
-// largest key is the largest logit with the lowest index.  E <= 1024, k <= 16.
-DEV void topk_token(const float* lrow, int E, int k, int32_t* ids, float* wts) {
-  const int lane = threadIdx.x & 63;
-  uint64_t key[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int e = lane + 64 * i;
-    key[i] = (e < E) ? (((uint64_t)f32_order_key(lrow[e]) << 32) | (uint32_t)(E - 1 - e)) : 0ull;
-  }
-  int my_id = 0;
-  float my_val = 0.f, top = 0.f;
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    if (j < k) {
-      uint64_t best = 0;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) best = key[i] > best ? key[i] : best;
-      best = wave_max_u64(best);
-      const int e = E - 1 - (int)(uint32_t)best;
-      const float val = f32_from_order_key((uint32_t)(best >> 32));
-      if (j == 0) top = val;
-      if (lane == j) { my_id = e; my_val = val; }
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        if (lane + 64 * i == e) key[i] = 0ull;
-    }
-  }
-  float ex = (lane < k) ? expf(my_val - top) : 0.f;
-  float sum = ex;
-#pragma unroll
-  for (int m = 1; m < 16; m <<= 1) sum += __shfl_xor(sum, m);
-  sum = __shfl(sum, 0);
-  if (lane < k) {
-    ids[lane] = my_id;
-    wts[lane] = ex / sum;
-  }
-}
-
 // Max of a 64-bit key over the 16 lanes of a DPP row (the same four moves as
 // row_max16), returned to every lane of the row.
 template <int CTRL>
@@ -243,6 +203,61 @@ DEV float row_sum16(float v) {
   v += dpp_mov<0x141>(v);
   v += dpp_mov<0x140>(v);
   return v;
+}
+
+// Max of a 64-bit key over the whole wave: row maxima by DPP, then the
+// gfx950 lane swaps across row pairs and wave halves.
+DEV uint64_t wave_max64(uint64_t v) {
+  v = row_max16_u64(v);
+  uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  const auto l16 = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+  const auto h16 = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+  uint64_t a = ((uint64_t)h16[0] << 32) | l16[0], b = ((uint64_t)h16[1] << 32) | l16[1];
+  v = a > b ? a : b;
+  lo = (uint32_t)v; hi = (uint32_t)(v >> 32);
+  const auto l32 = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+  const auto h32 = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+  a = ((uint64_t)h32[0] << 32) | l32[0];
+  b = ((uint64_t)h32[1] << 32) | l32[1];
+  return a > b ? a : b;
+}
+
+// Top-k of one token's logits by one wave.  Keys pack the order-preserving
+// image of the logit in the high word and (E-1-e) in the low word, so the
+// largest key is the largest logit with the lowest index.  E <= 1024, k <= 16.
+DEV void topk_token(const float* lrow, int E, int k, int32_t* ids, float* wts) {
+  const int lane = threadIdx.x & 63;
+  uint64_t key[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int e = lane + 64 * i;
+    key[i] = (e < E) ? (((uint64_t)f32_order_key(lrow[e]) << 32) | (uint32_t)(E - 1 - e)) : 0ull;
+  }
+  int my_id = 0;
+  float my_val = 0.f, top = 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    if (j < k) {
+      uint64_t best = key[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) best = key[i] > best ? key[i] : best;
+      best = wave_max64(best);
+      const int e = E - 1 - (int)(uint32_t)best;
+      const float val = f32_from_order_key((uint32_t)(best >> 32));
+      if (j == 0) top = val;
+      if (lane == j) { my_id = e; my_val = val; }
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (lane + 64 * i == e) key[i] = 0ull;
+    }
+  }
+  // the k <= 16 selected values sit in lanes 0..k-1 (the first DPP row)
+  const float ex = (lane < k) ? expf(my_val - top) : 0.f;
+  const float sum = row_sum16(ex);
+  if (lane < k) {
+    ids[lane] = my_id;
+    wts[lane] = ex / sum;
+  }
 }
 
 // Top-k of one token per DPP row (16 lanes), E <= 256, k <= 16: lane i of
