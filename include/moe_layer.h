@@ -142,7 +142,9 @@ size_t moe_permute_workspace_size(const moe_desc* d);
 
 /* Byte offsets, inside the moe_forward workspace, of the layer's internal
  * buffers, for inspection after the call has completed on its stream:
- *   logits        [T][E] fp32 router logits (bias included)
+ *   logits        [T][E] fp32 router logits (bias included); when T is small
+ *                 the region also holds the router's partial sums over
+ *                 slices of H, of which the logits are the first [T][E]
  *   perm, row_of  [T*top_k] int32 (used only when the caller passes no perm)
  *   offsets       [E+1] int32 (used only when the caller passes none)
  *   inter         [T*top_k][I] intermediate activations in permuted row

@@ -27,6 +27,7 @@ struct Plan {
   int routing_given;
   int nblk;                    // 256-token blocks
   int nTR, nER;                // router tiles (kRouterTokens x kRouterExperts)
+  int nKS;                     // router K slices (partial logits summed by the top-k)
   int max_tiles;
   int tile_rows;               // rows of a full GEMM tile
   int nnb1, nnb2;              // N blocks of gate|up (128 channels) and down (256 columns)
@@ -39,6 +40,7 @@ struct Plan {
   int32_t* err;                // device error word (byte offset 0)
   int32_t* ctr;                // [CTR_NUM]
   int32_t* rdone;              // [nTR]    router items finished per token tile
+  int32_t* rtile;              // [nTR*nER] K slices finished per router tile
   int32_t* tkdone;             // [nblk]   top-k items finished per 256-token block
   int32_t* done1;              // [max_tiles] gate|up items finished per tile
   int32_t* done2;              // [nnb2]   down items finished per N block

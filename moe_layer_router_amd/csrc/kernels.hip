@@ -16,10 +16,24 @@ __global__ void k_zero(int32_t* p, size_t n) {
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = 0;
 }
 
+// K slice ks of nks: router steps [s0, s1) of H/128.
+DEV void router_slice(int H, int ks, int nks, int* s0, int* s1) {
+  const int nsteps = H / 128;
+  *s0 = ks * nsteps / nks;
+  *s1 = (ks + 1) * nsteps / nks;
+}
+
+// Router tiles (blockIdx.x: 64 experts, .y: 128 tokens, .z: K slice); slice
+// ks writes its partial logits to a.logits + ks*T*E, and the last slice of a
+// tile to finish sums them into slice 0 (tile_cnt: one counter per tile).
 template <int AF>
-__global__ void __launch_bounds__(256) k_router(RouterArgs a) {
+__global__ void __launch_bounds__(256) k_router(RouterArgs a, int nks, int32_t* tile_cnt) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
-  router_tile<AF>(a, blockIdx.y * kRouterTokens, blockIdx.x * kRouterExperts, lds);
+  int s0, s1;
+  router_slice(a.H, blockIdx.z, nks, &s0, &s1);
+  const int t0 = blockIdx.y * kRouterTokens, e0 = blockIdx.x * kRouterExperts;
+  router_tile<AF>(a, t0, e0, lds, s0, s1, a.logits + (size_t)blockIdx.z * a.T * a.E, blockIdx.z == 0);
+  if (nks > 1) router_reduce(a, t0, e0, nks, &tile_cnt[blockIdx.y * gridDim.x + blockIdx.x]);
 }
 
 constexpr int kTopkTokens = 32;   // tokens per top-k workgroup (separate mode)
@@ -165,7 +179,7 @@ DEV void signal_add(int32_t* c0, int32_t* c1 = nullptr) {
 // has been claimed by a running workgroup, so no wait can deadlock whatever
 // the grid size:
 //   head queue:   router tiles (128 tokens x 64 experts) -> rdone[token tile]
-//                 top-k of 128 tokens                    -> tkdone[256-token block]
+//                 top-k of 32 tokens                     -> tkdone[256-token block]
 //                 expert histogram of 256 tokens        -> COUNT_DONE
 //                 scan (offsets, block bases, tiles)    -> SCAN_FLAG
 //                 stable scatter of 256 tokens          -> SCATTER_DONE
@@ -184,14 +198,19 @@ __device__ __forceinline__ void mega_gemm_item(const Plan& p, Tile tl, int nb, i
   expert_gemm_item<AF, WF, STAGE, 1>(gemm_args(p), tl, nb, lds, signal_prev);
 }
 template <int AF>
-__device__ __noinline__ void mega_router_item(Plan p, int tt, int et) {
+__device__ __noinline__ void mega_router_item(Plan p, int tt, int et, int ks) {
   MEGA_LDS;
   RouterArgs ra{p.x, p.x_scales, p.wr, p.bias, p.logits, p.T, p.H, p.E, p.act_fp8};
-  router_tile<AF>(ra, tt * kRouterTokens, et * kRouterExperts, lds);
+  int s0, s1;
+  router_slice(p.H, ks, p.nKS, &s0, &s1);
+  router_tile<AF>(ra, tt * kRouterTokens, et * kRouterExperts, lds, s0, s1, p.logits + (size_t)ks * p.T * p.E,
+                  ks == 0);
+  if (p.nKS > 1) router_reduce(ra, tt * kRouterTokens, et * kRouterExperts, p.nKS, &p.rtile[tt * p.nER + et]);
 }
-__device__ __noinline__ void mega_topk_item(Plan p, int tt) {
-  const int t0 = tt * kRouterTokens;
-  topk_tokens(p.logits, p.E, p.k, t0, min(kRouterTokens, p.T - t0), p.ids, p.wts);
+constexpr int kTopkItemTokens = 32;        // tokens per top-k item of the persistent kernel
+__device__ __noinline__ void mega_topk_item(Plan p, int i) {
+  const int t0 = i * kTopkItemTokens;
+  topk_tokens(p.logits, p.E, p.k, t0, min(kTopkItemTokens, p.T - t0), p.ids, p.wts);
 }
 __device__ __noinline__ void mega_count_item(Plan p, int b) {
   MEGA_LDS;
@@ -216,8 +235,8 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_wav
 k_mega(Plan p) {
   __shared__ int s_q, s_ok, s_first[kXcds + 1];
   const int tid = threadIdx.x;
-  const int nR = p.routing_given ? 0 : p.nTR * p.nER;
-  const int nK = p.routing_given ? 0 : p.nTR;
+  const int nR = p.routing_given ? 0 : p.nTR * p.nER * p.nKS;
+  const int nK = p.routing_given ? 0 : (p.T + kTopkItemTokens - 1) / kTopkItemTokens;
   const int q_topk = nR, q_count = nR + nK, q_scan = q_count + p.nblk;
   const int q_scat = q_scan + 1, q_end = q_scat + p.nblk;
 
@@ -229,20 +248,21 @@ k_mega(Plan p) {
     __syncthreads();
     if (q >= q_end) break;
     if (q < q_topk) {
-      const int tt = q / p.nER, et = q % p.nER;
-      mega_router_item<AF>(p, tt, et);
+      const int per_tt = p.nER * p.nKS;
+      const int tt = q / per_tt, et = (q % per_tt) / p.nKS, ks = q % p.nKS;
+      mega_router_item<AF>(p, tt, et, ks);
       signal_add(&p.rdone[tt]);
     } else if (q < q_count) {
-      const int tt = q - q_topk;
-      if (!wait_counter(&p.rdone[tt], p.nER, p.err, &s_ok)) return;
-      mega_topk_item(p, tt);
-      signal_add(&p.tkdone[tt / (kPermBlock / kRouterTokens)]);
+      const int i = q - q_topk;                          // tokens [32i, 32i+32)
+      if (!wait_counter(&p.rdone[i / (kRouterTokens / kTopkItemTokens)], p.nER * p.nKS, p.err, &s_ok)) return;
+      mega_topk_item(p, i);
+      signal_add(&p.tkdone[i / (kPermBlock / kTopkItemTokens)]);
     } else if (q < q_scan) {
       const int b = q - q_count;
       if (!p.routing_given) {
-        constexpr int kPer = kPermBlock / kRouterTokens;   // router token tiles per block
-        const int tiles_in_block = min(kPer, p.nTR - kPer * b);
-        if (!wait_counter(&p.tkdone[b], tiles_in_block, p.err, &s_ok)) return;
+        constexpr int kPer = kPermBlock / kTopkItemTokens;   // top-k items per block
+        const int items_in_block = min(kPer, nK - kPer * b);
+        if (!wait_counter(&p.tkdone[b], items_in_block, p.err, &s_ok)) return;
       }
       mega_count_item(p, b);
       signal_add(&p.ctr[CTR_COUNT_DONE]);
@@ -342,9 +362,9 @@ moe_status fail(moe_status s, const char* fmt, ...) {
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t err, zero_begin, ctr, rdone, tkdone, done1, done2, zero_end;
+  size_t err, zero_begin, ctr, rdone, rtile, tkdone, done1, done2, zero_end;
   size_t logits, blockcnt, base, offsets, perm, row_of, tiles, meta, aq, sa, staging, total;
-  int nblk, nTR, nER, max_tiles, nnb1, nnb2;
+  int nblk, nTR, nER, nKS, max_tiles, nnb1, nnb2;
 };
 
 Layout make_layout(const moe_desc* d) {
@@ -353,6 +373,20 @@ Layout make_layout(const moe_desc* d) {
   L.nblk = (int)((T + kPermBlock - 1) / kPermBlock);
   L.nTR = (int)((T + kRouterTokens - 1) / kRouterTokens);
   L.nER = (int)((E + kRouterExperts - 1) / kRouterExperts);
+  // K slices of the router: when the token x expert tiles are too few to
+  // fill the GPU (small T, as in decode), each tile's channels are split
+  // into up to H/512 slices whose partial logits the top-k sums
+  {
+    const int tiles = L.nTR * L.nER, nsteps = (int)(H / 128);
+    int s = 1;
+    if (tiles < 128) {
+      s = (256 + tiles - 1) / tiles;
+      s = s < nsteps / 4 ? s : nsteps / 4;
+      s = s < 8 ? s : 8;
+      s = s > 1 ? s : 1;
+    }
+    L.nKS = s;
+  }
   L.max_tiles = (int)(E + (T * k + kMinTileRows - 1) / kMinTileRows);
   L.nnb1 = (int)(I / 128);
   L.nnb2 = (int)((H + 255) / 256);
@@ -361,12 +395,13 @@ Layout make_layout(const moe_desc* d) {
   L.zero_begin = o;
   L.ctr = o; o += CTR_NUM * 4;
   L.rdone = o; o += (size_t)L.nTR * 4;
+  L.rtile = o; o += (size_t)L.nTR * L.nER * 4;
   L.tkdone = o; o += (size_t)L.nblk * 4;
   L.done1 = o; o += (size_t)L.max_tiles * 4;
   L.done2 = o; o += (size_t)L.nnb2 * 4;
   L.zero_end = o;
   o = align256(o);
-  L.logits = o; o = align256(o + T * E * 4);
+  L.logits = o; o = align256(o + (size_t)L.nKS * T * E * 4);
   L.blockcnt = o; o = align256(o + (size_t)L.nblk * E * 4);
   L.base = o; o = align256(o + (size_t)L.nblk * E * 4);
   L.offsets = o; o = align256(o + (E + 1) * 4);
@@ -456,13 +491,14 @@ moe_status fill_plan(const moe_desc* d, const Layout& L, char* ws, Plan* P) {
   p.act_fp8 = d->act_dtype == MOE_DTYPE_FP8_E4M3;
   p.wdt = d->weight_dtype == MOE_DTYPE_FP8_E4M3 ? W_FP8 : d->weight_dtype == MOE_DTYPE_FP4_E2M1 ? W_FP4 : W_BF16;
   p.routing_given = (d->flags & MOE_FLAG_ROUTING_GIVEN) != 0;
-  p.nblk = L.nblk; p.nTR = L.nTR; p.nER = L.nER; p.max_tiles = L.max_tiles;
+  p.nblk = L.nblk; p.nTR = L.nTR; p.nER = L.nER; p.nKS = L.nKS; p.max_tiles = L.max_tiles;
   p.tile_rows = p.act_fp8 ? GemmLds<ACT_FP8>::kRows : GemmLds<ACT_BF16>::kRows;
   p.nnb1 = L.nnb1; p.nnb2 = L.nnb2;
   p.nCT = (d->T + kCombineTokens - 1) / kCombineTokens;
   p.err = reinterpret_cast<int32_t*>(ws + L.err);
   p.ctr = reinterpret_cast<int32_t*>(ws + L.ctr);
   p.rdone = reinterpret_cast<int32_t*>(ws + L.rdone);
+  p.rtile = reinterpret_cast<int32_t*>(ws + L.rtile);
   p.tkdone = reinterpret_cast<int32_t*>(ws + L.tkdone);
   p.done1 = reinterpret_cast<int32_t*>(ws + L.done1);
   p.done2 = reinterpret_cast<int32_t*>(ws + L.done2);
@@ -512,14 +548,16 @@ int mega_lds(const Plan& p) {
   return b;
 }
 
-moe_status launch_route(const Plan& p, float* logits, hipStream_t st) {
+// nks: K slices (partials at logits + ks*T*E; the top-k leaves the logits in
+// slice 0).
+moe_status launch_route(const Plan& p, float* logits, int nks, hipStream_t st) {
   RouterArgs ra{p.x, p.x_scales, p.wr, p.bias, logits, p.T, p.H, p.E, p.act_fp8};
   if (p.act_fp8) {
     TRY(set_lds_limit(k_router<ACT_FP8>, kRouterLds));
-    hipLaunchKernelGGL(k_router<ACT_FP8>, dim3(p.nER, p.nTR), dim3(256), kRouterLds, st, ra);
+    hipLaunchKernelGGL(k_router<ACT_FP8>, dim3(p.nER, p.nTR, nks), dim3(256), kRouterLds, st, ra, nks, p.rtile);
   } else {
     TRY(set_lds_limit(k_router<ACT_BF16>, kRouterLds));
-    hipLaunchKernelGGL(k_router<ACT_BF16>, dim3(p.nER, p.nTR), dim3(256), kRouterLds, st, ra);
+    hipLaunchKernelGGL(k_router<ACT_BF16>, dim3(p.nER, p.nTR, nks), dim3(256), kRouterLds, st, ra, nks, p.rtile);
   }
   HIP_TRY(hipGetLastError());
   hipLaunchKernelGGL(k_topk, dim3((p.T + kTopkTokens - 1) / kTopkTokens), dim3(256), 0, st, logits, p.T, p.E, p.k,
@@ -545,7 +583,7 @@ moe_status launch_layer(const Plan& p, const DevInfo& di, int mode, hipStream_t 
   hipLaunchKernelGGL(k_zero, dim3(16), dim3(256), 0, st, p.err, zero_ints);
   HIP_TRY(hipGetLastError());
   if (mode == MOE_MODE_SEPARATE) {
-    if (!p.routing_given) TRY(launch_route(p, p.logits, st));
+    if (!p.routing_given) TRY(launch_route(p, p.logits, p.nKS, st));
     TRY(launch_permute(p, p.row_of, st));
     const GemmArgs g = gemm_args(p);
     const int lds = gemm_lds(AF == ACT_FP8);
@@ -678,7 +716,7 @@ moe_status moe_route(const moe_desc* d, const void* x, const float* x_scales, co
   p.x = static_cast<const uint8_t*>(x); p.x_scales = x_scales;
   p.wr = static_cast<const uint16_t*>(router_w); p.bias = router_bias;
   p.ids = topk_ids; p.wts = topk_weights;
-  return launch_route(p, logits ? logits : p.logits, static_cast<hipStream_t>(stream));
+  return launch_route(p, logits ? logits : p.logits, 1, static_cast<hipStream_t>(stream));
 }
 
 moe_status moe_permute(const moe_desc* d, const int32_t* topk_ids, int32_t* expert_offsets, int32_t* perm,

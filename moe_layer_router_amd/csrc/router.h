@@ -32,7 +32,9 @@ constexpr int kRouterSc = kRouterX + 128 * 256;
 constexpr int kRouterStage = kRouterSc + 4 * 256;
 constexpr int kRouterLds = kRouterStages * kRouterStage;
 
-// Logits of tokens [t0, t0+128) x experts [e0, e0+64) on 256 threads.
+// Logits of tokens [t0, t0+128) x experts [e0, e0+64) on 256 threads, over
+// the K steps [s0, s1) (128 channels each), written to `out` ([T][E]); the
+// bias is added when add_bias (the K slice that starts at channel 0).
 //
 // The logits are a dense [T, H] x [H, E] product, so the tile runs on 16x16x32
 // BF16 MFMAs: E4M3 activations convert exactly to BF16 with the gfx950
@@ -47,7 +49,7 @@ constexpr int kRouterLds = kRouterStages * kRouterStage;
 // lane reads contiguous bytes.  E4M3: each step's partial sum is scaled by the
 // token's scale of that 128-channel block and added to the fp32 logits.
 template <int AF>
-DEV void router_tile(const RouterArgs& a, int t0, int e0, char* lds) {
+DEV void router_tile(const RouterArgs& a, int t0, int e0, char* lds, int s0, int s1, float* out, bool add_bias) {
   constexpr int XB = (AF == ACT_FP8) ? 128 : 256;          // activation bytes per token per step
   constexpr int NW = 4;                                      // weight loads per wave per step (1 KB each)
   constexpr int NX = XB * 128 / 1024 / 4;                    // activation loads per wave per step
@@ -55,7 +57,6 @@ DEV void router_tile(const RouterArgs& a, int t0, int e0, char* lds) {
   constexpr int NLOAD = NW + NX + NS;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
-  const int nsteps = a.H / 128;
 
   const rsrc_t wrs = make_rsrc(a.wr, (uint32_t)a.E * (uint32_t)a.H * 2);
   const rsrc_t xrs = make_rsrc(a.x, (uint32_t)a.T * (uint32_t)a.H * (XB / 128));
@@ -101,12 +102,12 @@ DEV void router_tile(const RouterArgs& a, int t0, int e0, char* lds) {
     for (int c = 0; c < 4; ++c) acc[st][c] = v4f{0.f, 0.f, 0.f, 0.f};
 
 #pragma unroll
-  for (int j = 0; j < NLOAD; ++j) issue(0, j);
+  for (int j = 0; j < NLOAD; ++j) issue(s0, j);
 #pragma unroll
-  for (int j = 0; j < NLOAD; ++j) issue(1, j);
+  for (int j = 0; j < NLOAD; ++j) issue(s0 + 1, j);
   barrier_vmcnt<NLOAD>();
 
-  for (int s = 0; s < nsteps; ++s) {
+  for (int s = s0; s < s1; ++s) {
     const char* st = lds + (s % kRouterStages) * kRouterStage;
     // A operands of both token subtiles
     v8bf av[2][4];
@@ -170,14 +171,52 @@ DEV void router_tile(const RouterArgs& a, int t0, int e0, char* lds) {
   for (int c = 0; c < 4; ++c) {
     const int e = e0 + 16 * c + c16;
     if (e >= a.E) continue;
-    const float b = a.bias ? a.bias[e] : 0.f;
+    const float b = (add_bias && a.bias) ? a.bias[e] : 0.f;
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int t = t0 + 32 * w + 16 * sub + 4 * g + v;
-        if (t < a.T) a.logits[(size_t)t * a.E + e] = acc[sub][c][v] + b;
+        if (t < a.T) out[(size_t)t * a.E + e] = acc[sub][c][v] + b;
       }
+  }
+}
+
+// With the channels split into S slices (partials at a.logits + s*T*E),
+// the last of the S tiles of (t0, e0) to finish (counted in *tile_cnt) sums
+// the partials of the tile, in slice order, into slice 0.
+DEV void router_reduce(const RouterArgs& a, int t0, int e0, int S, int32_t* tile_cnt) {
+  __shared__ int s_last;
+  __threadfence();                                 // publish this slice's partials
+  __syncthreads();
+  if (threadIdx.x == 0) s_last = (atomicAdd(tile_cnt, 1) == S - 1);
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();                                 // the other slices' partials are visible
+  const size_t stride = (size_t)a.T * a.E;
+  const int ne = min(kRouterExperts, a.E - e0), nt = min(kRouterTokens, a.T - t0);
+  const int n = nt * ne;
+  constexpr int kB = 4, kMaxS = 16;                // elements per batch; all their loads in flight
+  for (int i0 = threadIdx.x * kB; i0 < n; i0 += blockDim.x * kB) {
+    float v[kB], p[kB][kMaxS];
+    size_t off[kB];
+#pragma unroll
+    for (int u = 0; u < kB; ++u) {
+      const int i = min(i0 + u, n - 1);
+      off[u] = (size_t)(t0 + i / ne) * a.E + e0 + i % ne;
+#pragma unroll
+      for (int s = 0; s < kMaxS; ++s) p[u][s] = (s < S) ? a.logits[s * stride + off[u]] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < kB; ++u) {
+      v[u] = p[u][0];
+#pragma unroll
+      for (int s = 1; s < kMaxS; ++s)
+        if (s < S) v[u] += p[u][s];
+    }
+#pragma unroll
+    for (int u = 0; u < kB; ++u)
+      if (i0 + u < n) a.logits[off[u]] = v[u];
   }
 }
 
@@ -299,6 +338,7 @@ DEV void topk_token16(const float* lrow, bool valid, int E, int k, int32_t* ids,
 // Top-k for `count` consecutive tokens starting at t0: one token per DPP row
 // (16 per workgroup pass) when E <= 256, else one wave per token.
 DEV void topk_tokens(const float* logits, int E, int k, int t0, int count, int32_t* ids, float* wts) {
+
   if (E <= 256) {
     const int rowid = threadIdx.x >> 4, nrows = blockDim.x >> 4;
     for (int i0 = 0; i0 < count; i0 += nrows) {
