@@ -375,7 +375,8 @@ Layout make_layout(const moe_desc* d) {
   L.nER = (int)((E + kRouterExperts - 1) / kRouterExperts);
   // K slices of the router: when the token x expert tiles are too few to
   // fill the GPU (small T, as in decode), each tile's channels are split
-  // into up to H/512 slices whose partial logits the top-k sums
+  // into up to H/512 slices (at most 8), whose partial logits the last
+  // slice of each tile to finish sums
   {
     const int tiles = L.nTR * L.nER, nsteps = (int)(H / 128);
     int s = 1;

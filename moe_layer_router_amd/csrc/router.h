@@ -196,7 +196,7 @@ DEV void router_reduce(const RouterArgs& a, int t0, int e0, int S, int32_t* tile
   const size_t stride = (size_t)a.T * a.E;
   const int ne = min(kRouterExperts, a.E - e0), nt = min(kRouterTokens, a.T - t0);
   const int n = nt * ne;
-  constexpr int kB = 4, kMaxS = 16;                // elements per batch; all their loads in flight
+  constexpr int kB = 8, kMaxS = 8;                 // elements per batch; all their loads in flight
   for (int i0 = threadIdx.x * kB; i0 < n; i0 += blockDim.x * kB) {
     float v[kB], p[kB][kMaxS];
     size_t off[kB];
