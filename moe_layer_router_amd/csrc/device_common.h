@@ -137,6 +137,19 @@ typedef __attribute__((address_space(3))) void lds_void;
 DEV rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
 }
+// A buffer's base, size and scalar offset are wave-uniform by contract (the
+// instruction takes them from scalar registers).  Non-inlined device
+// functions receive their arguments in vector registers, so the compiler
+// cannot see that and would wrap each access in a loop over the distinct
+// values; reading the first lane states the uniformity.  Code that runs in
+// such functions builds its buffers with make_rsrc_u and passes scalar
+// offsets through uni().
+DEV uint32_t uni(uint32_t v) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)v); }
+DEV rsrc_t make_rsrc_u(const void* base, uint32_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint64_t bu = ((uint64_t)uni((uint32_t)(b >> 32)) << 32) | uni((uint32_t)b);
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(bu), 0, (int)uni(bytes), 0x00020000);
+}
 // Cache policy of a buffer access (the instruction's cache-coherence bits):
 // 0 = default; kCoherent (sc1) = device-scope coherent.  The L2 of each XCD
 // is not coherent with the others: data that one workgroup writes and a

@@ -636,7 +636,7 @@ DEV void expert_gemm_item(const GemmArgs& g, const Tile& t, int nb, char* lds, i
 // lies in one (row, 256-column block), written once per launch, write-through,
 // before the block's counter that the caller waits for.
 DEV void combine_rows(const uint16_t* staging, uint16_t* y, int T, int H, int k, int t0, int t1, int n0, int n1) {
-  const rsrc_t srs = make_rsrc(staging, (uint32_t)T * (uint32_t)k * (uint32_t)H * 2);
+  const rsrc_t srs = make_rsrc_u(staging, (uint32_t)T * (uint32_t)k * (uint32_t)H * 2);
   const int cpt = (n1 - n0) / 8;
   const int total = (t1 - t0) * cpt;
   // U (token, 8-channel) pairs per thread and pass, rows read four j at a

@@ -190,6 +190,22 @@ DEV void signal_add(int32_t* c0, int32_t* c1 = nullptr) {
 // that register allocation sees one phase at a time.  Each declares the
 // dynamic LDS array itself so that its accesses compile to LDS instructions.
 #define MEGA_LDS extern __shared__ __attribute__((aligned(16))) char lds[]
+// Their arguments arrive in vector registers, where the compiler cannot tell
+// that they are the same in every lane: buffer accesses would then loop over
+// distinct descriptors and loops over plan sizes would run as divergent
+// loops.  Every argument is wave-uniform, so each phase starts by taking
+// them from the first lane.
+static_assert(sizeof(Plan) % 4 == 0, "plan words");
+DEV Plan uniform_plan(const Plan& in) {
+  uint32_t w[sizeof(Plan) / 4];
+  __builtin_memcpy(w, &in, sizeof(Plan));
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(Plan) / 4); ++i) w[i] = uni(w[i]);
+  Plan p;
+  __builtin_memcpy(&p, w, sizeof(Plan));
+  return p;
+}
+DEV int uni_i(int v) { return __builtin_amdgcn_readfirstlane(v); }
 // The GEMM items are inlined into the kernel: as a called function they
 // would save and restore the callee-saved VGPRs they use on every item.
 template <int AF, int WF, int STAGE>
@@ -198,8 +214,10 @@ __device__ __forceinline__ void mega_gemm_item(const Plan& p, Tile tl, int nb, i
   expert_gemm_item<AF, WF, STAGE, 1>(gemm_args(p), tl, nb, lds, signal_prev);
 }
 template <int AF>
-__device__ __noinline__ void mega_router_item(Plan p, int tt, int et, int ks) {
+__device__ __noinline__ void mega_router_item(Plan pv, int tt_, int et_, int ks_) {
   MEGA_LDS;
+  const Plan p = uniform_plan(pv);
+  const int tt = uni_i(tt_), et = uni_i(et_), ks = uni_i(ks_);
   RouterArgs ra{p.x, p.x_scales, p.wr, p.bias, p.logits, p.T, p.H, p.E, p.act_fp8};
   int s0, s1;
   router_slice(p.H, ks, p.nKS, &s0, &s1);
@@ -208,24 +226,31 @@ __device__ __noinline__ void mega_router_item(Plan p, int tt, int et, int ks) {
   if (p.nKS > 1) router_reduce(ra, tt * kRouterTokens, et * kRouterExperts, p.nKS, &p.rtile[tt * p.nER + et]);
 }
 constexpr int kTopkItemTokens = 32;        // tokens per top-k item of the persistent kernel
-__device__ __noinline__ void mega_topk_item(Plan p, int i) {
-  const int t0 = i * kTopkItemTokens;
+__device__ __noinline__ void mega_topk_item(Plan pv, int i) {
+  const Plan p = uniform_plan(pv);
+  const int t0 = uni_i(i) * kTopkItemTokens;
   topk_tokens(p.logits, p.E, p.k, t0, min(kTopkItemTokens, p.T - t0), p.ids, p.wts);
 }
-__device__ __noinline__ void mega_count_item(Plan p, int b) {
+__device__ __noinline__ void mega_count_item(Plan pv, int b_) {
   MEGA_LDS;
+  const Plan p = uniform_plan(pv);
+  const int b = uni_i(b_);
   perm_count_block(p.ids, p.T, p.k, p.E, b, p.blockcnt, reinterpret_cast<int*>(lds));
 }
-__device__ __noinline__ void mega_scan_item(Plan p) {
+__device__ __noinline__ void mega_scan_item(Plan pv) {
   MEGA_LDS;
+  const Plan p = uniform_plan(pv);
   perm_scan(p.blockcnt, p.nblk, p.E, p.tile_rows, p.base, p.offsets, p.tiles, p.meta, reinterpret_cast<int*>(lds));
 }
-__device__ __noinline__ void mega_scatter_item(Plan p, int b) {
+__device__ __noinline__ void mega_scatter_item(Plan pv, int b_) {
   MEGA_LDS;
+  const Plan p = uniform_plan(pv);
+  const int b = uni_i(b_);
   perm_scatter_block(p.ids, p.T, p.k, p.E, b, p.base, p.perm, p.row_of, reinterpret_cast<uint64_t*>(lds));
 }
-__device__ __noinline__ void mega_combine_item(Plan p, int nb, int c) {
-  const int t0 = c * kCombineTokens;
+__device__ __noinline__ void mega_combine_item(Plan pv, int nb_, int c) {
+  const Plan p = uniform_plan(pv);
+  const int nb = uni_i(nb_), t0 = uni_i(c) * kCombineTokens;
   combine_rows(p.staging, p.y, p.T, p.H, p.k, t0, min(p.T, t0 + kCombineTokens), nb * 256,
                   min(p.H, nb * 256 + 256));
 }

@@ -58,9 +58,9 @@ DEV void router_tile(const RouterArgs& a, int t0, int e0, char* lds, int s0, int
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
 
-  const rsrc_t wrs = make_rsrc(a.wr, (uint32_t)a.E * (uint32_t)a.H * 2);
-  const rsrc_t xrs = make_rsrc(a.x, (uint32_t)a.T * (uint32_t)a.H * (XB / 128));
-  const rsrc_t srs = make_rsrc(a.x_scales, (AF == ACT_FP8) ? (uint32_t)a.T * (uint32_t)(a.H / 128) * 4 : 0u);
+  const rsrc_t wrs = make_rsrc_u(a.wr, (uint32_t)a.E * (uint32_t)a.H * 2);
+  const rsrc_t xrs = make_rsrc_u(a.x, (uint32_t)a.T * (uint32_t)a.H * (XB / 128));
+  const rsrc_t srs = make_rsrc_u(a.x_scales, (AF == ACT_FP8) ? (uint32_t)a.T * (uint32_t)(a.H / 128) * 4 : 0u);
   // per-lane global offsets (step 0) of this wave's loads
   uint32_t woff[NW], xoff[NX];
 #pragma unroll
@@ -85,13 +85,13 @@ DEV void router_tile(const RouterArgs& a, int t0, int e0, char* lds, int s0, int
   auto issue = [&](int s, int j) __attribute__((always_inline)) {   // load j of step s
     char* st = lds + (s % kRouterStages) * kRouterStage;
     if (j < NW) {
-      buf_ld16_lds(wrs, st + kRouterW + (16 * w + 4 * j) * 256, woff[j], (uint32_t)s * 256);
+      buf_ld16_lds(wrs, st + kRouterW + (16 * w + 4 * j) * 256, woff[j], uni((uint32_t)s * 256));
     } else if (j < NW + NX) {
       const int jx = j - NW;
       const int rows = (AF == ACT_FP8) ? 8 : 4;
-      buf_ld16_lds(xrs, st + kRouterX + (32 * w + rows * jx) * XB, xoff[jx], (uint32_t)s * 128 * (XB / 128));
+      buf_ld16_lds(xrs, st + kRouterX + (32 * w + rows * jx) * XB, xoff[jx], uni((uint32_t)s * 128 * (XB / 128)));
     } else {
-      buf_ld4_lds(srs, st + kRouterSc + w * 256, soff, (uint32_t)s * 4);
+      buf_ld4_lds(srs, st + kRouterSc + w * 256, soff, uni((uint32_t)s * 4));
     }
   };
 
