@@ -7,6 +7,7 @@
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
@@ -31,10 +32,14 @@ DEV uint32_t f32_to_e4m3(float v) {
   v = fminf(fmaxf(v, -448.0f), 448.0f);
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v, 0.0f, 0, false) & 0xFFu;
 }
-DEV uint32_t f32x2_to_e4m3x2(float v0, float v1) {
+// Four E4M3 codes packed little-endian (v0 in the low byte), as above.
+DEV uint32_t f32x4_to_e4m3x4(float v0, float v1, float v2, float v3) {
   v0 = fminf(fmaxf(v0, -448.0f), 448.0f);
   v1 = fminf(fmaxf(v1, -448.0f), 448.0f);
-  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false) & 0xFFFFu;
+  v2 = fminf(fmaxf(v2, -448.0f), 448.0f);
+  v3 = fminf(fmaxf(v3, -448.0f), 448.0f);
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v2, v3, lo, true);
 }
 
 // Monotone map of fp32 onto uint32 (larger float -> larger key); -0 and +0
@@ -59,8 +64,9 @@ DEV float f32_from_order_key(uint32_t k) {
 DEV v4f mfma_fp8_fp8(const v8i& a, const v8i& b, const v4f& c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
-DEV v4f mfma_fp8_fp4(const v8i& a, const v8i& b, const v4f& c, int bscale) {
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 4, 0, 127, 0, bscale);
+// 4-bit A (E2M1, with its E8M0 scales) times 8-bit B (E4M3, unit scale).
+DEV v4f mfma_fp4_fp8(const v8i& a, const v8i& b, const v4f& c, int ascale) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 0, 0, ascale, 0, 127);
 }
 // 16x16x32 BF16 MFMA: lane l holds row/column l%16, 8 K of group l/16.
 DEV v4f mfma_bf16(const v8bf& a, const v8bf& b, const v4f& c) {
@@ -85,10 +91,15 @@ DEV float row_max16(float v) {
   return v;
 }
 
-// Value of lane (l & ~3) | V for every lane l (a DPP quad broadcast).
-template <int V>
-DEV float quad_bcast(float x) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), V * 0x55, 0xF, 0xF, true));
+// Max over the four lanes l % 16 + 16 g (g = 0..3), returned to each of
+// them: swap neighbouring rows of 16 lanes, then the two halves of the wave.
+DEV float max_row_groups(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto r16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+  const uint32_t h = __float_as_uint(x);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(h, h, false, false);
+  return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
 }
 
 // Inclusive prefix sum over a workgroup of `nthreads` (multiple of 64) ints.

@@ -286,10 +286,12 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
       chunk = 4 * i + gq;
     a_rd[i] = opaque(L::kA + c16 * AB + (a_swz<CPR>(c16, chunk) << 4));
   }
-  // this lane's row within a subtile for the DPP scale broadcast (MFMA output
-  // lane l holds rows 4*(l/16) + v; lane v of each quad fetches row 4*(l/16)+v)
+  // With FP8 activations the product is formed transposed: the weights are
+  // the MFMA's A operand and the activation rows its B operand, so output
+  // lane l holds row l%16 of the subtile (channels 4*(l/16) + v) and the
+  // promotion scale of its four values is one number per lane and subtile.
   constexpr int NSET = (STAGE == 1 && WF == W_FP8) ? 2 : 1;
-  const uint32_t sc_rd = opaque(L::kSC + (4 * gq + (c16 & 3)) * L::kMaxRs * 4 +
+  const uint32_t sc_rd = opaque(L::kSC + c16 * L::kMaxRs * 4 +
                                 ((STAGE == 2 && WF == W_FP8 && w >= 2) ? L::kScRows * 4 : 0));
 
   v4f acc[RS][4];
@@ -359,29 +361,20 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
             if (WF == W_FP8) {
               const v8i bv = {b.d[cs][0][0], b.d[cs][0][1], b.d[cs][0][2], b.d[cs][0][3],
                               b.d[cs][1][0], b.d[cs][1][1], b.d[cs][1][2], b.d[cs][1][3]};
-              p[rs & 1][cs] = mfma_fp8_fp8(av, bv, zero);
+              p[rs & 1][cs] = mfma_fp8_fp8(bv, av, zero);
             } else {
               const v8i bv = {b.d[cs][0][0], b.d[cs][0][1], b.d[cs][0][2], b.d[cs][0][3], 0, 0, 0, 0};
-              p[rs & 1][cs] = mfma_fp8_fp4(av, bv, zero, b.sc[cs]);
+              p[rs & 1][cs] = mfma_fp4_fp8(bv, av, zero, b.sc[cs]);
             }
           }
         }
         if (rs > 0) {
           const int q = rs - 1;
-          float bc[NSET][4];
-#pragma unroll
-          for (int st = 0; st < NSET; ++st) {
-            const float x = scv[st][q >> 2][q & 3];
-            bc[st][0] = quad_bcast<0>(x);
-            bc[st][1] = quad_bcast<1>(x);
-            bc[st][2] = quad_bcast<2>(x);
-            bc[st][3] = quad_bcast<3>(x);
-          }
 #pragma unroll
           for (int cs = 0; cs < 4; ++cs) {
-            const int st = (NSET == 2 && cs >= 2) ? 1 : 0;
+            const float sc = scv[(NSET == 2 && cs >= 2) ? 1 : 0][q >> 2][q & 3];
 #pragma unroll
-            for (int v = 0; v < 4; ++v) acc[q][cs][v] = __builtin_fmaf(p[q & 1][cs][v], bc[st][v], acc[q][cs][v]);
+            for (int v = 0; v < 4; ++v) acc[q][cs][v] = __builtin_fmaf(p[q & 1][cs][v], sc, acc[q][cs][v]);
           }
         }
         // One wave per SIMD: the matrix core only overlaps vector ALU work
@@ -391,7 +384,7 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);   // VALU
+            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // VALU
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
             __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // global load
           }
@@ -522,16 +515,18 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
     }
     auto av = [&](int rs, int q, int v) __attribute__((always_inline)) { return acc[rs][q][v]; };
     if (AF == ACT_FP8) {
+      // lane: row rs*16 + c16, channels 32w + 16q + 4gq + v of the item's 128
       float* RSC = reinterpret_cast<float*>(lds + L::kRsc);
-      const uint32_t amax_wr = opaque(L::kAmax + w * L::kRows * 4 + 16 * gq);
 #pragma unroll
-      for (int rs = 0; rs < RS; ++rs)
+      for (int rs = 0; rs < RS; ++rs) {
+        float mx = 0.f;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          float mx = fmaxf(fabsf(av(rs, 0, v)), fabsf(av(rs, 1, v)));
-          mx = row_max16(mx);
-          if (c16 == 0) lds_st(lds, amax_wr + (rs * 16 + v) * 4, mx);
-        }
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) mx = fmaxf(mx, fabsf(av(rs, q, v)));
+        mx = max_row_groups(mx);
+        if (gq == 0) lds_st(lds, L::kAmax + (w * L::kRows + rs * 16 + c16) * 4, mx);
+      }
       __syncthreads();
       if (tid < R) {
         const float* AMAX = reinterpret_cast<const float*>(lds + L::kAmax);
@@ -542,26 +537,26 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
         reinterpret_cast<float*>(lds + L::kRinv)[tid] = 1.0f / sc;
       }
       __syncthreads();
-      const uint32_t rinv_rd = opaque(L::kRinv + 16 * gq);
-      // Staging rows hold their 16-byte chunks permuted: chunk c of row r at
-      // c ^ ((r >> 2) & 3), so that the four row groups of one byte write
-      // (rows 4g + v, g = l/16) fall in different LDS banks.
-      const uint32_t wr0 = opaque(L::kA + 4 * gq * 128 + 16 * ((2 * w) ^ gq) + c16);
-      const uint32_t wr1 = opaque(L::kA + 4 * gq * 128 + 16 * ((2 * w + 1) ^ gq) + c16);
+      // Staging rows of 128 codes hold their 16-byte chunks permuted: chunk c
+      // of row r at c ^ ((r >> 1) & 7), so that the 16 rows of one 4-byte
+      // write (one per lane group position) spread over the LDS banks.
 #pragma unroll
-      for (int rs = 0; rs < RS; ++rs)
+      for (int rs = 0; rs < RS; ++rs) {
+        const int r = rs * 16 + c16;
+        const float inv = lds_ld<float>(lds, L::kRinv + r * 4);
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const float inv = lds_ld<float>(lds, rinv_rd + (rs * 16 + v) * 4);
-          lds_st(lds, wr0 + (rs * 16 + v) * 128, (uint8_t)f32_to_e4m3(av(rs, 0, v) * inv));
-          lds_st(lds, wr1 + (rs * 16 + v) * 128, (uint8_t)f32_to_e4m3(av(rs, 1, v) * inv));
+        for (int q = 0; q < 2; ++q) {
+          const uint32_t codes = f32x4_to_e4m3x4(av(rs, q, 0) * inv, av(rs, q, 1) * inv, av(rs, q, 2) * inv,
+                                                 av(rs, q, 3) * inv);
+          lds_st(lds, L::kA + r * 128 + (((2 * w + q) ^ ((r >> 1) & 7)) << 4) + 4 * gq, codes);
         }
+      }
       __syncthreads();
       for (int q = tid; q < R * 8; q += kGemmThreads) {
         const int row = q >> 3, c = q & 7;
         if (row < m)
           buf_st16<CP>(aqw, (uint32_t)(r0 + row) * g.I + c0 + c * 16,
-                       ld16(lds + L::kA + row * 128 + (c ^ ((row >> 2) & 3)) * 16));
+                       ld16(lds + L::kA + row * 128 + ((c ^ ((row >> 1) & 7)) << 4)));
       }
       if (tid < m) buf_stf<CP>(saw, ((uint32_t)(r0 + tid) * (g.I / 128) + c0 / 128) * 4, RSC[tid]);
     } else {
@@ -584,10 +579,41 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
                        ld16(lds + L::kA + row * 256 + (c ^ (((row >> 2) & 3) << 1)) * 16));
       }
     }
-  } else {
-    // chunks of CH row subtiles (at most 64 rows x 256 columns of BF16 = 32 KB)
+  } else if (AF == ACT_FP8) {
+    // lane: row rs*16 + c16, columns 64w + 16cs + 4gq + v of the N block.
+    // Chunks of CH row subtiles (at most 64 rows x 256 columns of BF16 =
+    // 32 KB); chunk c (16 bytes) of staging row r at c ^ (r & 15), so that
+    // the 16 rows of one 8-byte write spread over the LDS banks.
     constexpr int CH = (RS < 4) ? RS : 4;
-    // chunk c of staging row r at c ^ (((r >> 2) & 3) << 1) (bank spread)
+#pragma unroll
+    for (int h = 0; h < RS / CH; ++h) {
+      if (h > 0) __syncthreads();                  // previous chunk's copy-out is done
+#pragma unroll
+      for (int rs = CH * h; rs < CH * h + CH; ++rs) {
+        const int rl = (rs - CH * h) * 16 + c16;
+        const float rw = lds_ld<float>(lds, L::kRowW + (rs * 16 + c16) * 4);
+#pragma unroll
+        for (int cs = 0; cs < 4; ++cs) {
+          const uint32_t lo = f32_to_bf16_rne(acc[rs][cs][0] * rw) | (f32_to_bf16_rne(acc[rs][cs][1] * rw) << 16);
+          const uint32_t hi = f32_to_bf16_rne(acc[rs][cs][2] * rw) | (f32_to_bf16_rne(acc[rs][cs][3] * rw) << 16);
+          const int c = 8 * w + 2 * cs + (gq >> 1);
+          lds_st(lds, L::kA + rl * 512 + ((c ^ (rl & 15)) << 4) + 8 * (gq & 1), v2u{lo, hi});
+        }
+      }
+      __syncthreads();
+      for (int q = tid; q < CH * 16 * 32; q += kGemmThreads) {
+        const int rl = q >> 5, c = q & 31;
+        const int row = CH * 16 * h + rl, col = n0 + c * 8;
+        if (row < m && col < g.H)
+          buf_st16<CP>(stw, ((uint32_t)ROWI[row] * g.H + col) * 2, ld16(lds + L::kA + rl * 512 + ((c ^ (rl & 15)) << 4)));
+      }
+    }
+  } else {
+    // BF16 activations (product not transposed): lane holds rows 4gq + v,
+    // column 16cs + c16 of its 64.  Chunks of CH row subtiles (at most 64
+    // rows x 256 columns of BF16 = 32 KB); chunk c of staging row r at
+    // c ^ (((r >> 2) & 3) << 1) (bank spread).
+    constexpr int CH = (RS < 4) ? RS : 4;
     uint32_t wrc[4];
 #pragma unroll
     for (int cs = 0; cs < 4; ++cs)
