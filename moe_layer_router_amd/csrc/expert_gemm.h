@@ -123,8 +123,14 @@ DEV int a_swz(int row, int c) {
 // once the stores of this workgroup's previous item have completed: the
 // prologue's barrier below waits for every older memory operation of each
 // wave, so the previous item is signalled without a wait of its own.
-template <int AF, int WF, int STAGE, int RS, int COH>
-DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char* lds, int32_t* signal_prev) {
+// `at_loop_end()` is called by every thread once the K loop has ended,
+// before the epilogue.
+struct NoHook {
+  DEV void operator()() const {}
+};
+template <int AF, int WF, int STAGE, int RS, int COH, typename Hook>
+DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char* lds, int32_t* signal_prev,
+                          const Hook& at_loop_end) {
   constexpr int CP = COH ? kCoherent : 0;            // cache policy of cross-item data
   using L = GemmLds<AF>;
   static_assert(RS >= 1 && RS <= L::kMaxRs, "row subtiles");
@@ -495,6 +501,7 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
   }
   wait_vmcnt<0>();                                 // the last steps' overrun loads
   __syncthreads();
+  at_loop_end();
 
   // ---- epilogues (the A stages are reused as the output staging tile)
   const uint32_t nrows = (uint32_t)(g.T * g.k);
@@ -645,15 +652,16 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
 }
 
 // Dispatch a tile to the GEMM variant with the tile's number of row subtiles.
-template <int AF, int WF, int STAGE, int COH>
-DEV void expert_gemm_item(const GemmArgs& g, const Tile& t, int nb, char* lds, int32_t* signal_prev = nullptr) {
+template <int AF, int WF, int STAGE, int COH, typename Hook = NoHook>
+DEV void expert_gemm_item(const GemmArgs& g, const Tile& t, int nb, char* lds, int32_t* signal_prev = nullptr,
+                          const Hook& at_loop_end = Hook{}) {
   constexpr int FULL = GemmLds<AF>::kMaxRs;
   if (t.rs <= 1)
-    expert_gemm_tile<AF, WF, STAGE, 1, COH>(g, t.e, t.r0, t.rows, nb, lds, signal_prev);
+    expert_gemm_tile<AF, WF, STAGE, 1, COH>(g, t.e, t.r0, t.rows, nb, lds, signal_prev, at_loop_end);
   else if (t.rs <= 4)
-    expert_gemm_tile<AF, WF, STAGE, 4, COH>(g, t.e, t.r0, t.rows, nb, lds, signal_prev);
+    expert_gemm_tile<AF, WF, STAGE, 4, COH>(g, t.e, t.r0, t.rows, nb, lds, signal_prev, at_loop_end);
   else
-    expert_gemm_tile<AF, WF, STAGE, FULL, COH>(g, t.e, t.r0, t.rows, nb, lds, signal_prev);
+    expert_gemm_tile<AF, WF, STAGE, FULL, COH>(g, t.e, t.r0, t.rows, nb, lds, signal_prev, at_loop_end);
 }
 
 // y[t, n0:n1] = BF16( sum_j staging[t*k + j, n0:n1] ) for tokens [t0, t1),

@@ -61,8 +61,13 @@ __global__ void __launch_bounds__(256) k_scatter(const int32_t* ids, int T, int 
 
 // Persistent grid (one workgroup per CU) over (tile, N block) items taken
 // from the per-class queues.  Workgroup b runs on XCD b % 8 (round-robin
-// dispatch) and starts on that class.  Thread 0 claims the next item while
-// the current one runs, so the atomic's latency is hidden.
+// dispatch) and starts on that class.  Thread 0 claims the next item when
+// the current one's K loop ends, so the atomic's latency is hidden behind
+// the epilogue, and items claimed one after the other also start one after
+// the other: the row tiles that share a weight slab and the N blocks that
+// share a row tile then stream their common operand through the XCD's L2
+// at nearly the same time.  (Claiming a whole item ahead would start each
+// item when the workgroup's previous, unrelated item happens to end.)
 template <int AF, int WF, int STAGE>
 __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 k_gemm(GemmArgs g, const Tile* tiles, const int32_t* meta, int nnb, int32_t* queues) {
@@ -74,11 +79,13 @@ k_gemm(GemmArgs g, const Tile* tiles, const int32_t* meta, int nnb, int32_t* que
   if (threadIdx.x == 0) s_item = pop_class_item(queues, s_first, nnb, &cls);
   __syncthreads();
   for (int i = s_item; i >= 0;) {
-    __syncthreads();                                          // everyone has read s_item
-    if (threadIdx.x == 0) s_item = pop_class_item(queues, s_first, nnb, &cls);
     int t, nb;
     gemm_item_of(tiles, nnb, i, &t, &nb);
-    expert_gemm_item<AF, WF, STAGE, 0>(g, tiles[t], nb, lds, nullptr);   // starts with a barrier
+    // starts with a barrier, after which every thread has read s_item
+    expert_gemm_item<AF, WF, STAGE, 0>(g, tiles[t], nb, lds, nullptr, [&]() {
+      if (threadIdx.x == 0) s_item = pop_class_item(queues, s_first, nnb, &cls);
+    });
+    __syncthreads();                                          // s_item is written
     i = s_item;
   }
 }
@@ -208,10 +215,11 @@ DEV Plan uniform_plan(const Plan& in) {
 DEV int uni_i(int v) { return __builtin_amdgcn_readfirstlane(v); }
 // The GEMM items are inlined into the kernel: as a called function they
 // would save and restore the callee-saved VGPRs they use on every item.
-template <int AF, int WF, int STAGE>
-__device__ __forceinline__ void mega_gemm_item(const Plan& p, Tile tl, int nb, int32_t* signal_prev) {
+template <int AF, int WF, int STAGE, typename Hook>
+__device__ __forceinline__ void mega_gemm_item(const Plan& p, Tile tl, int nb, int32_t* signal_prev,
+                                               const Hook& at_loop_end) {
   MEGA_LDS;
-  expert_gemm_item<AF, WF, STAGE, 1>(gemm_args(p), tl, nb, lds, signal_prev);
+  expert_gemm_item<AF, WF, STAGE, 1>(gemm_args(p), tl, nb, lds, signal_prev, at_loop_end);
 }
 template <int AF>
 __device__ __noinline__ void mega_router_item(Plan pv, int tt_, int et_, int ks_) {
@@ -312,13 +320,15 @@ k_mega(Plan p) {
   int32_t* pending = nullptr;              // counter of the previous item, not yet signalled
   if (tid == 0) s_q = pop_class_item(p.ctr + CTR_Q1, s_first, p.nnb1, &cls);
   __syncthreads();
+  // (the next item is claimed when the current one's K loop ends, as in k_gemm)
   for (int i = s_q; i >= 0;) {
-    __syncthreads();
-    if (tid == 0) s_q = pop_class_item(p.ctr + CTR_Q1, s_first, p.nnb1, &cls);
     int t, nb;
     gemm_item_of(p.tiles, p.nnb1, i, &t, &nb);
-    mega_gemm_item<AF, WF, 1>(p, p.tiles[t], nb, pending);
+    mega_gemm_item<AF, WF, 1>(p, p.tiles[t], nb, pending, [&]() {
+      if (tid == 0) s_q = pop_class_item(p.ctr + CTR_Q1, s_first, p.nnb1, &cls);
+    });
     pending = &p.done1[t];                 // signalled once its stores have completed
+    __syncthreads();
     i = s_q;
   }
   if (pending) signal_coherent(pending);
@@ -332,13 +342,14 @@ k_mega(Plan p) {
   if (tid == 0) s_q = pop_class_item(p.ctr + CTR_Q2, s_first, p.nnb2, &cls);
   __syncthreads();
   for (int i = s_q; i >= 0;) {
-    __syncthreads();
-    if (tid == 0) s_q = pop_class_item(p.ctr + CTR_Q2, s_first, p.nnb2, &cls);
     int t, nb;
     gemm_item_of(p.tiles, p.nnb2, i, &t, &nb);
     if (!wait_counter(&p.done1[t], p.nnb1, p.err, &s_ok, false)) return;
-    mega_gemm_item<AF, WF, 2>(p, p.tiles[t], nb, pending);
+    mega_gemm_item<AF, WF, 2>(p, p.tiles[t], nb, pending, [&]() {
+      if (tid == 0) s_q = pop_class_item(p.ctr + CTR_Q2, s_first, p.nnb2, &cls);
+    });
     pending = &p.done2[nb];
+    __syncthreads();
     i = s_q;
   }
   if (pending) signal_coherent(pending);
