@@ -109,6 +109,32 @@ DEV int a_swz(int row, int c) {
   return c ^ (row & 15);
 }
 
+// Copy a staged output tile from LDS to global memory: N pieces of 16 bytes,
+// `piece(q, &lds_off, &dst_off)` gives the offsets of piece q and whether
+// it is stored.  A thread issues all of its LDS reads before its stores, so
+// it waits for LDS once rather than once per piece.
+template <int N, int CP, typename F>
+DEV void copy_pieces(rsrc_t dst, const char* lds, const F& piece) {
+  constexpr int NQ = (N + kGemmThreads - 1) / kGemmThreads;
+  v4i d[NQ];
+  uint32_t off[NQ];
+  bool ok[NQ];
+#pragma unroll
+  for (int it = 0; it < NQ; ++it) {
+    const int q = threadIdx.x + it * kGemmThreads;
+    uint32_t lo = 0;
+    ok[it] = (N % kGemmThreads == 0 || q < N) && piece(q, &lo, &off[it]);
+    d[it] = ld16(lds + lo);
+  }
+#pragma unroll
+  for (int it = 0; it < NQ; ++it)
+    if (ok[it]) buf_st16<CP>(dst, off[it], d[it]);
+}
+
+struct NoHook {
+  DEV void operator()() const {}
+};
+
 // One work item: `RS` 16-row subtiles (rows [r0, r0+m), m <= 16*RS) of
 // expert e times one N block nb.  256 threads, one wave per SIMD.  With COH
 // (inside the persistent kernel, where producer and consumer items may run
@@ -125,9 +151,6 @@ DEV int a_swz(int row, int c) {
 // wave, so the previous item is signalled without a wait of its own.
 // `at_loop_end()` is called by every thread once the K loop has ended,
 // before the epilogue.
-struct NoHook {
-  DEV void operator()() const {}
-};
 template <int AF, int WF, int STAGE, int RS, int COH, typename Hook>
 DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char* lds, int32_t* signal_prev,
                           const Hook& at_loop_end) {
@@ -559,12 +582,12 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
         }
       }
       __syncthreads();
-      for (int q = tid; q < R * 8; q += kGemmThreads) {
+      copy_pieces<R * 8, CP>(aqw, lds, [&](int q, uint32_t* lo, uint32_t* go) {
         const int row = q >> 3, c = q & 7;
-        if (row < m)
-          buf_st16<CP>(aqw, (uint32_t)(r0 + row) * g.I + c0 + c * 16,
-                       ld16(lds + L::kA + row * 128 + ((c ^ ((row >> 1) & 7)) << 4)));
-      }
+        *lo = L::kA + row * 128 + ((c ^ ((row >> 1) & 7)) << 4);
+        *go = (uint32_t)(r0 + row) * g.I + c0 + c * 16;
+        return row < m;
+      });
       if (tid < m) buf_stf<CP>(saw, ((uint32_t)(r0 + tid) * (g.I / 128) + c0 / 128) * 4, RSC[tid]);
     } else {
       // chunk c of staging row r at c ^ (((r >> 2) & 3) << 1) (bank spread)
@@ -579,12 +602,12 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
           lds_st(lds, wr1 + (rs * 16 + v) * 256, (uint16_t)f32_to_bf16_rne(av(rs, 1, v)));
         }
       __syncthreads();
-      for (int q = tid; q < R * 16; q += kGemmThreads) {
+      copy_pieces<R * 16, CP>(aqw, lds, [&](int q, uint32_t* lo, uint32_t* go) {
         const int row = q >> 4, c = q & 15;
-        if (row < m)
-          buf_st16<CP>(aqw, ((uint32_t)(r0 + row) * g.I + c0) * 2 + c * 16,
-                       ld16(lds + L::kA + row * 256 + (c ^ (((row >> 2) & 3) << 1)) * 16));
-      }
+        *lo = L::kA + row * 256 + (c ^ (((row >> 2) & 3) << 1)) * 16;
+        *go = ((uint32_t)(r0 + row) * g.I + c0) * 2 + c * 16;
+        return row < m;
+      });
     }
   } else if (AF == ACT_FP8) {
     // lane: row rs*16 + c16, columns 64w + 16cs + 4gq + v of the N block.
@@ -608,12 +631,13 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
         }
       }
       __syncthreads();
-      for (int q = tid; q < CH * 16 * 32; q += kGemmThreads) {
+      copy_pieces<CH * 16 * 32, CP>(stw, lds, [&](int q, uint32_t* lo, uint32_t* go) {
         const int rl = q >> 5, c = q & 31;
         const int row = CH * 16 * h + rl, col = n0 + c * 8;
-        if (row < m && col < g.H)
-          buf_st16<CP>(stw, ((uint32_t)ROWI[row] * g.H + col) * 2, ld16(lds + L::kA + rl * 512 + ((c ^ (rl & 15)) << 4)));
-      }
+        *lo = L::kA + rl * 512 + ((c ^ (rl & 15)) << 4);
+        *go = ((uint32_t)ROWI[row] * g.H + col) * 2;
+        return row < m && col < g.H;
+      });
     }
   } else {
     // BF16 activations (product not transposed): lane holds rows 4gq + v,
@@ -640,13 +664,13 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
                    (uint16_t)f32_to_bf16_rne(acc[rs][cs][v] * rw));
         }
       __syncthreads();
-      for (int q = tid; q < CH * 16 * 32; q += kGemmThreads) {
+      copy_pieces<CH * 16 * 32, CP>(stw, lds, [&](int q, uint32_t* lo, uint32_t* go) {
         const int rl = q >> 5, c = q & 31;
         const int row = CH * 16 * h + rl, col = n0 + c * 8;
-        if (row < m && col < g.H)
-          buf_st16<CP>(stw, ((uint32_t)ROWI[row] * g.H + col) * 2,
-                       ld16(lds + L::kA + rl * 512 + (c ^ (((rl >> 2) & 3) << 1)) * 16));
-      }
+        *lo = L::kA + rl * 512 + (c ^ (((rl >> 2) & 3) << 1)) * 16;
+        *go = ((uint32_t)ROWI[row] * g.H + col) * 2;
+        return row < m && col < g.H;
+      });
     }
   }
 }
