@@ -161,6 +161,18 @@ DEV rsrc_t make_rsrc_u(const void* base, uint32_t bytes) {
   const uint64_t bu = ((uint64_t)uni((uint32_t)(b >> 32)) << 32) | uni((uint32_t)b);
   return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(bu), 0, (int)uni(bytes), 0x00020000);
 }
+// Device-coherent scalar accesses (relaxed, device scope): the store writes
+// through to memory and the load does not take a line that another XCD's
+// L2 may hold stale.  For data that one workgroup hands to another inside a
+// kernel, ordered by a relaxed counter after the producer's stores have
+// completed (no device-wide fence).
+template <typename T>
+DEV T ld_coh(const T* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+template <typename T>
+DEV void st_coh(T* p, T v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+// Wait until this wave's stores have completed.
+DEV void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // Cache policy of a buffer access (the instruction's cache-coherence bits):
 // 0 = default; kCoherent (sc1) = device-scope coherent.  The L2 of each XCD
 // is not coherent with the others: data that one workgroup writes and a

@@ -611,10 +611,12 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
     }
   } else if (AF == ACT_FP8) {
     // lane: row rs*16 + c16, columns 64w + 16cs + 4gq + v of the N block.
-    // Chunks of CH row subtiles (at most 64 rows x 256 columns of BF16 =
-    // 32 KB); chunk c (16 bytes) of staging row r at c ^ (r & 15), so that
-    // the 16 rows of one 8-byte write spread over the LDS banks.
-    constexpr int CH = (RS < 4) ? RS : 4;
+    // The whole tile (up to 128 rows x 256 columns of BF16 = 64 KB, the A
+    // stages' space) is staged at once; chunk c (16 bytes) of staging row r
+    // at c ^ (r & 15), so that the 16 rows of one 8-byte write spread over
+    // the LDS banks.
+    constexpr int CH = RS;
+    static_assert(CH * 16 * 512 <= L::kAStages * L::kASlot, "staging fits the A stages");
 #pragma unroll
     for (int h = 0; h < RS / CH; ++h) {
       if (h > 0) __syncthreads();                  // previous chunk's copy-out is done

@@ -155,28 +155,21 @@ DEV bool wait_counter(const int32_t* c, int target, int32_t* err, int* s_ok, boo
   return ok != 0;
 }
 
-// Publish this workgroup's coherent (kCoherent, write-through) stores, then
-// add 1 to each counter: each wave waits until its stores have completed,
-// the workgroup synchronises, and one thread increments.  No device-wide
-// fence: the data was written past the L2, and no cache holds an older copy
-// of it (see expert_gemm_tile), so the relaxed counter is the only ordering
-// needed.  (Used by the gate|up and down items.)
+// Publish this workgroup's coherent (write-through) stores, then add 1 to
+// each counter: each wave waits until its stores have completed, the
+// workgroup synchronises, and one thread increments.  No device-wide fence:
+// the data was written past the L2, and its readers use coherent loads or
+// lines that no cache can hold an older copy of (see expert_gemm_tile), so
+// the relaxed counter is the only ordering needed.  A release fence per item
+// would write back the XCD's whole L2 and the matching acquire would
+// invalidate it, taking cached weights and activations from every
+// workgroup on the XCD.
 DEV void signal_coherent(int32_t* c0, int32_t* c1 = nullptr) {
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  wait_stores();
   __syncthreads();
   if (threadIdx.x == 0) {
     __hip_atomic_fetch_add(c0, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (c1) __hip_atomic_fetch_add(c1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-}
-
-// Publish this workgroup's global writes, then add 1 to each counter.
-DEV void signal_add(int32_t* c0, int32_t* c1 = nullptr) {
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    __hip_atomic_fetch_add(c0, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    if (c1) __hip_atomic_fetch_add(c1, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -284,34 +277,36 @@ k_mega(Plan p) {
       const int per_tt = p.nER * p.nKS;
       const int tt = q / per_tt, et = (q % per_tt) / p.nKS, ks = q % p.nKS;
       mega_router_item<AF>(p, tt, et, ks);
-      signal_add(&p.rdone[tt]);
+      signal_coherent(&p.rdone[tt]);
     } else if (q < q_count) {
       const int i = q - q_topk;                          // tokens [32i, 32i+32)
-      if (!wait_counter(&p.rdone[i / (kRouterTokens / kTopkItemTokens)], p.nER * p.nKS, p.err, &s_ok)) return;
+      if (!wait_counter(&p.rdone[i / (kRouterTokens / kTopkItemTokens)], p.nER * p.nKS, p.err, &s_ok, false)) return;
       mega_topk_item(p, i);
-      signal_add(&p.tkdone[i / (kPermBlock / kTopkItemTokens)]);
+      signal_coherent(&p.tkdone[i / (kPermBlock / kTopkItemTokens)]);
     } else if (q < q_scan) {
       const int b = q - q_count;
       if (!p.routing_given) {
         constexpr int kPer = kPermBlock / kTopkItemTokens;   // top-k items per block
         const int items_in_block = min(kPer, nK - kPer * b);
-        if (!wait_counter(&p.tkdone[b], items_in_block, p.err, &s_ok)) return;
+        if (!wait_counter(&p.tkdone[b], items_in_block, p.err, &s_ok, false)) return;
       }
       mega_count_item(p, b);
-      signal_add(&p.ctr[CTR_COUNT_DONE]);
+      signal_coherent(&p.ctr[CTR_COUNT_DONE]);
     } else if (q == q_scan) {
-      if (!wait_counter(&p.ctr[CTR_COUNT_DONE], p.nblk, p.err, &s_ok)) return;
+      if (!wait_counter(&p.ctr[CTR_COUNT_DONE], p.nblk, p.err, &s_ok, false)) return;
       mega_scan_item(p);
-      signal_add(&p.ctr[CTR_SCAN_FLAG]);
+      signal_coherent(&p.ctr[CTR_SCAN_FLAG]);
     } else {
-      if (!wait_counter(&p.ctr[CTR_SCAN_FLAG], 1, p.err, &s_ok)) return;
+      if (!wait_counter(&p.ctr[CTR_SCAN_FLAG], 1, p.err, &s_ok, false)) return;
       mega_scatter_item(p, q - q_scat);
-      signal_add(&p.ctr[CTR_SCATTER_DONE]);
+      signal_coherent(&p.ctr[CTR_SCATTER_DONE]);
     }
   }
 
   // 2. gate|up items from the per-class queues (every head item has been
-  // claimed by a running workgroup, so these waits end)
+  // claimed by a running workgroup, so these waits end).  The GEMM items
+  // read the permutation, tiles and weights with ordinary loads: one acquire
+  // per workgroup here drops any older copy of them from the L2.
   if (!wait_counter(&p.ctr[CTR_SCATTER_DONE], p.nblk, p.err, &s_ok)) return;
   if (tid <= kXcds) s_first[tid] = __hip_atomic_load(&p.meta[1 + tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();

@@ -8,7 +8,10 @@
 // routing bullet: token-to-expert mapping).  Permuted row r holds the flat
 // index p = t*k + j; rows of one expert are contiguous and in ascending token
 // order.  Everything is integer and deterministic: the only atomics are LDS
-// counters and bit-ors whose results do not depend on their order.
+// counters and bit-ors whose results do not depend on their order.  Data
+// handed from one step to the next (ids, block counts, bases, tiles) is
+// written and read with device-coherent accesses, so that the persistent
+// kernel orders the steps with relaxed counters and no device-wide fence.
 #pragma once
 #include "device_common.h"
 
@@ -23,6 +26,7 @@ constexpr int kMinTileRows = 64;     // smallest full GEMM row tile (bounds the 
 struct Tile {
   int e, r0, rows, rs, g0, gn;
 };
+static_assert(sizeof(Tile) == 6 * sizeof(int32_t), "tile fields are stored one by one");
 
 // Work item i of a GEMM over (tile, N block) pairs with nnb N blocks.  Items
 // are ordered expert by expert, then by N block, then by the expert's tiles,
@@ -40,7 +44,7 @@ DEV int tile_variant(int rows, int full_rs) { return rows <= 16 ? 1 : rows <= 64
 // Expert id of entry i, clamped into [0, E): ids produced by the router are
 // always in range; given ids outside it are treated as E-1 so that every
 // write stays inside its buffer.
-DEV int expert_of(const int32_t* ids, size_t i, int E) { return min(max(ids[i], 0), E - 1); }
+DEV int expert_of(const int32_t* ids, size_t i, int E) { return min(max(ld_coh(ids + i), 0), E - 1); }
 
 // Per-block expert histogram: blockcnt[b][e] = number of (t, j) with
 // ids[t][j] == e for tokens t of block b.  LDS: E ints.
@@ -51,7 +55,7 @@ DEV void perm_count_block(const int32_t* ids, int T, int k, int E, int b, int32_
   const int n = min(kPermBlock, T - t0) * k;
   for (int i = threadIdx.x; i < n; i += blockDim.x) atomicAdd(&lds[expert_of(ids, (size_t)t0 * k + i, E)], 1);
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += blockDim.x) blockcnt[(size_t)b * E + e] = lds[e];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) st_coh(blockcnt + (size_t)b * E + e, lds[e]);
   __syncthreads();
 }
 
@@ -104,7 +108,7 @@ DEV void perm_scan(const int32_t* blockcnt, int nblk, int E, int tile_rows, int3
     for (int b0 = 0; b0 < nblk; b0 += kBatch) {
       int c[kBatch];
 #pragma unroll
-      for (int i = 0; i < kBatch; ++i) c[i] = (b0 + i < nblk) ? blockcnt[(size_t)(b0 + i) * E + e] : 0;
+      for (int i = 0; i < kBatch; ++i) c[i] = (b0 + i < nblk) ? ld_coh(blockcnt + (size_t)(b0 + i) * E + e) : 0;
 #pragma unroll
       for (int i = 0; i < kBatch; ++i) run += c[i];
     }
@@ -118,30 +122,36 @@ DEV void perm_scan(const int32_t* blockcnt, int nblk, int E, int tile_rows, int3
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
     const int off = cnt[e];
     const int c = ((e + 1 < E) ? cnt[e + 1] : tot_rows) - off;
-    offsets[e] = off;
+    st_coh(offsets + e, off);
     // pass 2: base[b][e] = off + rows of e in blocks before b
     int run = off;
     for (int b0 = 0; b0 < nblk; b0 += kBatch) {
       int cb[kBatch];
 #pragma unroll
-      for (int i = 0; i < kBatch; ++i) cb[i] = (b0 + i < nblk) ? blockcnt[(size_t)(b0 + i) * E + e] : 0;
+      for (int i = 0; i < kBatch; ++i) cb[i] = (b0 + i < nblk) ? ld_coh(blockcnt + (size_t)(b0 + i) * E + e) : 0;
 #pragma unroll
       for (int i = 0; i < kBatch; ++i) {
-        if (b0 + i < nblk) base[(size_t)(b0 + i) * E + e] = run;
+        if (b0 + i < nblk) st_coh(base + (size_t)(b0 + i) * E + e, run);
         run += cb[i];
       }
     }
     const int g0 = tcl[class_pos(e, E8)], gn = (c + tile_rows - 1) / tile_rows;
     for (int i = 0; i < gn; ++i) {
       const int rows = min(tile_rows, c - i * tile_rows);
-      tiles[g0 + i] = Tile{e, off + i * tile_rows, rows, tile_variant(rows, tile_rows / 16), g0, gn};
+      int32_t* tf = reinterpret_cast<int32_t*>(tiles + g0 + i);
+      st_coh(tf + 0, e);
+      st_coh(tf + 1, off + i * tile_rows);
+      st_coh(tf + 2, rows);
+      st_coh(tf + 3, tile_variant(rows, tile_rows / 16));
+      st_coh(tf + 4, g0);
+      st_coh(tf + 5, gn);
     }
   }
   if (threadIdx.x == 0) {
-    offsets[E] = tot_rows;
-    meta[0] = tot_tiles;
-    for (int x = 0; x < kXcds; ++x) meta[1 + x] = tcl[x * E8];
-    meta[1 + kXcds] = tot_tiles;
+    st_coh(offsets + E, tot_rows);
+    st_coh(meta, tot_tiles);
+    for (int x = 0; x < kXcds; ++x) st_coh(meta + 1 + x, tcl[x * E8]);
+    st_coh(meta + 1 + kXcds, tot_tiles);
   }
   __syncthreads();
 }
@@ -170,10 +180,10 @@ DEV void perm_scatter_block(const int32_t* ids, int T, int k, int E, int b, cons
       const int e = expert_of(ids, (size_t)(t0 + tl) * k + j, E);
       int rank = __popcll(masks[(size_t)w * E + e] & ((1ull << lane) - 1ull));
       for (int u = 0; u < w; ++u) rank += __popcll(masks[(size_t)u * E + e]);
-      const int r = base[(size_t)b * E + e] + rank;
+      const int r = ld_coh(base + (size_t)b * E + e) + rank;
       const int p = (t0 + tl) * k + j;
-      perm[r] = p;
-      if (row_of) row_of[p] = r;
+      st_coh(perm + r, p);
+      if (row_of) st_coh(row_of + p, r);
     }
   }
   __syncthreads();

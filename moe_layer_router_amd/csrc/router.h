@@ -177,7 +177,7 @@ DEV void router_tile(const RouterArgs& a, int t0, int e0, char* lds, int s0, int
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int t = t0 + 32 * w + 16 * sub + 4 * g + v;
-        if (t < a.T) out[(size_t)t * a.E + e] = acc[sub][c][v] + b;
+        if (t < a.T) st_coh(out + (size_t)t * a.E + e, acc[sub][c][v] + b);
       }
   }
 }
@@ -187,12 +187,13 @@ DEV void router_tile(const RouterArgs& a, int t0, int e0, char* lds, int s0, int
 // the partials of the tile, in slice order, into slice 0.
 DEV void router_reduce(const RouterArgs& a, int t0, int e0, int S, int32_t* tile_cnt) {
   __shared__ int s_last;
-  __threadfence();                                 // publish this slice's partials
+  wait_stores();                                   // this slice's partials are in memory
   __syncthreads();
   if (threadIdx.x == 0) s_last = (atomicAdd(tile_cnt, 1) == S - 1);
   __syncthreads();
   if (!s_last) return;
-  __threadfence();                                 // the other slices' partials are visible
+  // the other slices' partials were in memory before their count; they are
+  // read coherently
   const size_t stride = (size_t)a.T * a.E;
   const int ne = min(kRouterExperts, a.E - e0), nt = min(kRouterTokens, a.T - t0);
   const int n = nt * ne;
@@ -205,7 +206,7 @@ DEV void router_reduce(const RouterArgs& a, int t0, int e0, int S, int32_t* tile
       const int i = min(i0 + u, n - 1);
       off[u] = (size_t)(t0 + i / ne) * a.E + e0 + i % ne;
 #pragma unroll
-      for (int s = 0; s < kMaxS; ++s) p[u][s] = (s < S) ? a.logits[s * stride + off[u]] : 0.f;
+      for (int s = 0; s < kMaxS; ++s) p[u][s] = (s < S) ? ld_coh(a.logits + s * stride + off[u]) : 0.f;
     }
 #pragma unroll
     for (int u = 0; u < kB; ++u) {
@@ -216,7 +217,7 @@ DEV void router_reduce(const RouterArgs& a, int t0, int e0, int S, int32_t* tile
     }
 #pragma unroll
     for (int u = 0; u < kB; ++u)
-      if (i0 + u < n) a.logits[off[u]] = v[u];
+      if (i0 + u < n) st_coh(a.logits + off[u], v[u]);
   }
 }
 
@@ -270,7 +271,7 @@ DEV void topk_token(const float* lrow, int E, int k, int32_t* ids, float* wts) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int e = lane + 64 * i;
-    key[i] = (e < E) ? (((uint64_t)f32_order_key(lrow[e]) << 32) | (uint32_t)(E - 1 - e)) : 0ull;
+    key[i] = (e < E) ? (((uint64_t)f32_order_key(ld_coh(lrow + e)) << 32) | (uint32_t)(E - 1 - e)) : 0ull;
   }
   int my_id = 0;
   float my_val = 0.f, top = 0.f;
@@ -294,8 +295,8 @@ DEV void topk_token(const float* lrow, int E, int k, int32_t* ids, float* wts) {
   const float ex = (lane < k) ? expf(my_val - top) : 0.f;
   const float sum = row_sum16(ex);
   if (lane < k) {
-    ids[lane] = my_id;
-    wts[lane] = ex / sum;
+    st_coh(ids + lane, my_id);
+    st_coh(wts + lane, ex / sum);
   }
 }
 
@@ -307,7 +308,7 @@ DEV void topk_token16(const float* lrow, bool valid, int E, int k, int32_t* ids,
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     const int e = li + 16 * j;
-    key[j] = (valid && e < E) ? (((uint64_t)f32_order_key(lrow[e]) << 32) | (uint32_t)(E - 1 - e)) : 0ull;
+    key[j] = (valid && e < E) ? (((uint64_t)f32_order_key(ld_coh(lrow + e)) << 32) | (uint32_t)(E - 1 - e)) : 0ull;
   }
   int my_id = 0;
   float my_val = 0.f, top = 0.f;
@@ -330,8 +331,8 @@ DEV void topk_token16(const float* lrow, bool valid, int E, int k, int32_t* ids,
   const float ex = (li < k) ? expf(my_val - top) : 0.f;
   const float sum = row_sum16(ex);
   if (valid && li < k) {
-    ids[li] = my_id;
-    wts[li] = ex / sum;
+    st_coh(ids + li, my_id);
+    st_coh(wts + li, ex / sum);
   }
 }
 
