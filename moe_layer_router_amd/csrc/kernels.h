@@ -11,8 +11,7 @@ namespace moe {
 enum {
   CTR_QUEUE = 0,      // persistent-kernel work queue head
   CTR_COUNT_DONE,     // histogram items finished
-  CTR_SCAN_FLAG,      // 1 once offsets / base / tiles are written
-  CTR_SCATTER_DONE,   // scatter items finished
+  CTR_SCATTER_DONE,   // scan-and-scatter items finished
   CTR_G1_DONE,        // gate|up items finished
   CTR_QUEUE2,         // persistent kernel: queue head after the gate|up items
   CTR_Q1 = 8,         // [kXcds] gate|up item queues, one per expert class

@@ -181,8 +181,9 @@ DEV void signal_coherent(int32_t* c0, int32_t* c1 = nullptr) {
 //   head queue:   router tiles (128 tokens x 64 experts) -> rdone[token tile]
 //                 top-k of 32 tokens                     -> tkdone[256-token block]
 //                 expert histogram of 256 tokens        -> COUNT_DONE
-//                 scan (offsets, block bases, tiles)    -> SCAN_FLAG
-//                 stable scatter of 256 tokens          -> SCATTER_DONE
+//                   (only with more than one 256-token block)
+//                 scan and stable scatter of 256 tokens -> SCATTER_DONE
+//                   (block 0 also writes offsets, tiles)
 //   class queues: gate|up items (tile, 128 channels)    -> done1[tile]
 //   class queues: down items (tile, 256 columns)        -> done2[N block]
 //   tail queue:   combine items (N block, 256 tokens)
@@ -238,16 +239,12 @@ __device__ __noinline__ void mega_count_item(Plan pv, int b_) {
   const int b = uni_i(b_);
   perm_count_block(p.ids, p.T, p.k, p.E, b, p.blockcnt, reinterpret_cast<int*>(lds));
 }
-__device__ __noinline__ void mega_scan_item(Plan pv) {
-  MEGA_LDS;
-  const Plan p = uniform_plan(pv);
-  perm_scan(p.blockcnt, p.nblk, p.E, p.tile_rows, p.base, p.offsets, p.tiles, p.meta, reinterpret_cast<int*>(lds));
-}
 __device__ __noinline__ void mega_scatter_item(Plan pv, int b_) {
   MEGA_LDS;
   const Plan p = uniform_plan(pv);
   const int b = uni_i(b_);
-  perm_scatter_block(p.ids, p.T, p.k, p.E, b, p.base, p.perm, p.row_of, reinterpret_cast<uint64_t*>(lds));
+  perm_scan_scatter_block(p.ids, p.T, p.k, p.E, b, p.nblk, p.blockcnt, p.tile_rows, p.offsets, p.tiles, p.meta,
+                          p.perm, p.row_of, lds);
 }
 __device__ __noinline__ void mega_combine_item(Plan pv, int nb_, int c) {
   const Plan p = uniform_plan(pv);
@@ -263,8 +260,11 @@ k_mega(Plan p) {
   const int tid = threadIdx.x;
   const int nR = p.routing_given ? 0 : p.nTR * p.nER * p.nKS;
   const int nK = p.routing_given ? 0 : (p.T + kTopkItemTokens - 1) / kTopkItemTokens;
-  const int q_topk = nR, q_count = nR + nK, q_scan = q_count + p.nblk;
-  const int q_scat = q_scan + 1, q_end = q_scat + p.nblk;
+  // histogram items only when there are several 256-token blocks (a single
+  // block counts itself in its scatter item)
+  const int nC = (p.nblk > 1) ? p.nblk : 0;
+  const int q_topk = nR, q_count = nR + nK, q_scat = q_count + nC, q_end = q_scat + p.nblk;
+  constexpr int kPer = kPermBlock / kTopkItemTokens;   // top-k items per 256-token block
 
   // 1. routing and permutation items from the head queue
   for (;;) {
@@ -283,22 +283,21 @@ k_mega(Plan p) {
       if (!wait_counter(&p.rdone[i / (kRouterTokens / kTopkItemTokens)], p.nER * p.nKS, p.err, &s_ok, false)) return;
       mega_topk_item(p, i);
       signal_coherent(&p.tkdone[i / (kPermBlock / kTopkItemTokens)]);
-    } else if (q < q_scan) {
+    } else if (q < q_scat) {
       const int b = q - q_count;
-      if (!p.routing_given) {
-        constexpr int kPer = kPermBlock / kTopkItemTokens;   // top-k items per block
-        const int items_in_block = min(kPer, nK - kPer * b);
-        if (!wait_counter(&p.tkdone[b], items_in_block, p.err, &s_ok, false)) return;
-      }
+      if (!p.routing_given && !wait_counter(&p.tkdone[b], min(kPer, nK - kPer * b), p.err, &s_ok, false)) return;
       mega_count_item(p, b);
       signal_coherent(&p.ctr[CTR_COUNT_DONE]);
-    } else if (q == q_scan) {
-      if (!wait_counter(&p.ctr[CTR_COUNT_DONE], p.nblk, p.err, &s_ok, false)) return;
-      mega_scan_item(p);
-      signal_coherent(&p.ctr[CTR_SCAN_FLAG]);
     } else {
-      if (!wait_counter(&p.ctr[CTR_SCAN_FLAG], 1, p.err, &s_ok, false)) return;
-      mega_scatter_item(p, q - q_scat);
+      // scan and scatter of one block, once every histogram is in (or, with
+      // a single block, once its top-k items are done)
+      const int b = q - q_scat;
+      if (nC > 0) {
+        if (!wait_counter(&p.ctr[CTR_COUNT_DONE], nC, p.err, &s_ok, false)) return;
+      } else if (!p.routing_given && !wait_counter(&p.tkdone[0], nK, p.err, &s_ok, false)) {
+        return;
+      }
+      mega_scatter_item(p, b);
       signal_coherent(&p.ctr[CTR_SCATTER_DONE]);
     }
   }
@@ -575,13 +574,13 @@ int gemm_lds(int act_fp8) { return act_fp8 ? GemmLds<ACT_FP8>::kBytes : GemmLds<
 int mega_lds(const Plan& p) {
   int b = gemm_lds(p.act_fp8);
   b = b > kRouterLds ? b : kRouterLds;
-  b = b > 4 * p.E * 8 ? b : 4 * p.E * 8;
-  b = b > (2 * p.E + 72) * 4 ? b : (2 * p.E + 72) * 4;
+  const int scat = 4 * p.E * 8 + (2 * p.E + kXcds * ((p.E + kXcds - 1) / kXcds) + 64) * 4;   // scan and scatter
+  b = b > scat ? b : scat;
   return b;
 }
 
-// nks: K slices (partials at logits + ks*T*E; the top-k leaves the logits in
-// slice 0).
+// nks: K slices (partials at logits + ks*T*E, summed into slice 0 by the
+// last slice of each tile).
 moe_status launch_route(const Plan& p, float* logits, int nks, hipStream_t st) {
   RouterArgs ra{p.x, p.x_scales, p.wr, p.bias, logits, p.T, p.H, p.E, p.act_fp8};
   if (p.act_fp8) {

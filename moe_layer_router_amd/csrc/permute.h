@@ -156,13 +156,14 @@ DEV void perm_scan(const int32_t* blockcnt, int nblk, int E, int tile_rows, int3
   __syncthreads();
 }
 
-// Stable scatter of block b: row base[b][e] + (rank of token t among the
+// Stable scatter of block b: row base(e) + (rank of token t among the
 // block's tokens choosing e) receives p = t*k + j.  The rank is a popcount
 // of per-wave 64-bit membership masks built with LDS bit-ors.  Needs exactly
 // 256 threads: wave w owns tokens 64w .. 64w+63 of the block.
 // LDS: 4 * E * 8 bytes.
-DEV void perm_scatter_block(const int32_t* ids, int T, int k, int E, int b, const int32_t* base,
-                            int32_t* perm, int32_t* row_of, uint64_t* masks) {
+template <typename BaseF>
+DEV void scatter_block(const int32_t* ids, int T, int k, int E, int b, const BaseF& base_of, int32_t* perm,
+                       int32_t* row_of, uint64_t* masks) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   for (int i = threadIdx.x; i < 4 * E; i += 256) masks[i] = 0ull;
   __syncthreads();
@@ -180,13 +181,95 @@ DEV void perm_scatter_block(const int32_t* ids, int T, int k, int E, int b, cons
       const int e = expert_of(ids, (size_t)(t0 + tl) * k + j, E);
       int rank = __popcll(masks[(size_t)w * E + e] & ((1ull << lane) - 1ull));
       for (int u = 0; u < w; ++u) rank += __popcll(masks[(size_t)u * E + e]);
-      const int r = ld_coh(base + (size_t)b * E + e) + rank;
+      const int r = base_of(e) + rank;
       const int p = (t0 + tl) * k + j;
       st_coh(perm + r, p);
       if (row_of) st_coh(row_of + p, r);
     }
   }
   __syncthreads();
+}
+DEV void perm_scatter_block(const int32_t* ids, int T, int k, int E, int b, const int32_t* base,
+                            int32_t* perm, int32_t* row_of, uint64_t* masks) {
+  scatter_block(ids, T, k, E, b, [&](int e) { return ld_coh(base + (size_t)b * E + e); }, perm, row_of, masks);
+}
+
+// Scan and stable scatter of block b in one step (persistent kernel): the
+// block sums the histograms of all nblk blocks itself, both the rows per
+// expert and the rows of each expert in blocks before b, so no separate scan
+// step, with its hand-off through memory, sits between the histograms and
+// the scatters.  With nblk == 1 the block counts its own tokens and needs no
+// histogram step at all.  Block 0 also writes offsets, tiles and meta,
+// exactly as perm_scan does.  LDS: 4*E*8 bytes + (2*E + 8*ceil(E/8) + 64)
+// ints.  Needs exactly 256 threads.
+DEV void perm_scan_scatter_block(const int32_t* ids, int T, int k, int E, int b, int nblk, const int32_t* blockcnt,
+                                 int tile_rows, int32_t* offsets, Tile* tiles, int32_t* meta, int32_t* perm,
+                                 int32_t* row_of, char* lds) {
+  const int E8 = (E + kXcds - 1) / kXcds;
+  uint64_t* masks = reinterpret_cast<uint64_t*>(lds);
+  int* cnt = reinterpret_cast<int*>(lds + (size_t)4 * E * 8);   // [E] rows per expert, then offsets
+  int* pre = cnt + E;                                            // [E] rows of e in blocks before b
+  int* tcl = pre + E;                                            // [kXcds * E8]
+  int* scratch = tcl + kXcds * E8;                               // [64]
+  if (nblk == 1) {
+    for (int e = threadIdx.x; e < E; e += blockDim.x) { cnt[e] = 0; pre[e] = 0; }
+    __syncthreads();
+    const int n = min(kPermBlock, T) * k;
+    for (int i = threadIdx.x; i < n; i += blockDim.x) atomicAdd(&cnt[expert_of(ids, i, E)], 1);
+  } else {
+    constexpr int kBatch = 16;
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+      int tot = 0, before = 0;
+      for (int b0 = 0; b0 < nblk; b0 += kBatch) {
+        int c[kBatch];
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) c[i] = (b0 + i < nblk) ? ld_coh(blockcnt + (size_t)(b0 + i) * E + e) : 0;
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) {
+          tot += c[i];
+          if (b0 + i < b) before += c[i];
+        }
+      }
+      cnt[e] = tot;
+      pre[e] = before;
+    }
+  }
+  __syncthreads();
+  if (b == 0) {
+    for (int i = threadIdx.x; i < kXcds * E8; i += blockDim.x) tcl[i] = 0;
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += blockDim.x) tcl[class_pos(e, E8)] = (cnt[e] + tile_rows - 1) / tile_rows;
+    __syncthreads();
+  }
+  const int tot_rows = lds_exclusive_scan(cnt, E, scratch);      // cnt[e] = first row of expert e
+  if (b == 0) {
+    const int tot_tiles = lds_exclusive_scan(tcl, kXcds * E8, scratch);
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+      const int off = cnt[e];
+      const int c = ((e + 1 < E) ? cnt[e + 1] : tot_rows) - off;
+      st_coh(offsets + e, off);
+      const int g0 = tcl[class_pos(e, E8)], gn = (c + tile_rows - 1) / tile_rows;
+      for (int i = 0; i < gn; ++i) {
+        const int rows = min(tile_rows, c - i * tile_rows);
+        int32_t* tf = reinterpret_cast<int32_t*>(tiles + g0 + i);
+        st_coh(tf + 0, e);
+        st_coh(tf + 1, off + i * tile_rows);
+        st_coh(tf + 2, rows);
+        st_coh(tf + 3, tile_variant(rows, tile_rows / 16));
+        st_coh(tf + 4, g0);
+        st_coh(tf + 5, gn);
+      }
+    }
+    if (threadIdx.x == 0) {
+      st_coh(offsets + E, tot_rows);
+      st_coh(meta, tot_tiles);
+      for (int x = 0; x < kXcds; ++x) st_coh(meta + 1 + x, tcl[x * E8]);
+      st_coh(meta + 1 + kXcds, tot_tiles);
+    }
+  }
+  for (int e = threadIdx.x; e < E; e += blockDim.x) pre[e] += cnt[e];   // base of expert e in block b
+  __syncthreads();
+  scatter_block(ids, T, k, E, b, [&](int e) { return pre[e]; }, perm, row_of, masks);
 }
 
 }  // namespace moe

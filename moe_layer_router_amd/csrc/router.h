@@ -197,27 +197,29 @@ DEV void router_reduce(const RouterArgs& a, int t0, int e0, int S, int32_t* tile
   const size_t stride = (size_t)a.T * a.E;
   const int ne = min(kRouterExperts, a.E - e0), nt = min(kRouterTokens, a.T - t0);
   const int n = nt * ne;
-  constexpr int kB = 8, kMaxS = 8;                 // elements per batch; all their loads in flight
-  for (int i0 = threadIdx.x * kB; i0 < n; i0 += blockDim.x * kB) {
-    float v[kB], p[kB][kMaxS];
+  // kB elements per thread and pass, consecutive threads on consecutive
+  // elements (each load instruction reads whole lines); all loads of a pass
+  // are in flight together
+  constexpr int kB = 8, kMaxS = 8;
+  const int nthr = blockDim.x;
+  for (int i0 = 0; i0 < n; i0 += nthr * kB) {
+    float p[kB][kMaxS];
     size_t off[kB];
 #pragma unroll
     for (int u = 0; u < kB; ++u) {
-      const int i = min(i0 + u, n - 1);
+      const int i = min(i0 + u * nthr + (int)threadIdx.x, n - 1);
       off[u] = (size_t)(t0 + i / ne) * a.E + e0 + i % ne;
 #pragma unroll
       for (int s = 0; s < kMaxS; ++s) p[u][s] = (s < S) ? ld_coh(a.logits + s * stride + off[u]) : 0.f;
     }
 #pragma unroll
     for (int u = 0; u < kB; ++u) {
-      v[u] = p[u][0];
+      float v = p[u][0];
 #pragma unroll
       for (int s = 1; s < kMaxS; ++s)
-        if (s < S) v[u] += p[u][s];
+        if (s < S) v += p[u][s];
+      if (i0 + u * nthr + (int)threadIdx.x < n) st_coh(a.logits + off[u], v);
     }
-#pragma unroll
-    for (int u = 0; u < kB; ++u)
-      if (i0 + u < n) st_coh(a.logits + off[u], v[u]);
   }
 }
 
