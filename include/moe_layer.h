@@ -51,12 +51,14 @@
  * N = H, K = I for w_down), let BS be the bytes of one row per 128 columns
  * (BF16 256, FP8 128, FP4 64) and nsteps = K/128.  The tiled matrix of
  * expert e (same size and position as the row-major one) is the sequence of
- * blocks (t, s), t = 0 .. N/16-1, s = 0 .. nsteps-1, block (t, s) at byte
- * (t*nsteps + s)*16*BS, each made of BS/64 pieces of 1024 bytes: byte
+ * blocks (s, t), s = 0 .. nsteps-1, t = 0 .. N/16-1, block (s, t) at byte
+ * (s*(N/16) + t)*16*BS, each made of BS/64 pieces of 1024 bytes: byte
  * 16*l + j of piece p (l = 0..63, j = 0..15) is byte BS*s + 64*p + 16*(l/16)
- * + j of row 16*t + l%16 of the row-major matrix.  FP4 E8M0 scales: block
- * (t, s) is 64 bytes at (t*nsteps + s)*64, byte l holding the scale of row
- * 16*t + l%16 for K group 4*s + l/16.  FP8 fp32 block scales stay row-major.
+ * + j of row 16*t + l%16 of the row-major matrix.  (K step major, so that
+ * the blocks one K step of a GEMM item reads are adjacent and spread over
+ * the memory channels.)  FP4 E8M0 scales: block (s, t) is 64 bytes at
+ * (s*(N/16) + t)*64, byte l holding the scale of row 16*t + l%16 for K group
+ * 4*s + l/16.  FP8 fp32 block scales stay row-major.
  * moe_pack_weights converts row-major weights into this layout.
  *
  * Supported dtype pairs (act x weight): BF16 x BF16, FP8 x FP8, FP8 x FP4.
@@ -90,7 +92,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2   /* 2: packed weight blocks ordered K step major */
 
 typedef enum moe_status {
   MOE_OK = 0,

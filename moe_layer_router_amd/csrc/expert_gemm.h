@@ -192,18 +192,19 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
   const rsrc_t srs = make_rsrc(reinterpret_cast<const uint8_t*>(Sbase) + (size_t)e * N * (K / 32),
                                (WF == W_FP4) ? (uint32_t)N * (K / 32) : 0u);
   // Weights are in the MFMA-tiled layout (see moe_pack_weights): for each
-  // 16-row tile and 128-K step, a block of 16*BS bytes made of 1 KB pieces,
-  // piece p holding in its 16 bytes at 16*l the row 16t + l%16, bytes
-  // BS*s + 64p + 16*(l/16) .. +15 of the row-major matrix.  One piece is
-  // exactly one B operand load of a wave: 1 KB contiguous.
+  // 128-K step s and 16-row tile t, a block of 16*BS bytes at
+  // (s*(N/16) + t)*16*BS made of 1 KB pieces, piece p holding in its 16
+  // bytes at 16*l the row 16t + l%16, bytes BS*s + 64p + 16*(l/16) .. +15 of
+  // the row-major matrix.  One piece is exactly one B operand load of a
+  // wave: 1 KB contiguous; the blocks of one step are adjacent.
   constexpr uint32_t BS = (WF == W_FP8) ? 128 : (WF == W_BF16) ? 256 : 64;   // bytes per row per K step
   uint32_t boff[4], bsoff[4];                      // this lane's piece offsets (and E8M0 offsets)
 #pragma unroll
   for (int cs = 0; cs < 4; ++cs) {
     const int nt = ((STAGE == 1) ? ((cs < 2) ? c0 : g.I + c0) + 32 * w + 16 * (cs & 1) : n0 + 64 * w + 16 * cs) / 16;
     const int ntc = wave_ok ? nt : 0;
-    boff[cs] = (uint32_t)ntc * (uint32_t)nsteps * 16u * BS + 16u * lane;
-    bsoff[cs] = (uint32_t)ntc * (uint32_t)nsteps * 64u + lane;
+    boff[cs] = (uint32_t)ntc * 16u * BS + 16u * lane;
+    bsoff[cs] = (uint32_t)ntc * 64u + lane;
   }
   // fp32 weight-scale rows (FP8): two 128-blocks of N per item
   const int sb0 = (STAGE == 1) ? c0 / 128 : n0 / 128;
@@ -283,15 +284,20 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
     SC[(par * 2 + 1) * L::kScRows + pos] = sa * w1;
   };
 
-  // ---- B loads (HBM straight to registers), one instruction per piece q
+  // ---- B loads (HBM straight to registers), one instruction per piece q.
+  // Steps past the last (issued so that the step stays branch-free) load
+  // the last step again.
+  auto bstep = [&](int s) __attribute__((always_inline)) -> uint32_t {
+    return (uint32_t)min(s, nsteps - 1) * (uint32_t)N * BS;
+  };
   auto load_b_piece = [&](int s, BFrag& b, int q) __attribute__((always_inline)) {
     if (WF == W_FP8) {
-      b.d[q >> 1][q & 1] = buf_ld16(wrs, boff[q >> 1] + 1024 * (q & 1), (uint32_t)s * 16 * BS);
+      b.d[q >> 1][q & 1] = buf_ld16(wrs, boff[q >> 1] + 1024 * (q & 1), bstep(s));
     } else if (WF == W_FP4) {
-      if ((q & 1) == 0) b.d[q >> 1][0] = buf_ld16(wrs, boff[q >> 1], (uint32_t)s * 16 * BS);
-      else b.sc[q >> 1] = (int)buf_ldu8(srs, bsoff[q >> 1], (uint32_t)s * 64);
+      if ((q & 1) == 0) b.d[q >> 1][0] = buf_ld16(wrs, boff[q >> 1], bstep(s));
+      else b.sc[q >> 1] = (int)buf_ldu8(srs, bsoff[q >> 1], (uint32_t)min(s, nsteps - 1) * (uint32_t)N * 4u);
     } else {
-      b.d[q >> 2][q & 3] = buf_ld16(wrs, boff[q >> 2] + 1024 * (q & 3), (uint32_t)s * 16 * BS);
+      b.d[q >> 2][q & 3] = buf_ld16(wrs, boff[q >> 2] + 1024 * (q & 3), bstep(s));
     }
   };
 

@@ -93,29 +93,34 @@ k_gemm(GemmArgs g, const Tile* tiles, const int32_t* meta, int nnb, int32_t* que
 // Row-major [E*N][K] weights -> MFMA-tiled blocks (a byte permutation; the
 // layout is defined in moe_layer.h).  One thread per 16-byte unit of the
 // destination, in destination order, so that the writes are contiguous.
-__global__ void __launch_bounds__(256) k_pack_weights(const uint8_t* src, uint8_t* dst, size_t rows, int nsteps,
-                                                      int bs) {
-  const int np = bs / 64;
+__global__ void __launch_bounds__(256) k_pack_weights(const uint8_t* src, uint8_t* dst, size_t rows, int n,
+                                                      int nsteps, int bs) {
+  const int np = bs / 64, nt = n / 16;
   const size_t units = rows * (size_t)nsteps * bs / 16;
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < units; i += (size_t)gridDim.x * blockDim.x) {
     const int l = (int)(i & 63);
-    size_t r = i >> 6;
+    size_t r = i >> 6;                               // (e, s, t, p)
     const int p = (int)(r % np);
     r /= np;
+    const int t = (int)(r % nt);
+    r /= nt;
     const int s = (int)(r % nsteps);
-    const size_t row = (r / nsteps) * 16 + (l & 15);
+    const size_t row = (r / nsteps) * n + (size_t)t * 16 + (l & 15);
     st16(dst + i * 16, ld16(src + row * ((size_t)nsteps * bs) + (size_t)bs * s + 64 * p + 16 * (l >> 4)));
   }
 }
 
-// E8M0 scales [E*N][K/32] -> 64-byte blocks per (16-row tile, K step).
-__global__ void __launch_bounds__(256) k_pack_e8m0(const uint8_t* src, uint8_t* dst, size_t rows, int nsteps) {
-  const size_t n = rows * (size_t)nsteps * 4;
-  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
+// E8M0 scales [E*N][K/32] -> 64-byte blocks per (K step, 16-row tile).
+__global__ void __launch_bounds__(256) k_pack_e8m0(const uint8_t* src, uint8_t* dst, size_t rows, int n, int nsteps) {
+  const int nt = n / 16;
+  const size_t total = rows * (size_t)nsteps * 4;
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
     const int l = (int)(i & 63);
-    const size_t r = i >> 6;
+    size_t r = i >> 6;                               // (e, s, t)
+    const int t = (int)(r % nt);
+    r /= nt;
     const int s = (int)(r % nsteps);
-    const size_t row = (r / nsteps) * 16 + (l & 15);
+    const size_t row = (r / nsteps) * n + (size_t)t * 16 + (l & 15);
     dst[i] = src[row * ((size_t)nsteps * 4) + 4 * s + (l >> 4)];
   }
 }
@@ -794,11 +799,11 @@ moe_status moe_pack_weights(const moe_desc* d, int32_t which, const void* src, c
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int grid = di.cus * 8;
   hipLaunchKernelGGL(k_pack_weights, dim3(grid), dim3(256), 0, st, static_cast<const uint8_t*>(src),
-                     static_cast<uint8_t*>(dst), rows, K / 128, bs);
+                     static_cast<uint8_t*>(dst), rows, (int)N, K / 128, bs);
   HIP_TRY(hipGetLastError());
   if (fp4) {
     hipLaunchKernelGGL(k_pack_e8m0, dim3(grid), dim3(256), 0, st, static_cast<const uint8_t*>(src_scales),
-                       static_cast<uint8_t*>(dst_scales), rows, K / 128);
+                       static_cast<uint8_t*>(dst_scales), rows, (int)N, K / 128);
     HIP_TRY(hipGetLastError());
   }
   return MOE_OK;

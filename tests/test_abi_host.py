@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert lib.moe_abi_version() == 1
+    assert lib.moe_abi_version() == 2
     assert lib.moe_status_string(lib.MOE_OK) == "MOE_OK"
     assert lib.moe_status_string(lib.MOE_ERR_WORKSPACE_TOO_SMALL) == "MOE_ERR_WORKSPACE_TOO_SMALL"
 

@@ -237,21 +237,21 @@ def test_intermediate_matches_oracle(L, cfg):
 # ------------------------------------------------------------ weight layout
 def _tiled_reference(w: np.ndarray, bs: int) -> np.ndarray:
     """The MFMA-tiled layout of moe_layer.h written out with numpy: w is the
-    row-major [E][N][K-bytes] byte matrix; block (t, s) of BS/64 pieces of
-    1 KB, byte 16*l + j of piece p = row 16t + l%16, byte BS*s + 64p +
-    16*(l//16) + j."""
+    row-major [E][N][K-bytes] byte matrix; blocks (s, t), K step major, of
+    BS/64 pieces of 1 KB, byte 16*l + j of piece p = row 16t + l%16, byte
+    BS*s + 64p + 16*(l//16) + j."""
     E, N, KB = w.shape
     nsteps, npieces = KB // bs, bs // 64
     v = w.reshape(E, N // 16, 16, nsteps, npieces, 4, 16)      # e, t, row%16, s, p, l//16, j
-    v = v.transpose(0, 1, 3, 4, 5, 2, 6)                        # e, t, s, p, l//16, row%16, j
+    v = v.transpose(0, 3, 1, 4, 5, 2, 6)                        # e, s, t, p, l//16, row%16, j
     return np.ascontiguousarray(v).reshape(E, N, KB)
 
 
 def _tiled_scales_reference(sc: np.ndarray) -> np.ndarray:
-    """E8M0 scales [E][N][K/32] -> per (t, s) 64 bytes, byte l = row 16t +
-    l%16, group 4s + l//16."""
+    """E8M0 scales [E][N][K/32] -> per (s, t), K step major, 64 bytes, byte
+    l = row 16t + l%16, group 4s + l//16."""
     E, N, G = sc.shape
-    v = sc.reshape(E, N // 16, 16, G // 4, 4).transpose(0, 1, 3, 4, 2)
+    v = sc.reshape(E, N // 16, 16, G // 4, 4).transpose(0, 3, 1, 4, 2)   # e, s, t, l//16, row%16
     return np.ascontiguousarray(v).reshape(E, N, G)
 
 
