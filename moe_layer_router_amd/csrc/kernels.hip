@@ -184,7 +184,9 @@ DEV void signal_coherent(int32_t* c0, int32_t* c1 = nullptr) {
 // has been claimed by a running workgroup, so no wait can deadlock whatever
 // the grid size:
 //   head queue:   router tiles (128 tokens x 64 experts) -> rdone[token tile]
-//                 top-k of 32 tokens                     -> tkdone[256-token block]
+//                   (with channel slices: -> rtile[tile], then 8 items
+//                   per tile sum the slices -> rdone[token tile])
+//                 top-k of 16 tokens                     -> tkdone[256-token block]
 //                 expert histogram of 256 tokens        -> COUNT_DONE
 //                   (only with more than one 256-token block)
 //                 scan and stable scatter of 256 tokens -> SCATTER_DONE
@@ -230,9 +232,20 @@ __device__ __noinline__ void mega_router_item(Plan pv, int tt_, int et_, int ks_
   router_slice(p.H, ks, p.nKS, &s0, &s1);
   router_tile<AF>(ra, tt * kRouterTokens, et * kRouterExperts, lds, s0, s1, p.logits + (size_t)ks * p.T * p.E,
                   ks == 0);
-  if (p.nKS > 1) router_reduce(ra, tt * kRouterTokens, et * kRouterExperts, p.nKS, &p.rtile[tt * p.nER + et]);
 }
-constexpr int kTopkItemTokens = 32;        // tokens per top-k item of the persistent kernel
+// Part `part` of kReduceParts of the sum of router tile (tt, et)'s channel
+// slices (run once every slice of the tile is done).
+constexpr int kReduceParts = 8;
+__device__ __noinline__ void mega_reduce_item(Plan pv, int tt_, int et_, int part_) {
+  const Plan p = uniform_plan(pv);
+  const int tt = uni_i(tt_), et = uni_i(et_), part = uni_i(part_);
+  RouterArgs ra{p.x, p.x_scales, p.wr, p.bias, p.logits, p.T, p.H, p.E, p.act_fp8};
+  const int t0 = tt * kRouterTokens, e0 = et * kRouterExperts;
+  const int n = router_tile_elems(ra, t0, e0);
+  const int per = (n + kReduceParts - 1) / kReduceParts;
+  router_sum_slices(ra, t0, e0, p.nKS, min(n, part * per), min(n, (part + 1) * per));
+}
+constexpr int kTopkItemTokens = 16;        // tokens per top-k item of the persistent kernel
 __device__ __noinline__ void mega_topk_item(Plan pv, int i) {
   const Plan p = uniform_plan(pv);
   const int t0 = uni_i(i) * kTopkItemTokens;
@@ -264,12 +277,16 @@ k_mega(Plan p) {
   __shared__ int s_q, s_ok, s_first[kXcds + 1];
   const int tid = threadIdx.x;
   const int nR = p.routing_given ? 0 : p.nTR * p.nER * p.nKS;
+  // with the router's channels in slices, kReduceParts items per router tile
+  // sum the slices once all of them are done
+  const int nRd = (p.routing_given || p.nKS == 1) ? 0 : p.nTR * p.nER * kReduceParts;
   const int nK = p.routing_given ? 0 : (p.T + kTopkItemTokens - 1) / kTopkItemTokens;
   // histogram items only when there are several 256-token blocks (a single
   // block counts itself in its scatter item)
   const int nC = (p.nblk > 1) ? p.nblk : 0;
-  const int q_topk = nR, q_count = nR + nK, q_scat = q_count + nC, q_end = q_scat + p.nblk;
+  const int q_red = nR, q_topk = q_red + nRd, q_count = q_topk + nK, q_scat = q_count + nC, q_end = q_scat + p.nblk;
   constexpr int kPer = kPermBlock / kTopkItemTokens;   // top-k items per 256-token block
+  const int rdone_target = p.nER * ((p.nKS == 1) ? 1 : kReduceParts);   // per token tile
 
   // 1. routing and permutation items from the head queue
   for (;;) {
@@ -278,14 +295,19 @@ k_mega(Plan p) {
     const int q = s_q;
     __syncthreads();
     if (q >= q_end) break;
-    if (q < q_topk) {
+    if (q < q_red) {
       const int per_tt = p.nER * p.nKS;
       const int tt = q / per_tt, et = (q % per_tt) / p.nKS, ks = q % p.nKS;
       mega_router_item<AF>(p, tt, et, ks);
-      signal_coherent(&p.rdone[tt]);
+      signal_coherent(p.nKS == 1 ? &p.rdone[tt] : &p.rtile[tt * p.nER + et]);
+    } else if (q < q_topk) {
+      const int r = q - q_red, tile = r / kReduceParts;   // tile = tt * nER + et
+      if (!wait_counter(&p.rtile[tile], p.nKS, p.err, &s_ok, false)) return;
+      mega_reduce_item(p, tile / p.nER, tile % p.nER, r % kReduceParts);
+      signal_coherent(&p.rdone[tile / p.nER]);
     } else if (q < q_count) {
-      const int i = q - q_topk;                          // tokens [32i, 32i+32)
-      if (!wait_counter(&p.rdone[i / (kRouterTokens / kTopkItemTokens)], p.nER * p.nKS, p.err, &s_ok, false)) return;
+      const int i = q - q_topk;                          // tokens [16i, 16i+16)
+      if (!wait_counter(&p.rdone[i / (kRouterTokens / kTopkItemTokens)], rdone_target, p.err, &s_ok, false)) return;
       mega_topk_item(p, i);
       signal_coherent(&p.tkdone[i / (kPermBlock / kTopkItemTokens)]);
     } else if (q < q_scat) {

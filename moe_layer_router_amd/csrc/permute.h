@@ -171,14 +171,19 @@ DEV void scatter_block(const int32_t* ids, int T, int k, int E, int b, const Bas
   const int nt = min(kPermBlock, T - t0);
   const int tl = w * 64 + lane;
   const bool ok = tl < nt;
+  int ev[16];                                      // the token's experts, loaded once (k <= 16)
+#pragma unroll
+  for (int j = 0; j < 16; ++j) ev[j] = (ok && j < k) ? expert_of(ids, (size_t)(t0 + tl) * k + j, E) : 0;
   if (ok)
-    for (int j = 0; j < k; ++j)
-      atomicOr((unsigned long long*)&masks[(size_t)w * E + expert_of(ids, (size_t)(t0 + tl) * k + j, E)],
-               1ull << lane);
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (j < k) atomicOr((unsigned long long*)&masks[(size_t)w * E + ev[j]], 1ull << lane);
   __syncthreads();
   if (ok) {
-    for (int j = 0; j < k; ++j) {
-      const int e = expert_of(ids, (size_t)(t0 + tl) * k + j, E);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (j >= k) break;
+      const int e = ev[j];
       int rank = __popcll(masks[(size_t)w * E + e] & ((1ull << lane) - 1ull));
       for (int u = 0; u < w; ++u) rank += __popcll(masks[(size_t)u * E + e]);
       const int r = base_of(e) + rank;

@@ -182,32 +182,23 @@ DEV void router_tile(const RouterArgs& a, int t0, int e0, char* lds, int s0, int
   }
 }
 
-// With the channels split into S slices (partials at a.logits + s*T*E),
-// the last of the S tiles of (t0, e0) to finish (counted in *tile_cnt) sums
-// the partials of the tile, in slice order, into slice 0.
-DEV void router_reduce(const RouterArgs& a, int t0, int e0, int S, int32_t* tile_cnt) {
-  __shared__ int s_last;
-  wait_stores();                                   // this slice's partials are in memory
-  __syncthreads();
-  if (threadIdx.x == 0) s_last = (atomicAdd(tile_cnt, 1) == S - 1);
-  __syncthreads();
-  if (!s_last) return;
-  // the other slices' partials were in memory before their count; they are
-  // read coherently
+// Sum of the S channel-slice partials (at a.logits + s*T*E, S <= 8) of
+// elements [i0, i1) of the tile (t0, e0) (element i = token i / ne, expert
+// i % ne), in slice order, into slice 0.  kB elements per thread and pass,
+// consecutive threads on consecutive elements (each load instruction reads
+// whole lines); all loads of a pass are in flight together.  The partials
+// are read coherently: their writers' stores completed before their counts.
+DEV void router_sum_slices(const RouterArgs& a, int t0, int e0, int S, int i0, int i1) {
   const size_t stride = (size_t)a.T * a.E;
-  const int ne = min(kRouterExperts, a.E - e0), nt = min(kRouterTokens, a.T - t0);
-  const int n = nt * ne;
-  // kB elements per thread and pass, consecutive threads on consecutive
-  // elements (each load instruction reads whole lines); all loads of a pass
-  // are in flight together
+  const int ne = min(kRouterExperts, a.E - e0);
   constexpr int kB = 8, kMaxS = 8;
   const int nthr = blockDim.x;
-  for (int i0 = 0; i0 < n; i0 += nthr * kB) {
+  for (int ib = i0; ib < i1; ib += nthr * kB) {
     float p[kB][kMaxS];
     size_t off[kB];
 #pragma unroll
     for (int u = 0; u < kB; ++u) {
-      const int i = min(i0 + u * nthr + (int)threadIdx.x, n - 1);
+      const int i = min(ib + u * nthr + (int)threadIdx.x, i1 - 1);
       off[u] = (size_t)(t0 + i / ne) * a.E + e0 + i % ne;
 #pragma unroll
       for (int s = 0; s < kMaxS; ++s) p[u][s] = (s < S) ? ld_coh(a.logits + s * stride + off[u]) : 0.f;
@@ -218,9 +209,26 @@ DEV void router_reduce(const RouterArgs& a, int t0, int e0, int S, int32_t* tile
 #pragma unroll
       for (int s = 1; s < kMaxS; ++s)
         if (s < S) v += p[u][s];
-      if (i0 + u * nthr + (int)threadIdx.x < n) st_coh(a.logits + off[u], v);
+      if (ib + u * nthr + (int)threadIdx.x < i1) st_coh(a.logits + off[u], v);
     }
   }
+}
+
+// Number of elements of tile (t0, e0).
+DEV int router_tile_elems(const RouterArgs& a, int t0, int e0) {
+  return min(kRouterTokens, a.T - t0) * min(kRouterExperts, a.E - e0);
+}
+
+// With the channels split into S slices, the last of the S tiles of
+// (t0, e0) to finish (counted in *tile_cnt) sums the tile's partials.
+DEV void router_reduce(const RouterArgs& a, int t0, int e0, int S, int32_t* tile_cnt) {
+  __shared__ int s_last;
+  wait_stores();                                   // this slice's partials are in memory
+  __syncthreads();
+  if (threadIdx.x == 0) s_last = (atomicAdd(tile_cnt, 1) == S - 1);
+  __syncthreads();
+  if (!s_last) return;
+  router_sum_slices(a, t0, e0, S, 0, router_tile_elems(a, t0, e0));
 }
 
 // Max of a 64-bit key over the 16 lanes of a DPP row (the same four moves as
