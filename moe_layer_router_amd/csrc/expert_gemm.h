@@ -632,8 +632,8 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
         const float rw = lds_ld<float>(lds, L::kRowW + (rs * 16 + c16) * 4);
 #pragma unroll
         for (int cs = 0; cs < 4; ++cs) {
-          const uint32_t lo = f32_to_bf16_rne(acc[rs][cs][0] * rw) | (f32_to_bf16_rne(acc[rs][cs][1] * rw) << 16);
-          const uint32_t hi = f32_to_bf16_rne(acc[rs][cs][2] * rw) | (f32_to_bf16_rne(acc[rs][cs][3] * rw) << 16);
+          const uint32_t lo = bf16x2_rne(acc[rs][cs][0] * rw, acc[rs][cs][1] * rw);
+          const uint32_t hi = bf16x2_rne(acc[rs][cs][2] * rw, acc[rs][cs][3] * rw);
           const int c = 8 * w + 2 * cs + (gq >> 1);
           lds_st(lds, L::kA + rl * 512 + ((c ^ (rl & 15)) << 4) + 8 * (gq & 1), v2u{lo, hi});
         }
@@ -757,7 +757,7 @@ DEV void combine_rows(const uint16_t* staging, uint16_t* y, int T, int H, int k,
       v4i o;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        o[i] = (int)(f32_to_bf16_rne(s[u][2 * i]) | (f32_to_bf16_rne(s[u][2 * i + 1]) << 16));
+        o[i] = (int)bf16x2_rne(s[u][2 * i], s[u][2 * i + 1]);
       st16(reinterpret_cast<uint8_t*>(y) + ((size_t)tt[u] * H + cc[u]) * 2, o);
     }
   }
