@@ -151,7 +151,8 @@ size_t moe_permute_workspace_size(const moe_desc* d);
  *   offsets       [E+1] int32 (used only when the caller passes none)
  *   inter         [T*top_k][I] intermediate activations in permuted row
  *                 order: E4M3 codes (FP8 layers) or BF16 (BF16 layers)
- *   inter_scales  [T*top_k][I/128] fp32 re-quantisation scales (FP8 layers)
+ *   inter_scales  [I/128][T*top_k] fp32 re-quantisation scales (FP8 layers),
+ *                 K block major: block c of permuted row r at c*T*top_k + r
  *   staging       [T*top_k][H] BF16 weighted expert outputs, row t*top_k+j
  * Returns MOE_OK, or the status of an invalid descriptor. */
 typedef struct moe_workspace_regions {

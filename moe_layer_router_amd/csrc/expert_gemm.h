@@ -55,7 +55,8 @@ struct GemmArgs {
   const uint8_t* w_d;        // [E][H][I] or [E][H][I/2]
   const void* w_d_scales;    // fp32 [E][H/128][I/128] or E8M0 [E][H][I/32]
   uint8_t* aq;               // [T*k][I] E4M3 (or BF16 for BF16 layers)
-  float* sa;                 // [T*k][I/128]
+  float* sa;                 // [I/128][T*k] (K block major, permuted rows)
+  const float* sxp;          // [H/128][T*k] x_scales in permuted row order, or NULL
   uint16_t* staging;         // [T*k][H] BF16, indexed by flat index p
   int T, H, E, I, k;
 };
@@ -143,12 +144,13 @@ struct NoHook {
 // consumer reads the intermediate codes with ordinary, cached loads: each
 // 128-byte line of them belongs to one (row, N block), is written once per
 // launch and is read only after its writer's counter is complete, so no L2
-// can hold an older copy of it.  The intermediate's row scales (64 bytes per
-// row at I = 2048, so a line can hold rows of two tiles) are read
-// coherently.  `signal_prev` (may be NULL) is a counter to increment
-// once the stores of this workgroup's previous item have completed: the
-// prologue's barrier below waits for every older memory operation of each
-// wave, so the previous item is signalled without a wait of its own.
+// can hold an older copy of it.  The intermediate's scales (one K block of
+// 32 consecutive permuted rows per 128-byte line, so a line can hold rows of
+// two tiles) are read coherently.  `signal_prev` (may be NULL) is a
+// counter to increment once the stores of this workgroup's previous item
+// have completed: the prologue's barrier below waits for every older memory
+// operation of each wave, so the previous item is signalled without a wait
+// of its own.
 // `at_loop_end()` is called by every thread once the K loop has ended,
 // before the epilogue.
 template <int AF, int WF, int STAGE, int RS, int COH, typename Hook>
@@ -260,14 +262,21 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
   // subtile with one or two 16-byte LDS reads.
   const int arow = 64 * (w & 1) + lane;
   const int srow = (arow < m) ? arow : 0;
+  // The intermediate's scales, and the activation scales when a permuted
+  // copy exists (g.sxp), are K block major over the permuted rows
+  // ([K/128][T*k]): the scales of one step for a tile's rows are contiguous.
+  // Otherwise each row reads its token's row of x_scales.
+  const uint32_t nrows_all = (uint32_t)(g.T * g.k);
+  const bool permuted = (STAGE == 2) || g.sxp != nullptr;
   const rsrc_t sars = (AF != ACT_FP8) ? make_rsrc(nullptr, 0)
-                      : (STAGE == 1) ? make_rsrc(g.x_scales, (uint32_t)g.T * (g.H / 128) * 4)
-                                     : make_rsrc(g.sa, (uint32_t)(g.T * g.k) * (g.I / 128) * 4);
-  const uint32_t saoff = (STAGE == 1) ? (uint32_t)ROWI[srow < R ? srow : 0] * (g.H / 128) * 4
-                                      : (uint32_t)(r0 + srow) * (g.I / 128) * 4;
+                      : (STAGE == 2) ? make_rsrc(g.sa, nrows_all * (uint32_t)(g.I / 128) * 4)
+                      : permuted     ? make_rsrc(g.sxp, nrows_all * (uint32_t)(g.H / 128) * 4)
+                                     : make_rsrc(g.x_scales, (uint32_t)g.T * (g.H / 128) * 4);
+  const uint32_t saoff = permuted ? (uint32_t)(r0 + srow) * 4 : (uint32_t)ROWI[srow] * (uint32_t)(g.H / 128) * 4;
+  const uint32_t sastep = permuted ? nrows_all * 4 : 4u;
   auto dma_sa = [&](int s, int slot) __attribute__((always_inline)) {   // slot = s % kSaSlots
     buf_ld4_lds<STAGE == 2 ? CP : 0>(sars, lds + L::kSA + slot * 512 + (w & 1) * 256, saoff,
-                                     (uint32_t)min(s, nsteps - 1) * 4);
+                                     (uint32_t)min(s, nsteps - 1) * sastep);
   };
   auto read_sa = [&](int slot) __attribute__((always_inline)) -> float {
     return (AF == ACT_FP8) ? lds_ld<float>(lds, L::kSA + slot * 512 + (tid & 127) * 4) : 1.f;
@@ -594,7 +603,7 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
         *go = (uint32_t)(r0 + row) * g.I + c0 + c * 16;
         return row < m;
       });
-      if (tid < m) buf_stf<CP>(saw, ((uint32_t)(r0 + tid) * (g.I / 128) + c0 / 128) * 4, RSC[tid]);
+      if (tid < m) buf_stf<CP>(saw, ((uint32_t)(c0 / 128) * nrows + (uint32_t)(r0 + tid)) * 4, RSC[tid]);
     } else {
       // chunk c of staging row r at c ^ (((r >> 2) & 3) << 1) (bank spread)
       const uint32_t lo = 2 * (c16 & 7), hc = c16 >> 3;

@@ -14,6 +14,7 @@ enum {
   CTR_SCATTER_DONE,   // scan-and-scatter items finished
   CTR_G1_DONE,        // gate|up items finished
   CTR_QUEUE2,         // persistent kernel: queue head after the gate|up items
+  CTR_SXP_DONE,       // permuted activation-scale items finished
   CTR_Q1 = 8,         // [kXcds] gate|up item queues, one per expert class
   CTR_Q2 = 16,        // [kXcds] down item queues (separate kernels)
   CTR_NUM = 32
@@ -47,6 +48,7 @@ struct Plan {
   float* logits; int32_t* blockcnt; int32_t* base; int32_t* row_of;
   Tile* tiles; int32_t* meta;
   uint8_t* aq; float* sa; uint16_t* staging;
+  float* sxp;                  // [H/128][T*k] activation scales, permuted rows, or NULL
 };
 
 constexpr int kCombineTokens = 256;
@@ -74,7 +76,7 @@ __host__ __device__ inline GemmArgs gemm_args(const Plan& p) {
   GemmArgs g;
   g.x = p.x; g.x_scales = p.x_scales; g.perm = p.perm; g.topk_w = p.wts;
   g.w_gu = p.w_gu; g.w_gu_scales = p.w_gu_scales; g.w_d = p.w_d; g.w_d_scales = p.w_d_scales;
-  g.aq = p.aq; g.sa = p.sa; g.staging = p.staging;
+  g.aq = p.aq; g.sa = p.sa; g.staging = p.staging; g.sxp = p.sxp;
   g.T = p.T; g.H = p.H; g.E = p.E; g.I = p.I; g.k = p.k;
   return g;
 }

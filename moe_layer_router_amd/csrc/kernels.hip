@@ -59,6 +59,13 @@ __global__ void __launch_bounds__(256) k_scatter(const int32_t* ids, int T, int 
   perm_scatter_block(ids, T, k, E, blockIdx.x, base, perm, row_of, reinterpret_cast<uint64_t*>(lds));
 }
 
+// Activation scales in permuted row order (FP8 layers): 256 rows per block.
+__global__ void __launch_bounds__(256) k_permute_scales(const int32_t* perm, const float* x_scales, int T, int k,
+                                                        int ns, float* sxp) {
+  const int r0 = blockIdx.x * 256;
+  permute_scales(perm, x_scales, T, k, ns, r0, min(T * k, r0 + 256), sxp);
+}
+
 // Persistent grid (one workgroup per CU) over (tile, N block) items taken
 // from the per-class queues.  Workgroup b runs on XCD b % 8 (round-robin
 // dispatch) and starts on that class.  Thread 0 claims the next item when
@@ -191,6 +198,8 @@ DEV void signal_coherent(int32_t* c0, int32_t* c1 = nullptr) {
 //                   (only with more than one 256-token block)
 //                 scan and stable scatter of 256 tokens -> SCATTER_DONE
 //                   (block 0 also writes offsets, tiles)
+//                 FP8 layers: activation scales of 256 permuted rows,
+//                   K block major                       -> SXP_DONE
 //   class queues: gate|up items (tile, 128 channels)    -> done1[tile]
 //   class queues: down items (tile, 256 columns)        -> done2[N block]
 //   tail queue:   combine items (N block, 256 tokens)
@@ -264,6 +273,12 @@ __device__ __noinline__ void mega_scatter_item(Plan pv, int b_) {
   perm_scan_scatter_block(p.ids, p.T, p.k, p.E, b, p.nblk, p.blockcnt, p.tile_rows, p.offsets, p.tiles, p.meta,
                           p.perm, p.row_of, lds);
 }
+constexpr int kSxpRows = 256;             // permuted rows per activation-scale item
+__device__ __noinline__ void mega_sxp_item(Plan pv, int i_) {
+  const Plan p = uniform_plan(pv);
+  const int r0 = uni_i(i_) * kSxpRows;
+  permute_scales(p.perm, p.x_scales, p.T, p.k, p.H / 128, r0, min(p.T * p.k, r0 + kSxpRows), p.sxp);
+}
 __device__ __noinline__ void mega_combine_item(Plan pv, int nb_, int c) {
   const Plan p = uniform_plan(pv);
   const int nb = uni_i(nb_), t0 = uni_i(c) * kCombineTokens;
@@ -284,7 +299,10 @@ k_mega(Plan p) {
   // histogram items only when there are several 256-token blocks (a single
   // block counts itself in its scatter item)
   const int nC = (p.nblk > 1) ? p.nblk : 0;
-  const int q_red = nR, q_topk = q_red + nRd, q_count = q_topk + nK, q_scat = q_count + nC, q_end = q_scat + p.nblk;
+  // FP8 layers: the activation scales in permuted row order, after the scatter
+  const int nX = p.sxp ? (p.T * p.k + kSxpRows - 1) / kSxpRows : 0;
+  const int q_red = nR, q_topk = q_red + nRd, q_count = q_topk + nK, q_scat = q_count + nC, q_sxp = q_scat + p.nblk;
+  const int q_end = q_sxp + nX;
   constexpr int kPer = kPermBlock / kTopkItemTokens;   // top-k items per 256-token block
   const int rdone_target = p.nER * ((p.nKS == 1) ? 1 : kReduceParts);   // per token tile
 
@@ -315,6 +333,10 @@ k_mega(Plan p) {
       if (!p.routing_given && !wait_counter(&p.tkdone[b], min(kPer, nK - kPer * b), p.err, &s_ok, false)) return;
       mega_count_item(p, b);
       signal_coherent(&p.ctr[CTR_COUNT_DONE]);
+    } else if (q >= q_sxp) {
+      if (!wait_counter(&p.ctr[CTR_SCATTER_DONE], p.nblk, p.err, &s_ok, false)) return;
+      mega_sxp_item(p, q - q_sxp);
+      signal_coherent(&p.ctr[CTR_SXP_DONE]);
     } else {
       // scan and scatter of one block, once every histogram is in (or, with
       // a single block, once its top-k items are done)
@@ -333,7 +355,11 @@ k_mega(Plan p) {
   // claimed by a running workgroup, so these waits end).  The GEMM items
   // read the permutation, tiles and weights with ordinary loads: one acquire
   // per workgroup here drops any older copy of them from the L2.
-  if (!wait_counter(&p.ctr[CTR_SCATTER_DONE], p.nblk, p.err, &s_ok)) return;
+  if (nX > 0) {
+    if (!wait_counter(&p.ctr[CTR_SXP_DONE], nX, p.err, &s_ok)) return;     // (after every scatter item)
+  } else if (!wait_counter(&p.ctr[CTR_SCATTER_DONE], p.nblk, p.err, &s_ok)) {
+    return;
+  }
   if (tid <= kXcds) s_first[tid] = __hip_atomic_load(&p.meta[1 + tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   const int ntiles = s_first[kXcds];
@@ -420,7 +446,7 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Layout {
   size_t err, zero_begin, ctr, rdone, rtile, tkdone, done1, done2, zero_end;
-  size_t logits, blockcnt, base, offsets, perm, row_of, tiles, meta, aq, sa, staging, total;
+  size_t logits, blockcnt, base, offsets, perm, row_of, tiles, meta, aq, sa, sxp, staging, total;
   int nblk, nTR, nER, nKS, max_tiles, nnb1, nnb2;
 };
 
@@ -469,6 +495,7 @@ Layout make_layout(const moe_desc* d) {
   L.meta = o; o = align256(o + 64);
   L.aq = o; o = align256(o + T * k * I * (d->act_dtype == MOE_DTYPE_FP8_E4M3 ? 1 : 2));
   L.sa = o; o = align256(o + T * k * (I / 128) * 4);
+  L.sxp = o; if (d->act_dtype == MOE_DTYPE_FP8_E4M3 && L.nblk > 1) o = align256(o + T * k * (H / 128) * 4);
   L.staging = o; o = align256(o + T * k * H * 2);
   L.total = o;
   return L;
@@ -571,6 +598,9 @@ moe_status fill_plan(const moe_desc* d, const Layout& L, char* ws, Plan* P) {
   p.meta = reinterpret_cast<int32_t*>(ws + L.meta);
   p.aq = reinterpret_cast<uint8_t*>(ws + L.aq);
   p.sa = reinterpret_cast<float*>(ws + L.sa);
+  // permuted activation scales when there are several 256-token blocks (for
+  // a single block the extra step costs more than it saves)
+  p.sxp = (p.act_fp8 && L.nblk > 1) ? reinterpret_cast<float*>(ws + L.sxp) : nullptr;
   p.staging = reinterpret_cast<uint16_t*>(ws + L.staging);
   return MOE_OK;
 }
@@ -643,6 +673,11 @@ moe_status launch_layer(const Plan& p, const DevInfo& di, int mode, hipStream_t 
   if (mode == MOE_MODE_SEPARATE) {
     if (!p.routing_given) TRY(launch_route(p, p.logits, p.nKS, st));
     TRY(launch_permute(p, p.row_of, st));
+    if (p.sxp) {
+      hipLaunchKernelGGL(k_permute_scales, dim3((p.T * p.k + 255) / 256), dim3(256), 0, st, p.perm, p.x_scales, p.T,
+                         p.k, p.H / 128, p.sxp);
+      HIP_TRY(hipGetLastError());
+    }
     const GemmArgs g = gemm_args(p);
     const int lds = gemm_lds(AF == ACT_FP8);
     TRY(set_lds_limit(k_gemm<AF, WF, 1>, lds));

@@ -277,4 +277,19 @@ DEV void perm_scan_scatter_block(const int32_t* ids, int T, int k, int E, int b,
   scatter_block(ids, T, k, E, b, [&](int e) { return pre[e]; }, perm, row_of, masks);
 }
 
+// Activation scales in permuted row order, K block major: for permuted rows
+// [r0, r1) (one per thread), sxp[s][r] = x_scales[perm[r] / k][s] for the
+// ns = H/128 blocks, so that a GEMM tile reads the scales of its rows for
+// one K step as one contiguous run.  The permutation is read coherently
+// (written earlier in the same kernel) and the copy is stored write-through.
+DEV void permute_scales(const int32_t* perm, const float* x_scales, int T, int k, int ns, int r0, int r1,
+                        float* sxp) {
+  const int n = T * k;
+  for (int r = r0 + (int)threadIdx.x; r < r1; r += blockDim.x) {
+    const int t = min(max(ld_coh(perm + r), 0), n - 1) / k;
+    const float* src = x_scales + (size_t)t * ns;
+    for (int s = 0; s < ns; ++s) st_coh(sxp + (size_t)s * n + r, src[s]);
+  }
+}
+
 }  // namespace moe

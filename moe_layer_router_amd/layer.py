@@ -99,7 +99,7 @@ def intermediate(out: dict):
     if desc.act_dtype == lib.MOE_DTYPE_FP8_E4M3:
         codes = ws[reg["inter"]: reg["inter"] + rows * I].view(rows, I)
         sc = ws[reg["inter_scales"]: reg["inter_scales"] + rows * (I // 128) * 4].view(torch.float32)
-        return codes, sc.view(rows, I // 128)
+        return codes, sc.view(I // 128, rows).t()       # stored K block major
     vals = ws[reg["inter"]: reg["inter"] + rows * I * 2].view(torch.bfloat16).view(rows, I)
     return vals, None
 
