@@ -517,7 +517,7 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
   // the scales of step s+1 into a register within the step: no loaded value
   // is carried across the loop's back edge, where the compiler would drain
   // every load in flight.
-  constexpr int UNR = (AF == ACT_FP8) ? 8 : 6;
+  constexpr int UNR = (AF == ACT_FP8) ? 16 : 6;
   static_assert(UNR % NBUF == 0 && UNR % 2 == 0 && UNR % L::kAStages == 0 && UNR % L::kSaSlots == 0,
                 "loop unroll");
   auto step = [&](int s, int u) __attribute__((always_inline)) {
