@@ -225,6 +225,24 @@ DEV Plan uniform_plan(const Plan& in) {
 DEV int uni_i(int v) { return __builtin_amdgcn_readfirstlane(v); }
 // The GEMM items are inlined into the kernel: as a called function they
 // would save and restore the callee-saved VGPRs they use on every item.
+// Tiles as the GEMM phases read them: through the scalar cache, as k_gemm
+// does (where the compiler chooses it by itself, the tiles being read-only
+// there).  In the persistent kernel the permutation items write them, in
+// lines of their own, before any GEMM item starts, and nothing reads them
+// through that cache earlier in the launch (it starts each launch empty), so
+// it cannot hold an older copy.  Ordinary loads would put two dependent
+// round trips to memory between every two items.
+typedef const __attribute__((address_space(4))) Tile KTile;
+DEV Tile tile_at(KTile* kt, int t) {
+  Tile x;
+  x.e = kt[t].e;
+  x.r0 = kt[t].r0;
+  x.rows = kt[t].rows;
+  x.rs = kt[t].rs;
+  x.g0 = kt[t].g0;
+  x.gn = kt[t].gn;
+  return x;
+}
 template <int AF, int WF, int STAGE, typename Hook>
 __device__ __forceinline__ void mega_gemm_item(const Plan& p, Tile tl, int nb, int32_t* signal_prev,
                                                const Hook& at_loop_end) {
@@ -368,10 +386,11 @@ k_mega(Plan p) {
   if (tid == 0) s_q = pop_class_item(p.ctr + CTR_Q1, s_first, p.nnb1, &cls);
   __syncthreads();
   // (the next item is claimed when the current one's K loop ends, as in k_gemm)
+  KTile* const ktiles = (KTile*)p.tiles;
   for (int i = s_q; i >= 0;) {
     int t, nb;
-    gemm_item_of(p.tiles, p.nnb1, i, &t, &nb);
-    mega_gemm_item<AF, WF, 1>(p, p.tiles[t], nb, pending, [&]() {
+    gemm_item_of(ktiles, p.nnb1, uni_i(i), &t, &nb);
+    mega_gemm_item<AF, WF, 1>(p, tile_at(ktiles, t), nb, pending, [&]() {
       if (tid == 0) s_q = pop_class_item(p.ctr + CTR_Q1, s_first, p.nnb1, &cls);
     });
     pending = &p.done1[t];                 // signalled once its stores have completed
@@ -390,9 +409,9 @@ k_mega(Plan p) {
   __syncthreads();
   for (int i = s_q; i >= 0;) {
     int t, nb;
-    gemm_item_of(p.tiles, p.nnb2, i, &t, &nb);
+    gemm_item_of(ktiles, p.nnb2, uni_i(i), &t, &nb);
     if (!wait_counter(&p.done1[t], p.nnb1, p.err, &s_ok, false)) return;
-    mega_gemm_item<AF, WF, 2>(p, p.tiles[t], nb, pending, [&]() {
+    mega_gemm_item<AF, WF, 2>(p, tile_at(ktiles, t), nb, pending, [&]() {
       if (tid == 0) s_q = pop_class_item(p.ctr + CTR_Q2, s_first, p.nnb2, &cls);
     });
     pending = &p.done2[nb];

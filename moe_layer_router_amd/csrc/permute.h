@@ -32,11 +32,14 @@ static_assert(sizeof(Tile) == 6 * sizeof(int32_t), "tile fields are stored one b
 // are ordered expert by expert, then by N block, then by the expert's tiles,
 // so that the items reading the same weight slab are adjacent in the queue
 // and run at the same time (the later reads hit the caches).
-DEV void gemm_item_of(const Tile* tiles, int nnb, int i, int* t, int* nb) {
-  const Tile& x = tiles[i / nnb];
-  const int local = i - x.g0 * nnb;
-  *nb = local / x.gn;
-  *t = x.g0 + local % x.gn;
+// (`tiles` is any pointer to Tile, also one into another address space.)
+template <typename TilePtr>
+DEV void gemm_item_of(TilePtr tiles, int nnb, int i, int* t, int* nb) {
+  const int j = i / nnb;
+  const int g0 = tiles[j].g0, gn = tiles[j].gn;
+  const int local = i - g0 * nnb;
+  *nb = local / gn;
+  *t = g0 + local % gn;
 }
 
 DEV int tile_variant(int rows, int full_rs) { return rows <= 16 ? 1 : rows <= 64 ? 4 : full_rs; }
