@@ -63,7 +63,9 @@
  *
  * Supported dtype pairs (act x weight): BF16 x BF16, FP8 x FP8, FP8 x FP4.
  * Limits: T >= 1; H and I multiples of 128 (H <= 16384, I <= 16384);
- * 1 <= top_k <= E; E <= 1024; top_k <= 16.  Pointers must be 16-byte aligned.
+ * 1 <= top_k <= E; E <= 1024; top_k <= 16; T * top_k * max(H, I) * 2 < 4 GiB
+ * (the staging and intermediate rows are addressed with 32-bit offsets).
+ * Pointers must be 16-byte aligned.
  *
  * Ownership and asynchrony.  The library never allocates device memory in
  * moe_forward / moe_route / moe_permute: every buffer, including the

@@ -534,6 +534,12 @@ moe_status check_desc(const moe_desc* d) {
   if (d->H > 16384) return fail(MOE_ERR_UNSUPPORTED, "H > 16384 is not supported (got %d)", d->H);
   if (d->I > 16384) return fail(MOE_ERR_UNSUPPORTED, "I > 16384 is not supported (got %d)", d->I);
   if ((long long)d->T * d->top_k > (1LL << 30)) return fail(MOE_ERR_UNSUPPORTED, "T * top_k too large");
+  // whole-array buffers are addressed with 32-bit byte offsets; the staging
+  // rows (T*top_k*H BF16) and the intermediate rows (T*top_k*I, at most
+  // 2 bytes each) are the largest of them
+  if ((long long)d->T * d->top_k * (d->H > d->I ? d->H : d->I) * 2 > 0xFFFFFFFFLL)
+    return fail(MOE_ERR_UNSUPPORTED, "T * top_k * max(H, I) * 2 must be below 4 GiB (got T=%d, top_k=%d, H=%d, I=%d)",
+                d->T, d->top_k, d->H, d->I);
   const bool pair_ok = (d->act_dtype == MOE_DTYPE_BF16 && d->weight_dtype == MOE_DTYPE_BF16) ||
                        (d->act_dtype == MOE_DTYPE_FP8_E4M3 && d->weight_dtype == MOE_DTYPE_FP8_E4M3) ||
                        (d->act_dtype == MOE_DTYPE_FP8_E4M3 && d->weight_dtype == MOE_DTYPE_FP4_E2M1);

@@ -111,7 +111,12 @@ DEV void perm_scan(const int32_t* blockcnt, int nblk, int E, int tile_rows, int3
     for (int b0 = 0; b0 < nblk; b0 += kBatch) {
       int c[kBatch];
 #pragma unroll
-      for (int i = 0; i < kBatch; ++i) c[i] = (b0 + i < nblk) ? ld_coh(blockcnt + (size_t)(b0 + i) * E + e) : 0;
+      for (int i = 0; i < kBatch; ++i) {
+        // (an in-range address, the value dropped after the load: a load
+        // under a condition is a branch that waits for it)
+        const int32_t v = ld_coh(blockcnt + (size_t)min(b0 + i, nblk - 1) * E + e);
+        c[i] = (b0 + i < nblk) ? v : 0;
+      }
 #pragma unroll
       for (int i = 0; i < kBatch; ++i) run += c[i];
     }
@@ -131,7 +136,12 @@ DEV void perm_scan(const int32_t* blockcnt, int nblk, int E, int tile_rows, int3
     for (int b0 = 0; b0 < nblk; b0 += kBatch) {
       int cb[kBatch];
 #pragma unroll
-      for (int i = 0; i < kBatch; ++i) cb[i] = (b0 + i < nblk) ? ld_coh(blockcnt + (size_t)(b0 + i) * E + e) : 0;
+      for (int i = 0; i < kBatch; ++i) {
+        // (an in-range address, the value dropped after the load: a load
+        // under a condition is a branch that waits for it)
+        const int32_t v = ld_coh(blockcnt + (size_t)min(b0 + i, nblk - 1) * E + e);
+        cb[i] = (b0 + i < nblk) ? v : 0;
+      }
 #pragma unroll
       for (int i = 0; i < kBatch; ++i) {
         if (b0 + i < nblk) st_coh(base + (size_t)(b0 + i) * E + e, run);
@@ -174,9 +184,13 @@ DEV void scatter_block(const int32_t* ids, int T, int k, int E, int b, const Bas
   const int nt = min(kPermBlock, T - t0);
   const int tl = w * 64 + lane;
   const bool ok = tl < nt;
-  int ev[16];                                      // the token's experts, loaded once (k <= 16)
+  // The token's experts, loaded once (k <= 16): every load from an in-range
+  // address and all of them before any use (a load under a condition is a
+  // branch that waits for it).
+  int ev[16];
+  const size_t ib = (size_t)min(t0 + tl, T - 1) * k;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) ev[j] = (ok && j < k) ? expert_of(ids, (size_t)(t0 + tl) * k + j, E) : 0;
+  for (int j = 0; j < 16; ++j) ev[j] = expert_of(ids, ib + min(j, k - 1), E);
   if (ok)
 #pragma unroll
     for (int j = 0; j < 16; ++j)
@@ -231,7 +245,12 @@ DEV void perm_scan_scatter_block(const int32_t* ids, int T, int k, int E, int b,
       for (int b0 = 0; b0 < nblk; b0 += kBatch) {
         int c[kBatch];
 #pragma unroll
-        for (int i = 0; i < kBatch; ++i) c[i] = (b0 + i < nblk) ? ld_coh(blockcnt + (size_t)(b0 + i) * E + e) : 0;
+        for (int i = 0; i < kBatch; ++i) {
+          // (an in-range address, the value dropped after the load: a load
+          // under a condition is a branch that waits for it)
+          const int32_t v = ld_coh(blockcnt + (size_t)min(b0 + i, nblk - 1) * E + e);
+          c[i] = (b0 + i < nblk) ? v : 0;
+        }
 #pragma unroll
         for (int i = 0; i < kBatch; ++i) {
           tot += c[i];
@@ -291,7 +310,18 @@ DEV void permute_scales(const int32_t* perm, const float* x_scales, int T, int k
   for (int r = r0 + (int)threadIdx.x; r < r1; r += blockDim.x) {
     const int t = min(max(ld_coh(perm + r), 0), n - 1) / k;
     const float* src = x_scales + (size_t)t * ns;
-    for (int s = 0; s < ns; ++s) st_coh(sxp + (size_t)s * n + r, src[s]);
+    // a chunk of the row's scales is loaded before any of it is stored: the
+    // stores could alias the source, so loads after a store would wait for
+    // it, one round trip to memory per scale
+    constexpr int kChunk = 32;
+    for (int s0 = 0; s0 < ns; s0 += kChunk) {
+      float v[kChunk];
+#pragma unroll
+      for (int j = 0; j < kChunk; ++j) v[j] = src[min(s0 + j, ns - 1)];
+#pragma unroll
+      for (int j = 0; j < kChunk; ++j)
+        if (s0 + j < ns) st_coh(sxp + (size_t)(s0 + j) * n + r, v[j]);
+    }
   }
 }
 

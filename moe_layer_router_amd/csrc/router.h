@@ -166,18 +166,26 @@ DEV void router_tile(const RouterArgs& a, int t0, int e0, char* lds, int s0, int
   wait_vmcnt<0>();                                 // loads issued for steps past the end
   __syncthreads();
 
-  // accumulator element v of tile (sub, c): token 32w + 16sub + 4g + v, expert 16c + c16
+  // accumulator element v of tile (sub, c): token 32w + 16sub + 4g + v, expert 16c + c16.
+  // Write-through buffer stores, with the elements outside [T) x [E) given
+  // an offset past the buffer's end, which the hardware drops: stores under
+  // a condition would each be a branch with a wait.
+  // (the biases are loaded before the first store, which could alias them)
+  const rsrc_t ors = make_rsrc_u(out, (uint32_t)a.T * (uint32_t)a.E * 4u);
+  float bias[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) bias[c] = (add_bias && a.bias) ? a.bias[min(e0 + 16 * c + c16, a.E - 1)] : 0.f;
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     const int e = e0 + 16 * c + c16;
-    if (e >= a.E) continue;
-    const float b = (add_bias && a.bias) ? a.bias[e] : 0.f;
+    const float b = bias[c];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int t = t0 + 32 * w + 16 * sub + 4 * g + v;
-        if (t < a.T) st_coh(out + (size_t)t * a.E + e, acc[sub][c][v] + b);
+        const uint32_t off = (t < a.T && e < a.E) ? ((uint32_t)t * (uint32_t)a.E + (uint32_t)e) * 4u : 0xFFFFFFF0u;
+        buf_stf<kCoherent>(ors, off, acc[sub][c][v] + b);
       }
   }
 }
@@ -193,6 +201,10 @@ DEV void router_sum_slices(const RouterArgs& a, int t0, int e0, int S, int i0, i
   const int ne = min(kRouterExperts, a.E - e0);
   constexpr int kB = 8, kMaxS = 8;
   const int nthr = blockDim.x;
+  // write-through buffer stores; an element past i1 gets an offset past the
+  // buffer's end, which the hardware drops (a store under a condition would
+  // be a branch with a wait)
+  const rsrc_t lrs = make_rsrc_u(a.logits, (uint32_t)a.T * (uint32_t)a.E * 4u);
   for (int ib = i0; ib < i1; ib += nthr * kB) {
     float p[kB][kMaxS];
     size_t off[kB];
@@ -200,8 +212,15 @@ DEV void router_sum_slices(const RouterArgs& a, int t0, int e0, int S, int i0, i
     for (int u = 0; u < kB; ++u) {
       const int i = min(ib + u * nthr + (int)threadIdx.x, i1 - 1);
       off[u] = (size_t)(t0 + i / ne) * a.E + e0 + i % ne;
+    }
+    // the loads of one slice for all kB elements under one (uniform)
+    // condition, before any of them is used
 #pragma unroll
-      for (int s = 0; s < kMaxS; ++s) p[u][s] = (s < S) ? ld_coh(a.logits + s * stride + off[u]) : 0.f;
+    for (int s = 0; s < kMaxS; ++s) {
+      if (s < S) {
+#pragma unroll
+        for (int u = 0; u < kB; ++u) p[u][s] = ld_coh(a.logits + s * stride + off[u]);
+      }
     }
 #pragma unroll
     for (int u = 0; u < kB; ++u) {
@@ -209,7 +228,8 @@ DEV void router_sum_slices(const RouterArgs& a, int t0, int e0, int S, int i0, i
 #pragma unroll
       for (int s = 1; s < kMaxS; ++s)
         if (s < S) v += p[u][s];
-      if (ib + u * nthr + (int)threadIdx.x < i1) st_coh(a.logits + off[u], v);
+      const bool ok = ib + u * nthr + (int)threadIdx.x < i1;
+      buf_stf<kCoherent>(lrs, ok ? (uint32_t)off[u] * 4u : 0xFFFFFFF0u, v);
     }
   }
 }
@@ -277,11 +297,18 @@ DEV uint64_t wave_max64(uint64_t v) {
 // largest key is the largest logit with the lowest index.  E <= 1024, k <= 16.
 DEV void topk_token(const float* lrow, int E, int k, int32_t* ids, float* wts) {
   const int lane = threadIdx.x & 63;
+  // All 16 loads first, each from an in-range address, the unused keys
+  // cleared afterwards: a load under a condition is a branch that waits for
+  // it, and coherent loads stay in program order with the arithmetic between
+  // them, so either way each load would wait for the one before.
+  float v[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] = ld_coh(lrow + min(lane + 64 * i, E - 1));
   uint64_t key[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int e = lane + 64 * i;
-    key[i] = (e < E) ? (((uint64_t)f32_order_key(ld_coh(lrow + e)) << 32) | (uint32_t)(E - 1 - e)) : 0ull;
+    key[i] = (e < E) ? (((uint64_t)f32_order_key(v[i]) << 32) | (uint32_t)(E - 1 - e)) : 0ull;
   }
   int my_id = 0;
   float my_val = 0.f, top = 0.f;
@@ -314,11 +341,14 @@ DEV void topk_token(const float* lrow, int E, int k, int32_t* ids, float* wts) {
 // the row holds experts i + 16j.  Same keys and order as topk_token.
 DEV void topk_token16(const float* lrow, bool valid, int E, int k, int32_t* ids, float* wts) {
   const int li = threadIdx.x & 15;
+  float v[16];                                     // (loads first: see topk_token)
+#pragma unroll
+  for (int j = 0; j < 16; ++j) v[j] = ld_coh(lrow + min(li + 16 * j, E - 1));
   uint64_t key[16];
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     const int e = li + 16 * j;
-    key[j] = (valid && e < E) ? (((uint64_t)f32_order_key(ld_coh(lrow + e)) << 32) | (uint32_t)(E - 1 - e)) : 0ull;
+    key[j] = (valid && e < E) ? (((uint64_t)f32_order_key(v[j]) << 32) | (uint32_t)(E - 1 - e)) : 0ull;
   }
   int my_id = 0;
   float my_val = 0.f, top = 0.f;

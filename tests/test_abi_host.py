@@ -77,6 +77,8 @@ def test_validate_accepts_good_arguments():
     ((10, 512, 2048, 256, 4), lib.MOE_ERR_UNSUPPORTED),         # E > 1024
     ((10, 512, 64, 256, 17), lib.MOE_ERR_UNSUPPORTED),          # k > 16
     ((10, 32768, 16, 256, 4), lib.MOE_ERR_UNSUPPORTED),         # H > 16384
+    ((65536, 7168, 256, 2048, 8), lib.MOE_ERR_UNSUPPORTED),     # staging rows T*k*H*2 >= 4 GiB
+    ((65536, 256, 256, 16384, 4), lib.MOE_ERR_UNSUPPORTED),     # intermediate rows T*k*I*2 >= 4 GiB
 ])
 def test_validate_rejects_bad_shapes(shape, status):
     assert _validate(lib.make_desc(*shape)) == status
