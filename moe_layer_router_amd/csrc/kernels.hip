@@ -149,8 +149,12 @@ DEV bool wait_counter(const int32_t* c, int target, int32_t* err, int* s_ok, boo
   if (threadIdx.x == 0) {
     int ok = 1;
     unsigned spins = 0;
-    while (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-      if (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) { ok = 0; break; }
+    for (;;) {
+      // both words read in one round trip per poll
+      const int v = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int e = __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (v >= target) break;
+      if (e != 0) { ok = 0; break; }
       __builtin_amdgcn_s_sleep(8);
       if (++spins > kSpinLimit) {
         __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
