@@ -42,13 +42,23 @@ R7  FP8 weights carry one fp32 scale per 128 x 128 block of the stored [N, K]
 R8  The permuted (expert-contiguous) row order sorts the flat index
     p = t*k + j by expert, stably, so rows of one expert are in ascending token
     order.
-R10 FP8 re-quantisation near-ties: the device forms a with fp32 (and
-    MFMA-internal) accumulation, so its a / s differs from the fp64 value
-    by up to a small amount relative to the row's largest element.  Where
-    the window a / s +- TIE_EPS straddles an E4M3 rounding boundary, every
-    value the window rounds to is a correct result of the method.  The
-    oracle then accepts a code supplied by the caller, but only at such
-    positions and only inside the window.
+R10 Where the device's result is one rounding step away from the oracle's
+    (an FP8 code of the intermediate, its fp32 scale, a BF16 intermediate,
+    or the order of two router logits), both are results of the method if
+    the device's inputs to that rounding lie within a bound derived here
+    from the arithmetic: fp32 accumulation (every product of a dot product
+    passes through at most n additions, each erring by at most one unit in
+    the last place of its fp32 result, u = 2**-23, so the sum is off by at
+    most gamma_n * sum|x*w| with gamma_n = n*u/(1-n*u)), zero where every
+    partial sum is exactly representable in fp32, plus the documented
+    accuracy of the matrix core and of the exponential and reciprocal the
+    SiLU uses (one unit in the last place each).  The oracle accepts a
+    caller-supplied value only where that bound makes more than one value
+    correct, and only inside that range.
+R11 a / s is formed on the device as a times the correctly rounded fp32
+    reciprocal of s; those two roundings (2**-24 relative each) are part of
+    the R10 bound.  The oracle's own code is the E4M3 rounding of the exact
+    a / s.
 R9  The combine is the weighted sum over j of w[t, j] * expert_output.  The
     reference result is the unrounded fp64 sum; the device sums in fp32 in
     ascending j and rounds the result to BF16.
@@ -166,58 +176,211 @@ def swiglu(g: np.ndarray, u: np.ndarray) -> np.ndarray:
     return silu(g) * u
 
 
-# Half-width of the window around a / s (whose largest magnitude is 448)
-# within which the device's own pre-quantisation value may lie (reading
-# R10): 448 * 2**-13, about five times the largest device-versus-fp64
-# difference of a / s observed with fp32 accumulation.
-TIE_EPS = F.E4M3_MAX * 2.0 ** -13
+# --------------------------------------------- device deviation bounds (R10)
+# One unit in the last place of an fp32 result, relative: the bound taken for
+# every floating-point operation of the device (matrix-core additions, vector
+# additions and multiplies, the exponential and the reciprocal).  Correctly
+# rounded operations err by half of it.
+U1 = 2.0 ** -23
 
 
-def tie_window(v: np.ndarray):
-    """For each value of a / s, the smallest and largest E4M3 value that the
-    round-to-nearest-even encoding of any value within TIE_EPS of it can
-    give.  Where they differ, every E4M3 value between them (inclusive) is a
-    correct re-quantisation result (reading R10)."""
-    lo = F.E4M3_TABLE[F.e4m3_encode(v - TIE_EPS)]
-    hi = F.E4M3_TABLE[F.e4m3_encode(v + TIE_EPS)]
-    return lo != hi, lo, hi
+def gamma(n) -> float:
+    """gamma_n = n*u / (1 - n*u): the relative bound of n chained roundings
+    of at most u each (the classic bound for recursive summation)."""
+    return n * U1 / (1.0 - n * U1)
 
 
-def requant_fp8(a: np.ndarray, resolve=None):
+def _lowest_bit_exponent(v: np.ndarray) -> int:
+    """Exponent of the lowest set bit over the nonzero values of v (all
+    finite): every value of v is an integer multiple of 2**result."""
+    v = np.asarray(v, dtype=np.float64).ravel()
+    v = v[v != 0]
+    if v.size == 0:
+        return 1 << 20
+    m, e = np.frexp(v)                                    # v = m * 2**e, 0.5 <= |m| < 1
+    M = np.abs(np.ldexp(m, 53)).astype(np.int64)          # integer significand
+    tz = np.zeros(M.shape, dtype=np.int64)
+    rest = M.copy()
+    while True:
+        even = (rest & 1) == 0
+        if not even.any():
+            break
+        tz += even
+        rest = np.where(even, rest >> 1, rest)
+    return int((e - 53 + tz).min())
+
+
+def fp32_sums_exact(xrows: np.ndarray, w: np.ndarray, scales_pow2: bool) -> np.ndarray:
+    """Whether every partial sum of the dot products xrows @ w.T is exactly
+    representable in fp32, whatever the order and grouping of the additions:
+    all products are integer multiples of 2**(qx + qw) (the lowest set bits of
+    the two operands), and with power-of-two block scales every partial sum is
+    a multiple of that bounded by sum|x*w| < 2**24 * 2**(qx + qw).  Returns a
+    boolean [m, N] (all False unless scales_pow2)."""
+    if not scales_pow2:
+        return np.zeros((xrows.shape[0], w.shape[0]), dtype=bool)
+    q = _lowest_bit_exponent(xrows) + _lowest_bit_exponent(w)
+    S = np.abs(xrows) @ np.abs(w).T
+    return S < np.ldexp(1.0, 24 + q)
+
+
+def additions_per_product(spec: Spec, K: int) -> int:
+    """How many roundings one product of a length-K dot product of the expert
+    GEMMs can pass through on the device.  FP8 activations: up to 128 additions
+    inside one block-scaled MFMA (one 128-wide K block), the fp32 product of
+    the two block scales and the promotion FMA, then one addition per K block.
+    BF16: up to 32 additions inside one MFMA and one per chained MFMA."""
+    if spec.act == "bf16":
+        return 32 + K // 32 + 1
+    return 128 + 2 + K // 128
+
+
+def accumulation_bound(spec: Spec, xrows: np.ndarray, w: np.ndarray, scales_pow2: bool) -> np.ndarray:
+    """Absolute bound on |device - exact| of each element of xrows @ w.T
+    (reading R10): gamma_n * sum_k |x_k * w_k|, and 0 where every partial sum
+    is exact in fp32."""
+    S = np.abs(xrows) @ np.abs(w).T
+    e = gamma(additions_per_product(spec, xrows.shape[1])) * S
+    return np.where(fp32_sums_exact(xrows, w, scales_pow2), 0.0, e)
+
+
+# |SiLU'(z)| = |sigma(z) (1 + z (1 - sigma(z)))| is at most 1.0999 (at z ~ 2.4).
+SILU_LIPSCHITZ = 1.1
+
+
+def swiglu_bound(g, u, eg, eu):
+    """Absolute bound on |device - exact| of a = SiLU(g) * u when the device's
+    g and u are within eg and eu of the exact ones (reading R10).
+
+    The device forms exp(-g) as 2**(-g * log2 e) (one rounded multiply by the
+    rounded constant: relative argument error <= 2 * 2**-24 = U1, hence a
+    relative error |g| * U1 of the exponential; the exponential instruction
+    itself <= U1), adds 1 (<= U1/2), takes the reciprocal (<= U1) and
+    multiplies by g and by u (<= U1/2 each): relative error <= (|g| + 4) U1 of
+    its own result.  Below g = -80 the exponential overflows and the device's
+    a is 0, which is within |a| of the exact value."""
+    g, u, eg, eu = (np.asarray(v, dtype=np.float64) for v in (g, u, eg, eu))
+    sg = silu(g)
+    dsilu = SILU_LIPSCHITZ * eg
+    prop = dsilu * (np.abs(u) + eu) + np.abs(sg) * eu        # from the inputs' error
+    mag = (np.abs(sg) + dsilu) * (np.abs(u) + eu)             # bound on |device a|
+    rnd = mag * (np.abs(g) + eg + 4.0) * U1 * (1 + 1e-6)      # the device's own evaluation
+    ea = prop + rnd
+    return np.where(g - eg < -80.0, np.maximum(ea, 2.0 * mag + 1e-300), ea)
+
+
+def intermediate_bound(spec: Spec, xrows: np.ndarray, w_gu: np.ndarray, scales_pow2: bool):
+    """(a, ea): the exact SwiGLU intermediate of one expert's rows and the
+    bound on the device's deviation from it (R10)."""
+    G = xrows @ w_gu.T
+    eG = accumulation_bound(spec, xrows, w_gu, scales_pow2)
+    g, u = G[:, : spec.I], G[:, spec.I:]
+    return swiglu(g, u), swiglu_bound(g, u, eG[:, : spec.I], eG[:, spec.I:])
+
+
+def requant_window(a: np.ndarray, ea: np.ndarray, s: np.ndarray):
+    """For the block scales s [m, C/128], the exact a / s [m, C/128, 128] and
+    the smallest and largest E4M3 values that the device may produce there:
+    the device's pre-rounding value lies within ea / s of a / s, plus the two
+    roundings of the reciprocal multiply (R11)."""
+    m, C = a.shape
+    A = a.reshape(m, C // 128, 128)
+    EA = np.broadcast_to(np.asarray(ea, dtype=np.float64), a.shape).reshape(m, C // 128, 128)
+    sc = s[:, :, None]
+    v = A / sc
+    ev = EA / sc + 1.01 * U1 * (np.abs(A) + EA) / sc
+    lo = F.E4M3_TABLE[F.e4m3_encode(v - ev)]
+    hi = F.E4M3_TABLE[F.e4m3_encode(v + ev)]
+    return v, lo, hi
+
+
+def scale_window(a: np.ndarray, ea: np.ndarray):
+    """Smallest and largest fp32 block scale fl32(amax / 448) the device may
+    compute from its own block maximum (within ea of the exact one), per row
+    and 128-channel block; a zero maximum gives 1."""
+    m, C = a.shape
+    A = np.abs(a).reshape(m, C // 128, 128)
+    EA = np.broadcast_to(np.asarray(ea, dtype=np.float64), a.shape).reshape(m, C // 128, 128)
+    amax_lo = np.maximum(A - EA, 0.0).max(axis=2)
+    amax_hi = (A + EA).max(axis=2)
+    s_lo = F.f32_round(amax_lo / F.E4M3_MAX)
+    s_hi = F.f32_round(amax_hi / F.E4M3_MAX)
+    return s_lo, s_hi, amax_lo == 0.0, amax_hi == 0.0
+
+
+def requant_fp8(a: np.ndarray, a_err=None, resolve=None, resolve_scales=None):
     """Per-row, per-128-channel FP8 re-quantisation of the intermediate
     (Tile Kernels section, quantisation bullet, fused with SwiGLU; reading R6).
 
-    resolve: optional uint8 [m, C] codes chosen by another implementation;
-    they replace the oracle's code only where the tie window of a / s holds
-    more than one value (reading R10), and must there lie in the window.
+    Without a_err: s = fl32(amax / 448) (1 for a zero block), codes =
+    E4M3_RNE_sat(a / s).  With a_err (the R10 bound of another
+    implementation's a) and its scales and codes:
+    * resolve_scales [m, C/128] must lie within the scale window of each block
+      (scale_window) and are then used as that block's s;
+    * resolve [m, C] codes replace the oracle's where the value window of a / s
+      holds more than one E4M3 value, and must lie in it; elsewhere they must
+      equal the oracle's code (compared by value, so +0 and -0 agree).
+    ValueError otherwise.
 
-    Returns (codes uint8 [m, C], scales fp32-valued float64 [m, C/128],
+    Returns (codes uint8 [m, C], scales float64 [m, C/128] (fp32 values),
     dequantised float64 [m, C])."""
     m, C = a.shape
     blocks = a.reshape(m, C // 128, 128)
     amax = np.abs(blocks).max(axis=2)
     s = F.f32_round(amax / F.E4M3_MAX)
     s = np.where(amax == 0.0, 1.0, s)
+    if a_err is not None and resolve_scales is not None:
+        rs = np.asarray(resolve_scales, dtype=np.float64).reshape(m, C // 128)
+        s_lo, s_hi, may_zero, must_zero = scale_window(a, a_err)
+        ok = ((rs >= s_lo) & (rs <= s_hi) & ~must_zero) | ((rs == 1.0) & may_zero)
+        if not np.all(ok):
+            r, b = np.argwhere(~ok)[0]
+            raise ValueError(f"a supplied scale {rs[r, b]!r} (row {r}, block {b}) lies outside "
+                             f"[{s_lo[r, b]!r}, {s_hi[r, b]!r}]")
+        s = rs
     v = blocks / s[:, :, None]
     codes = F.e4m3_encode(v)
-    if resolve is not None:
-        amb, lo, hi = tie_window(v)
+    if a_err is not None and resolve is not None:
+        _, lo, hi = requant_window(a, a_err, s)
+        amb = lo != hi
         r = np.asarray(resolve, dtype=np.uint8).reshape(m, C // 128, 128)
-        rv = F.E4M3_TABLE[r]
-        valid = (rv >= lo) & (rv <= hi)
-        if not np.all(valid[amb]):
-            raise ValueError("a supplied code at a re-quantisation near-tie lies outside its tie window")
+        rv, cv = F.E4M3_TABLE[r], F.E4M3_TABLE[codes]
+        inside = (rv >= lo) & (rv <= hi)
+        if not np.all(inside[amb]):
+            raise ValueError("a supplied code at a re-quantisation near-tie lies outside its window")
+        if not np.all(rv[~amb] == cv[~amb]):
+            bad = np.argwhere(~amb & (rv != cv))[0]
+            raise ValueError(f"a supplied code differs from the oracle's away from a near-tie at "
+                             f"(row, block, channel) {tuple(int(i) for i in bad)}")
         codes = np.where(amb, r, codes)
     deq = F.E4M3_TABLE[codes] * s[:, :, None]
     return codes.reshape(m, C), s, deq.reshape(m, C)
 
 
-def quantise_intermediate(spec: Spec, a: np.ndarray, resolve=None) -> np.ndarray:
-    """The value GEMM2 consumes: FP8 re-quantised (R6, R10), or BF16-rounded
-    for all-BF16 layers."""
+def bf16_window(a: np.ndarray, ea: np.ndarray):
+    """Smallest and largest BF16 value the device's rounding of an a within ea
+    of the exact one can give (R10)."""
+    return F.bf16_round(a - ea), F.bf16_round(a + ea)
+
+
+def quantise_intermediate(spec: Spec, a: np.ndarray, a_err=None, resolve=None, resolve_scales=None) -> np.ndarray:
+    """The value GEMM2 consumes: FP8 re-quantised (R6, R10, R11), or
+    BF16-rounded for all-BF16 layers.  With a_err and resolve (the device's
+    BF16 values), those replace the oracle's where the BF16 window holds two
+    values and must equal them elsewhere."""
     if spec.act == "bf16":
-        return F.bf16_round(a)
-    return requant_fp8(a, resolve)[2]
+        r = F.bf16_round(a)
+        if a_err is not None and resolve is not None:
+            lo, hi = bf16_window(a, a_err)
+            amb = lo != hi
+            rv = F.bf16_decode(resolve)
+            if not np.all(((rv >= lo) & (rv <= hi))[amb]):
+                raise ValueError("a supplied BF16 intermediate at a rounding near-tie lies outside its window")
+            if not np.all(rv[~amb] == r[~amb]):
+                raise ValueError("a supplied BF16 intermediate differs from the oracle's away from a near-tie")
+            r = np.where(amb, rv, r)
+        return r
+    return requant_fp8(a, a_err, resolve, resolve_scales)[2]
 
 
 def expert_intermediate(spec: Spec, xrows: np.ndarray, w_gu: np.ndarray) -> np.ndarray:
@@ -226,14 +389,45 @@ def expert_intermediate(spec: Spec, xrows: np.ndarray, w_gu: np.ndarray) -> np.n
     return swiglu(G[:, : spec.I], G[:, spec.I:])
 
 
-def expert_ffn(spec: Spec, xrows: np.ndarray, w_gu: np.ndarray, w_d: np.ndarray, resolve=None) -> np.ndarray:
+def expert_ffn(spec: Spec, xrows: np.ndarray, w_gu: np.ndarray, w_d: np.ndarray) -> np.ndarray:
     """One expert on its gathered rows: linear 1 (gate|up), SwiGLU, requant,
     linear 2 (Mega MoE section: 线性变换 -> SwiGLU -> 线性变换).
 
     xrows [m, H] fp64; w_gu [2I, H] and w_d [H, I] dequantised fp64."""
     a = expert_intermediate(spec, xrows, w_gu)
-    ahat = quantise_intermediate(spec, a, resolve)
+    ahat = quantise_intermediate(spec, a)
     return ahat @ w_d.T                       # [m, H]
+
+
+def powers_of_two(v) -> bool:
+    """True when every value of v is a positive power of two."""
+    v = np.asarray(v, dtype=np.float64)
+    m, _ = np.frexp(v)
+    return bool(np.all(m == 0.5))
+
+
+# ------------------------------------------------------------------- routing
+def router_additions(H: int) -> int:
+    """Roundings a product of the router's dot product can pass through on the
+    device: up to 132 inside the four chained BF16 MFMAs of one 128-channel
+    block, the multiply by the activation scale and one addition per block,
+    up to 8 additions of channel-slice partial sums, and the bias."""
+    return 132 + 2 + H // 128 + 8 + 1
+
+
+def logit_bound(spec: Spec, xhat: np.ndarray, router_w, router_bias=None, x_scales=None) -> np.ndarray:
+    """Absolute bound [T, E] on |device logit - exact logit| (R10):
+    gamma_n * (sum_h |x_h Wr_h| + |b|), and 0 where every partial sum is exact
+    in fp32 (power-of-two activation scales, grid-aligned operands and bias)."""
+    wr = F.bf16_decode(router_w)
+    b = np.zeros(wr.shape[0]) if router_bias is None else np.asarray(router_bias, dtype=np.float32).astype(np.float64)
+    S = np.abs(xhat) @ np.abs(wr).T + np.abs(b)[None, :]
+    e = gamma(router_additions(xhat.shape[1])) * S
+    pow2 = spec.act == "bf16" or x_scales is None or powers_of_two(x_scales)
+    if pow2:
+        q = min(_lowest_bit_exponent(xhat) + _lowest_bit_exponent(wr), _lowest_bit_exponent(b))
+        e = np.where(S < np.ldexp(1.0, 24 + q), 0.0, e)
+    return e
 
 
 # ----------------------------------------------------------------- the layer
@@ -246,7 +440,7 @@ def route(spec: Spec, inputs: dict):
     return xhat, logits, ids, w
 
 
-def layer(spec: Spec, inputs: dict, ids=None, tokens=None, inter_codes=None) -> dict:
+def layer(spec: Spec, inputs: dict, ids=None, tokens=None, inter=None, inter_scales=None) -> dict:
     """The whole layer in fp64.
 
     inputs: dict with x, x_scales, router_w, router_bias, w_gate_up,
@@ -260,6 +454,12 @@ def layer(spec: Spec, inputs: dict, ids=None, tokens=None, inter_codes=None) -> 
     y is computed only for those tokens (routing and permutation are always
     computed for all tokens).
 
+    inter, inter_scales: another implementation's intermediate in permuted
+    row order (E4M3 codes [T*k, I] with fp32 scales [T*k, I/128], or BF16 bit
+    patterns [T*k, I]).  Where the R10 bound of that implementation makes more
+    than one value correct, its value is used (it must lie in the window);
+    elsewhere it must equal the oracle's (ValueError otherwise).
+
     Returns dict(y, logits, ids, weights, counts, offsets, perm, row_of),
     y being the unrounded fp64 output rows (of `tokens` when given)."""
     xhat, logits, sel, _ = route(spec, inputs)
@@ -268,6 +468,7 @@ def layer(spec: Spec, inputs: dict, ids=None, tokens=None, inter_codes=None) -> 
     ids = np.asarray(ids, dtype=np.int64)
     w = topk_weights(logits, ids)
     counts, offsets, perm, row_of = permutation(ids, spec.E)
+    x_scales = inputs.get("x_scales")
 
     T, k = spec.T, spec.k
     tok_list = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
@@ -282,14 +483,22 @@ def layer(spec: Spec, inputs: dict, ids=None, tokens=None, inter_codes=None) -> 
         if not np.any(keep):
             continue
         rows, toks = rows[keep], toks[keep]
-        resolve = None
-        if inter_codes is not None:
-            resolve = np.asarray(inter_codes[np.arange(offsets[e], offsets[e + 1])[keep]])
         wgu_s = None if inputs.get("w_gate_up_scales") is None else np.asarray(inputs["w_gate_up_scales"][e])
         wd_s = None if inputs.get("w_down_scales") is None else np.asarray(inputs["w_down_scales"][e])
         w_gu = decode_weight(spec, np.asarray(inputs["w_gate_up"][e]), wgu_s)
         w_d = decode_weight(spec, np.asarray(inputs["w_down"][e]), wd_s)
-        O = expert_ffn(spec, xhat[toks], w_gu, w_d, resolve)
+        xr = xhat[toks]
+        if inter is None:
+            a = expert_intermediate(spec, xr, w_gu)
+            ahat = quantise_intermediate(spec, a)
+        else:
+            prow = np.arange(offsets[e], offsets[e + 1])[keep]
+            pow2 = (spec.act == "bf16" or powers_of_two(np.asarray(x_scales)[toks])) and \
+                   (spec.weight != "fp8" or powers_of_two(wgu_s))
+            a, ea = intermediate_bound(spec, xr, w_gu, pow2)
+            sc = None if inter_scales is None else np.asarray(inter_scales[prow])
+            ahat = quantise_intermediate(spec, a, ea, np.asarray(inter[prow]), sc)
+        O = ahat @ w_d.T
         wt = w.reshape(-1)[rows]
         # Tokens are distinct within one expert, so these row updates never
         # collide; the sum over j is formed across the expert loop.

@@ -314,36 +314,3 @@ def test_given_ids_are_used():
     r = O.layer(spec, inp, ids=ids)
     assert np.array_equal(r["ids"], ids)
     assert r["counts"].tolist() == [10, 0, 0, 10]
-
-
-def test_requant_near_tie_resolution():
-    # a / s placed just off three rounding midpoints (336 between 320 and
-    # 352, -2.375 between -2.25 and -2.5, 15.5 between 15 and 16), plus a
-    # value far from any midpoint.  Row max 448 makes s = 1 exactly.
-    a = np.zeros((1, 128))
-    a[0, :5] = [448.0, 336.0 + 1e-3, -2.375 - 1e-5, 15.5 + 2e-4, 101.5]
-    codes, s, deq = O.requant_fp8(a)
-    assert s[0, 0] == 1.0
-    assert deq[0, 1:5].tolist() == [352.0, -2.5, 16.0, 104.0]
-    amb, lo, hi = O.tie_window(a[:, :5])
-    assert amb[0].tolist() == [False, True, True, True, False]
-    assert (lo[0, 1], hi[0, 1]) == (320.0, 352.0)
-    # the other neighbour is accepted inside the window, ignored elsewhere
-    other = codes.copy()
-    other[0, 1] = F.e4m3_encode(np.array([320.0]))[0]
-    other[0, 2] = F.e4m3_encode(np.array([-2.25]))[0]
-    other[0, 4] = F.e4m3_encode(np.array([96.0]))[0]        # not a near-tie: ignored
-    c2, _, d2 = O.requant_fp8(a, resolve=other)
-    assert d2[0, 1:5].tolist() == [320.0, -2.25, 16.0, 104.0]
-    # a code outside the window is rejected
-    bad = codes.copy()
-    bad[0, 3] = F.e4m3_encode(np.array([18.0]))[0]
-    with pytest.raises(ValueError):
-        O.requant_fp8(a, resolve=bad)
-    # exactly at the midpoint: round-half-even picks 320 (even mantissa)
-    a2 = np.zeros((1, 128))
-    a2[0, :2] = [448.0, 336.0]
-    assert O.requant_fp8(a2)[2][0, 1] == 320.0
-    # tiny values: the window spans several codes (and zero)
-    amb3, lo3, hi3 = O.tie_window(np.array([0.002]))
-    assert amb3[0] and lo3[0] < 0 < hi3[0]
