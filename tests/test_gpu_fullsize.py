@@ -2,14 +2,19 @@
 configuration bench.py times (persistent kernel, one workgroup per CU):
 
 - routing (ids, order, weights) against the fp64 oracle for every token,
-  bit-exact except at near-ties of the fp64 logits;
+  bit-exact except at near-ties within the derived logit bound;
 - expert offsets and the permutation bit-exact against the oracle's
   permutation of the device's ids;
-- the output rows of a sample of tokens against the oracle computed for
-  those tokens only (the oracle is fed the device's ids and, for FP8
-  layers, the device's intermediate codes, which must lie inside the
-  re-quantisation tie windows);
-- the separate-kernel pipeline bitwise equal to the persistent kernel.
+- the output rows of a sample of tokens, element by element, against the
+  oracle computed for those tokens only (fed the device's ids and its
+  intermediate codes and scales, which must lie in the derived windows).
+  The sample covers every active expert (its first and last permuted row),
+  every 16-row subtile position of the 128-row GEMM tiles, and the last row
+  of every expert's last tile; the decode workload samples every token;
+- the separate-kernel pipeline bitwise equal to the persistent kernel, the
+  persistent kernel run on a workspace filled with NaN bytes first, so that
+  a read of any intermediate or staging row before its writer has finished
+  would show.
 """
 
 import numpy as np
@@ -24,6 +29,8 @@ from tests._helpers import check_output, check_routing
 pytestmark = pytest.mark.gpu
 
 FULL = ["dsv3_fp8", "dsv3_fp8xfp4", "decode_fp8_zipf", "mega_e1024_fp4_zipf"]
+TILE_ROWS = 128          # rows of a full GEMM row tile for FP8 activations
+SUBTILE = 16
 
 
 @pytest.fixture(scope="module")
@@ -32,30 +39,71 @@ def L(gpu_lib):
     return layer
 
 
+def coverage_tokens(offsets: np.ndarray, perm: np.ndarray, k: int, T: int, min_tokens: int, seed: int = 0):
+    """Tokens whose permuted rows cover, for every active expert, its first
+    row and its last row (the last row of its last tile) and, in each of its
+    tiles, one row at subtile position (e + 3 i) % 8 and lane (e % 16); the
+    eight subtile positions are then each covered by many experts.  Topped up
+    with random tokens to min_tokens."""
+    rows = []
+    E = offsets.size - 1
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        rows += [lo, hi - 1]
+        for i in range((hi - lo + TILE_ROWS - 1) // TILE_ROWS):
+            r = lo + i * TILE_ROWS + SUBTILE * ((e + 3 * i) % (TILE_ROWS // SUBTILE)) + e % SUBTILE
+            if r < hi:
+                rows.append(r)
+    toks = set((perm[np.array(rows)] // k).tolist()) | {0, T - 1}
+    rng = np.random.default_rng(seed)
+    while len(toks) < min(min_tokens, T):
+        toks.add(int(rng.integers(T)))
+    return np.array(sorted(toks)), np.array(rows)
+
+
 @pytest.mark.parametrize("name", FULL)
 def test_full_size_workload(L, name):
     cfg = gen.CONFIGS[name]
+    print(f"[fullsize] {name}: generating inputs", flush=True)
     raw = gen.make_inputs(cfg, seed=0, device="cuda")
     inp = L.pack_weights(raw)
-    out = L.forward(inp, cfg.k, mode="mega")
-    sep = L.forward(inp, cfg.k, mode="separate")
+    ws = L.Workspace("cuda")
+    desc = L.desc_from_inputs(inp, cfg.k, "mega")
+    ws.get(L.lib.moe_workspace_size(desc)).fill_(0xFF)       # NaN in every fp32 / BF16 / E4M3 slot
+    torch.cuda.synchronize()
+    print(f"[fullsize] {name}: persistent kernel on a NaN-filled workspace, then separate kernels", flush=True)
+    out = L.forward(inp, cfg.k, mode="mega", workspace=ws)
     torch.cuda.synchronize()
     assert int(out["workspace"][:4].view(torch.int32).item()) == 0, "device watchdog fired"
-    for key in ("y", "topk_ids", "topk_weights", "perm", "expert_offsets"):
-        assert torch.equal(out[key], sep[key]), f"{name}: separate kernels differ from the persistent kernel in {key}"
+    inter, isc = L.intermediate(out)
+    inter, isc = inter.cpu().numpy(), isc.cpu().numpy()
+    mega = {key: out[key].clone() for key in ("y", "topk_ids", "topk_weights", "perm", "expert_offsets")}
+    sep = L.forward(inp, cfg.k, mode="separate")
+    torch.cuda.synchronize()
+    for key in mega:
+        assert torch.equal(mega[key], sep[key]), f"{name}: separate kernels differ from the persistent kernel in {key}"
+    assert torch.isfinite(mega["y"].float()).all()
 
+    print(f"[fullsize] {name}: oracle routing", flush=True)
     spec = gen.spec_of(cfg)
     ov = gen.oracle_view(raw, lazy_weights=True)
     xh, logits, ids_ref, _ = O.route(spec, ov)
-    ids = out["topk_ids"].cpu().numpy().astype(np.int64)
-    check_routing(ids, out["topk_weights"].cpu().numpy(), logits, ids_ref, cfg.k, 1e-5)
+    lerr = O.logit_bound(spec, xh, ov["router_w"], ov["router_bias"], ov["x_scales"])
+    ids = mega["topk_ids"].cpu().numpy().astype(np.int64)
+    n_tie = check_routing(ids, mega["topk_weights"].cpu().numpy(), logits, ids_ref, cfg.k, lerr)
     counts, offsets, perm, _ = O.permutation(ids, cfg.E)
-    assert np.array_equal(out["expert_offsets"].cpu().numpy(), offsets)
-    assert np.array_equal(out["perm"].cpu().numpy(), perm)
+    assert np.array_equal(mega["expert_offsets"].cpu().numpy(), offsets)
+    assert np.array_equal(mega["perm"].cpu().numpy(), perm)
 
-    rng = np.random.default_rng(1234)
-    sample = np.unique(np.concatenate([[0, cfg.T - 1], rng.choice(cfg.T, size=2, replace=False)]))
-    codes = L.intermediate(out)[0].cpu().numpy() if cfg.act == "fp8" else None
-    ref = O.layer(spec, ov, ids=ids, tokens=sample, inter_codes=codes)
-    y = out["y"][torch.as_tensor(sample, device="cuda")].float().cpu().numpy()
-    check_output(y, ref["y"], name)
+    sample, rows = coverage_tokens(offsets, perm, cfg.k, cfg.T, min_tokens=256)
+    if cfg.T <= 256:
+        sample = np.arange(cfg.T)
+    pos = (rows - np.repeat(offsets[:-1], np.diff(offsets))[rows]) % TILE_ROWS // SUBTILE
+    assert set(pos.tolist()) == set(range(TILE_ROWS // SUBTILE)) or counts.max() <= TILE_ROWS // 2
+    print(f"[fullsize] {name}: oracle output of {sample.size} tokens ({n_tie} near-tie routings)", flush=True)
+    ref = O.layer(spec, ov, ids=ids, tokens=sample, inter=inter, inter_scales=isc)
+    y = mega["y"][torch.as_tensor(sample, device="cuda")].float().cpu().numpy()
+    err = check_output(y, ref["y"], name)
+    print(f"[fullsize] {name}: max element error {err[0]:.2e}, max token L2 {err[1]:.2e}", flush=True)

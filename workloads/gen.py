@@ -222,6 +222,58 @@ def make_exact_router_inputs(T: int, H: int, E: int, seed: int = 0, dup_pairs=()
     return {k: (None if v is None else v.to(device)) for k, v in out.items()}
 
 
+def make_exact_layer_inputs(cfg: LayerConfig, seed: int = 0, device="cpu") -> dict:
+    """Layer inputs on which the gate|up GEMM is exact in fp32 whatever the
+    order and grouping of its additions: every product lies on a common grid
+    and the sums stay below 2**24 grid units, with power-of-two scales.
+
+    x: FP8 codes of multiples of 0.5 in [-4, 4], scales drawn from
+    {1/4, 1/2, 1} (BF16 layers: the same values in BF16).  Router: as
+    make_exact_router_inputs.  Weights: FP8 codes of n * 2**-6 (|n| <= 15)
+    with block scales from {1/8 .. 1}; FP4 random E2M1 codes with E8M0 scales
+    2**-6 .. 2**-3; BF16 n * 2**-6.  For H <= 2048 every product is a
+    multiple of 2**-12 (FP4: 2**-10) of magnitude below 4, so partial sums stay
+    below 2**23 grid units.  The down GEMM is not exact (its intermediate
+    scales are amax / 448)."""
+    T, H, E, I = cfg.T, cfg.H, cfg.E, cfg.I
+    assert H <= 2048
+    r = make_exact_router_inputs(T, H, E, seed=seed)
+    gx = _gen("cpu", _seed(seed, cfg.name, "exact_x"))
+    if cfg.act == "bf16":
+        xv = torch.randint(-8, 9, (T, H), generator=gx).to(torch.float32) * 0.5
+        x, sx = xv.to(torch.bfloat16), None
+    else:
+        x = r["x"]
+        sx = 2.0 ** (-torch.randint(0, 3, (T, H // 128), generator=gx).to(torch.float32))
+
+    def weights(N, K, tensor, e):
+        g = _gen("cpu", _seed(seed, cfg.name, tensor, e))
+        if cfg.weight == "fp4":
+            codes = torch.randint(0, 16, (N, K), generator=g, dtype=torch.int32).to(torch.uint8)
+            packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).contiguous()
+            sc = (121 + torch.randint(0, 4, (N, K // 32), generator=g, dtype=torch.int32)).to(torch.uint8)
+            return packed, sc
+        v = torch.randint(-15, 16, (N, K), generator=g).to(torch.float32) * 2.0 ** -6
+        if cfg.weight == "bf16":
+            return v.to(torch.bfloat16), None
+        sc = 2.0 ** (-torch.randint(0, 4, (N // 128, K // 128), generator=g).to(torch.float32))
+        return _fp8_bytes(v), sc.contiguous()
+
+    gu, gus, d, ds = [], [], [], []
+    for e in range(E):
+        q, s = weights(2 * I, H, "w_gate_up", e)
+        gu.append(q)
+        gus.append(s)
+        q, s = weights(H, I, "w_down", e)
+        d.append(q)
+        ds.append(s)
+    out = dict(x=x.contiguous(), x_scales=sx, router_w=r["router_w"], router_bias=None,
+               w_gate_up=torch.stack(gu), w_down=torch.stack(d),
+               w_gate_up_scales=None if gus[0] is None else torch.stack(gus),
+               w_down_scales=None if ds[0] is None else torch.stack(ds))
+    return {k: (None if v is None else v.to(device)) for k, v in out.items()}
+
+
 # ------------------------------------------------------- host-side views
 def _np(t: torch.Tensor) -> np.ndarray:
     t = t.detach().cpu()
