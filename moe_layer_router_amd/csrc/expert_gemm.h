@@ -246,10 +246,15 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
     const uint32_t rbase = (STAGE == 1) ? (uint32_t)ROWI[rowc] * g.H : (uint32_t)(r0 + rowc) * g.I;
     aoff[j] = rbase * ESZ + c * 16;
   }
-  // stage `slot` (= s % kAStages) receives A(s)
+  // stage `slot` (= s % kAStages) receives A(s).  Steps past the last
+  // (issued so that the step stays branch-free) load the last step again:
+  // an unclamped offset would reach into the next permuted row, which in
+  // the persistent kernel may belong to a tile whose gate|up item has not
+  // yet written it, and an ordinary load would leave that stale line in
+  // this XCD's L2 for a later reader.
   auto dma_a = [&](int s, int slot, int j) __attribute__((always_inline)) {
     char* dst = lds + L::kA + slot * L::kASlot + w * 1024;
-    buf_ld16_lds<0>(ars, dst + j * 4096, aoff[j], (uint32_t)s * 128 * ESZ);
+    buf_ld16_lds<0>(ars, dst + j * 4096, aoff[j], (uint32_t)min(s, nsteps - 1) * 128 * ESZ);
   };
 
   // ---- per-row scales (FP8 activations).  The activation scales of step s
