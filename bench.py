@@ -100,6 +100,48 @@ def roofline(cfg, f_exp, f_router, nbytes, t_s):
             "frac": round(ach / peak, 4)}, t_mfma, t_hbm
 
 
+def measure_peaks(dev, cus: int):
+    """Measured matrix-core rates (per operand format) and HBM read bandwidth
+    on this device, with the library's microbenchmarks (moe_peaks.h): one
+    workgroup per SIMD quad on every CU, 8 independent MFMA chains per wave;
+    a 4 GiB read with 16-byte loads."""
+    import torch
+    from moe_layer_router_amd import lib
+    out = {}
+    blocks = cus * 2
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    cyc = torch.empty(blocks * 4, dtype=torch.int64, device=dev)
+    for kind in lib.MOE_PEAK_KINDS:
+        iters = 2000 if "32" not in kind else 1000
+        lib.moe_peak_mfma(kind, 50, blocks, sink, cyc)              # warm-up
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        lib.moe_peak_mfma(kind, iters, blocks, sink, cyc)
+        b.record()
+        torch.cuda.synchronize()
+        t = a.elapsed_time(b) / 1e3
+        per_instr = float(np.median(cyc.cpu().numpy())) / (iters * 8)
+        out[kind] = {"tflops": round(lib.moe_peak_mfma_flops(kind, iters, blocks) / t / 1e12, 1),
+                     "cycles_per_instr_per_wave": round(per_instr, 2)}
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(3)
+    rsink = torch.empty(cus * 8 * 256, dtype=torch.int32, device=dev)
+    lib.moe_peak_hbm_read(buf, nbytes, cus * 8, rsink)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(5):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        lib.moe_peak_hbm_read(buf, nbytes, cus * 8, rsink)
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b) / 1e3)
+    out["hbm_read_gbs"] = round(nbytes / min(ts) / 1e9, 1)
+    del buf
+    return out
+
+
 def cpu_baseline(cfg, inputs, n_experts=4):
     """The oracle as it stands, on a bounded sample of the same workload:
     routing and the permutation for all T tokens, then the complete expert
@@ -152,6 +194,8 @@ def main():
     ap.add_argument("--no-ablation", action="store_true", help="skip timing the other mode")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one device copy of 1 GiB (a counter calibration point for profiling runs)")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the peak-rate microbenchmarks")
+    ap.add_argument("--no-evict", action="store_true", help="skip the cache-evicted per-call timing")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): the layer is measured on a "
@@ -210,6 +254,25 @@ def main():
 
     out, ms, per = timed(args.mode)
     counts = np.diff(out["expert_offsets"].cpu().numpy())
+    evicted = None
+    if not args.no_evict:
+        # per-call times with the 256 MB last-level cache overwritten before
+        # each call (a 1 GiB write between calls, outside the timed calls)
+        junk = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        ev = []
+        for _ in range(max(5, min(args.steps, 20))):
+            junk.fill_(7)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            layer.forward(inputs, cfg.k, mode=args.mode, workspace=ws, out=out)
+            b.record(stream)
+            torch.cuda.synchronize()
+            ev.append(a.elapsed_time(b))
+        del junk
+        ev = np.array(ev)
+        evicted = {"median_ms": round(float(np.median(ev)), 4), "min_ms": round(float(ev.min()), 4),
+                   "mean_ms": round(float(ev.mean()), 4), "calls": int(ev.size)}
+        print(f"[bench] {args.mode}: cache-evicted per-call median {np.median(ev):.4f} ms", file=sys.stderr, flush=True)
     other = "separate" if args.mode == "mega" else "mega"
     ablation = None
     if not args.no_ablation:
@@ -250,7 +313,21 @@ def main():
                            "kernel_ms": round(t_launch * 1e3, 4),
                            "roofline_frac": round(max(t_mfma, t_hbm) / t_launch, 4)},
         "ablation": ablation,
+        "per_call_ms": {"median": round(float(np.median(per)), 4), "min": round(float(per.min()), 4),
+                        "mean": round(float(per.mean()), 4)},
+        "per_call_cache_evicted_ms": evicted,
     }
+    if not args.no_peaks:
+        print("[bench] peak-rate microbenchmarks", file=sys.stderr, flush=True)
+        cus = torch.cuda.get_device_properties(dev).multi_processor_count
+        pk = measure_peaks(dev, cus)
+        result["measured_peaks"] = pk
+        kind = {"fp8": "mfma16_fp8_fp8", "fp4": "mfma16_fp4_fp8", "bf16": "mfma16_bf16"}[cfg.weight]
+        result["roofline_model"]["measured_peak_tflops"] = pk[kind]["tflops"]
+        result["roofline_model"]["measured_hbm_gbs"] = pk["hbm_read_gbs"]
+        t_m = f_exp / (pk[kind]["tflops"] * 1e12) + f_router / (pk["mfma16_bf16"]["tflops"] * 1e12)
+        t_h = nbytes / (pk["hbm_read_gbs"] * 1e9)
+        result["roofline_model"]["roofline_frac_measured_peaks"] = round(max(t_m, t_h) / t_launch, 4)
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on a bounded sample (host cores)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(cfg, raw, args.cpu_experts)

@@ -94,7 +94,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2   /* 2: packed weight blocks ordered K step major */
+#define MOE_ABI_VERSION 3   /* 3: moe_desc.weight_layout and moe_desc.inter_scale */
 
 typedef enum moe_status {
   MOE_OK = 0,
@@ -118,6 +118,24 @@ typedef enum moe_mode {
 /* moe_desc.flags */
 #define MOE_FLAG_ROUTING_GIVEN 1  /* topk_ids / topk_weights are inputs: skip the router */
 
+/* Layout of the expert weights (and FP4 E8M0 scales) a call receives.
+ * moe_forward reads only the MFMA-tiled layout that moe_pack_weights
+ * writes; a descriptor that says row-major is rejected there, so weights
+ * that were never packed cannot be read as if they were. */
+typedef enum moe_weight_layout {
+  MOE_LAYOUT_ROW_MAJOR = 0,       /* [E][N][K] as generated / loaded          */
+  MOE_LAYOUT_TILED = 1            /* moe_pack_weights output                  */
+} moe_weight_layout;
+
+/* Scale of the FP8 re-quantisation of the intermediate activation (FP8
+ * activation layers; ignored for BF16 layers).  The quantisation options of
+ * youleyou, "DeepSeek 模型更新解读 Tile Kernels 与 DeepEP V2 新特性", section
+ * "Tile Kernels" (per-token / per-block FP8 scaling). */
+typedef enum moe_inter_scale {
+  MOE_INTER_SCALE_F32 = 0,        /* s = fl32(amax / 448) per row per 128 channels   */
+  MOE_INTER_SCALE_POW2 = 1        /* s = the smallest power of two >= amax / 448      */
+} moe_inter_scale;
+
 typedef struct moe_desc {
   int32_t T;             /* tokens                                   */
   int32_t H;             /* hidden size (K of linear 1, N of linear 2) */
@@ -128,6 +146,8 @@ typedef struct moe_desc {
   int32_t weight_dtype;  /* moe_dtype of expert weights              */
   int32_t mode;          /* moe_mode                                 */
   int32_t flags;         /* MOE_FLAG_*                               */
+  int32_t weight_layout; /* moe_weight_layout of the expert weights  */
+  int32_t inter_scale;   /* moe_inter_scale                          */
 } moe_desc;
 
 typedef void* moe_stream_t;   /* hipStream_t */
@@ -174,7 +194,11 @@ moe_status moe_validate(const moe_desc* d,
 
 /* The whole layer (router, top-k, permutation, gate|up GEMM + SwiGLU + FP8
  * requant, down GEMM, weighted combine).  expert_offsets and perm may be
- * NULL.  Layouts and errors: see the top of this file. */
+ * NULL.  Layouts and errors: see the top of this file.  The weights must
+ * be in the MFMA-tiled layout (d->weight_layout == MOE_LAYOUT_TILED; a
+ * row-major descriptor returns MOE_ERR_INVALID_ARGUMENT).
+ * d->inter_scale selects the intermediate's re-quantisation scale
+ * (MOE_INTER_SCALE_POW2: FP8 activations only). */
 moe_status moe_forward(const moe_desc* d,
                        const void* x, const float* x_scales,
                        const void* router_w, const float* router_bias,
@@ -184,20 +208,30 @@ moe_status moe_forward(const moe_desc* d,
                        int32_t* expert_offsets, int32_t* perm,
                        void* workspace, size_t workspace_bytes, moe_stream_t stream);
 
-/* Gating only: router logits (optional output, [T][E] fp32, bias included),
- * top-k ids and renormalised softmax weights.  Same layouts as moe_forward;
- * needs moe_route_workspace_size(d) bytes of workspace.  d->I and the
- * weight dtype are not used beyond validation. */
+/* Gating only (youleyou, "DeepSeek 模型更新解读 Tile Kernels 与 DeepEP V2
+ * 新特性", section "Tile Kernels", gating bullet: top-k expert selection and
+ * scoring): router logits l = xhat Wr^T + bias (optional output, [T][E]
+ * fp32), the top_k experts per token by logit, descending, ties to the
+ * lower index, and their weights, the softmax over the selected logits.
+ * Same layouts and error behaviour as moe_forward; needs
+ * moe_route_workspace_size(d) bytes of workspace.  d->I, the weight dtype
+ * and layout are not used beyond validation. */
 moe_status moe_route(const moe_desc* d,
                      const void* x, const float* x_scales,
                      const void* router_w, const float* router_bias,
                      float* logits, int32_t* topk_ids, float* topk_weights,
                      void* workspace, size_t workspace_bytes, moe_stream_t stream);
 
-/* Dispatch as a local permutation: from topk_ids [T][top_k] build
- * expert_offsets [E+1], perm [T*top_k] and (optional) row_of [T*top_k], the
- * inverse of perm.  Rows are grouped by expert in ascending token order.
- * Needs moe_permute_workspace_size(d) bytes of workspace. */
+/* Dispatch as a local permutation (机器之心, "DeepSeek悄悄更新：Mega MoE、FP4
+ * Indexer来了", section "Mega MoE 是什么？": tokens are dispatched to their
+ * experts; youleyou, section "Tile Kernels", MoE routing bullet: the
+ * token-to-expert mapping): from topk_ids [T][top_k] (every id in [0, E);
+ * ids out of range are clamped) build expert_offsets [E+1], perm
+ * [T*top_k] (the flat index t*top_k + j held by each permuted row) and
+ * (optional) row_of [T*top_k], the inverse of perm.  Rows are grouped by
+ * expert in ascending token order (a stable sort of the flat index by
+ * expert).  Needs moe_permute_workspace_size(d) bytes of workspace; errors
+ * as moe_forward. */
 moe_status moe_permute(const moe_desc* d, const int32_t* topk_ids,
                        int32_t* expert_offsets, int32_t* perm, int32_t* row_of,
                        void* workspace, size_t workspace_bytes, moe_stream_t stream);
@@ -213,7 +247,8 @@ moe_status moe_permute(const moe_desc* d, const int32_t* topk_ids,
  * both required); for BF16 / FP8 weights the scale pointers must be NULL
  * (FP8 block scales are used as they are).  Out of place: dst must not
  * overlap src.  A pure byte permutation, enqueued on `stream`; run it once
- * when the weights are loaded. */
+ * when the weights are loaded.  src is row-major whatever d->weight_layout
+ * says; pass dst to moe_forward with weight_layout = MOE_LAYOUT_TILED. */
 moe_status moe_pack_weights(const moe_desc* d, int32_t which, const void* src, const void* src_scales,
                             void* dst, void* dst_scales, moe_stream_t stream);
 

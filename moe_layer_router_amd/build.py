@@ -2,7 +2,8 @@
 
     python -m moe_layer_router_amd.build
 
-produces moe_layer_router_amd/libmoe_layer.so from csrc/kernels.hip.
+produces moe_layer_router_amd/libmoe_layer.so from csrc/kernels.hip (the
+layer) and csrc/peaks.hip (peak-rate microbenchmarks).
 """
 
 import os
@@ -13,7 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB_DIR = PKG
 LIB = os.path.join(LIB_DIR, "libmoe_layer.so")
-SOURCES = [os.path.join(PKG, "csrc", "kernels.hip")]
+SOURCES = [os.path.join(PKG, "csrc", "kernels.hip"), os.path.join(PKG, "csrc", "peaks.hip")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

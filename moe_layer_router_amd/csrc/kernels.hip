@@ -553,6 +553,12 @@ moe_status check_desc(const moe_desc* d) {
   if (d->mode != MOE_MODE_MEGA && d->mode != MOE_MODE_SEPARATE)
     return fail(MOE_ERR_INVALID_ARGUMENT, "unknown mode %d", d->mode);
   if (d->flags & ~MOE_FLAG_ROUTING_GIVEN) return fail(MOE_ERR_INVALID_ARGUMENT, "unknown flags 0x%x", d->flags);
+  if (d->weight_layout != MOE_LAYOUT_ROW_MAJOR && d->weight_layout != MOE_LAYOUT_TILED)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "unknown weight_layout %d", d->weight_layout);
+  if (d->inter_scale != MOE_INTER_SCALE_F32 && d->inter_scale != MOE_INTER_SCALE_POW2)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "unknown inter_scale %d", d->inter_scale);
+  if (d->inter_scale == MOE_INTER_SCALE_POW2)
+    return fail(MOE_ERR_UNSUPPORTED, "inter_scale MOE_INTER_SCALE_POW2 is not supported by this build");
   return MOE_OK;
 }
 
@@ -773,6 +779,10 @@ moe_status moe_validate(const moe_desc* d, const void* x, const float* x_scales,
                         const void* w_down, const void* w_down_scales, const void* y, const int32_t* topk_ids,
                         const float* topk_weights, const void* workspace, size_t workspace_bytes) {
   TRY(check_desc(d));
+  if (d->weight_layout != MOE_LAYOUT_TILED)
+    return fail(MOE_ERR_INVALID_ARGUMENT,
+                "the expert weights must be in the MFMA-tiled layout: convert them with moe_pack_weights and set "
+                "weight_layout = MOE_LAYOUT_TILED");
   const bool given = (d->flags & MOE_FLAG_ROUTING_GIVEN) != 0;
   TRY(check_ptr(x, "x", !given));
   TRY(check_ptr(x_scales, "x_scales", d->act_dtype == MOE_DTYPE_FP8_E4M3 && !given));

@@ -12,7 +12,7 @@ def pack_weights(inputs: dict, top_k: int = 1, stream=None) -> dict:
     is not modified; the result carries "weights_packed": True."""
     if inputs.get("weights_packed"):
         return inputs
-    desc = desc_from_inputs(inputs, top_k)
+    desc = desc_from_inputs(inputs, top_k, layout="row_major")
     fp4 = desc.weight_dtype == lib.MOE_DTYPE_FP4_E2M1
     out = dict(inputs)
     for which, w, sc in ((lib.MOE_WEIGHTS_GATE_UP, "w_gate_up", "w_gate_up_scales"),
@@ -28,7 +28,8 @@ def pack_weights(inputs: dict, top_k: int = 1, stream=None) -> dict:
     return out
 
 
-def desc_from_inputs(inputs: dict, top_k: int, mode: str = "mega", flags: int = 0, I=None) -> lib.MoeDesc:
+def desc_from_inputs(inputs: dict, top_k: int, mode: str = "mega", flags: int = 0, I=None, layout=None,
+                     inter_scale: str = "f32") -> lib.MoeDesc:
     x = inputs["x"]
     T, H = x.shape
     E = inputs["w_gate_up"].shape[0]
@@ -42,7 +43,9 @@ def desc_from_inputs(inputs: dict, top_k: int, mode: str = "mega", flags: int = 
         weight = "fp8"
     else:
         weight = "fp4"
-    return lib.make_desc(T, H, E, I, top_k, act, weight, mode, flags)
+    if layout is None:
+        layout = "tiled" if inputs.get("weights_packed") else "row_major"
+    return lib.make_desc(T, H, E, I, top_k, act, weight, mode, flags, layout, inter_scale)
 
 
 class Workspace:

@@ -40,6 +40,15 @@ MOE_MODE_MEGA = 0
 MOE_MODE_SEPARATE = 1
 # flags
 MOE_FLAG_ROUTING_GIVEN = 1
+# moe_weight_layout
+MOE_LAYOUT_ROW_MAJOR = 0
+MOE_LAYOUT_TILED = 1
+# moe_inter_scale
+MOE_INTER_SCALE_F32 = 0
+MOE_INTER_SCALE_POW2 = 1
+# moe_peak_kind
+MOE_PEAK_KINDS = {"mfma16_fp8_fp8": 0, "mfma16_fp4_fp8": 1, "mfma16_fp4_fp4": 2, "mfma16_bf16": 3,
+                  "mfma32_fp8_fp8": 4, "mfma32_fp4_fp8": 5}
 # moe_pack_weights `which`
 MOE_WEIGHTS_GATE_UP = 0
 MOE_WEIGHTS_DOWN = 1
@@ -51,7 +60,8 @@ MODES = {"mega": MOE_MODE_MEGA, "separate": MOE_MODE_SEPARATE}
 class MoeDesc(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("E", ctypes.c_int32),
                 ("I", ctypes.c_int32), ("top_k", ctypes.c_int32), ("act_dtype", ctypes.c_int32),
-                ("weight_dtype", ctypes.c_int32), ("mode", ctypes.c_int32), ("flags", ctypes.c_int32)]
+                ("weight_dtype", ctypes.c_int32), ("mode", ctypes.c_int32), ("flags", ctypes.c_int32),
+                ("weight_layout", ctypes.c_int32), ("inter_scale", ctypes.c_int32)]
 
 
 class MoeWorkspaceRegions(ctypes.Structure):
@@ -86,14 +96,26 @@ _lib.moe_permute.restype = ctypes.c_int
 _lib.moe_permute.argtypes = [ctypes.POINTER(MoeDesc)] + [_P] * 4 + [_P, ctypes.c_size_t, _P]
 _lib.moe_pack_weights.restype = ctypes.c_int
 _lib.moe_pack_weights.argtypes = [ctypes.POINTER(MoeDesc), ctypes.c_int32] + [_P] * 4 + [_P]
+_lib.moe_peak_mfma_flops.restype = ctypes.c_double
+_lib.moe_peak_mfma_flops.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+_lib.moe_peak_mfma.restype = ctypes.c_int
+_lib.moe_peak_mfma.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P, _P]
+_lib.moe_peak_hbm_read.restype = ctypes.c_int
+_lib.moe_peak_hbm_read.argtypes = [_P, ctypes.c_size_t, ctypes.c_int32, _P, _P]
 _lib.moe_status_string.restype = ctypes.c_char_p
 _lib.moe_status_string.argtypes = [ctypes.c_int]
 _lib.moe_last_error.restype = ctypes.c_char_p
 _lib.moe_last_error.argtypes = []
 
 
-def make_desc(T, H, E, I, top_k, act="fp8", weight="fp8", mode="mega", flags=0) -> MoeDesc:
-    return MoeDesc(T, H, E, I, top_k, DTYPES[act], DTYPES[weight], MODES.get(mode, mode), flags)
+LAYOUTS = {"row_major": MOE_LAYOUT_ROW_MAJOR, "tiled": MOE_LAYOUT_TILED}
+INTER_SCALES = {"f32": MOE_INTER_SCALE_F32, "pow2": MOE_INTER_SCALE_POW2}
+
+
+def make_desc(T, H, E, I, top_k, act="fp8", weight="fp8", mode="mega", flags=0, layout="tiled",
+              inter_scale="f32") -> MoeDesc:
+    return MoeDesc(T, H, E, I, top_k, DTYPES[act], DTYPES[weight], MODES.get(mode, mode), flags,
+                   LAYOUTS.get(layout, layout), INTER_SCALES.get(inter_scale, inter_scale))
 
 
 def _ptr(t):
@@ -192,8 +214,22 @@ def moe_pack_weights(desc, which, src, src_scales, dst, dst_scales, stream=None)
     _check(st, "moe_pack_weights")
 
 
+def moe_peak_mfma_flops(kind, iters, blocks) -> float:
+    return _lib.moe_peak_mfma_flops(MOE_PEAK_KINDS.get(kind, kind), iters, blocks)
+
+
+def moe_peak_mfma(kind, iters, blocks, sink, cycles, stream=None):
+    _check(_lib.moe_peak_mfma(MOE_PEAK_KINDS.get(kind, kind), iters, blocks, _ptr(sink), _ptr(cycles),
+                              _stream(stream)), "moe_peak_mfma")
+
+
+def moe_peak_hbm_read(buf, nbytes, blocks, sink, stream=None):
+    _check(_lib.moe_peak_hbm_read(_ptr(buf), nbytes, blocks, _ptr(sink), _stream(stream)), "moe_peak_hbm_read")
+
+
 def exported_symbols():
     """Names of the C entry points this binding wraps (for ABI checks)."""
     return ["moe_abi_version", "moe_workspace_size", "moe_route_workspace_size",
             "moe_permute_workspace_size", "moe_get_workspace_regions", "moe_validate", "moe_forward", "moe_route",
-            "moe_permute", "moe_pack_weights", "moe_status_string", "moe_last_error"]
+            "moe_permute", "moe_pack_weights", "moe_status_string", "moe_last_error",
+            "moe_peak_mfma_flops", "moe_peak_mfma", "moe_peak_hbm_read"]

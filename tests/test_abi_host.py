@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert lib.moe_abi_version() == 2
+    assert lib.moe_abi_version() == 3
     assert lib.moe_status_string(lib.MOE_OK) == "MOE_OK"
     assert lib.moe_status_string(lib.MOE_ERR_WORKSPACE_TOO_SMALL) == "MOE_ERR_WORKSPACE_TOO_SMALL"
 
@@ -90,6 +90,21 @@ def test_validate_rejects_bad_dtype_pairs_and_modes():
     assert _validate(lib.make_desc(10, 512, 16, 256, 4, "fp8", "bf16")) == lib.MOE_ERR_UNSUPPORTED
     assert _validate(lib.make_desc(10, 512, 16, 256, 4, mode=7)) == lib.MOE_ERR_INVALID_ARGUMENT
     assert _validate(lib.make_desc(10, 512, 16, 256, 4, flags=8)) == lib.MOE_ERR_INVALID_ARGUMENT
+
+
+def test_validate_rejects_unpacked_weights_and_unknown_fields():
+    """A descriptor that says the expert weights are row-major is rejected
+    (only moe_pack_weights output can be read), so a zero-initialised
+    descriptor cannot run the layer on unpacked weights by accident."""
+    d = lib.make_desc(100, 512, 16, 256, 4, layout="row_major")
+    assert _validate(d) == lib.MOE_ERR_INVALID_ARGUMENT
+    assert "moe_pack_weights" in lib.moe_last_error()
+    zero = lib.MoeDesc()
+    zero.T, zero.H, zero.E, zero.I, zero.top_k = 100, 512, 16, 256, 4
+    zero.act_dtype = zero.weight_dtype = lib.MOE_DTYPE_FP8_E4M3
+    assert _validate(zero) == lib.MOE_ERR_INVALID_ARGUMENT
+    assert _validate(lib.make_desc(100, 512, 16, 256, 4, layout=5)) == lib.MOE_ERR_INVALID_ARGUMENT
+    assert _validate(lib.make_desc(100, 512, 16, 256, 4, inter_scale=9)) == lib.MOE_ERR_INVALID_ARGUMENT
 
 
 def test_validate_rejects_bad_pointers_and_workspace():
