@@ -208,6 +208,29 @@ moe_status moe_forward(const moe_desc* d,
                        int32_t* expert_offsets, int32_t* perm,
                        void* workspace, size_t workspace_bytes, moe_stream_t stream);
 
+/* Bytes of the library's own device workspace used by moe_forward_static. */
+#define MOE_STATIC_WORKSPACE_BYTES ((size_t)64 << 20)
+
+/* moe_forward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same layer and arguments, with the workspace taken from
+ * a static device array of MOE_STATIC_WORKSPACE_BYTES (64 MiB) that the
+ * library holds on every GPU it runs on until the process ends (decode-sized
+ * batches fit: T = 256, H = 7168, E = 256, top-8, I = 2048 needs 34 MiB).
+ * The call allocates and frees nothing.  Layers whose moe_workspace_size
+ * exceeds the array return MOE_ERR_WORKSPACE_TOO_SMALL.  Every call on one
+ * GPU uses that GPU's array, which keeps the last call's contents (each call
+ * clears what must start at zero); calls that overlap on one GPU (other
+ * streams, other threads) race on it and must be serialised by the caller.
+ * The array's intermediate buffers are not readable through the ABI. */
+moe_status moe_forward_static(const moe_desc* d,
+                              const void* x, const float* x_scales,
+                              const void* router_w, const float* router_bias,
+                              const void* w_gate_up, const void* w_gate_up_scales,
+                              const void* w_down, const void* w_down_scales,
+                              void* y, int32_t* topk_ids, float* topk_weights,
+                              int32_t* expert_offsets, int32_t* perm, moe_stream_t stream);
+
 /* Gating only (youleyou, "DeepSeek 模型更新解读 Tile Kernels 与 DeepEP V2
  * 新特性", section "Tile Kernels", gating bullet: top-k expert selection and
  * scoring): router logits l = xhat Wr^T + bias (optional output, [T][E]

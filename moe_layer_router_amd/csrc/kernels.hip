@@ -604,6 +604,29 @@ moe_status device_info(DevInfo* out) {
   return MOE_OK;
 }
 
+// The workspace of moe_forward_static: a file-scope device array, one copy
+// per GPU.  In host code `scratch` names a host-side stand-in, not device
+// memory; its device address on the current GPU is looked up once per device
+// (hipGetSymbolAddress, with that device current) and only that address is
+// ever passed to kernels.
+static __device__ __align__(256) char scratch[MOE_STATIC_WORKSPACE_BYTES];
+void* g_scratch_ptr[64];
+
+moe_status static_workspace(void** out) {
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  if (dev < 0 || dev >= 64) return fail(MOE_ERR_UNSUPPORTED, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    HIP_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p) return fail(MOE_ERR_HIP, "hipGetSymbolAddress returned a null address for the static workspace");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
 moe_status fill_plan(const moe_desc* d, const Layout& L, char* ws, Plan* P) {
   Plan& p = *P;
   memset(&p, 0, sizeof p);
@@ -826,6 +849,22 @@ moe_status moe_forward(const moe_desc* d, const void* x, const float* x_scales, 
   if (p.act_fp8 && p.wdt == W_FP8) return launch_layer<ACT_FP8, W_FP8>(p, di, d->mode, st);
   if (p.act_fp8 && p.wdt == W_FP4) return launch_layer<ACT_FP8, W_FP4>(p, di, d->mode, st);
   return launch_layer<ACT_BF16, W_BF16>(p, di, d->mode, st);
+}
+
+moe_status moe_forward_static(const moe_desc* d, const void* x, const float* x_scales, const void* router_w,
+                              const float* router_bias, const void* w_gate_up, const void* w_gate_up_scales,
+                              const void* w_down, const void* w_down_scales, void* y, int32_t* topk_ids,
+                              float* topk_weights, int32_t* expert_offsets, int32_t* perm, moe_stream_t stream) {
+  TRY(check_desc(d));
+  const size_t need = workspace_need(d, WS_LAYER);
+  if (need > MOE_STATIC_WORKSPACE_BYTES)
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL,
+                "this layer needs %zu bytes of workspace; moe_forward_static has %zu (pass a workspace to moe_forward)",
+                need, (size_t)MOE_STATIC_WORKSPACE_BYTES);
+  void* ws = nullptr;
+  TRY(static_workspace(&ws));
+  return moe_forward(d, x, x_scales, router_w, router_bias, w_gate_up, w_gate_up_scales, w_down, w_down_scales, y,
+                     topk_ids, topk_weights, expert_offsets, perm, ws, MOE_STATIC_WORKSPACE_BYTES, stream);
 }
 
 moe_status moe_route(const moe_desc* d, const void* x, const float* x_scales, const void* router_w,

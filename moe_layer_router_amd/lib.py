@@ -90,6 +90,8 @@ _lib.moe_validate.restype = ctypes.c_int
 _lib.moe_validate.argtypes = [ctypes.POINTER(MoeDesc)] + [_P] * 11 + [_P, ctypes.c_size_t]
 _lib.moe_forward.restype = ctypes.c_int
 _lib.moe_forward.argtypes = [ctypes.POINTER(MoeDesc)] + [_P] * 13 + [_P, ctypes.c_size_t, _P]
+_lib.moe_forward_static.restype = ctypes.c_int
+_lib.moe_forward_static.argtypes = [ctypes.POINTER(MoeDesc)] + [_P] * 13 + [_P]
 _lib.moe_route.restype = ctypes.c_int
 _lib.moe_route.argtypes = [ctypes.POINTER(MoeDesc)] + [_P] * 7 + [_P, ctypes.c_size_t, _P]
 _lib.moe_permute.restype = ctypes.c_int
@@ -194,6 +196,18 @@ def moe_forward(desc, x, x_scales, router_w, router_bias, w_gate_up, w_gate_up_s
     _check(st, "moe_forward")
 
 
+def moe_forward_static(desc, x, x_scales, router_w, router_bias, w_gate_up, w_gate_up_scales, w_down,
+                       w_down_scales, y, topk_ids, topk_weights, expert_offsets, perm, stream=None):
+    st = _lib.moe_forward_static(ctypes.byref(desc), _ptr(x), _ptr(x_scales), _ptr(router_w), _ptr(router_bias),
+                                 _ptr(w_gate_up), _ptr(w_gate_up_scales), _ptr(w_down), _ptr(w_down_scales),
+                                 _ptr(y), _ptr(topk_ids), _ptr(topk_weights), _ptr(expert_offsets), _ptr(perm),
+                                 _stream(stream))
+    _check(st, "moe_forward_static")
+
+
+MOE_STATIC_WORKSPACE_BYTES = 64 << 20
+
+
 def moe_route(desc, x, x_scales, router_w, router_bias, logits, topk_ids, topk_weights, workspace,
               stream=None):
     st = _lib.moe_route(ctypes.byref(desc), _ptr(x), _ptr(x_scales), _ptr(router_w), _ptr(router_bias),
@@ -229,7 +243,7 @@ def moe_peak_hbm_read(buf, nbytes, blocks, sink, stream=None):
 
 def exported_symbols():
     """Names of the C entry points this binding wraps (for ABI checks)."""
-    return ["moe_abi_version", "moe_workspace_size", "moe_route_workspace_size",
+    return ["moe_abi_version", "moe_workspace_size", "moe_forward_static", "moe_route_workspace_size",
             "moe_permute_workspace_size", "moe_get_workspace_regions", "moe_validate", "moe_forward", "moe_route",
             "moe_permute", "moe_pack_weights", "moe_status_string", "moe_last_error",
             "moe_peak_mfma_flops", "moe_peak_mfma", "moe_peak_hbm_read"]
