@@ -59,6 +59,16 @@ R11 a / s is formed on the device as a times the correctly rounded fp32
     reciprocal of s; those two roundings (2**-24 relative each) are part of
     the R10 bound.  The oracle's own code is the E4M3 rounding of the exact
     a / s.
+R12 Input quantisation (the per-token FP8 quantisation of the Tile Kernels
+    section's quantisation bullet, in front of the router): per token and
+    128 channels, amax = max |x|; s = fl32(amax / 448) (fp32 division), a
+    zero block gets s = 1; or, for power-of-two scales, s = 2**e with e the
+    smallest integer such that 448 * 2**e >= amax, clamped to [-127, 127]
+    (an E8M0-representable scale).  Codes are E4M3_RNE_sat(x * fl32(1 / s))
+    with the product rounded to fp32: the rounding decision is taken in the
+    kernel's precision, so codes are bit-exact.  When the layer quantises its
+    input, the router reads the unquantised BF16 activations and the experts
+    the quantised ones.
 R9  The combine is the weighted sum over j of w[t, j] * expert_output.  The
     reference result is the unrounded fp64 sum; the device sums in fp32 in
     ascending j and rounds the result to BF16.
@@ -78,17 +88,26 @@ class Spec:
     E: int
     k: int
     I: int
-    act: str = "fp8"      # "fp8" or "bf16"
+    act: str = "fp8"      # "fp8" (quantised input), "bf16" (all-BF16 layer) or
+                          # "bf16_fp8" (BF16 input quantised to FP8 in the layer, R12)
     weight: str = "fp8"   # "fp8", "fp4" or "bf16"
+    scales: str = "f32"   # scales of the layer's own FP8 quantisations: "f32" or "pow2"
 
 
 # ------------------------------------------------------------------ decoding
 def decode_activations(spec: Spec, x, x_scales=None) -> np.ndarray:
-    """Dequantise the input activations to fp64 [T, H] (reading R7).
+    """The activations the expert GEMMs read, in fp64 [T, H] (readings R7,
+    R12).
 
-    FP8: value = E4M3(x[t, h]) * x_scales[t, h // 128].  BF16: exact."""
+    FP8: value = E4M3(x[t, h]) * x_scales[t, h // 128].  BF16: exact.
+    BF16 quantised in the layer: the per-token FP8 quantisation of x,
+    dequantised."""
     if spec.act == "bf16":
         return F.bf16_decode(x)
+    if spec.act == "bf16_fp8":
+        codes, s = quantise_tokens_fp8(F.bf16_decode(x), spec.scales == "pow2")
+        T, H = codes.shape
+        return (F.E4M3_TABLE[codes].reshape(T, H // 128, 128) * s[:, :, None]).reshape(T, H)
     q = np.asarray(x, dtype=np.uint8)
     s = np.asarray(x_scales, dtype=np.float32).astype(np.float64)
     T, H = q.shape
@@ -174,6 +193,49 @@ def silu(z: np.ndarray) -> np.ndarray:
 def swiglu(g: np.ndarray, u: np.ndarray) -> np.ndarray:
     """SwiGLU activation between the two linear maps (Mega MoE section; R5)."""
     return silu(g) * u
+
+
+# --------------------------------------------------- input quantisation (R12)
+def pow2_scale_exponent(amax: np.ndarray) -> np.ndarray:
+    """Smallest integer e with 448 * 2**e >= amax (amax > 0), clamped to
+    [-127, 127]; 0 where amax == 0 (scale 1).  Exact: 448 * 2**e is exact in
+    fp64 for every e in range."""
+    amax = np.asarray(amax, dtype=np.float64)
+    e = np.ceil(np.log2(np.where(amax > 0, amax, 1.0) / F.E4M3_MAX)).astype(np.int64)
+    # correct the floating-point log2 by one step either way, exactly
+    e = np.where(np.ldexp(F.E4M3_MAX, e - 1) >= amax, e - 1, e)
+    e = np.where(np.ldexp(F.E4M3_MAX, e) < amax, e + 1, e)
+    e = np.clip(e, -127, 127)
+    return np.where(amax > 0, e, 0)
+
+
+def quantise_tokens_fp8(x: np.ndarray, pow2: bool = False):
+    """Per-token, per-128-channel FP8 quantisation of activations (reading
+    R12).  x: [T, H] values exactly representable in fp32 (BF16 or fp32
+    inputs).  Returns (codes uint8 [T, H], scales float64 [T, H/128]
+    (fp32 values; powers of two when pow2)).
+
+    Steps in the kernel's precision (fp32, IEEE round to nearest even):
+    s = fl32(amax / 448), inv = fl32(1 / s), v = fl32(x * inv), then E4M3
+    round-to-nearest-even with saturation.  With pow2, s = 2**e and v = x / s
+    is exact."""
+    x = np.asarray(x, dtype=np.float64)
+    T, H = x.shape
+    b = x.reshape(T, H // 128, 128)
+    if not np.all(np.isfinite(b)) or not np.array_equal(b, b.astype(np.float32).astype(np.float64)):
+        raise ValueError("quantise_tokens_fp8 takes finite values representable in fp32")
+    amax = np.abs(b).max(axis=2)
+    if pow2:
+        s = np.ldexp(1.0, pow2_scale_exponent(amax))
+        v = b / s[:, :, None]                                   # exact (power-of-two scaling)
+    else:
+        a32 = amax.astype(np.float32)
+        s32 = np.where(a32 > 0, a32 / np.float32(F.E4M3_MAX), np.float32(1.0)).astype(np.float32)
+        inv = (np.float32(1.0) / s32).astype(np.float32)
+        v = (b.astype(np.float32) * inv[:, :, None]).astype(np.float32).astype(np.float64)
+        s = s32.astype(np.float64)
+    codes = F.e4m3_encode(v)
+    return codes.reshape(T, H), s
 
 
 # --------------------------------------------- device deviation bounds (R10)
@@ -415,15 +477,27 @@ def router_additions(H: int) -> int:
     return 132 + 2 + H // 128 + 8 + 1
 
 
-def logit_bound(spec: Spec, xhat: np.ndarray, router_w, router_bias=None, x_scales=None) -> np.ndarray:
+def router_input(spec: Spec, inputs: dict) -> np.ndarray:
+    """The activations the router reads: the dequantised FP8 input, or the
+    BF16 input itself (all-BF16 layers, and layers that quantise their input:
+    R3, R12)."""
+    if spec.act in ("bf16", "bf16_fp8"):
+        return F.bf16_decode(inputs["x"])
+    return decode_activations(spec, inputs["x"], inputs.get("x_scales"))
+
+
+def logit_bound(spec: Spec, inputs: dict) -> np.ndarray:
     """Absolute bound [T, E] on |device logit - exact logit| (R10):
     gamma_n * (sum_h |x_h Wr_h| + |b|), and 0 where every partial sum is exact
     in fp32 (power-of-two activation scales, grid-aligned operands and bias)."""
+    xhat = router_input(spec, inputs)
+    router_w, router_bias = inputs["router_w"], inputs.get("router_bias")
+    x_scales = inputs.get("x_scales") if spec.act == "fp8" else None
     wr = F.bf16_decode(router_w)
     b = np.zeros(wr.shape[0]) if router_bias is None else np.asarray(router_bias, dtype=np.float32).astype(np.float64)
     S = np.abs(xhat) @ np.abs(wr).T + np.abs(b)[None, :]
     e = gamma(router_additions(xhat.shape[1])) * S
-    pow2 = spec.act == "bf16" or x_scales is None or powers_of_two(x_scales)
+    pow2 = x_scales is None or powers_of_two(x_scales)
     if pow2:
         q = min(_lowest_bit_exponent(xhat) + _lowest_bit_exponent(wr), _lowest_bit_exponent(b))
         e = np.where(S < np.ldexp(1.0, 24 + q), 0.0, e)
@@ -432,9 +506,12 @@ def logit_bound(spec: Spec, xhat: np.ndarray, router_w, router_bias=None, x_scal
 
 # ----------------------------------------------------------------- the layer
 def route(spec: Spec, inputs: dict):
-    """Gating for all tokens: (xhat, logits, ids, weights)."""
+    """Gating for all tokens: (xhat, logits, ids, weights).  xhat are the
+    activations the experts read; the router reads the BF16 input itself
+    when the layer quantises it (R12)."""
     xhat = decode_activations(spec, inputs["x"], inputs.get("x_scales"))
-    logits = router_logits(xhat, inputs["router_w"], inputs.get("router_bias"))
+    xr = router_input(spec, inputs) if spec.act == "bf16_fp8" else xhat
+    logits = router_logits(xr, inputs["router_w"], inputs.get("router_bias"))
     ids = topk_select(logits, spec.k)
     w = topk_weights(logits, ids)
     return xhat, logits, ids, w
@@ -468,7 +545,10 @@ def layer(spec: Spec, inputs: dict, ids=None, tokens=None, inter=None, inter_sca
     ids = np.asarray(ids, dtype=np.int64)
     w = topk_weights(logits, ids)
     counts, offsets, perm, row_of = permutation(ids, spec.E)
+    # the scales of the activations the experts read (None for BF16 layers)
     x_scales = inputs.get("x_scales")
+    if spec.act == "bf16_fp8":
+        x_scales = quantise_tokens_fp8(F.bf16_decode(inputs["x"]), spec.scales == "pow2")[1]
 
     T, k = spec.T, spec.k
     tok_list = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)

@@ -90,7 +90,7 @@ def test_full_size_workload(L, name):
     spec = gen.spec_of(cfg)
     ov = gen.oracle_view(raw, lazy_weights=True)
     xh, logits, ids_ref, _ = O.route(spec, ov)
-    lerr = O.logit_bound(spec, xh, ov["router_w"], ov["router_bias"], ov["x_scales"])
+    lerr = O.logit_bound(spec, ov)
     ids = mega["topk_ids"].cpu().numpy().astype(np.int64)
     n_tie = check_routing(ids, mega["topk_weights"].cpu().numpy(), logits, ids_ref, cfg.k, lerr)
     counts, offsets, perm, _ = O.permutation(ids, cfg.E)

@@ -71,7 +71,7 @@ def test_router_gaussian_near_tie_rule(L):
     xh, logits, ids, w = O.route(spec, gen.oracle_view(inp))
     lg = out["logits"].cpu().numpy().astype(np.float64)
     ov = gen.oracle_view(inp)
-    lerr = O.logit_bound(spec, xh, ov["router_w"], ov["router_bias"], ov["x_scales"])
+    lerr = O.logit_bound(spec, ov)
     assert np.all(np.abs(lg - logits) <= lerr), "device logits outside the derived accumulation bound"
     check_routing(out["topk_ids"].cpu().numpy(), out["topk_weights"].cpu().numpy(), logits, ids, 8, lerr)
 
@@ -143,7 +143,7 @@ def _layer_check(L, cfg, mode, inp=None, routing=None, seed=0, exact=False):
     ids_gpu = out["topk_ids"].cpu().numpy().astype(np.int64)
     if routing is None:
         xh, logits, ids_ref, _ = O.route(spec, ov)
-        lerr = O.logit_bound(spec, xh, ov["router_w"], ov["router_bias"], ov["x_scales"])
+        lerr = O.logit_bound(spec, ov)
         check_routing(ids_gpu, out["topk_weights"].cpu().numpy(), logits, ids_ref, cfg.k, lerr)
     inter, isc = device_intermediate(L, out, cfg.act)
     ref = O.layer(spec, ov, ids=ids_gpu, inter=inter, inter_scales=isc)

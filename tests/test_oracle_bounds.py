@@ -221,11 +221,15 @@ def test_logit_bound_zero_on_exact_inputs_and_contains_fp32():
     wr = rng.integers(-64, 65, size=(E, H)) * 2.0 ** -6
     wr_bits = (wr.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
     bias = (rng.integers(-64, 65, size=E) * 2.0 ** -6).astype(np.float32)
-    assert np.all(O.logit_bound(spec, x, wr_bits, bias, np.ones((T, H // 128), np.float32)) == 0)
+    xcodes = F.e4m3_encode(x)
+    ones = np.ones((T, H // 128), np.float32)
+    inp = dict(x=xcodes, x_scales=ones, router_w=wr_bits, router_bias=bias)
+    assert np.all(O.logit_bound(spec, inp) == 0)
     # Gaussian activations with fp32 scales: the bound contains fp32 sums
-    xg = F.f32_round(rng.standard_normal((T, H)) * 0.37)
-    sx = np.full((T, H // 128), 0.37, dtype=np.float32)
-    b = O.logit_bound(spec, xg, wr_bits, bias, sx)
+    gcodes = F.e4m3_encode(rng.standard_normal((T, H)) * 50)
+    sx = np.full((T, H // 128), 0.0073, dtype=np.float32)
+    xg = O.decode_activations(spec, gcodes, sx)
+    b = O.logit_bound(spec, dict(x=gcodes, x_scales=sx, router_w=wr_bits, router_bias=bias))
     assert np.all(b > 0)
     ex = xg @ F.bf16_decode(wr_bits).T + bias
     for t in range(T):

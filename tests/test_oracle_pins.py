@@ -314,3 +314,130 @@ def test_given_ids_are_used():
     r = O.layer(spec, inp, ids=ids)
     assert np.array_equal(r["ids"], ids)
     assert r["counts"].tolist() == [10, 0, 0, 10]
+
+
+# ------------------------------------------------------- input quantisation
+def test_input_quant_amax_maps_to_448_and_zero_block():
+    rng = np.random.default_rng(20)
+    x = F.bf16_decode(_bf16_bits(rng.standard_normal((5, 384)) * np.array([1e-3, 1.0, 300.0]).repeat(128)))
+    x[4, 128:256] = 0.0
+    for pow2 in (False, True):
+        codes, s = O.quantise_tokens_fp8(x, pow2)
+        b = np.abs(x).reshape(5, 3, 128)
+        cb = codes.reshape(5, 3, 128)
+        amax = b.max(axis=2)
+        arg = b.argmax(axis=2)
+        assert s[4, 1] == 1.0 and np.all(cb[4, 1] & 0x7F == 0)
+        nz = amax > 0
+        if pow2:
+            assert O.powers_of_two(s[nz])
+            assert np.all(448.0 * s[nz] >= amax[nz]) and np.all(224.0 * s[nz] < amax[nz])
+        else:
+            # the amax element maps to +-448 (the reciprocal multiply may land a
+            # hair above 448, which saturates)
+            for r in range(5):
+                for blk in range(3):
+                    if nz[r, blk]:
+                        assert cb[r, blk, arg[r, blk]] & 0x7F == 0x7E
+            assert np.array_equal(s[nz], np.float32(amax[nz].astype(np.float32) / np.float32(448)).astype(np.float64))
+
+
+def test_input_quant_reciprocal_multiply_matches_exact_rational():
+    # fl32(x * fl32(1/s)) recomputed with exact rationals and one rounding per
+    # step: catches a division taken in fp64, a missing fp32 rounding of the
+    # reciprocal, or the product not rounded to fp32 before the E4M3 rounding.
+    from fractions import Fraction
+    rng = np.random.default_rng(21)
+    x = F.bf16_decode(_bf16_bits(rng.standard_normal((3, 256)) * 7.3))
+    codes, s = O.quantise_tokens_fp8(x)
+
+    def rnd32(q: Fraction) -> float:
+        # round a rational to the nearest fp32 (ties to even) via fp64 bracketing
+        f = float(q)                               # correctly rounded to fp64
+        c = np.float32(f)
+        cands = [np.nextafter(c, np.float32(-np.inf)), c, np.nextafter(c, np.float32(np.inf))]
+        best = min(cands, key=lambda y: (abs(Fraction(float(y)) - q),
+                                         int(np.frombuffer(np.float32(y).tobytes(), np.uint32)[0]) & 1))
+        return float(best)
+
+    # blocks where the fp32 reciprocal multiply and an exact division round to
+    # different codes (found by search): amax 880 with x = 0.013427734375,
+    # amax 800 with x = 150 and with x = 1.171875
+    special = np.zeros((3, 256))
+    special[0, 0], special[0, 1] = 880.0, 0.013427734375
+    special[1, 0], special[1, 1] = 800.0, 150.0
+    special[2, 0], special[2, 1] = 800.0, 1.171875
+    sc, ss = O.quantise_tokens_fp8(special)
+    exact_div = F.e4m3_encode(special[:, 1] / ss[:, 0])
+    assert np.all(sc[:, 1] != exact_div)                       # the cases do tell the two apart
+    x = np.concatenate([x, special])
+    codes, s = O.quantise_tokens_fp8(x)
+    for t in range(6):
+        for blk in range(2):
+            seg = x[t, blk * 128:(blk + 1) * 128]
+            amax = Fraction(float(np.abs(seg).max()))
+            s32 = rnd32(amax / 448) if amax > 0 else 1.0
+            inv = rnd32(1 / Fraction(s32))
+            assert s[t, blk] == s32
+            for i in (0, 1, 17, 64, 127):
+                v = rnd32(Fraction(float(seg[i])) * Fraction(inv))
+                assert codes[t, blk * 128 + i] == F.e4m3_encode(np.array([v]))[0]
+
+
+def test_input_quant_midpoints_with_unit_scale():
+    # with a 448 in each block the scale is exactly 1 and v = x: codes are the
+    # E4M3 round-to-nearest-even of x itself, ties to the even code
+    x = np.zeros((1, 256))
+    x[0, 0] = 448.0
+    x[0, 1:6] = [336.0, -2.375, 15.5, 0.013671875, 1000.0 / 1024]   # ties: 320|352, -2.25|-2.5, 15|16
+    x[0, 128] = -448.0
+    x[0, 129] = 0.001953125 * 1.5                                     # between subnormals 2^-9 and 2^-8
+    codes, s = O.quantise_tokens_fp8(x)
+    assert s[0, 0] == 1.0 and s[0, 1] == 1.0
+    vals = F.E4M3_TABLE[codes[0]]
+    assert vals[1] == 320.0 and vals[2] == -2.5 and vals[3] == 16.0       # the even mantissa each time
+    assert vals[129] == 0.00390625                                    # tie 1.5 * 2^-9 -> 2 * 2^-9 (even)
+    assert np.array_equal(codes[0], F.e4m3_encode(x[0]))
+
+
+def test_input_quant_pow2_exponent_exact():
+    amax = np.array([448.0, 448.0000001, 224.0, 224.0 * (1 + 2 ** -20), 1e-45, 3.0e38, 0.0])
+    e = O.pow2_scale_exponent(amax)
+    assert e.tolist()[:4] == [0, 1, -1, 0]
+    assert e[4] == -127 and e[5] == 120 and e[6] == 0          # 448 * 2**119 < 3e38 <= 448 * 2**120
+    # dequantised values are within half an E4M3 step of x, in the normal range
+    rng = np.random.default_rng(22)
+    x = F.bf16_decode(_bf16_bits(rng.standard_normal((4, 128)) * 50))
+    codes, s = O.quantise_tokens_fp8(x, pow2=True)
+    deq = F.E4M3_TABLE[codes] * np.repeat(s, 128, axis=1)
+    normal = np.abs(x) / np.repeat(s, 128, axis=1) >= 2.0 ** -6
+    assert np.all(np.abs(deq - x)[normal] <= 2.0 ** -4 * np.abs(x)[normal])
+
+
+def test_layer_quantising_its_input_equals_prequantised_layer():
+    # A BF16-input layer that quantises its input (R12) computes exactly the
+    # pre-quantised FP8 layer on the codes and scales of quantise_tokens_fp8,
+    # except that its router reads the BF16 input.
+    cfg = G.LayerConfig("pin_q", 29, 256, 6, 2, 128, "bf16", "fp8")
+    inp = G.make_inputs(cfg, seed=23)
+    wcfg = G.LayerConfig("pin_q", 29, 256, 6, 2, 128, "fp8", "fp8")
+    winp = G.make_inputs(wcfg, seed=23)           # FP8 weights of the same shapes
+    ov = G.oracle_view(inp)
+    ov_w = G.oracle_view(winp)
+    for key in ("w_gate_up", "w_gate_up_scales", "w_down", "w_down_scales"):
+        ov[key] = ov_w[key]
+    spec_q = O.Spec(29, 256, 6, 2, 128, "bf16_fp8", "fp8")
+    xb = F.bf16_decode(ov["x"])
+    codes, s = O.quantise_tokens_fp8(xb)
+    ov_p = dict(ov, x=codes, x_scales=s.astype(np.float32))
+    spec_p = O.Spec(29, 256, 6, 2, 128, "fp8", "fp8")
+    rq = O.layer(spec_q, ov)
+    # the router reads the BF16 input
+    assert np.array_equal(rq["logits"], xb @ F.bf16_decode(ov["router_w"]).T)
+    rp = O.layer(spec_p, ov_p, ids=rq["ids"])
+    # the experts read exactly the quantised input
+    assert np.array_equal(rq["xhat"], rp["xhat"])
+    assert np.array_equal(rq["xhat"], F.E4M3_TABLE[codes] * np.repeat(s, 128, axis=1))
+    # and the whole layer equals the mask-weighted dense brute force over it
+    bf = _dense_bruteforce(spec_q, ov)
+    assert np.allclose(rq["y"], bf, rtol=1e-12, atol=1e-12 * np.abs(bf).max())

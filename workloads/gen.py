@@ -45,6 +45,7 @@ class LayerConfig:
     weight: str         # "bf16" | "fp8" | "fp4"
     zipf: Optional[float] = None
     note: str = ""
+    scales: str = "f32"  # the layer's own FP8 quantisation scales: "f32" or "pow2"
 
 
 CONFIGS = {
@@ -65,7 +66,9 @@ CONFIGS = {
 def spec_of(cfg: LayerConfig):
     """The oracle's Spec for a config (a plain tuple of shapes and dtypes)."""
     from oracle.moe_oracle import Spec  # imported lazily: tests only
-    return Spec(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.act, cfg.weight)
+    # BF16 activations with FP8 / FP4 weights: the layer quantises its input
+    act = "bf16_fp8" if cfg.act == "bf16" and cfg.weight != "bf16" else cfg.act
+    return Spec(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, act, cfg.weight, cfg.scales)
 
 
 _TENSOR_IDS = {"x": 1, "router_w": 2, "w_gate_up": 3, "w_down": 4, "zipf_rank": 5,
