@@ -34,7 +34,9 @@ R5  gate|up weights are one [2I, H] matrix per expert (stored K-contiguous):
 R6  The intermediate activation is re-quantised to FP8 E4M3 per row and per
     128 channels: s = fl32(amax / 448), q = E4M3_RNE_saturating(a / s), and a
     block of zeros gets s = 1.  (For all-BF16 layers the intermediate is
-    rounded to BF16 instead.)
+    rounded to BF16 instead.)  The power-of-two variant of the quantisation
+    options takes s = the smallest power of two >= amax / 448 (as R12), an
+    E8M0 number that scaled matrix-core instructions apply exactly.
 R7  FP8 weights carry one fp32 scale per 128 x 128 block of the stored [N, K]
     matrix; FP4 weights carry one E8M0 scale per 32 consecutive K elements of
     each output row, two E2M1 values per byte with the even K index in the low
@@ -340,41 +342,55 @@ def intermediate_bound(spec: Spec, xrows: np.ndarray, w_gu: np.ndarray, scales_p
     return swiglu(g, u), swiglu_bound(g, u, eG[:, : spec.I], eG[:, spec.I:])
 
 
-def requant_window(a: np.ndarray, ea: np.ndarray, s: np.ndarray):
+def requant_window(a: np.ndarray, ea: np.ndarray, s: np.ndarray, pow2: bool = False):
     """For the block scales s [m, C/128], the exact a / s [m, C/128, 128] and
     the smallest and largest E4M3 values that the device may produce there:
     the device's pre-rounding value lies within ea / s of a / s, plus the two
-    roundings of the reciprocal multiply (R11)."""
+    roundings of the reciprocal multiply (R11; none for power-of-two scales,
+    where the scaling is exact)."""
     m, C = a.shape
     A = a.reshape(m, C // 128, 128)
     EA = np.broadcast_to(np.asarray(ea, dtype=np.float64), a.shape).reshape(m, C // 128, 128)
     sc = s[:, :, None]
     v = A / sc
-    ev = EA / sc + 1.01 * U1 * (np.abs(A) + EA) / sc
+    ev = EA / sc + (0.0 if pow2 else 1.01 * U1) * (np.abs(A) + EA) / sc
     lo = F.E4M3_TABLE[F.e4m3_encode(v - ev)]
     hi = F.E4M3_TABLE[F.e4m3_encode(v + ev)]
     return v, lo, hi
 
 
-def scale_window(a: np.ndarray, ea: np.ndarray):
-    """Smallest and largest fp32 block scale fl32(amax / 448) the device may
-    compute from its own block maximum (within ea of the exact one), per row
-    and 128-channel block; a zero maximum gives 1."""
+def block_scale(amax: np.ndarray, pow2: bool = False) -> np.ndarray:
+    """The re-quantisation scale of a block with maximum amax (R6 / R12):
+    fl32(amax / 448), or the smallest power of two >= amax / 448; 1 for a
+    zero block."""
+    if pow2:
+        return np.ldexp(1.0, pow2_scale_exponent(amax))
+    return np.where(amax == 0.0, 1.0, F.f32_round(amax / F.E4M3_MAX))
+
+
+def scale_window(a: np.ndarray, ea: np.ndarray, pow2: bool = False):
+    """Smallest and largest block scale the device may compute from its own
+    block maximum (within ea of the exact one), per row and 128-channel
+    block; a zero maximum gives 1.  Returns (s_lo, s_hi, may_be_zero,
+    must_be_zero)."""
     m, C = a.shape
     A = np.abs(a).reshape(m, C // 128, 128)
     EA = np.broadcast_to(np.asarray(ea, dtype=np.float64), a.shape).reshape(m, C // 128, 128)
     amax_lo = np.maximum(A - EA, 0.0).max(axis=2)
     amax_hi = (A + EA).max(axis=2)
-    s_lo = F.f32_round(amax_lo / F.E4M3_MAX)
-    s_hi = F.f32_round(amax_hi / F.E4M3_MAX)
+    # a device maximum anywhere in [amax_lo, amax_hi]; where that range reaches
+    # zero, any scale up to s_hi (or 1, for a maximum of exactly zero)
+    s_lo = np.where(amax_lo > 0, block_scale(amax_lo, pow2), 0.0)
+    s_hi = block_scale(amax_hi, pow2)
     return s_lo, s_hi, amax_lo == 0.0, amax_hi == 0.0
 
 
-def requant_fp8(a: np.ndarray, a_err=None, resolve=None, resolve_scales=None):
+def requant_fp8(a: np.ndarray, a_err=None, resolve=None, resolve_scales=None, pow2: bool = False):
     """Per-row, per-128-channel FP8 re-quantisation of the intermediate
     (Tile Kernels section, quantisation bullet, fused with SwiGLU; reading R6).
 
-    Without a_err: s = fl32(amax / 448) (1 for a zero block), codes =
+    Without a_err: s = fl32(amax / 448) (1 for a zero block), or with pow2 the
+    smallest power of two >= amax / 448 (R12's rule), codes =
     E4M3_RNE_sat(a / s).  With a_err (the R10 bound of another
     implementation's a) and its scales and codes:
     * resolve_scales [m, C/128] must lie within the scale window of each block
@@ -389,11 +405,10 @@ def requant_fp8(a: np.ndarray, a_err=None, resolve=None, resolve_scales=None):
     m, C = a.shape
     blocks = a.reshape(m, C // 128, 128)
     amax = np.abs(blocks).max(axis=2)
-    s = F.f32_round(amax / F.E4M3_MAX)
-    s = np.where(amax == 0.0, 1.0, s)
+    s = block_scale(amax, pow2)
     if a_err is not None and resolve_scales is not None:
         rs = np.asarray(resolve_scales, dtype=np.float64).reshape(m, C // 128)
-        s_lo, s_hi, may_zero, must_zero = scale_window(a, a_err)
+        s_lo, s_hi, may_zero, must_zero = scale_window(a, a_err, pow2)
         ok = ((rs >= s_lo) & (rs <= s_hi) & ~must_zero) | ((rs == 1.0) & may_zero)
         if not np.all(ok):
             r, b = np.argwhere(~ok)[0]
@@ -403,7 +418,7 @@ def requant_fp8(a: np.ndarray, a_err=None, resolve=None, resolve_scales=None):
     v = blocks / s[:, :, None]
     codes = F.e4m3_encode(v)
     if a_err is not None and resolve is not None:
-        _, lo, hi = requant_window(a, a_err, s)
+        _, lo, hi = requant_window(a, a_err, s, pow2)
         amb = lo != hi
         r = np.asarray(resolve, dtype=np.uint8).reshape(m, C // 128, 128)
         rv, cv = F.E4M3_TABLE[r], F.E4M3_TABLE[codes]
@@ -442,7 +457,7 @@ def quantise_intermediate(spec: Spec, a: np.ndarray, a_err=None, resolve=None, r
                 raise ValueError("a supplied BF16 intermediate differs from the oracle's away from a near-tie")
             r = np.where(amb, rv, r)
         return r
-    return requant_fp8(a, a_err, resolve, resolve_scales)[2]
+    return requant_fp8(a, a_err, resolve, resolve_scales, spec.scales == "pow2")[2]
 
 
 def expert_intermediate(spec: Spec, xrows: np.ndarray, w_gu: np.ndarray) -> np.ndarray:

@@ -245,3 +245,31 @@ def test_gamma_closed_form():
     assert O._lowest_bit_exponent(np.array([3 * 2.0 ** -7, 5 * 2.0 ** -3, 0.0])) == -7
     assert O._lowest_bit_exponent(np.array([6.0])) == 1
     assert O.powers_of_two([1.0, 0.5, 2.0 ** -30]) and not O.powers_of_two([1.0, 3.0])
+
+
+def test_pow2_requant_scale_codes_and_windows():
+    rng = np.random.default_rng(16)
+    a = rng.standard_normal((4, 256)) * np.array([0.01, 3.0, 700.0, 1e-30]).repeat(64)[None, :]
+    codes, s, deq = O.requant_fp8(a, pow2=True)
+    blocks = np.abs(a).reshape(4, 2, 128)
+    amax = blocks.max(axis=2)
+    assert O.powers_of_two(s)
+    assert np.all((224.0 * s < amax) & (amax <= 448.0 * s))
+    # the scaling is exact: the codes are the E4M3 rounding of a / s itself
+    assert np.array_equal(codes, F.e4m3_encode((a.reshape(4, 2, 128) / s[:, :, None]).reshape(4, 256)))
+    # idempotent on its own output
+    c2, s2, d2 = O.requant_fp8(deq, pow2=True)
+    assert np.array_equal(d2, deq) and np.array_equal(s2, s)
+    # windows: with no device error only exact midpoints are ambiguous (no
+    # reciprocal-multiply term for power-of-two scales)
+    ea = np.zeros_like(a)
+    _, lo, hi = O.requant_window(a, ea, s, pow2=True)
+    assert np.all(lo == hi)
+    # a device maximum a hair above a power-of-two boundary may double the scale
+    b = np.zeros((1, 128))
+    b[0, 0] = 448.0
+    s_lo, s_hi, _, _ = O.scale_window(b, np.full_like(b, 1e-3), pow2=True)
+    assert s_lo[0, 0] == 1.0 and s_hi[0, 0] == 2.0
+    O.requant_fp8(b, np.full_like(b, 1e-3), resolve=F.e4m3_encode(b / 2), resolve_scales=np.array([[2.0]]), pow2=True)
+    with pytest.raises(ValueError):
+        O.requant_fp8(b, np.zeros_like(b), resolve=F.e4m3_encode(b / 2), resolve_scales=np.array([[2.0]]), pow2=True)

@@ -255,9 +255,11 @@ def _dense_bruteforce(spec, inp):
     return y
 
 
-@pytest.mark.parametrize("act,weight", [("bf16", "bf16"), ("fp8", "fp8"), ("fp8", "fp4")])
-def test_layer_equals_dense_bruteforce(act, weight):
+@pytest.mark.parametrize("act,weight,scales", [("bf16", "bf16", "f32"), ("fp8", "fp8", "f32"), ("fp8", "fp4", "f32"),
+                                               ("fp8", "fp4", "pow2"), ("fp8", "fp8", "pow2")])
+def test_layer_equals_dense_bruteforce(act, weight, scales):
     spec, inp = _random_layer(37, 256, 6, 3, 256, act, weight, seed=5)
+    spec = O.Spec(spec.T, spec.H, spec.E, spec.k, spec.I, spec.act, spec.weight, scales)
     r = O.layer(spec, inp)
     ref = _dense_bruteforce(spec, inp)
     assert np.allclose(r["y"], ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
