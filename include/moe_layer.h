@@ -61,7 +61,11 @@
  * 4*s + l/16.  FP8 fp32 block scales stay row-major.
  * moe_pack_weights converts row-major weights into this layout.
  *
- * Supported dtype pairs (act x weight): BF16 x BF16, FP8 x FP8, FP8 x FP4.
+ * Supported dtype pairs (act x weight): BF16 x BF16, FP8 x FP8, FP8 x FP4,
+ * and BF16 x FP8 / BF16 x FP4: BF16 activations that the layer quantises
+ * itself (moe_quantize_input's per-token FP8 quantisation, into the
+ * workspace) for the expert GEMMs, while the router reads the BF16 input;
+ * x_scales must then be NULL.
  * Limits: T >= 1; H and I multiples of 128 (H <= 16384, I <= 16384);
  * 1 <= top_k <= E; E <= 1024; top_k <= 16; T * top_k * max(H, I) * 2 < 4 GiB
  * (the staging and intermediate rows are addressed with 32-bit offsets).
@@ -107,7 +111,8 @@ typedef enum moe_status {
 typedef enum moe_dtype {
   MOE_DTYPE_BF16 = 0,
   MOE_DTYPE_FP8_E4M3 = 1,         /* OCP E4M3 "fn": bias 7, max 448, no inf     */
-  MOE_DTYPE_FP4_E2M1 = 2          /* OCP MX E2M1 with E8M0 scales per 32        */
+  MOE_DTYPE_FP4_E2M1 = 2,         /* OCP MX E2M1 with E8M0 scales per 32        */
+  MOE_DTYPE_F32 = 3               /* IEEE binary32 (moe_quantize_input only)    */
 } moe_dtype;
 
 typedef enum moe_mode {
@@ -207,6 +212,23 @@ moe_status moe_forward(const moe_desc* d,
                        void* y, int32_t* topk_ids, float* topk_weights,
                        int32_t* expert_offsets, int32_t* perm,
                        void* workspace, size_t workspace_bytes, moe_stream_t stream);
+
+/* Per-token FP8 quantisation of activations, the step in front of the
+ * router (youleyou, "DeepSeek 模型更新解读 Tile Kernels 与 DeepEP V2 新特性",
+ * section "Tile Kernels", quantisation bullet: per-token FP8 quantisation).
+ * For each token t and 128-channel block c of x [T][H] (in_dtype
+ * MOE_DTYPE_BF16 or MOE_DTYPE_F32, finite values): amax = max |x|;
+ * scale_mode MOE_INTER_SCALE_F32: s = fl32(amax / 448), codes = E4M3
+ * round-to-nearest-even, saturating to +-448, of fl32(x * fl32(1 / s));
+ * MOE_INTER_SCALE_POW2: s = the smallest power of two with 448 s >= amax
+ * (clamped to 2^-127 .. 2^127) and codes of x / s (exact scaling); a block
+ * of zeros gets s = 1.  (In F32 mode, blocks whose maximum is below
+ * 448 * 2^-127 are out of contract: 1/s overflows.)  Outputs xq [T][H] E4M3
+ * bytes and x_scales [T][H/128] fp32, the layout moe_forward takes.  1 <= T,
+ * H a multiple of 128, T * H < 2^31; pointers 16-byte aligned.  Enqueued
+ * on `stream`; errors as moe_forward. */
+moe_status moe_quantize_input(int32_t T, int32_t H, int32_t in_dtype, int32_t scale_mode, const void* x,
+                              uint8_t* xq, float* x_scales, moe_stream_t stream);
 
 /* Bytes of the library's own device workspace used by moe_forward_static. */
 #define MOE_STATIC_WORKSPACE_BYTES ((size_t)64 << 20)

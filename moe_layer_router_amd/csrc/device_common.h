@@ -199,6 +199,10 @@ DEV void buf_st16(rsrc_t r, uint32_t voff, const v4i& v) {
   __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)voff, 0, AUX);
 }
 template <int AUX = 0>
+DEV void buf_st8(rsrc_t r, uint32_t voff, const v2u& v) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)voff, 0, AUX);
+}
+template <int AUX = 0>
 DEV void buf_stf(rsrc_t r, uint32_t voff, float v) {
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, v), r, (int)voff, 0, AUX);
 }

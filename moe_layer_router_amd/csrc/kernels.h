@@ -3,6 +3,7 @@
 #include "device_common.h"
 #include "expert_gemm.h"
 #include "permute.h"
+#include "quant.h"
 #include "router.h"
 
 namespace moe {
@@ -15,6 +16,7 @@ enum {
   CTR_G1_DONE,        // gate|up items finished
   CTR_QUEUE2,         // persistent kernel: queue head after the gate|up items
   CTR_SXP_DONE,       // permuted activation-scale items finished
+  CTR_QUANT_DONE,     // input quantisation items finished
   CTR_Q1 = 8,         // [kXcds] gate|up item queues, one per expert class
   CTR_Q2 = 16,        // [kXcds] down item queues (separate kernels)
   CTR_NUM = 32
@@ -23,7 +25,9 @@ enum {
 // Everything a kernel needs: shapes, caller buffers and workspace regions.
 struct Plan {
   int T, H, E, I, k;
-  int act_fp8, wdt;            // ACT_*, W_*
+  int act_fp8, wdt;            // ACT_*, W_* (act_fp8: the expert GEMMs read FP8 activations)
+  int quant_in;                // BF16 input quantised in the layer: router reads xb, experts x
+  int pow2;                    // power-of-two scales for the layer's own quantisations
   int routing_given;
   int nblk;                    // 256-token blocks
   int nTR, nER;                // router tiles (kRouterTokens x kRouterExperts)
@@ -34,6 +38,7 @@ struct Plan {
   int nCT;                     // combine token chunks per N block
   // caller buffers
   const uint8_t* x; const float* x_scales; const uint16_t* wr; const float* bias;
+  const uint16_t* xb;          // BF16 input (quant_in), the router's input
   const uint8_t* w_gu; const void* w_gu_scales; const uint8_t* w_d; const void* w_d_scales;
   uint16_t* y; int32_t* ids; float* wts; int32_t* offsets; int32_t* perm;
   // workspace

@@ -59,6 +59,15 @@ __global__ void __launch_bounds__(256) k_scatter(const int32_t* ids, int T, int 
   perm_scatter_block(ids, T, k, E, blockIdx.x, base, perm, row_of, reinterpret_cast<uint64_t*>(lds));
 }
 
+// Input quantisation: 16 blocks of 128 channels per workgroup and pass.
+template <int IN>
+__global__ void __launch_bounds__(256) k_quant(const void* x, int T, int H, int pow2, uint8_t* xq, float* xs) {
+  const int nblk = T * (H / 128);
+  const int per = 16 * 4;                  // blocks per workgroup
+  const int b0 = blockIdx.x * per;
+  quant_blocks<IN>(x, T, H, b0, min(nblk, b0 + per), pow2 != 0, xq, xs, threadIdx.x, 256);
+}
+
 // Activation scales in permuted row order (FP8 layers): 256 rows per block.
 __global__ void __launch_bounds__(256) k_permute_scales(const int32_t* perm, const float* x_scales, int T, int k,
                                                         int ns, float* sxp) {
@@ -258,11 +267,25 @@ __device__ __noinline__ void mega_router_item(Plan pv, int tt_, int et_, int ks_
   MEGA_LDS;
   const Plan p = uniform_plan(pv);
   const int tt = uni_i(tt_), et = uni_i(et_), ks = uni_i(ks_);
-  RouterArgs ra{p.x, p.x_scales, p.wr, p.bias, p.logits, p.T, p.H, p.E, p.act_fp8};
   int s0, s1;
   router_slice(p.H, ks, p.nKS, &s0, &s1);
-  router_tile<AF>(ra, tt * kRouterTokens, et * kRouterExperts, lds, s0, s1, p.logits + (size_t)ks * p.T * p.E,
-                  ks == 0);
+  if (AF == ACT_FP8 && p.quant_in) {       // the router reads the BF16 input
+    RouterArgs ra{reinterpret_cast<const uint8_t*>(p.xb), nullptr, p.wr, p.bias, p.logits, p.T, p.H, p.E, 0};
+    router_tile<ACT_BF16>(ra, tt * kRouterTokens, et * kRouterExperts, lds, s0, s1,
+                          p.logits + (size_t)ks * p.T * p.E, ks == 0);
+  } else {
+    RouterArgs ra{p.x, p.x_scales, p.wr, p.bias, p.logits, p.T, p.H, p.E, p.act_fp8};
+    router_tile<AF>(ra, tt * kRouterTokens, et * kRouterExperts, lds, s0, s1, p.logits + (size_t)ks * p.T * p.E,
+                    ks == 0);
+  }
+}
+constexpr int kQuantItemBlocks = 256;     // 128-channel blocks per quantisation item
+__device__ __noinline__ void mega_quant_item(Plan pv, int i_) {
+  const Plan p = uniform_plan(pv);
+  const int b0 = uni_i(i_) * kQuantItemBlocks;
+  quant_blocks<QIN_BF16, kCoherent>(p.xb, p.T, p.H, b0, min(p.T * (p.H / 128), b0 + kQuantItemBlocks),
+                                    p.pow2 != 0, const_cast<uint8_t*>(p.x), const_cast<float*>(p.x_scales),
+                                    threadIdx.x, blockDim.x);
 }
 // Part `part` of kReduceParts of the sum of router tile (tt, et)'s channel
 // slices (run once every slice of the tile is done).
@@ -323,7 +346,12 @@ k_mega(Plan p) {
   const int nC = (p.nblk > 1) ? p.nblk : 0;
   // FP8 layers: the activation scales in permuted row order, after the scatter
   const int nX = p.sxp ? (p.T * p.k + kSxpRows - 1) / kSxpRows : 0;
-  const int q_red = nR, q_topk = q_red + nRd, q_count = q_topk + nK, q_scat = q_count + nC, q_sxp = q_scat + p.nblk;
+  // BF16 input quantised in the layer: quantisation items come first (they
+  // depend on nothing; the activation-scale items and the GEMMs wait for them)
+  const int nQ = p.quant_in ? (p.T * (p.H / 128) + kQuantItemBlocks - 1) / kQuantItemBlocks : 0;
+  const int q_rt = nQ;
+  const int q_red = q_rt + nR, q_topk = q_red + nRd, q_count = q_topk + nK, q_scat = q_count + nC,
+            q_sxp = q_scat + p.nblk;
   const int q_end = q_sxp + nX;
   constexpr int kPer = kPermBlock / kTopkItemTokens;   // top-k items per 256-token block
   const int rdone_target = p.nER * ((p.nKS == 1) ? 1 : kReduceParts);   // per token tile
@@ -335,9 +363,13 @@ k_mega(Plan p) {
     const int q = s_q;
     __syncthreads();
     if (q >= q_end) break;
-    if (q < q_red) {
+    if (q < q_rt) {
+      mega_quant_item(p, q);
+      signal_coherent(&p.ctr[CTR_QUANT_DONE]);
+    } else if (q < q_red) {
+      const int r = q - q_rt;
       const int per_tt = p.nER * p.nKS;
-      const int tt = q / per_tt, et = (q % per_tt) / p.nKS, ks = q % p.nKS;
+      const int tt = r / per_tt, et = (r % per_tt) / p.nKS, ks = r % p.nKS;
       mega_router_item<AF>(p, tt, et, ks);
       signal_coherent(p.nKS == 1 ? &p.rdone[tt] : &p.rtile[tt * p.nER + et]);
     } else if (q < q_topk) {
@@ -357,6 +389,7 @@ k_mega(Plan p) {
       signal_coherent(&p.ctr[CTR_COUNT_DONE]);
     } else if (q >= q_sxp) {
       if (!wait_counter(&p.ctr[CTR_SCATTER_DONE], p.nblk, p.err, &s_ok, false)) return;
+      if (nQ > 0 && !wait_counter(&p.ctr[CTR_QUANT_DONE], nQ, p.err, &s_ok, false)) return;
       mega_sxp_item(p, q - q_sxp);
       signal_coherent(&p.ctr[CTR_SXP_DONE]);
     } else {
@@ -377,6 +410,7 @@ k_mega(Plan p) {
   // claimed by a running workgroup, so these waits end).  The GEMM items
   // read the permutation, tiles and weights with ordinary loads: one acquire
   // per workgroup here drops any older copy of them from the L2.
+  if (nQ > 0 && !wait_counter(&p.ctr[CTR_QUANT_DONE], nQ, p.err, &s_ok, false)) return;
   if (nX > 0) {
     if (!wait_counter(&p.ctr[CTR_SXP_DONE], nX, p.err, &s_ok)) return;     // (after every scatter item)
   } else if (!wait_counter(&p.ctr[CTR_SCATTER_DONE], p.nblk, p.err, &s_ok)) {
@@ -469,7 +503,7 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Layout {
   size_t err, zero_begin, ctr, rdone, rtile, tkdone, done1, done2, zero_end;
-  size_t logits, blockcnt, base, offsets, perm, row_of, tiles, meta, aq, sa, sxp, staging, total;
+  size_t logits, blockcnt, base, offsets, perm, row_of, tiles, meta, aq, sa, sxp, xq, xs, staging, total;
   int nblk, nTR, nER, nKS, max_tiles, nnb1, nnb2;
 };
 
@@ -516,9 +550,13 @@ Layout make_layout(const moe_desc* d) {
   L.row_of = o; o = align256(o + T * k * 4);
   L.tiles = o; o = align256(o + (size_t)L.max_tiles * sizeof(Tile));
   L.meta = o; o = align256(o + 64);
-  L.aq = o; o = align256(o + T * k * I * (d->act_dtype == MOE_DTYPE_FP8_E4M3 ? 1 : 2));
+  L.aq = o; o = align256(o + T * k * I * (d->weight_dtype != MOE_DTYPE_BF16 ? 1 : 2));
   L.sa = o; o = align256(o + T * k * (I / 128) * 4);
-  L.sxp = o; if (d->act_dtype == MOE_DTYPE_FP8_E4M3 && L.nblk > 1) o = align256(o + T * k * (H / 128) * 4);
+  const bool quant_in = d->act_dtype == MOE_DTYPE_BF16 && d->weight_dtype != MOE_DTYPE_BF16;
+  const bool fp8_experts = d->act_dtype == MOE_DTYPE_FP8_E4M3 || quant_in;
+  L.sxp = o; if (fp8_experts && L.nblk > 1) o = align256(o + T * k * (H / 128) * 4);
+  L.xq = o; if (quant_in) o = align256(o + T * H);
+  L.xs = o; if (quant_in) o = align256(o + T * (H / 128) * 4);
   L.staging = o; o = align256(o + T * k * H * 2);
   L.total = o;
   return L;
@@ -544,11 +582,12 @@ moe_status check_desc(const moe_desc* d) {
   if ((long long)d->T * d->top_k * (d->H > d->I ? d->H : d->I) * 2 > 0xFFFFFFFFLL)
     return fail(MOE_ERR_UNSUPPORTED, "T * top_k * max(H, I) * 2 must be below 4 GiB (got T=%d, top_k=%d, H=%d, I=%d)",
                 d->T, d->top_k, d->H, d->I);
-  const bool pair_ok = (d->act_dtype == MOE_DTYPE_BF16 && d->weight_dtype == MOE_DTYPE_BF16) ||
-                       (d->act_dtype == MOE_DTYPE_FP8_E4M3 && d->weight_dtype == MOE_DTYPE_FP8_E4M3) ||
-                       (d->act_dtype == MOE_DTYPE_FP8_E4M3 && d->weight_dtype == MOE_DTYPE_FP4_E2M1);
+  const bool wq = d->weight_dtype == MOE_DTYPE_FP8_E4M3 || d->weight_dtype == MOE_DTYPE_FP4_E2M1;
+  const bool pair_ok = (d->act_dtype == MOE_DTYPE_BF16 && (d->weight_dtype == MOE_DTYPE_BF16 || wq)) ||
+                       (d->act_dtype == MOE_DTYPE_FP8_E4M3 && wq);
   if (!pair_ok)
-    return fail(MOE_ERR_UNSUPPORTED, "unsupported dtype pair act=%d weight=%d (supported: bf16xbf16, fp8xfp8, fp8xfp4)",
+    return fail(MOE_ERR_UNSUPPORTED,
+                "unsupported dtype pair act=%d weight=%d (supported: bf16xbf16, fp8xfp8, fp8xfp4, bf16xfp8, bf16xfp4)",
                 d->act_dtype, d->weight_dtype);
   if (d->mode != MOE_MODE_MEGA && d->mode != MOE_MODE_SEPARATE)
     return fail(MOE_ERR_INVALID_ARGUMENT, "unknown mode %d", d->mode);
@@ -631,7 +670,9 @@ moe_status fill_plan(const moe_desc* d, const Layout& L, char* ws, Plan* P) {
   Plan& p = *P;
   memset(&p, 0, sizeof p);
   p.T = d->T; p.H = d->H; p.E = d->E; p.I = d->I; p.k = d->top_k;
-  p.act_fp8 = d->act_dtype == MOE_DTYPE_FP8_E4M3;
+  p.quant_in = d->act_dtype == MOE_DTYPE_BF16 && d->weight_dtype != MOE_DTYPE_BF16;
+  p.act_fp8 = d->act_dtype == MOE_DTYPE_FP8_E4M3 || p.quant_in;
+  p.pow2 = d->inter_scale == MOE_INTER_SCALE_POW2;
   p.wdt = d->weight_dtype == MOE_DTYPE_FP8_E4M3 ? W_FP8 : d->weight_dtype == MOE_DTYPE_FP4_E2M1 ? W_FP4 : W_BF16;
   p.routing_given = (d->flags & MOE_FLAG_ROUTING_GIVEN) != 0;
   p.nblk = L.nblk; p.nTR = L.nTR; p.nER = L.nER; p.nKS = L.nKS; p.max_tiles = L.max_tiles;
@@ -660,6 +701,10 @@ moe_status fill_plan(const moe_desc* d, const Layout& L, char* ws, Plan* P) {
   // a single block the extra step costs more than it saves)
   p.sxp = (p.act_fp8 && L.nblk > 1) ? reinterpret_cast<float*>(ws + L.sxp) : nullptr;
   p.staging = reinterpret_cast<uint16_t*>(ws + L.staging);
+  if (p.quant_in) {          // the experts read the layer's own quantisation of x
+    p.x = reinterpret_cast<const uint8_t*>(ws + L.xq);
+    p.x_scales = reinterpret_cast<const float*>(ws + L.xs);
+  }
   return MOE_OK;
 }
 
@@ -698,7 +743,9 @@ int mega_lds(const Plan& p) {
 // last slice of each tile).
 moe_status launch_route(const Plan& p, float* logits, int nks, hipStream_t st) {
   RouterArgs ra{p.x, p.x_scales, p.wr, p.bias, logits, p.T, p.H, p.E, p.act_fp8};
-  if (p.act_fp8) {
+  if (p.quant_in) ra = RouterArgs{reinterpret_cast<const uint8_t*>(p.xb), nullptr, p.wr, p.bias, logits, p.T, p.H,
+                                  p.E, 0};
+  if (ra.act_fp8) {
     TRY(set_lds_limit(k_router<ACT_FP8>, kRouterLds));
     hipLaunchKernelGGL(k_router<ACT_FP8>, dim3(p.nER, p.nTR, nks), dim3(256), kRouterLds, st, ra, nks, p.rtile);
   } else {
@@ -729,6 +776,12 @@ moe_status launch_layer(const Plan& p, const DevInfo& di, int mode, hipStream_t 
   hipLaunchKernelGGL(k_zero, dim3(16), dim3(256), 0, st, p.err, zero_ints);
   HIP_TRY(hipGetLastError());
   if (mode == MOE_MODE_SEPARATE) {
+    if (p.quant_in) {
+      const int nb = p.T * (p.H / 128);
+      hipLaunchKernelGGL(k_quant<QIN_BF16>, dim3((nb + 63) / 64), dim3(256), 0, st, (const void*)p.xb, p.T, p.H,
+                         p.pow2, const_cast<uint8_t*>(p.x), const_cast<float*>(p.x_scales));
+      HIP_TRY(hipGetLastError());
+    }
     if (!p.routing_given) TRY(launch_route(p, p.logits, p.nKS, st));
     TRY(launch_permute(p, p.row_of, st));
     if (p.sxp) {
@@ -809,6 +862,8 @@ moe_status moe_validate(const moe_desc* d, const void* x, const float* x_scales,
   const bool given = (d->flags & MOE_FLAG_ROUTING_GIVEN) != 0;
   TRY(check_ptr(x, "x", !given));
   TRY(check_ptr(x_scales, "x_scales", d->act_dtype == MOE_DTYPE_FP8_E4M3 && !given));
+  if (d->act_dtype == MOE_DTYPE_BF16 && d->weight_dtype != MOE_DTYPE_BF16 && x_scales)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "x_scales must be NULL when the layer quantises its BF16 input");
   TRY(check_ptr(router_w, "router_w", !given));
   TRY(check_ptr(router_bias, "router_bias", false));
   TRY(check_ptr(w_gate_up, "w_gate_up"));
@@ -838,7 +893,12 @@ moe_status moe_forward(const moe_desc* d, const void* x, const float* x_scales, 
   const Layout L = make_layout(d);
   Plan p;
   TRY(fill_plan(d, L, static_cast<char*>(workspace), &p));
-  p.x = static_cast<const uint8_t*>(x); p.x_scales = x_scales;
+  if (p.quant_in) {
+    p.xb = static_cast<const uint16_t*>(x);
+  } else {
+    p.x = static_cast<const uint8_t*>(x);
+    p.x_scales = x_scales;
+  }
   p.wr = static_cast<const uint16_t*>(router_w); p.bias = router_bias;
   p.w_gu = static_cast<const uint8_t*>(w_gate_up); p.w_gu_scales = w_gate_up_scales;
   p.w_d = static_cast<const uint8_t*>(w_down); p.w_d_scales = w_down_scales;
@@ -849,6 +909,31 @@ moe_status moe_forward(const moe_desc* d, const void* x, const float* x_scales, 
   if (p.act_fp8 && p.wdt == W_FP8) return launch_layer<ACT_FP8, W_FP8>(p, di, d->mode, st);
   if (p.act_fp8 && p.wdt == W_FP4) return launch_layer<ACT_FP8, W_FP4>(p, di, d->mode, st);
   return launch_layer<ACT_BF16, W_BF16>(p, di, d->mode, st);
+}
+
+moe_status moe_quantize_input(int32_t T, int32_t H, int32_t in_dtype, int32_t scale_mode, const void* x, uint8_t* xq,
+                              float* x_scales, moe_stream_t stream) {
+  if (T < 1) return fail(MOE_ERR_INVALID_ARGUMENT, "T must be >= 1 (got %d)", T);
+  if (H < 128 || H % 128) return fail(MOE_ERR_INVALID_ARGUMENT, "H must be a positive multiple of 128 (got %d)", H);
+  if ((long long)T * H >= (1LL << 31)) return fail(MOE_ERR_UNSUPPORTED, "T * H must be below 2^31");
+  if (in_dtype != MOE_DTYPE_BF16 && in_dtype != MOE_DTYPE_F32)
+    return fail(MOE_ERR_UNSUPPORTED, "in_dtype must be MOE_DTYPE_BF16 or MOE_DTYPE_F32 (got %d)", in_dtype);
+  if (scale_mode != MOE_INTER_SCALE_F32 && scale_mode != MOE_INTER_SCALE_POW2)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "unknown scale_mode %d", scale_mode);
+  TRY(check_ptr(x, "x"));
+  TRY(check_ptr(xq, "xq"));
+  TRY(check_ptr(x_scales, "x_scales"));
+  DevInfo di;
+  TRY(device_info(&di));
+  const int nb = T * (H / 128);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int pow2 = scale_mode == MOE_INTER_SCALE_POW2;
+  if (in_dtype == MOE_DTYPE_BF16)
+    hipLaunchKernelGGL(k_quant<QIN_BF16>, dim3((nb + 63) / 64), dim3(256), 0, st, x, T, H, pow2, xq, x_scales);
+  else
+    hipLaunchKernelGGL(k_quant<QIN_F32>, dim3((nb + 63) / 64), dim3(256), 0, st, x, T, H, pow2, xq, x_scales);
+  HIP_TRY(hipGetLastError());
+  return MOE_OK;
 }
 
 moe_status moe_forward_static(const moe_desc* d, const void* x, const float* x_scales, const void* router_w,
@@ -884,6 +969,10 @@ moe_status moe_route(const moe_desc* d, const void* x, const float* x_scales, co
   const Layout L = make_layout(d);
   Plan p;
   TRY(fill_plan(d, L, static_cast<char*>(workspace), &p));
+  // the router reads x as the descriptor's activation dtype says (BF16 input
+  // is read as BF16 whatever the weights are)
+  p.quant_in = 0;
+  p.act_fp8 = d->act_dtype == MOE_DTYPE_FP8_E4M3;
   p.x = static_cast<const uint8_t*>(x); p.x_scales = x_scales;
   p.wr = static_cast<const uint16_t*>(router_w); p.bias = router_bias;
   p.ids = topk_ids; p.wts = topk_weights;

@@ -99,12 +99,22 @@ def intermediate(out: dict):
     desc, ws = out["desc"], out["workspace"]
     reg = lib.moe_get_workspace_regions(desc)
     rows, I = desc.T * desc.top_k, desc.I
-    if desc.act_dtype == lib.MOE_DTYPE_FP8_E4M3:
+    if desc.weight_dtype != lib.MOE_DTYPE_BF16:     # FP8 / FP4 experts: E4M3 intermediate
         codes = ws[reg["inter"]: reg["inter"] + rows * I].view(rows, I)
         sc = ws[reg["inter_scales"]: reg["inter_scales"] + rows * (I // 128) * 4].view(torch.float32)
         return codes, sc.view(I // 128, rows).t()       # stored K block major
     vals = ws[reg["inter"]: reg["inter"] + rows * I * 2].view(torch.bfloat16).view(rows, I)
     return vals, None
+
+
+def quantize_input(x: torch.Tensor, scale_mode: str = "f32", stream=None):
+    """Per-token FP8 quantisation of [T, H] BF16 / fp32 activations
+    (moe_quantize_input): returns (codes uint8 [T, H], scales float32 [T, H/128])."""
+    T, H = x.shape
+    xq = torch.empty(T, H, dtype=torch.uint8, device=x.device)
+    xs = torch.empty(T, H // 128, dtype=torch.float32, device=x.device)
+    lib.moe_quantize_input(x.contiguous(), xq, xs, scale_mode, stream)
+    return xq, xs
 
 
 def route(inputs: dict, top_k: int, E: int, I: int = 128, workspace: Workspace = None, stream=None) -> dict:

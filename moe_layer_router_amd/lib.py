@@ -35,6 +35,7 @@ MOE_ERR_HIP = 4
 MOE_DTYPE_BF16 = 0
 MOE_DTYPE_FP8_E4M3 = 1
 MOE_DTYPE_FP4_E2M1 = 2
+MOE_DTYPE_F32 = 3
 # moe_mode
 MOE_MODE_MEGA = 0
 MOE_MODE_SEPARATE = 1
@@ -53,7 +54,7 @@ MOE_PEAK_KINDS = {"mfma16_fp8_fp8": 0, "mfma16_fp4_fp8": 1, "mfma16_fp4_fp4": 2,
 MOE_WEIGHTS_GATE_UP = 0
 MOE_WEIGHTS_DOWN = 1
 
-DTYPES = {"bf16": MOE_DTYPE_BF16, "fp8": MOE_DTYPE_FP8_E4M3, "fp4": MOE_DTYPE_FP4_E2M1}
+DTYPES = {"bf16": MOE_DTYPE_BF16, "fp8": MOE_DTYPE_FP8_E4M3, "fp4": MOE_DTYPE_FP4_E2M1, "f32": MOE_DTYPE_F32}
 MODES = {"mega": MOE_MODE_MEGA, "separate": MOE_MODE_SEPARATE}
 
 
@@ -90,6 +91,8 @@ _lib.moe_validate.restype = ctypes.c_int
 _lib.moe_validate.argtypes = [ctypes.POINTER(MoeDesc)] + [_P] * 11 + [_P, ctypes.c_size_t]
 _lib.moe_forward.restype = ctypes.c_int
 _lib.moe_forward.argtypes = [ctypes.POINTER(MoeDesc)] + [_P] * 13 + [_P, ctypes.c_size_t, _P]
+_lib.moe_quantize_input.restype = ctypes.c_int
+_lib.moe_quantize_input.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P]
 _lib.moe_forward_static.restype = ctypes.c_int
 _lib.moe_forward_static.argtypes = [ctypes.POINTER(MoeDesc)] + [_P] * 13 + [_P]
 _lib.moe_route.restype = ctypes.c_int
@@ -208,6 +211,15 @@ def moe_forward_static(desc, x, x_scales, router_w, router_bias, w_gate_up, w_ga
 MOE_STATIC_WORKSPACE_BYTES = 64 << 20
 
 
+def moe_quantize_input(x, xq, x_scales, scale_mode="f32", stream=None):
+    """x: [T, H] bfloat16 or float32 tensor; xq [T, H] uint8; x_scales [T, H/128] float32."""
+    import torch
+    T, H = x.shape
+    in_dtype = MOE_DTYPE_BF16 if x.dtype == torch.bfloat16 else MOE_DTYPE_F32
+    _check(_lib.moe_quantize_input(T, H, in_dtype, INTER_SCALES.get(scale_mode, scale_mode), _ptr(x), _ptr(xq),
+                                   _ptr(x_scales), _stream(stream)), "moe_quantize_input")
+
+
 def moe_route(desc, x, x_scales, router_w, router_bias, logits, topk_ids, topk_weights, workspace,
               stream=None):
     st = _lib.moe_route(ctypes.byref(desc), _ptr(x), _ptr(x_scales), _ptr(router_w), _ptr(router_bias),
@@ -243,7 +255,7 @@ def moe_peak_hbm_read(buf, nbytes, blocks, sink, stream=None):
 
 def exported_symbols():
     """Names of the C entry points this binding wraps (for ABI checks)."""
-    return ["moe_abi_version", "moe_workspace_size", "moe_forward_static", "moe_route_workspace_size",
+    return ["moe_abi_version", "moe_workspace_size", "moe_forward_static", "moe_quantize_input", "moe_route_workspace_size",
             "moe_permute_workspace_size", "moe_get_workspace_regions", "moe_validate", "moe_forward", "moe_route",
             "moe_permute", "moe_pack_weights", "moe_status_string", "moe_last_error",
             "moe_peak_mfma_flops", "moe_peak_mfma", "moe_peak_hbm_read"]

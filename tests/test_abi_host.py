@@ -86,8 +86,14 @@ def test_validate_rejects_bad_shapes(shape, status):
 
 
 def test_validate_rejects_bad_dtype_pairs_and_modes():
-    assert _validate(lib.make_desc(10, 512, 16, 256, 4, "bf16", "fp8")) == lib.MOE_ERR_UNSUPPORTED
+    # BF16 input with FP8 / FP4 weights: the layer quantises x itself, so
+    # x_scales must be NULL
+    assert _validate(lib.make_desc(10, 512, 16, 256, 4, "bf16", "fp8")) == lib.MOE_ERR_INVALID_ARGUMENT
+    assert "x_scales" in lib.moe_last_error()
+    assert _validate(lib.make_desc(10, 512, 16, 256, 4, "bf16", "fp8"), x_scales=None) == lib.MOE_OK
+    assert _validate(lib.make_desc(10, 512, 16, 256, 4, "bf16", "fp4"), x_scales=None) == lib.MOE_OK
     assert _validate(lib.make_desc(10, 512, 16, 256, 4, "fp8", "bf16")) == lib.MOE_ERR_UNSUPPORTED
+    assert _validate(lib.make_desc(10, 512, 16, 256, 4, "f32", "fp8")) == lib.MOE_ERR_UNSUPPORTED
     assert _validate(lib.make_desc(10, 512, 16, 256, 4, mode=7)) == lib.MOE_ERR_INVALID_ARGUMENT
     assert _validate(lib.make_desc(10, 512, 16, 256, 4, flags=8)) == lib.MOE_ERR_INVALID_ARGUMENT
 
@@ -145,3 +151,15 @@ def test_pack_weights_rejects_bad_arguments_without_device():
     assert st(ctypes.byref(d4), lib.MOE_WEIGHTS_GATE_UP, ok_src, None, ok_dst, None, None) == lib.MOE_ERR_INVALID_ARGUMENT
     assert st(ctypes.byref(d4), lib.MOE_WEIGHTS_GATE_UP, ok_src + 8, 0x20000, ok_dst, 0x9000000, None) == \
         lib.MOE_ERR_INVALID_ARGUMENT   # misaligned
+
+
+def test_quantize_input_rejects_bad_arguments_without_device():
+    q = lib._lib.moe_quantize_input
+    A = 0x100000
+    assert q(0, 256, lib.MOE_DTYPE_BF16, 0, A, A, A, None) == lib.MOE_ERR_INVALID_ARGUMENT
+    assert q(4, 200, lib.MOE_DTYPE_BF16, 0, A, A, A, None) == lib.MOE_ERR_INVALID_ARGUMENT
+    assert q(4, 256, lib.MOE_DTYPE_FP8_E4M3, 0, A, A, A, None) == lib.MOE_ERR_UNSUPPORTED
+    assert q(4, 256, lib.MOE_DTYPE_F32, 7, A, A, A, None) == lib.MOE_ERR_INVALID_ARGUMENT
+    assert q(4, 256, lib.MOE_DTYPE_F32, 0, None, A, A, None) == lib.MOE_ERR_INVALID_ARGUMENT
+    assert q(4, 256, lib.MOE_DTYPE_F32, 0, A, A + 4, A, None) == lib.MOE_ERR_INVALID_ARGUMENT
+    assert q(1 << 20, 4096, lib.MOE_DTYPE_F32, 0, A, A, A, None) == lib.MOE_ERR_UNSUPPORTED

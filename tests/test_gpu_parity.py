@@ -119,14 +119,17 @@ SMALL = [
     gen.LayerConfig("s_max_h", 40, 16384, 2, 1, 128, "fp8", "fp8"),           # largest H
     gen.LayerConfig("s_max_i", 40, 128, 2, 2, 16384, "fp8", "fp4"),           # largest I
     gen.LayerConfig("s_k_eq_e", 50, 256, 4, 4, 128, "bf16", "bf16"),          # every expert for every token
+    gen.LayerConfig("s_bf16in_fp8", 300, 512, 16, 4, 256, "bf16", "fp8"),     # BF16 input quantised in the layer
+    gen.LayerConfig("s_bf16in_fp4", 600, 384, 8, 2, 256, "bf16", "fp4"),      # (several 256-token blocks)
 ]
 
 
-def device_intermediate(L, out, act):
+def device_intermediate(L, out, weight):
     """The device's intermediate in the form the oracle takes: (E4M3 codes
-    [T*k, I], fp32 scales [T*k, I/128]) or (BF16 bit patterns, None)."""
+    [T*k, I], fp32 scales [T*k, I/128]) for FP8 / FP4 experts, or (BF16 bit
+    patterns, None) for all-BF16 layers."""
     inter, sc = L.intermediate(out)
-    if act == "fp8":
+    if weight != "bf16":
         return inter.cpu().numpy(), sc.cpu().numpy()
     return inter.cpu().view(torch.int16).numpy().view(np.uint16), None
 
@@ -145,7 +148,7 @@ def _layer_check(L, cfg, mode, inp=None, routing=None, seed=0, exact=False):
         xh, logits, ids_ref, _ = O.route(spec, ov)
         lerr = O.logit_bound(spec, ov)
         check_routing(ids_gpu, out["topk_weights"].cpu().numpy(), logits, ids_ref, cfg.k, lerr)
-    inter, isc = device_intermediate(L, out, cfg.act)
+    inter, isc = device_intermediate(L, out, cfg.weight)
     ref = O.layer(spec, ov, ids=ids_gpu, inter=inter, inter_scales=isc)
     y = out["y"].float().cpu().numpy()
     err = check_output(y, ref["y"], f"{cfg.name}/{mode}")
@@ -203,7 +206,7 @@ def test_given_routing_skew_and_empty_experts(L, mode):
     counts, offsets, perm, _ = O.permutation(ids.astype(np.int64), 8)
     assert np.array_equal(out["perm"].cpu().numpy(), perm)
     assert np.array_equal(out["expert_offsets"].cpu().numpy(), offsets)
-    inter, isc = device_intermediate(L, out, cfg.act)
+    inter, isc = device_intermediate(L, out, cfg.weight)
     xh = O.decode_activations(spec, ov["x"], ov["x_scales"])
     y = np.zeros((333, 512))
     for j, e in enumerate((5, 0)):
@@ -232,7 +235,7 @@ def test_intermediate_matches_oracle(L, cfg, exact):
     torch.cuda.synchronize()
     spec = gen.spec_of(cfg)
     ov = gen.oracle_view(inp)
-    inter, isc = device_intermediate(L, out, cfg.act)
+    inter, isc = device_intermediate(L, out, cfg.weight)
     perm = out["perm"].cpu().numpy()
     offs = out["expert_offsets"].cpu().numpy()
     xh = O.decode_activations(spec, ov["x"], ov["x_scales"])
