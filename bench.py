@@ -195,6 +195,8 @@ def main():
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one device copy of 1 GiB (a counter calibration point for profiling runs)")
     ap.add_argument("--no-peaks", action="store_true", help="skip the peak-rate microbenchmarks")
+    ap.add_argument("--inter-scale", default="f32", choices=["f32", "pow2"],
+                    help="scale rule of the layer's own FP8 quantisations (moe_desc.inter_scale)")
     ap.add_argument("--no-evict", action="store_true", help="skip the cache-evicted per-call timing")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -227,13 +229,13 @@ def main():
         """Warm-up, then K back-to-back layer calls on the current stream,
         timed as a whole and per call (one event pair per call: the counter
         clearing kernel (a few microseconds) and the layer's kernels)."""
-        out = layer.forward(inputs, cfg.k, mode=mode, workspace=ws)
+        out = layer.forward(inputs, cfg.k, mode=mode, workspace=ws, inter_scale=args.inter_scale)
         torch.cuda.synchronize()
         if int(out["workspace"][:4].view(torch.int32).item()) != 0:
             raise RuntimeError("device watchdog fired")
         print(f"[bench] {mode}: warmup {args.warmup}", file=sys.stderr, flush=True)
         for _ in range(args.warmup):
-            layer.forward(inputs, cfg.k, mode=mode, workspace=ws, out=out)
+            layer.forward(inputs, cfg.k, mode=mode, workspace=ws, out=out, inter_scale=args.inter_scale)
         starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
         ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
         t_begin = torch.cuda.Event(enable_timing=True)
@@ -242,7 +244,7 @@ def main():
         t_begin.record(stream)
         for i in range(args.steps):
             starts[i].record(stream)
-            layer.forward(inputs, cfg.k, mode=mode, workspace=ws, out=out)
+            layer.forward(inputs, cfg.k, mode=mode, workspace=ws, out=out, inter_scale=args.inter_scale)
             ends[i].record(stream)
         t_end.record(stream)
         torch.cuda.synchronize()
@@ -264,7 +266,7 @@ def main():
             junk.fill_(7)
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
-            layer.forward(inputs, cfg.k, mode=args.mode, workspace=ws, out=out)
+            layer.forward(inputs, cfg.k, mode=args.mode, workspace=ws, out=out, inter_scale=args.inter_scale)
             b.record(stream)
             torch.cuda.synchronize()
             ev.append(a.elapsed_time(b))
@@ -302,6 +304,7 @@ def main():
         "data": "synthetic (seeded N(0,1) activations, N(0,1/fan_in) weights, quantised; no real weights)",
         "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "E": cfg.E, "top_k": cfg.k, "I": cfg.I,
                    "act": cfg.act, "weight": cfg.weight, "zipf": cfg.zipf, "mode": args.mode,
+                   "inter_scale": args.inter_scale,
                    "active_experts": active},
         "tflops": round(tflops, 1),
         "mfma_peak_frac": round(tflops / PEAK_TFLOPS[exp_fmt], 4),

@@ -202,8 +202,12 @@ moe_status moe_validate(const moe_desc* d,
  * NULL.  Layouts and errors: see the top of this file.  The weights must
  * be in the MFMA-tiled layout (d->weight_layout == MOE_LAYOUT_TILED; a
  * row-major descriptor returns MOE_ERR_INVALID_ARGUMENT).
- * d->inter_scale selects the intermediate's re-quantisation scale
- * (MOE_INTER_SCALE_POW2: FP8 activations only). */
+ * d->inter_scale selects the scale rule of the layer's own FP8
+ * quantisations: the intermediate's re-quantisation and, for BF16 input
+ * with FP8 / FP4 weights, the input quantisation (ignored by all-BF16
+ * layers).  With MOE_INTER_SCALE_POW2 and FP4 weights those products carry
+ * only power-of-two scales, which the matrix-core instruction applies
+ * itself (no fp32 promotion). */
 moe_status moe_forward(const moe_desc* d,
                        const void* x, const float* x_scales,
                        const void* router_w, const float* router_bias,

@@ -67,10 +67,14 @@ DEV float f32_from_order_key(uint32_t k) {
 DEV v4f mfma_fp8_fp8(const v8i& a, const v8i& b, const v4f& c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
-// 4-bit A (E2M1, with its E8M0 scales) times 8-bit B (E4M3, unit scale).
-DEV v4f mfma_fp4_fp8(const v8i& a, const v8i& b, const v4f& c, int ascale) {
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 0, 0, ascale, 0, 127);
+// 4-bit A (E2M1, with its E8M0 scales) times 8-bit B (E4M3, with E8M0
+// scales, 127 = 1).
+DEV v4f mfma_fp4_fp8(const v8i& a, const v8i& b, const v4f& c, int ascale, int bscale = 127) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 0, 0, ascale, 0, bscale);
 }
+// E8M0 code of a positive power of two held in fp32 (2^-127, the subnormal
+// 0x00400000, gives 0 = 2^-127 as well): its biased exponent field.
+DEV int e8m0_of_pow2(float s) { return (int)(__float_as_uint(s) >> 23); }
 // 16x16x32 BF16 MFMA: lane l holds row/column l%16, 8 K of group l/16.
 DEV v4f mfma_bf16(const v8bf& a, const v8bf& b, const v4f& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);

@@ -39,6 +39,7 @@
 #pragma once
 #include "device_common.h"
 #include "permute.h"
+#include "quant.h"
 
 namespace moe {
 
@@ -59,6 +60,8 @@ struct GemmArgs {
   const float* sxp;          // [H/128][T*k] x_scales in permuted row order, or NULL
   uint16_t* staging;         // [T*k][H] BF16, indexed by flat index p
   int T, H, E, I, k;
+  int pow2;                  // re-quantise the intermediate with power-of-two scales
+  int pow2_x;                // the activation scales are powers of two (the layer's own quantisation)
 };
 
 constexpr int kGemmThreads = 256;
@@ -153,9 +156,14 @@ struct NoHook {
 // of its own.
 // `at_loop_end()` is called by every thread once the K loop has ended,
 // before the epilogue.
-template <int AF, int WF, int STAGE, int RS, int COH, typename Hook>
+// E8 (FP4 weights with power-of-two activation scales): every scale of the
+// product is a power of two, so the activation scale goes into the MFMA's
+// B scale operand next to the weights' E8M0 scales, and the MFMA accumulates
+// in place: no fp32 promotion.
+template <int AF, int WF, int STAGE, int RS, int COH, int E8, typename Hook>
 DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char* lds, int32_t* signal_prev,
                           const Hook& at_loop_end) {
+  static_assert(!E8 || (WF == W_FP4 && AF == ACT_FP8), "power-of-two products need FP4 weights");
   constexpr int CP = COH ? kCoherent : 0;            // cache policy of cross-item data
   using L = GemmLds<AF>;
   static_assert(RS >= 1 && RS <= L::kMaxRs, "row subtiles");
@@ -411,13 +419,16 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
               const v8i bv = {b.d[cs][0][0], b.d[cs][0][1], b.d[cs][0][2], b.d[cs][0][3],
                               b.d[cs][1][0], b.d[cs][1][1], b.d[cs][1][2], b.d[cs][1][3]};
               p[rs & 1][cs] = mfma_fp8_fp8(bv, av, zero);
+            } else if (E8) {
+              const v8i bv = {b.d[cs][0][0], b.d[cs][0][1], b.d[cs][0][2], b.d[cs][0][3], 0, 0, 0, 0};
+              acc[rs][cs] = mfma_fp4_fp8(bv, av, acc[rs][cs], b.sc[cs], e8m0_of_pow2(scv[0][rs >> 2][rs & 3]));
             } else {
               const v8i bv = {b.d[cs][0][0], b.d[cs][0][1], b.d[cs][0][2], b.d[cs][0][3], 0, 0, 0, 0};
               p[rs & 1][cs] = mfma_fp4_fp8(bv, av, zero, b.sc[cs]);
             }
           }
         }
-        if (rs > 0) {
+        if (rs > 0 && !E8) {
           const int q = rs - 1;
 #pragma unroll
           for (int cs = 0; cs < 4; ++cs) {
@@ -582,9 +593,10 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
         const float* AMAX = reinterpret_cast<const float*>(lds + L::kAmax);
         const float mx = fmaxf(fmaxf(AMAX[tid], AMAX[L::kRows + tid]),
                                fmaxf(AMAX[2 * L::kRows + tid], AMAX[3 * L::kRows + tid]));
-        const float sc = (mx > 0.f) ? mx / 448.0f : 1.0f;
+        float sc, inv;
+        block_scale(mx, g.pow2 != 0, &sc, &inv);
         RSC[tid] = sc;
-        reinterpret_cast<float*>(lds + L::kRinv)[tid] = 1.0f / sc;
+        reinterpret_cast<float*>(lds + L::kRinv)[tid] = inv;
       }
       __syncthreads();
       // Staging rows of 128 codes hold their 16-byte chunks permuted: chunk c
@@ -698,16 +710,27 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
 }
 
 // Dispatch a tile to the GEMM variant with the tile's number of row subtiles.
+template <int AF, int WF, int STAGE, int COH, int E8, typename Hook>
+DEV void expert_gemm_rs(const GemmArgs& g, const Tile& t, int nb, char* lds, int32_t* signal_prev,
+                        const Hook& at_loop_end) {
+  constexpr int FULL = GemmLds<AF>::kMaxRs;
+  if (t.rs <= 1)
+    expert_gemm_tile<AF, WF, STAGE, 1, COH, E8>(g, t.e, t.r0, t.rows, nb, lds, signal_prev, at_loop_end);
+  else if (t.rs <= 4)
+    expert_gemm_tile<AF, WF, STAGE, 4, COH, E8>(g, t.e, t.r0, t.rows, nb, lds, signal_prev, at_loop_end);
+  else
+    expert_gemm_tile<AF, WF, STAGE, FULL, COH, E8>(g, t.e, t.r0, t.rows, nb, lds, signal_prev, at_loop_end);
+}
 template <int AF, int WF, int STAGE, int COH, typename Hook = NoHook>
 DEV void expert_gemm_item(const GemmArgs& g, const Tile& t, int nb, char* lds, int32_t* signal_prev = nullptr,
                           const Hook& at_loop_end = Hook{}) {
-  constexpr int FULL = GemmLds<AF>::kMaxRs;
-  if (t.rs <= 1)
-    expert_gemm_tile<AF, WF, STAGE, 1, COH>(g, t.e, t.r0, t.rows, nb, lds, signal_prev, at_loop_end);
-  else if (t.rs <= 4)
-    expert_gemm_tile<AF, WF, STAGE, 4, COH>(g, t.e, t.r0, t.rows, nb, lds, signal_prev, at_loop_end);
+  // FP4 weights with power-of-two activation scales (the intermediate for
+  // the down GEMM, the layer's own input quantisation for gate|up)
+  const bool e8 = (STAGE == 1) ? g.pow2_x != 0 : g.pow2 != 0;
+  if (WF == W_FP4 && AF == ACT_FP8 && e8)
+    expert_gemm_rs<AF, WF, STAGE, COH, (WF == W_FP4 && AF == ACT_FP8) ? 1 : 0>(g, t, nb, lds, signal_prev, at_loop_end);
   else
-    expert_gemm_tile<AF, WF, STAGE, FULL, COH>(g, t.e, t.r0, t.rows, nb, lds, signal_prev, at_loop_end);
+    expert_gemm_rs<AF, WF, STAGE, COH, 0>(g, t, nb, lds, signal_prev, at_loop_end);
 }
 
 // y[t, n0:n1] = BF16( sum_j staging[t*k + j, n0:n1] ) for tokens [t0, t1),

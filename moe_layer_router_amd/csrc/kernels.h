@@ -83,6 +83,8 @@ __host__ __device__ inline GemmArgs gemm_args(const Plan& p) {
   g.w_gu = p.w_gu; g.w_gu_scales = p.w_gu_scales; g.w_d = p.w_d; g.w_d_scales = p.w_d_scales;
   g.aq = p.aq; g.sa = p.sa; g.staging = p.staging; g.sxp = p.sxp;
   g.T = p.T; g.H = p.H; g.E = p.E; g.I = p.I; g.k = p.k;
+  g.pow2 = p.pow2;
+  g.pow2_x = p.pow2 && p.quant_in;
   return g;
 }
 

@@ -596,8 +596,6 @@ moe_status check_desc(const moe_desc* d) {
     return fail(MOE_ERR_INVALID_ARGUMENT, "unknown weight_layout %d", d->weight_layout);
   if (d->inter_scale != MOE_INTER_SCALE_F32 && d->inter_scale != MOE_INTER_SCALE_POW2)
     return fail(MOE_ERR_INVALID_ARGUMENT, "unknown inter_scale %d", d->inter_scale);
-  if (d->inter_scale == MOE_INTER_SCALE_POW2)
-    return fail(MOE_ERR_UNSUPPORTED, "inter_scale MOE_INTER_SCALE_POW2 is not supported by this build");
   return MOE_OK;
 }
 

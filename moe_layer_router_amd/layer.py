@@ -62,7 +62,7 @@ class Workspace:
 
 
 def forward(inputs: dict, top_k: int, mode: str = "mega", workspace: Workspace = None,
-            routing=None, want_perm: bool = True, stream=None, out=None) -> dict:
+            routing=None, want_perm: bool = True, stream=None, out=None, inter_scale: str = "f32") -> dict:
     """Run the layer on inputs whose weights went through pack_weights().
     routing=(topk_ids, topk_weights) feeds given routing
     (MOE_FLAG_ROUTING_GIVEN).  Returns dict(y, topk_ids, topk_weights,
@@ -70,7 +70,7 @@ def forward(inputs: dict, top_k: int, mode: str = "mega", workspace: Workspace =
     if not inputs.get("weights_packed"):
         raise ValueError("forward() needs MFMA-tiled weights: pass the inputs through pack_weights() first")
     flags = lib.MOE_FLAG_ROUTING_GIVEN if routing is not None else 0
-    desc = desc_from_inputs(inputs, top_k, mode, flags)
+    desc = desc_from_inputs(inputs, top_k, mode, flags, inter_scale=inter_scale)
     dev = inputs["x"].device
     T, H, E, k = desc.T, desc.H, desc.E, desc.top_k
     if out is None:

@@ -121,6 +121,12 @@ SMALL = [
     gen.LayerConfig("s_k_eq_e", 50, 256, 4, 4, 128, "bf16", "bf16"),          # every expert for every token
     gen.LayerConfig("s_bf16in_fp8", 300, 512, 16, 4, 256, "bf16", "fp8"),     # BF16 input quantised in the layer
     gen.LayerConfig("s_bf16in_fp4", 600, 384, 8, 2, 256, "bf16", "fp4"),      # (several 256-token blocks)
+    # power-of-two scales for the layer's own quantisations: FP8 weights keep
+    # the promotion; FP4 weights run the down GEMM (and, with BF16 input, the
+    # gate|up GEMM too) with every scale in the matrix-core instruction
+    gen.LayerConfig("s_fp8_pow2", 300, 512, 16, 4, 256, "fp8", "fp8", scales="pow2"),
+    gen.LayerConfig("s_fp4_pow2", 600, 512, 16, 4, 384, "fp8", "fp4", scales="pow2"),
+    gen.LayerConfig("s_bf16in_fp4_pow2", 300, 1024, 8, 2, 256, "bf16", "fp4", scales="pow2"),
 ]
 
 
@@ -137,7 +143,7 @@ def device_intermediate(L, out, weight):
 def _layer_check(L, cfg, mode, inp=None, routing=None, seed=0, exact=False):
     if inp is None:
         inp = (gen.make_exact_layer_inputs if exact else gen.make_inputs)(cfg, seed=seed)
-    out = L.forward(L.pack_weights(to_dev(inp)), cfg.k, mode=mode,
+    out = L.forward(L.pack_weights(to_dev(inp)), cfg.k, mode=mode, inter_scale=cfg.scales,
                     routing=None if routing is None else tuple(torch.as_tensor(r).cuda() for r in routing))
     torch.cuda.synchronize()
     assert int(out["workspace"][:4].view(torch.int32).item()) == 0, "device watchdog fired"
@@ -220,9 +226,14 @@ def test_given_routing_skew_and_empty_experts(L, mode):
     check_output(out["y"].float().cpu().numpy(), y, f"given/{mode}")
 
 
+POW2_EXACT = gen.LayerConfig("x_fp8_pow2", 300, 1024, 16, 4, 256, "fp8", "fp8", scales="pow2")
+
+
 @pytest.mark.parametrize("cfg,exact", [(SMALL[0], False), (SMALL[1], False), (SMALL[4], False), (SMALL[2], False),
-                                       (EXACT[0], True), (EXACT[1], True), (EXACT[2], True)],
-                         ids=["s_fp8", "s_fp4", "s_multitile", "s_bf16", "x_fp8", "x_fp4", "x_bf16"])
+                                       (EXACT[0], True), (EXACT[1], True), (EXACT[2], True),
+                                       (SMALL[12], False), (POW2_EXACT, True)],
+                         ids=["s_fp8", "s_fp4", "s_multitile", "s_bf16", "x_fp8", "x_fp4", "x_bf16", "s_fp8_pow2",
+                              "x_fp8_pow2"])
 def test_intermediate_matches_oracle(L, cfg, exact):
     """Gate|up GEMM, SwiGLU and the per-128 FP8 re-quantisation, row by row.
     The device's scales lie in the oracle's derived scale window and its E4M3
@@ -231,11 +242,12 @@ def test_intermediate_matches_oracle(L, cfg, exact):
     in that window.  On the exact-GEMM inputs the window is a few fp32 units
     of a wide, so codes and scales are bit-exact almost everywhere."""
     inp = (gen.make_exact_layer_inputs if exact else gen.make_inputs)(cfg, seed=6)
-    out = L.forward(L.pack_weights(to_dev(inp)), cfg.k, mode="separate")
+    out = L.forward(L.pack_weights(to_dev(inp)), cfg.k, mode="separate", inter_scale=cfg.scales)
     torch.cuda.synchronize()
     spec = gen.spec_of(cfg)
     ov = gen.oracle_view(inp)
     inter, isc = device_intermediate(L, out, cfg.weight)
+    pw = cfg.scales == "pow2"
     perm = out["perm"].cpu().numpy()
     offs = out["expert_offsets"].cpu().numpy()
     xh = O.decode_activations(spec, ov["x"], ov["x_scales"])
@@ -257,9 +269,9 @@ def test_intermediate_matches_oracle(L, cfg, exact):
             n_tot += a.size
             O.quantise_intermediate(spec, a, ea, inter[rows])      # raises outside the windows
             continue
-        _, s_ref, _ = O.requant_fp8(a)
-        codes, s_dev, _ = O.requant_fp8(a, ea, resolve=inter[rows], resolve_scales=isc[rows])   # raises
-        _, lo, hi = O.requant_window(a, ea, s_dev)
+        _, s_ref, _ = O.requant_fp8(a, pow2=pw)
+        codes, s_dev, _ = O.requant_fp8(a, ea, resolve=inter[rows], resolve_scales=isc[rows], pow2=pw)   # raises
+        _, lo, hi = O.requant_window(a, ea, s_dev, pw)
         n_amb += int((lo != hi).sum())
         n_tot += a.size
         n_sdiff += int((s_dev != s_ref).sum())
