@@ -69,8 +69,11 @@ constexpr int kGemmThreads = 256;
 // Full tiles: 128 rows for FP8 activations, 64 for BF16.  With one wave per
 // SIMD a wave holds 16*RS x 64 fp32 accumulators (4*RS*4 VGPRs), which must
 // stay in VALU-addressable registers for the per-128-K promotion, next to
-// three (FP8) or two (BF16) steps of B fragments.
-constexpr int kGemmMaxRsFp8 = 8;
+// three (FP8) or two (BF16) steps of B fragments.  144-row FP8 tiles: an
+// expert with up to 288 rows (a DeepSeek-V3-shaped layer has 256 +- 15 per
+// expert) needs two tiles, each streaming the expert's weight slab once,
+// instead of two full tiles and a small remainder that streams it again.
+constexpr int kGemmMaxRsFp8 = 9;
 constexpr int kGemmMaxRsBf16 = 4;
 
 template <int AF>
@@ -81,6 +84,11 @@ struct GemmLds {
   static constexpr int kASlot = kRows * kABytes;                 // one A stage
   static constexpr int kA = 0;                                   // [2] A stages
   static constexpr int kScRows = kGemmThreads;                   // every thread writes a scale
+  // SC position stride of a row: subtile-minor, padded to a multiple of four
+  // so that a lane's run of scales starts 16-byte aligned
+  static constexpr int kScStride = (kMaxRs + 3) / 4 * 4;
+  static_assert(16 * kScStride + 64 <= kScRows, "scale positions and the spare slots fit");
+  static constexpr int kSaRows = (kRows + 63) / 64 * 64;         // rows of an activation-scale slot
   static constexpr int kPd = (AF == ACT_FP8) ? 3 : 2;            // prefetch distance (steps)
   static constexpr int kAStages = kPd + 1;
   static constexpr int kSC = kA + kAStages * kASlot;             // [2][2][kScRows] fp32 row scales
@@ -91,8 +99,8 @@ struct GemmLds {
   static constexpr int kRinv = kRsc + kRows * 4;                 // [kRows] fp32 1/scale
   static constexpr int kScw = kRinv + kRows * 4;                 // [2][128] fp32 weight block scales
   static constexpr int kSaSlots = kPd + 1;
-  static constexpr int kSA = kScw + 2 * 128 * 4;                 // [kSaSlots][128] fp32 activation scales
-  static constexpr int kBytes = kSA + kSaSlots * 128 * 4;
+  static constexpr int kSA = kScw + 2 * 128 * 4;                 // [kSaSlots][kSaRows] fp32 activation scales
+  static constexpr int kBytes = kSA + kSaSlots * kSaRows * 4;
 };
 
 // One step's B fragments: d[cs][i] are 16-byte pieces of column tile cs
@@ -242,7 +250,10 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
   // ---- A rows: direct-to-LDS loads.  Wave w's DMA j fills rows
   // RPD*(4j+w) .. +RPD of a stage; lane l writes row + l / CPR, physical
   // chunk l % CPR, i.e. logical chunk a_swz(row, l % CPR).  Rows past the
-  // tile's valid count repeat row 0 (their results are never stored).
+  // tile's valid count repeat row 0 (their results are never stored).  A
+  // DMA whose rows lie past the variant's R rows (R not a multiple of 4*RPD)
+  // repeats the wave's DMA 0 instead (same bytes to the same place), so that
+  // every wave issues the same number of loads per step.
   const rsrc_t ars = (STAGE == 1) ? make_rsrc(g.x, (uint32_t)((size_t)g.T * g.H * ESZ))
                                   : make_rsrc(g.aq, (uint32_t)((size_t)g.T * g.k * g.I * ESZ));
   uint32_t aoff[NDMA];
@@ -262,18 +273,21 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
   // this XCD's L2 for a later reader.
   auto dma_a = [&](int s, int slot, int j) __attribute__((always_inline)) {
     char* dst = lds + L::kA + slot * L::kASlot + w * 1024;
-    buf_ld16_lds<0>(ars, dst + j * 4096, aoff[j], (uint32_t)min(s, nsteps - 1) * 128 * ESZ);
+    const bool in = (R % (4 * RPD) == 0) || RPD * (4 * j + w) < R;      // wave-uniform
+    buf_ld16_lds<0>(ars, dst + (in ? j : 0) * 4096, in ? aoff[j] : aoff[0],
+                    (uint32_t)min(s, nsteps - 1) * 128 * ESZ);
   };
 
   // ---- per-row scales (FP8 activations).  The activation scales of step s
   // are loaded straight into LDS slot s % kSaSlots, PD + 1 steps ahead: wave w
-  // loads rows 64*(w&1) + lane (waves 2 and 3 write the same values as 0 and
-  // 1), so that thread tid < 128 finds the scale of row tid where its own
-  // wave's load put it.  SC[par][set] holds sA[row] * sB[set] for the
+  // loads rows 64*(w % NSW) + lane (NSW waves cover the tile; the others
+  // write the same values as wave w % NSW), so that thread tid < kRows finds
+  // the scale of row tid.  SC[par][set] holds sA[row] * sB[set] for the
   // tile's rows, stored subtile-minor (row rs*16 + i at position
-  // i*kMaxRs + rs), so that a lane reads the scales of its row i for every
-  // subtile with one or two 16-byte LDS reads.
-  const int arow = 64 * (w & 1) + lane;
+  // i*kScStride + rs), so that a lane reads the scales of its row i for every
+  // subtile with one to three 16-byte LDS reads.
+  constexpr int NSW = L::kSaRows / 64;
+  const int arow = 64 * (w % NSW) + lane;
   const int srow = (arow < m) ? arow : 0;
   // The intermediate's scales, and the activation scales when a permuted
   // copy exists (g.sxp), are K block major over the permuted rows
@@ -288,11 +302,11 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
   const uint32_t saoff = permuted ? (uint32_t)(r0 + srow) * 4 : (uint32_t)ROWI[srow] * (uint32_t)(g.H / 128) * 4;
   const uint32_t sastep = permuted ? nrows_all * 4 : 4u;
   auto dma_sa = [&](int s, int slot) __attribute__((always_inline)) {   // slot = s % kSaSlots
-    buf_ld4_lds<STAGE == 2 ? CP : 0>(sars, lds + L::kSA + slot * 512 + (w & 1) * 256, saoff,
+    buf_ld4_lds<STAGE == 2 ? CP : 0>(sars, lds + L::kSA + slot * (L::kSaRows * 4) + (w % NSW) * 256, saoff,
                                      (uint32_t)min(s, nsteps - 1) * sastep);
   };
   auto read_sa = [&](int slot) __attribute__((always_inline)) -> float {
-    return (AF == ACT_FP8) ? lds_ld<float>(lds, L::kSA + slot * 512 + (tid & 127) * 4) : 1.f;
+    return (AF == ACT_FP8) ? lds_ld<float>(lds, L::kSA + slot * (L::kSaRows * 4) + (tid % L::kSaRows) * 4) : 1.f;
   };
   auto store_scale = [&](int s, int par, float sa) __attribute__((always_inline)) {   // par = s & 1
     if (AF != ACT_FP8) return;
@@ -301,7 +315,8 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
     const float w1 = (WF == W_FP8) ? SCW[128 + sc] : 1.f;
     // no branch here: a conditional block would let the compiler sink the
     // step's MFMAs below the step's closing barrier
-    const int pos = (tid < L::kRows) ? (tid & 15) * L::kMaxRs + (tid >> 4) : tid;   // spare threads: unused slots
+    // spare threads write to the unused positions past 16 * kScStride
+    const int pos = (tid < L::kRows) ? (tid & 15) * L::kScStride + (tid >> 4) : 16 * L::kScStride + (tid & 63);
     SC[(par * 2 + 0) * L::kScRows + pos] = sa * w0;
     SC[(par * 2 + 1) * L::kScRows + pos] = sa * w1;
   };
@@ -348,7 +363,7 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
   // lane l holds row l%16 of the subtile (channels 4*(l/16) + v) and the
   // promotion scale of its four values is one number per lane and subtile.
   constexpr int NSET = (STAGE == 1 && WF == W_FP8) ? 2 : 1;
-  const uint32_t sc_rd = opaque(L::kSC + c16 * L::kMaxRs * 4 +
+  const uint32_t sc_rd = opaque(L::kSC + c16 * L::kScStride * 4 +
                                 ((STAGE == 2 && WF == W_FP8 && w >= 2) ? L::kScRows * 4 : 0));
 
   v4f acc[RS][4];
@@ -718,6 +733,9 @@ DEV void expert_gemm_rs(const GemmArgs& g, const Tile& t, int nb, char* lds, int
     expert_gemm_tile<AF, WF, STAGE, 1, COH, E8>(g, t.e, t.r0, t.rows, nb, lds, signal_prev, at_loop_end);
   else if (t.rs <= 4)
     expert_gemm_tile<AF, WF, STAGE, 4, COH, E8>(g, t.e, t.r0, t.rows, nb, lds, signal_prev, at_loop_end);
+  else if (FULL > 8 && t.rs <= 8)
+    expert_gemm_tile<AF, WF, STAGE, (FULL > 8 ? 8 : FULL), COH, E8>(g, t.e, t.r0, t.rows, nb, lds, signal_prev,
+                                                                    at_loop_end);
   else
     expert_gemm_tile<AF, WF, STAGE, FULL, COH, E8>(g, t.e, t.r0, t.rows, nb, lds, signal_prev, at_loop_end);
 }

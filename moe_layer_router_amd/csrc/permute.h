@@ -42,7 +42,11 @@ DEV void gemm_item_of(TilePtr tiles, int nnb, int i, int* t, int* nb) {
   *t = g0 + local % gn;
 }
 
-DEV int tile_variant(int rows, int full_rs) { return rows <= 16 ? 1 : rows <= 64 ? 4 : full_rs; }
+// Variant (16-row subtiles computed) of a tile of `rows` rows whose full size
+// is full_rs subtiles: 1, 4, 8 (when the full size is larger) or full_rs.
+DEV int tile_variant(int rows, int full_rs) {
+  return rows <= 16 ? 1 : rows <= 64 ? 4 : (full_rs > 8 && rows <= 128) ? 8 : full_rs;
+}
 
 // Expert id of entry i, clamped into [0, E): ids produced by the router are
 // always in range; given ids outside it are treated as E-1 so that every
