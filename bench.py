@@ -195,6 +195,8 @@ def main():
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one device copy of 1 GiB (a counter calibration point for profiling runs)")
     ap.add_argument("--no-peaks", action="store_true", help="skip the peak-rate microbenchmarks")
+    ap.add_argument("--trace", action="store_true",
+                    help="one extra persistent-kernel call with per-workgroup phase stamps (reported as 'phases')")
     ap.add_argument("--inter-scale", default="f32", choices=["f32", "pow2"],
                     help="scale rule of the layer's own FP8 quantisations (moe_desc.inter_scale)")
     ap.add_argument("--no-evict", action="store_true", help="skip the cache-evicted per-call timing")
@@ -320,6 +322,13 @@ def main():
                         "mean": round(float(per.mean()), 4)},
         "per_call_cache_evicted_ms": evicted,
     }
+    if args.trace:
+        tws = layer.Workspace(dev)
+        tout = layer.forward(inputs, cfg.k, mode="mega", workspace=tws, inter_scale=args.inter_scale, trace=True)
+        torch.cuda.synchronize()
+        result["phases"] = layer.trace_phases(tout)
+        print(f"[bench] phases: {json.dumps(result['phases'])}", file=sys.stderr, flush=True)
+        del tws, tout
     if not args.no_peaks:
         print("[bench] peak-rate microbenchmarks", file=sys.stderr, flush=True)
         cus = torch.cuda.get_device_properties(dev).multi_processor_count

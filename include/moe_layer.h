@@ -122,6 +122,8 @@ typedef enum moe_mode {
 
 /* moe_desc.flags */
 #define MOE_FLAG_ROUTING_GIVEN 1  /* topk_ids / topk_weights are inputs: skip the router */
+#define MOE_FLAG_TRACE 2          /* persistent kernel: per-workgroup phase timestamps in the
+                                     workspace's trace region (see moe_get_workspace_regions) */
 
 /* Layout of the expert weights (and FP4 E8M0 scales) a call receives.
  * moe_forward reads only the MFMA-tiled layout that moe_pack_weights
@@ -181,9 +183,19 @@ size_t moe_permute_workspace_size(const moe_desc* d);
  *   inter_scales  [I/128][T*top_k] fp32 re-quantisation scales (FP8 layers),
  *                 K block major: block c of permuted row r at c*T*top_k + r
  *   staging       [T*top_k][H] BF16 weighted expert outputs, row t*top_k+j
+ *   trace         with MOE_FLAG_TRACE (persistent kernel): [1024][8] uint64,
+ *                 row b for workgroup b < 1024: the device's constant 100 MHz
+ *                 clock at 0 kernel entry, 1 the end of its routing phase
+ *                 (no routing item left to claim), 2 the start of its
+ *                 gate|up phase (routing done), 3 its last gate|up item
+ *                 done, 4 its last down item done, 5 its exit; then
+ *                 6 the number of gate|up items and 7 of down items it ran.
+ *                 Without the flag the region is empty (offset = total).
  * Returns MOE_OK, or the status of an invalid descriptor. */
+#define MOE_TRACE_GROUPS 1024
+#define MOE_TRACE_FIELDS 8
 typedef struct moe_workspace_regions {
-  size_t logits, perm, row_of, offsets, inter, inter_scales, staging, total;
+  size_t logits, perm, row_of, offsets, inter, inter_scales, staging, trace, total;
 } moe_workspace_regions;
 moe_status moe_get_workspace_regions(const moe_desc* d, moe_workspace_regions* out);
 

@@ -54,7 +54,19 @@ struct Plan {
   Tile* tiles; int32_t* meta;
   uint8_t* aq; float* sa; uint16_t* staging;
   float* sxp;                  // [H/128][T*k] activation scales, permuted rows, or NULL
+  uint64_t* trace;             // [MOE_TRACE_GROUPS][MOE_TRACE_FIELDS] phase stamps, or NULL
 };
+
+constexpr int kTraceGroups = 1024;
+constexpr int kTraceFields = 8;
+// Phase stamp i of the calling workgroup (thread 0; the constant-rate clock).
+DEV void trace_stamp(uint64_t* trace, int i) {
+  if (trace && threadIdx.x == 0 && blockIdx.x < kTraceGroups)
+    trace[blockIdx.x * kTraceFields + i] = __builtin_amdgcn_s_memrealtime();
+}
+DEV void trace_count(uint64_t* trace, int i, uint64_t n) {
+  if (trace && threadIdx.x == 0 && blockIdx.x < kTraceGroups) trace[blockIdx.x * kTraceFields + i] = n;
+}
 
 constexpr int kCombineTokens = 256;
 

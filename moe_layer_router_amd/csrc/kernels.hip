@@ -336,6 +336,7 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_wav
 k_mega(Plan p) {
   __shared__ int s_q, s_ok, s_first[kXcds + 1];
   const int tid = threadIdx.x;
+  trace_stamp(p.trace, 0);
   const int nR = p.routing_given ? 0 : p.nTR * p.nER * p.nKS;
   // with the router's channels in slices, kReduceParts items per router tile
   // sum the slices once all of them are done
@@ -406,6 +407,8 @@ k_mega(Plan p) {
     }
   }
 
+  trace_stamp(p.trace, 1);
+
   // 2. gate|up items from the per-class queues (every head item has been
   // claimed by a running workgroup, so these waits end).  The GEMM items
   // read the permutation, tiles and weights with ordinary loads: one acquire
@@ -419,8 +422,10 @@ k_mega(Plan p) {
   if (tid <= kXcds) s_first[tid] = __hip_atomic_load(&p.meta[1 + tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   const int ntiles = s_first[kXcds];
+  trace_stamp(p.trace, 2);
   int cls = blockIdx.x % kXcds;
   int32_t* pending = nullptr;              // counter of the previous item, not yet signalled
+  int n_items = 0;
   if (tid == 0) s_q = pop_class_item(p.ctr + CTR_Q1, s_first, p.nnb1, &cls);
   __syncthreads();
   // (the next item is claimed when the current one's K loop ends, as in k_gemm)
@@ -432,11 +437,15 @@ k_mega(Plan p) {
       if (tid == 0) s_q = pop_class_item(p.ctr + CTR_Q1, s_first, p.nnb1, &cls);
     });
     pending = &p.done1[t];                 // signalled once its stores have completed
+    ++n_items;
     __syncthreads();
     i = s_q;
   }
   if (pending) signal_coherent(pending);
   pending = nullptr;
+  trace_stamp(p.trace, 3);
+  trace_count(p.trace, 6, n_items);
+  n_items = 0;
 
   // 3. down items from the per-class queues (all gate|up items have been
   // claimed); an item waits for the gate|up items of its tile.  Relaxed
@@ -453,10 +462,13 @@ k_mega(Plan p) {
       if (tid == 0) s_q = pop_class_item(p.ctr + CTR_Q2, s_first, p.nnb2, &cls);
     });
     pending = &p.done2[nb];
+    ++n_items;
     __syncthreads();
     i = s_q;
   }
   if (pending) signal_coherent(pending);
+  trace_stamp(p.trace, 4);
+  trace_count(p.trace, 7, n_items);
 
   // 4. combine items (N block, 256 tokens) once every down item of the N
   // block is done (all down items have been claimed)
@@ -470,6 +482,7 @@ k_mega(Plan p) {
     if (!wait_counter(&p.done2[nb], ntiles, p.err, &s_ok, false)) return;
     mega_combine_item(p, nb, c);
   }
+  trace_stamp(p.trace, 5);
 }
 
 }  // namespace moe
@@ -503,7 +516,7 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Layout {
   size_t err, zero_begin, ctr, rdone, rtile, tkdone, done1, done2, zero_end;
-  size_t logits, blockcnt, base, offsets, perm, row_of, tiles, meta, aq, sa, sxp, xq, xs, staging, total;
+  size_t logits, blockcnt, base, offsets, perm, row_of, tiles, meta, aq, sa, sxp, xq, xs, staging, trace, total;
   int nblk, nTR, nER, nKS, max_tiles, nnb1, nnb2;
 };
 
@@ -558,6 +571,7 @@ Layout make_layout(const moe_desc* d) {
   L.xq = o; if (quant_in) o = align256(o + T * H);
   L.xs = o; if (quant_in) o = align256(o + T * (H / 128) * 4);
   L.staging = o; o = align256(o + T * k * H * 2);
+  L.trace = o; if (d->flags & MOE_FLAG_TRACE) o = align256(o + (size_t)kTraceGroups * kTraceFields * 8);
   L.total = o;
   return L;
 }
@@ -591,7 +605,8 @@ moe_status check_desc(const moe_desc* d) {
                 d->act_dtype, d->weight_dtype);
   if (d->mode != MOE_MODE_MEGA && d->mode != MOE_MODE_SEPARATE)
     return fail(MOE_ERR_INVALID_ARGUMENT, "unknown mode %d", d->mode);
-  if (d->flags & ~MOE_FLAG_ROUTING_GIVEN) return fail(MOE_ERR_INVALID_ARGUMENT, "unknown flags 0x%x", d->flags);
+  if (d->flags & ~(MOE_FLAG_ROUTING_GIVEN | MOE_FLAG_TRACE))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "unknown flags 0x%x", d->flags);
   if (d->weight_layout != MOE_LAYOUT_ROW_MAJOR && d->weight_layout != MOE_LAYOUT_TILED)
     return fail(MOE_ERR_INVALID_ARGUMENT, "unknown weight_layout %d", d->weight_layout);
   if (d->inter_scale != MOE_INTER_SCALE_F32 && d->inter_scale != MOE_INTER_SCALE_POW2)
@@ -699,6 +714,7 @@ moe_status fill_plan(const moe_desc* d, const Layout& L, char* ws, Plan* P) {
   // a single block the extra step costs more than it saves)
   p.sxp = (p.act_fp8 && L.nblk > 1) ? reinterpret_cast<float*>(ws + L.sxp) : nullptr;
   p.staging = reinterpret_cast<uint16_t*>(ws + L.staging);
+  p.trace = (d->flags & MOE_FLAG_TRACE) ? reinterpret_cast<uint64_t*>(ws + L.trace) : nullptr;
   if (p.quant_in) {          // the experts read the layer's own quantisation of x
     p.x = reinterpret_cast<const uint8_t*>(ws + L.xq);
     p.x_scales = reinterpret_cast<const float*>(ws + L.xs);
@@ -844,6 +860,7 @@ moe_status moe_get_workspace_regions(const moe_desc* d, moe_workspace_regions* o
   out->inter = L.aq;
   out->inter_scales = L.sa;
   out->staging = L.staging;
+  out->trace = L.trace;
   out->total = L.total;
   return MOE_OK;
 }

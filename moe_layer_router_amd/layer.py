@@ -62,14 +62,15 @@ class Workspace:
 
 
 def forward(inputs: dict, top_k: int, mode: str = "mega", workspace: Workspace = None,
-            routing=None, want_perm: bool = True, stream=None, out=None, inter_scale: str = "f32") -> dict:
+            routing=None, want_perm: bool = True, stream=None, out=None, inter_scale: str = "f32",
+            trace: bool = False) -> dict:
     """Run the layer on inputs whose weights went through pack_weights().
     routing=(topk_ids, topk_weights) feeds given routing
     (MOE_FLAG_ROUTING_GIVEN).  Returns dict(y, topk_ids, topk_weights,
     expert_offsets, perm)."""
     if not inputs.get("weights_packed"):
         raise ValueError("forward() needs MFMA-tiled weights: pass the inputs through pack_weights() first")
-    flags = lib.MOE_FLAG_ROUTING_GIVEN if routing is not None else 0
+    flags = (lib.MOE_FLAG_ROUTING_GIVEN if routing is not None else 0) | (lib.MOE_FLAG_TRACE if trace else 0)
     desc = desc_from_inputs(inputs, top_k, mode, flags, inter_scale=inter_scale)
     dev = inputs["x"].device
     T, H, E, k = desc.T, desc.H, desc.E, desc.top_k
@@ -83,6 +84,9 @@ def forward(inputs: dict, top_k: int, mode: str = "mega", workspace: Workspace =
         out["topk_ids"].copy_(routing[0])
         out["topk_weights"].copy_(routing[1])
     ws = (workspace or Workspace(dev)).get(lib.moe_workspace_size(desc))
+    if trace:      # rows of workgroups that do not run must read as unused
+        reg = lib.moe_get_workspace_regions(desc)
+        ws[reg["trace"]: reg["trace"] + lib.MOE_TRACE_GROUPS * lib.MOE_TRACE_FIELDS * 8].zero_()
     lib.moe_forward(desc, inputs["x"], inputs.get("x_scales"), inputs["router_w"], inputs.get("router_bias"),
                     inputs["w_gate_up"], inputs.get("w_gate_up_scales"), inputs["w_down"],
                     inputs.get("w_down_scales"), out["y"], out["topk_ids"], out["topk_weights"],
@@ -115,6 +119,29 @@ def quantize_input(x: torch.Tensor, scale_mode: str = "f32", stream=None):
     xs = torch.empty(T, H // 128, dtype=torch.float32, device=x.device)
     lib.moe_quantize_input(x.contiguous(), xq, xs, scale_mode, stream)
     return xq, xs
+
+
+def trace_phases(out: dict) -> dict:
+    """Phase timing of a finished forward(..., trace=True) call in the
+    persistent kernel, from the per-workgroup stamps (100 MHz clock):
+    microseconds from the first workgroup's entry to each phase boundary
+    (first / median / last workgroup), and the items per workgroup."""
+    import numpy as np
+    desc, ws = out["desc"], out["workspace"]
+    reg = lib.moe_get_workspace_regions(desc)
+    n = lib.MOE_TRACE_GROUPS * lib.MOE_TRACE_FIELDS
+    raw = ws[reg["trace"]: reg["trace"] + n * 8].view(torch.int64).cpu().numpy().reshape(lib.MOE_TRACE_GROUPS, -1)
+    used = raw[:, 0] > 0
+    t = raw[used, :6].astype(np.float64)
+    t0 = t[:, 0].min()
+    us = (t - t0) / 100.0
+    names = ["entry", "routing_end", "gateup_start", "gateup_end", "down_end", "exit"]
+    res = {nm: {"first": round(float(us[:, i].min()), 1), "median": round(float(np.median(us[:, i])), 1),
+                "last": round(float(us[:, i].max()), 1)} for i, nm in enumerate(names)}
+    res["gateup_items_per_wg"] = [int(raw[used, 6].min()), int(raw[used, 6].max())]
+    res["down_items_per_wg"] = [int(raw[used, 7].min()), int(raw[used, 7].max())]
+    res["workgroups"] = int(used.sum())
+    return res
 
 
 def route(inputs: dict, top_k: int, E: int, I: int = 128, workspace: Workspace = None, stream=None) -> dict:

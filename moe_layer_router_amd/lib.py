@@ -41,6 +41,9 @@ MOE_MODE_MEGA = 0
 MOE_MODE_SEPARATE = 1
 # flags
 MOE_FLAG_ROUTING_GIVEN = 1
+MOE_FLAG_TRACE = 2
+MOE_TRACE_GROUPS = 1024
+MOE_TRACE_FIELDS = 8
 # moe_weight_layout
 MOE_LAYOUT_ROW_MAJOR = 0
 MOE_LAYOUT_TILED = 1
@@ -67,7 +70,7 @@ class MoeDesc(ctypes.Structure):
 
 class MoeWorkspaceRegions(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
-                ("logits", "perm", "row_of", "offsets", "inter", "inter_scales", "staging", "total")]
+                ("logits", "perm", "row_of", "offsets", "inter", "inter_scales", "staging", "trace", "total")]
 
 
 class MoeError(RuntimeError):
