@@ -19,6 +19,7 @@ namespace moe {
 
 constexpr int kPermBlock = 256;      // tokens per histogram / scatter block
 constexpr int kMinTileRows = 64;     // smallest full GEMM row tile (bounds the tile count)
+constexpr int kSmallTileRows = 64;   // rows of the 4-subtile GEMM variant
 
 // One GEMM row tile: rows [r0, r0 + rows) of expert e, computed by the GEMM
 // variant with `rs` 16-row subtiles (the smallest of 1, 4 or the full tile
@@ -46,6 +47,32 @@ DEV void gemm_item_of(TilePtr tiles, int nnb, int i, int* t, int* nb) {
 // is full_rs subtiles: 1, 4, 8 (when the full size is larger) or full_rs.
 DEV int tile_variant(int rows, int full_rs) {
   return rows <= 16 ? 1 : rows <= 64 ? 4 : (full_rs > 8 && rows <= 128) ? 8 : full_rs;
+}
+
+// The c rows of expert e (permuted rows off .. off + c - 1) as
+// gn = ceil(c / tile_rows) tiles g0, g0 + 1, ...  Full tiles and a remainder
+// when the remainder fits the 64-row variant; otherwise gn tiles of equal
+// size to one row.  Equal siblings run the same GEMM variant at the same
+// speed: the items of one N block, adjacent in the queue, then stream the
+// weight slab they share in step, and the later reads hit the L2 (a full
+// tile and a remainder of more than 64 rows would drift apart by the
+// remainder's shorter run time and miss).  A small remainder costs little
+// either way, and equal tiles would compute more padded rows.
+DEV void store_expert_tiles(Tile* tiles, int e, int off, int c, int g0, int tile_rows) {
+  const int gn = (c + tile_rows - 1) / tile_rows;
+  const bool even = gn > 1 && c - (gn - 1) * tile_rows > kSmallTileRows;
+  const int q = even ? c / gn : tile_rows, rem = even ? c % gn : 0;
+  for (int i = 0; i < gn; ++i) {
+    const int r0 = i * q + min(i, rem);
+    const int rows = min(q + (i < rem ? 1 : 0), c - r0);
+    int32_t* tf = reinterpret_cast<int32_t*>(tiles + g0 + i);
+    st_coh(tf + 0, e);
+    st_coh(tf + 1, off + r0);
+    st_coh(tf + 2, rows);
+    st_coh(tf + 3, tile_variant(rows, tile_rows / 16));
+    st_coh(tf + 4, g0);
+    st_coh(tf + 5, gn);
+  }
 }
 
 // Expert id of entry i, clamped into [0, E): ids produced by the router are
@@ -94,7 +121,7 @@ DEV int lds_exclusive_scan(int* a, int n, int* scratch) {
 // Exclusive scans over blocks and experts, and the GEMM tile list.
 //   base[b][e]   = first permuted row of expert e's rows from block b
 //   offsets[e]   = first permuted row of expert e (offsets[E] = T*k)
-//   tiles        = ceil(count_e / tile_rows) tiles per expert, ordered by
+//   tiles        = ceil(count_e / tile_rows) tiles per expert (store_expert_tiles), ordered by
 //                  expert class, then expert (each expert's tiles adjacent)
 //   meta[0]      = number of tiles; meta[1 + x] = first tile of class x
 //                  (x = 0 .. kXcds, the last entry equal to meta[0])
@@ -152,17 +179,7 @@ DEV void perm_scan(const int32_t* blockcnt, int nblk, int E, int tile_rows, int3
         run += cb[i];
       }
     }
-    const int g0 = tcl[class_pos(e, E8)], gn = (c + tile_rows - 1) / tile_rows;
-    for (int i = 0; i < gn; ++i) {
-      const int rows = min(tile_rows, c - i * tile_rows);
-      int32_t* tf = reinterpret_cast<int32_t*>(tiles + g0 + i);
-      st_coh(tf + 0, e);
-      st_coh(tf + 1, off + i * tile_rows);
-      st_coh(tf + 2, rows);
-      st_coh(tf + 3, tile_variant(rows, tile_rows / 16));
-      st_coh(tf + 4, g0);
-      st_coh(tf + 5, gn);
-    }
+    store_expert_tiles(tiles, e, off, c, tcl[class_pos(e, E8)], tile_rows);
   }
   if (threadIdx.x == 0) {
     st_coh(offsets + E, tot_rows);
@@ -279,17 +296,7 @@ DEV void perm_scan_scatter_block(const int32_t* ids, int T, int k, int E, int b,
       const int off = cnt[e];
       const int c = ((e + 1 < E) ? cnt[e + 1] : tot_rows) - off;
       st_coh(offsets + e, off);
-      const int g0 = tcl[class_pos(e, E8)], gn = (c + tile_rows - 1) / tile_rows;
-      for (int i = 0; i < gn; ++i) {
-        const int rows = min(tile_rows, c - i * tile_rows);
-        int32_t* tf = reinterpret_cast<int32_t*>(tiles + g0 + i);
-        st_coh(tf + 0, e);
-        st_coh(tf + 1, off + i * tile_rows);
-        st_coh(tf + 2, rows);
-        st_coh(tf + 3, tile_variant(rows, tile_rows / 16));
-        st_coh(tf + 4, g0);
-        st_coh(tf + 5, gn);
-      }
+      store_expert_tiles(tiles, e, off, c, tcl[class_pos(e, E8)], tile_rows);
     }
     if (threadIdx.x == 0) {
       st_coh(offsets + E, tot_rows);

@@ -9,8 +9,9 @@ configuration bench.py times (persistent kernel, one workgroup per CU):
   oracle computed for those tokens only (fed the device's ids and its
   intermediate codes and scales, which must lie in the derived windows).
   The sample covers every active expert (its first and last permuted row),
-  every 16-row subtile position of the 128-row GEMM tiles, and the last row
-  of every expert's last tile; the decode workload samples every token;
+  every 16-row subtile position of its GEMM row tiles (ceil(rows / 144)
+  tiles per expert, see expert_tiles), and the last row of every
+  expert's last tile; the decode workload samples every token;
 - the separate-kernel pipeline bitwise equal to the persistent kernel, the
   persistent kernel run on a workspace filled with NaN bytes first, so that
   a read of any intermediate or staging row before its writer has finished
@@ -29,7 +30,7 @@ from tests._helpers import check_output, check_routing
 pytestmark = pytest.mark.gpu
 
 FULL = ["dsv3_fp8", "dsv3_fp8xfp4", "decode_fp8_zipf", "mega_e1024_fp4_zipf"]
-TILE_ROWS = 128          # rows of a full GEMM row tile for FP8 activations
+TILE_ROWS = 144          # most rows of a GEMM row tile for FP8 activations
 SUBTILE = 16
 
 
@@ -39,12 +40,29 @@ def L(gpu_lib):
     return layer
 
 
+def expert_tiles(lo: int, hi: int):
+    """The row tiles of an expert with permuted rows [lo, hi): g =
+    ceil(n / 144) tiles, full ones and a remainder when the remainder has at
+    most 64 rows, else g tiles of equal size to one row (the larger first)."""
+    n = hi - lo
+    gn = -(-n // TILE_ROWS)
+    if gn > 1 and n - (gn - 1) * TILE_ROWS > 64:
+        q, rem = divmod(n, gn)
+    else:
+        q, rem = TILE_ROWS, 0
+    out = []
+    for i in range(gn):
+        r0 = i * q + min(i, rem)
+        out.append((lo + r0, min(q + (i < rem), n - r0)))
+    return out
+
+
 def coverage_tokens(offsets: np.ndarray, perm: np.ndarray, k: int, T: int, min_tokens: int, seed: int = 0):
     """Tokens whose permuted rows cover, for every active expert, its first
     row and its last row (the last row of its last tile) and, in each of its
-    tiles, one row at subtile position (e + 3 i) % 8 and lane (e % 16); the
-    eight subtile positions are then each covered by many experts.  Topped up
-    with random tokens to min_tokens."""
+    tiles, one row at subtile position (e + 3 i) mod (the tile's subtiles) and
+    lane (e % 16); the subtile positions are then each covered by many
+    experts.  Topped up with random tokens to min_tokens."""
     rows = []
     E = offsets.size - 1
     for e in range(E):
@@ -52,15 +70,28 @@ def coverage_tokens(offsets: np.ndarray, perm: np.ndarray, k: int, T: int, min_t
         if hi == lo:
             continue
         rows += [lo, hi - 1]
-        for i in range((hi - lo + TILE_ROWS - 1) // TILE_ROWS):
-            r = lo + i * TILE_ROWS + SUBTILE * ((e + 3 * i) % (TILE_ROWS // SUBTILE)) + e % SUBTILE
-            if r < hi:
-                rows.append(r)
+        for i, (r0, n) in enumerate(expert_tiles(lo, hi)):
+            ps = (e + 3 * i) % (-(-n // SUBTILE))
+            rows.append(r0 + SUBTILE * ps + min(e % SUBTILE, n - 1 - SUBTILE * ps))
     toks = set((perm[np.array(rows)] // k).tolist()) | {0, T - 1}
     rng = np.random.default_rng(seed)
     while len(toks) < min(min_tokens, T):
         toks.add(int(rng.integers(T)))
-    return np.array(sorted(toks)), np.array(rows)
+    return np.array(sorted(toks))
+
+
+def subtile_positions(tokens: np.ndarray, offsets: np.ndarray, perm: np.ndarray, k: int):
+    """The 16-row subtile positions (within their GEMM row tiles) of the
+    permuted rows of the given tokens, and the positions any tile has."""
+    row_of = np.empty_like(perm)
+    row_of[perm] = np.arange(perm.size)
+    rows = set(row_of[(tokens[:, None] * k + np.arange(k)).ravel()].tolist())
+    got, have = set(), set()
+    for e in range(offsets.size - 1):
+        for r0, n in expert_tiles(int(offsets[e]), int(offsets[e + 1])):
+            have |= set(range(-(-n // SUBTILE)))
+            got |= {(r - r0) // SUBTILE for r in range(r0, r0 + n) if r in rows}
+    return got, have
 
 
 @pytest.mark.parametrize("name", FULL)
@@ -97,11 +128,11 @@ def test_full_size_workload(L, name):
     assert np.array_equal(mega["expert_offsets"].cpu().numpy(), offsets)
     assert np.array_equal(mega["perm"].cpu().numpy(), perm)
 
-    sample, rows = coverage_tokens(offsets, perm, cfg.k, cfg.T, min_tokens=256)
+    sample = coverage_tokens(offsets, perm, cfg.k, cfg.T, min_tokens=256)
     if cfg.T <= 256:
         sample = np.arange(cfg.T)
-    pos = (rows - np.repeat(offsets[:-1], np.diff(offsets))[rows]) % TILE_ROWS // SUBTILE
-    assert set(pos.tolist()) == set(range(TILE_ROWS // SUBTILE)) or counts.max() <= TILE_ROWS // 2
+    got, have = subtile_positions(sample, offsets, perm, cfg.k)
+    assert got == have, (got, have)
     print(f"[fullsize] {name}: oracle output of {sample.size} tokens ({n_tie} near-tie routings)", flush=True)
     ref = O.layer(spec, ov, ids=ids, tokens=sample, inter=inter, inter_scales=isc)
     y = mega["y"][torch.as_tensor(sample, device="cuda")].float().cpu().numpy()
