@@ -80,14 +80,30 @@ DEV void store_expert_tiles(Tile* tiles, int e, int off, int c, int g0, int tile
 // write stays inside its buffer.
 DEV int expert_of(const int32_t* ids, size_t i, int E) { return min(max(ld_coh(ids + i), 0), E - 1); }
 
+// cnt[e] += number of entries ids[i0 .. i0 + n) equal to e (LDS atomics),
+// by the whole workgroup.  Each thread loads its (up to) 16 entries of a
+// pass before counting any: a coherent load between LDS atomics would wait
+// for the one before, one memory round trip per entry.
+DEV void count_experts(const int32_t* ids, size_t i0, int n, int E, int* cnt) {
+  constexpr int kU = 16;
+  const int nthr = blockDim.x;
+  for (int p0 = 0; p0 < n; p0 += kU * nthr) {
+    int ev[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) ev[u] = expert_of(ids, i0 + min(p0 + u * nthr + (int)threadIdx.x, n - 1), E);
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+      if (p0 + u * nthr + (int)threadIdx.x < n) atomicAdd(&cnt[ev[u]], 1);
+  }
+}
+
 // Per-block expert histogram: blockcnt[b][e] = number of (t, j) with
 // ids[t][j] == e for tokens t of block b.  LDS: E ints.
 DEV void perm_count_block(const int32_t* ids, int T, int k, int E, int b, int32_t* blockcnt, int* lds) {
   for (int e = threadIdx.x; e < E; e += blockDim.x) lds[e] = 0;
   __syncthreads();
   const int t0 = b * kPermBlock;
-  const int n = min(kPermBlock, T - t0) * k;
-  for (int i = threadIdx.x; i < n; i += blockDim.x) atomicAdd(&lds[expert_of(ids, (size_t)t0 * k + i, E)], 1);
+  count_experts(ids, (size_t)t0 * k, min(kPermBlock, T - t0) * k, E, lds);
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += blockDim.x) st_coh(blockcnt + (size_t)b * E + e, lds[e]);
   __syncthreads();
@@ -257,8 +273,7 @@ DEV void perm_scan_scatter_block(const int32_t* ids, int T, int k, int E, int b,
   if (nblk == 1) {
     for (int e = threadIdx.x; e < E; e += blockDim.x) { cnt[e] = 0; pre[e] = 0; }
     __syncthreads();
-    const int n = min(kPermBlock, T) * k;
-    for (int i = threadIdx.x; i < n; i += blockDim.x) atomicAdd(&cnt[expert_of(ids, i, E)], 1);
+    count_experts(ids, 0, min(kPermBlock, T) * k, E, cnt);
   } else {
     constexpr int kBatch = 16;
     for (int e = threadIdx.x; e < E; e += blockDim.x) {
