@@ -71,6 +71,12 @@ R12 Input quantisation (the per-token FP8 quantisation of the Tile Kernels
     kernel's precision, so codes are bit-exact.  When the layer quantises its
     input, the router reads the unquantised BF16 activations and the experts
     the quantised ones.
+R13 Per-channel weight scales (the per-channel option of the quantisation
+    bullet): an FP8 weight matrix [N, K] may carry one fp32 scale per output
+    channel (row n, all of K) instead of one per 128 x 128 block: value =
+    E4M3(q[n, k]) * s[n].  Only FP8 weights take it (FP4 weights keep the
+    E8M0-per-32 scaling of their format); activations keep their per-token
+    per-128 scales.
 R9  The combine is the weighted sum over j of w[t, j] * expert_output.  The
     reference result is the unrounded fp64 sum; the device sums in fp32 in
     ascending j and rounds the result to BF16.
@@ -94,6 +100,7 @@ class Spec:
                           # "bf16_fp8" (BF16 input quantised to FP8 in the layer, R12)
     weight: str = "fp8"   # "fp8", "fp4" or "bf16"
     scales: str = "f32"   # scales of the layer's own FP8 quantisations: "f32" or "pow2"
+    wscale: str = "block"  # FP8 weight scales: "block" (128 x 128) or "channel" (R13)
 
 
 # ------------------------------------------------------------------ decoding
@@ -118,9 +125,16 @@ def decode_activations(spec: Spec, x, x_scales=None) -> np.ndarray:
 
 
 def decode_weight(spec: Spec, w, w_scales=None) -> np.ndarray:
-    """Dequantise one expert's stored weight matrix [N, K] to fp64 (reading R7)."""
+    """Dequantise one expert's stored weight matrix [N, K] to fp64 (readings
+    R7, R13)."""
     if spec.weight == "bf16":
         return F.bf16_decode(w)
+    if spec.weight == "fp8" and spec.wscale == "channel":
+        q = np.asarray(w, dtype=np.uint8)
+        s = np.asarray(w_scales, dtype=np.float32).astype(np.float64)     # [N]
+        if s.shape != (q.shape[0],):
+            raise ValueError(f"per-channel scales must have shape ({q.shape[0]},), got {s.shape}")
+        return F.E4M3_TABLE[q] * s[:, None]
     if spec.weight == "fp8":
         q = np.asarray(w, dtype=np.uint8)
         N, K = q.shape

@@ -443,3 +443,70 @@ def test_layer_quantising_its_input_equals_prequantised_layer():
     # and the whole layer equals the mask-weighted dense brute force over it
     bf = _dense_bruteforce(spec_q, ov)
     assert np.allclose(rq["y"], bf, rtol=1e-12, atol=1e-12 * np.abs(bf).max())
+
+
+# --------------------------------------------- per-channel FP8 weight scales
+def test_fp8_weight_channel_scale_orientation():
+    # R13: one scale per output row n over all of K.  N != K and every code
+    # 1.0, so a scale applied per K column (or per 128-row block) fails.
+    N, K = 256, 384
+    q = np.full((N, K), 0x38, dtype=np.uint8)
+    s = (np.arange(N, dtype=np.float32) + 1) * 0.25
+    w = O.decode_weight(O.Spec(1, K, 1, 1, N // 2, "fp8", "fp8", wscale="channel"), q, s)
+    for n in (0, 1, 127, 128, 255):
+        assert np.all(w[n] == s[n])
+    with pytest.raises(ValueError):
+        O.decode_weight(O.Spec(1, K, 1, 1, N // 2, "fp8", "fp8", wscale="channel"), q, s[:K // 128])
+
+
+def test_channel_scales_equal_block_scales_constant_along_k():
+    # a block-scaled matrix whose scales do not change along K is the same
+    # matrix with one scale per row (each 128-row block's scale repeated)
+    rng = np.random.default_rng(3)
+    N, K = 256, 512
+    q = rng.integers(0, 256, (N, K), dtype=np.uint8)
+    q[(q & 0x7F) == 0x7F] = 0x38                                # no NaN codes
+    sb = np.repeat(rng.uniform(0.5, 2.0, (N // 128, 1)).astype(np.float32), K // 128, axis=1)
+    sc = np.repeat(sb[:, 0], 128)
+    wb = O.decode_weight(O.Spec(1, K, 1, 1, N // 2, "fp8", "fp8"), q, sb)
+    wc = O.decode_weight(O.Spec(1, K, 1, 1, N // 2, "fp8", "fp8", wscale="channel"), q, sc)
+    assert np.array_equal(wb, wc)
+
+
+def test_onehot_layer_with_channel_scales():
+    # one token, one expert, one nonzero weight per matrix, each with its own
+    # channel scale: y[h2] = silu(a * sg) * (b * su) * (c * sd), up to the
+    # exact-to-fp32 re-quantisation of a one-element block.  A scale taken
+    # from the wrong row (or the gate's scale applied to up) changes it.
+    H, I = 256, 128
+    h1, i1, h2 = 5, 7, 200
+    q_gu = np.zeros((1, 2 * I, H), dtype=np.uint8)
+    q_gu[0, i1, h1] = _fp8_bytes([1.5])[0]
+    q_gu[0, I + i1, h1] = _fp8_bytes([-2.0])[0]
+    q_d = np.zeros((1, H, I), dtype=np.uint8)
+    q_d[0, h2, i1] = _fp8_bytes([0.75])[0]
+    s_gu = np.ones((1, 2 * I), dtype=np.float32)
+    s_gu[0, i1], s_gu[0, I + i1] = 0.5, 4.0
+    s_d = np.ones((1, H), dtype=np.float32)
+    s_d[0, h2] = 0.125
+    x = np.zeros((1, H), dtype=np.uint8)
+    x[0, h1] = 0x38
+    inputs = dict(x=x, x_scales=np.ones((1, H // 128), dtype=np.float32),
+                  router_w=_bf16_bits(np.zeros((1, H))), router_bias=None,
+                  w_gate_up=q_gu, w_gate_up_scales=s_gu, w_down=q_d, w_down_scales=s_d)
+    spec = O.Spec(1, H, 1, 1, I, "fp8", "fp8", wscale="channel")
+    r = O.layer(spec, inputs)
+    g, u = 1.5 * 0.5, -2.0 * 4.0
+    want = g / (1 + math.exp(-g)) * u * (0.75 * 0.125)
+    assert abs(r["y"][0, h2] - want) <= 1e-6 * abs(want)
+    assert np.count_nonzero(r["y"]) == 1
+
+
+def test_layer_with_channel_scales_equals_dense_bruteforce():
+    cfg = G.LayerConfig("pin_chan", 37, 256, 6, 3, 256, "fp8", "fp8", wscale="channel")
+    inp = G.oracle_view(G.make_inputs(cfg, seed=5))
+    spec = G.spec_of(cfg)
+    assert inp["w_gate_up_scales"][0].shape == (2 * cfg.I,) and inp["w_down_scales"][0].shape == (cfg.H,)
+    r = O.layer(spec, inp)
+    ref = _dense_bruteforce(spec, inp)
+    assert np.allclose(r["y"], ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())

@@ -14,7 +14,7 @@ expert), so any one expert's weights can be regenerated alone):
 * router weights Wr ~ N(0, 1/H) [E, H], BF16.
 * gate|up weights ~ N(0, 1/H) stored [E, 2I, H]; down weights ~ N(0, 1/I)
   stored [E, H, I] (K-contiguous).  FP8: one fp32 scale amax / 448 per
-  128 x 128 block.  FP4: one E8M0 scale 2**(floor(log2 amax) - 2) per 32
+  128 x 128 block (or, for per-channel workloads, per output row).  FP4: one E8M0 scale 2**(floor(log2 amax) - 2) per 32
   consecutive K, E2M1 values rounded to nearest, two per byte (even K in the
   low nibble).
 * Skewed workloads add a popularity bias b_e = ln p_e to the router logits,
@@ -46,6 +46,7 @@ class LayerConfig:
     zipf: Optional[float] = None
     note: str = ""
     scales: str = "f32"  # the layer's own FP8 quantisation scales: "f32" or "pow2"
+    wscale: str = "block"  # FP8 weight scales: "block" (128 x 128) or "channel" (one per output row)
 
 
 CONFIGS = {
@@ -68,7 +69,7 @@ def spec_of(cfg: LayerConfig):
     from oracle.moe_oracle import Spec  # imported lazily: tests only
     # BF16 activations with FP8 / FP4 weights: the layer quantises its input
     act = "bf16_fp8" if cfg.act == "bf16" and cfg.weight != "bf16" else cfg.act
-    return Spec(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, act, cfg.weight, cfg.scales)
+    return Spec(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, act, cfg.weight, cfg.scales, cfg.wscale)
 
 
 _TENSOR_IDS = {"x": 1, "router_w": 2, "w_gate_up": 3, "w_down": 4, "zipf_rank": 5,
@@ -117,6 +118,14 @@ def quantise_blocks_fp8(w: torch.Tensor):
     return q.reshape(N, K), s.contiguous()
 
 
+def quantise_channels_fp8(w: torch.Tensor):
+    """[N, K] fp32 -> (uint8 [N, K], fp32 scales [N]): one scale amax / 448
+    per output row."""
+    amax = w.abs().amax(dim=1)
+    s = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+    return _fp8_bytes(w / s[:, None]), s.contiguous()
+
+
 _E2M1_MAGS = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
 
 
@@ -139,11 +148,11 @@ def quantise_fp4(w: torch.Tensor):
     return packed.contiguous(), (e + 127).to(torch.uint8).contiguous()
 
 
-def _quantise_weight(w: torch.Tensor, kind: str):
+def _quantise_weight(w: torch.Tensor, kind: str, wscale: str = "block"):
     if kind == "bf16":
         return w.to(torch.bfloat16), None
     if kind == "fp8":
-        return quantise_blocks_fp8(w)
+        return quantise_channels_fp8(w) if wscale == "channel" else quantise_blocks_fp8(w)
     if kind == "fp4":
         return quantise_fp4(w)
     raise ValueError(kind)
@@ -180,12 +189,12 @@ def make_inputs(cfg: LayerConfig, seed: int = 0, device="cpu") -> dict:
     gu_q, gu_s, d_q, d_s = [], [], [], []
     for e in range(E):
         wgu = _randn((2 * I, H), H ** -0.5, device, _seed(seed, name, "w_gate_up", e))
-        q, s = _quantise_weight(wgu, cfg.weight)
+        q, s = _quantise_weight(wgu, cfg.weight, cfg.wscale)
         gu_q.append(q)
         gu_s.append(s)
         del wgu
         wd = _randn((H, I), I ** -0.5, device, _seed(seed, name, "w_down", e))
-        q, s = _quantise_weight(wd, cfg.weight)
+        q, s = _quantise_weight(wd, cfg.weight, cfg.wscale)
         d_q.append(q)
         d_s.append(s)
         del wd
@@ -233,7 +242,7 @@ def make_exact_layer_inputs(cfg: LayerConfig, seed: int = 0, device="cpu") -> di
     x: FP8 codes of multiples of 0.5 in [-4, 4], scales drawn from
     {1/4, 1/2, 1} (BF16 layers: the same values in BF16).  Router: as
     make_exact_router_inputs.  Weights: FP8 codes of n * 2**-6 (|n| <= 15)
-    with block scales from {1/8 .. 1}; FP4 random E2M1 codes with E8M0 scales
+    with block (or per-channel) scales from {1/8 .. 1}; FP4 random E2M1 codes with E8M0 scales
     2**-6 .. 2**-3; BF16 n * 2**-6.  For H <= 2048 every product is a
     multiple of 2**-12 (FP4: 2**-10) of magnitude below 4, so partial sums stay
     below 2**23 grid units.  The down GEMM is not exact (its intermediate
@@ -259,7 +268,8 @@ def make_exact_layer_inputs(cfg: LayerConfig, seed: int = 0, device="cpu") -> di
         v = torch.randint(-15, 16, (N, K), generator=g).to(torch.float32) * 2.0 ** -6
         if cfg.weight == "bf16":
             return v.to(torch.bfloat16), None
-        sc = 2.0 ** (-torch.randint(0, 4, (N // 128, K // 128), generator=g).to(torch.float32))
+        shape = (N,) if cfg.wscale == "channel" else (N // 128, K // 128)
+        sc = 2.0 ** (-torch.randint(0, 4, shape, generator=g).to(torch.float32))
         return _fp8_bytes(v), sc.contiguous()
 
     gu, gus, d, ds = [], [], [], []
