@@ -12,6 +12,7 @@ bounded sample of the same workload timed on the host cores.
 """
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -200,6 +201,8 @@ def main():
     ap.add_argument("--inter-scale", default="f32", choices=["f32", "pow2"],
                     help="scale rule of the layer's own FP8 quantisations (moe_desc.inter_scale)")
     ap.add_argument("--no-evict", action="store_true", help="skip the cache-evicted per-call timing")
+    ap.add_argument("--wscale", default=None, choices=["block", "channel"],
+                    help="FP8 weight scale granularity (moe_desc.weight_scale; default: the workload's)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): the layer is measured on a "
@@ -211,6 +214,11 @@ def main():
     from workloads import gen
 
     cfg = gen.CONFIGS[args.workload]
+    if args.wscale is not None:
+        if cfg.weight != "fp8" and args.wscale == "channel":
+            print("--wscale channel needs FP8 weights", file=sys.stderr)
+            sys.exit(2)
+        cfg = dataclasses.replace(cfg, wscale=args.wscale)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     print(f"[bench] generating {cfg.name} inputs on {dev}", file=sys.stderr, flush=True)
@@ -288,7 +296,8 @@ def main():
     roof, t_mfma, t_hbm = roofline(cfg, f_exp, f_router, nbytes, t_launch)
     kernel = "k_mega" if args.mode == "mega" else "layer_separate"
     roof["kernel"] = kernel
-    roof["traffic"] = measured_traffic(kernel, cfg.name)
+    # (the committed counter summaries are of the workloads' own weight scales)
+    roof["traffic"] = measured_traffic(kernel, cfg.name) if cfg == gen.CONFIGS[cfg.name] else None
     tflops = (f_exp + f_router) / (ms / 1e3) / 1e12
     exp_fmt = cfg.weight if cfg.weight == "bf16" else "fp8"
     result = {
@@ -306,7 +315,7 @@ def main():
         "data": "synthetic (seeded N(0,1) activations, N(0,1/fan_in) weights, quantised; no real weights)",
         "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "E": cfg.E, "top_k": cfg.k, "I": cfg.I,
                    "act": cfg.act, "weight": cfg.weight, "zipf": cfg.zipf, "mode": args.mode,
-                   "inter_scale": args.inter_scale,
+                   "inter_scale": args.inter_scale, "weight_scale": cfg.wscale,
                    "active_experts": active},
         "tflops": round(tflops, 1),
         "mfma_peak_frac": round(tflops / PEAK_TFLOPS[exp_fmt], 4),

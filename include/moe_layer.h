@@ -31,11 +31,14 @@
  *                     [E][2I][H/2] FP4 E2M1, two per byte, even K in the low nibble
  *                     -- passed to moe_forward in the MFMA-tiled layout below
  *   w_gate_up_scales  [E][2I/128][H/128] fp32 (FP8, one per 128x128 block)
+ *                     [E][2I]            fp32 (FP8 with MOE_WSCALE_CHANNEL:
+ *                                        one per output channel, all of K)
  *                     [E][2I][H/32]      E8M0 bytes (FP4, one per 32 along K;
  *                                        MFMA-tiled for moe_forward)
  *                     NULL for BF16
  *   w_down            [E][H][I] (BF16 / FP8) or [E][H][I/2] (FP4), MFMA-tiled
- *   w_down_scales     [E][H/128][I/128] fp32 (FP8) or [E][H][I/32] E8M0 (FP4,
+ *   w_down_scales     [E][H/128][I/128] fp32 (FP8), [E][H] fp32 (FP8 with
+ *                     MOE_WSCALE_CHANNEL) or [E][H][I/32] E8M0 (FP4,
  *                     MFMA-tiled)
  *   y                 [T][H]    BF16 (output)
  *   topk_ids          [T][top_k] int32 (output; input with MOE_FLAG_ROUTING_GIVEN)
@@ -98,7 +101,8 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3   /* 3: moe_desc.weight_layout and moe_desc.inter_scale */
+#define MOE_ABI_VERSION 4   /* 3: moe_desc.weight_layout and moe_desc.inter_scale;
+                               4: moe_desc.weight_scale */
 
 typedef enum moe_status {
   MOE_OK = 0,
@@ -143,6 +147,17 @@ typedef enum moe_inter_scale {
   MOE_INTER_SCALE_POW2 = 1        /* s = the smallest power of two >= amax / 448      */
 } moe_inter_scale;
 
+/* Granularity of FP8 weight scales (FP8 weights only; FP4 weights always
+ * carry E8M0 scales per 32 along K, BF16 none).  The per-block and
+ * per-channel options of youleyou, "DeepSeek 模型更新解读 Tile Kernels 与
+ * DeepEP V2 新特性", section "Tile Kernels", quantisation bullet.  Channel
+ * scales are applied once to each output after its K sum, block scales to
+ * each 128-wide K block's partial sum. */
+typedef enum moe_weight_scale {
+  MOE_WSCALE_BLOCK = 0,           /* fp32 per 128 x 128 block of [N][K]        */
+  MOE_WSCALE_CHANNEL = 1          /* fp32 per output channel (row n of [N][K]) */
+} moe_weight_scale;
+
 typedef struct moe_desc {
   int32_t T;             /* tokens                                   */
   int32_t H;             /* hidden size (K of linear 1, N of linear 2) */
@@ -155,6 +170,7 @@ typedef struct moe_desc {
   int32_t flags;         /* MOE_FLAG_*                               */
   int32_t weight_layout; /* moe_weight_layout of the expert weights  */
   int32_t inter_scale;   /* moe_inter_scale                          */
+  int32_t weight_scale;  /* moe_weight_scale (FP8 weights)           */
 } moe_desc;
 
 typedef void* moe_stream_t;   /* hipStream_t */

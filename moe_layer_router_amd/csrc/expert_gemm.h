@@ -62,6 +62,7 @@ struct GemmArgs {
   int T, H, E, I, k;
   int pow2;                  // re-quantise the intermediate with power-of-two scales
   int pow2_x;                // the activation scales are powers of two (the layer's own quantisation)
+  int wchan;                 // FP8 weights: one fp32 scale per output channel ([E][N]), not per block
 };
 
 constexpr int kGemmThreads = 256;
@@ -224,10 +225,15 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
     boff[cs] = (uint32_t)ntc * 16u * BS + 16u * lane;
     bsoff[cs] = (uint32_t)ntc * 64u + lane;
   }
-  // fp32 weight-scale rows (FP8): two 128-blocks of N per item
+  // fp32 weight-scale rows (FP8): two 128-blocks of N per item; or, with
+  // per-channel scales, the scales of the item's 256 B-columns (applied in
+  // the epilogue, after the K sum)
   const int sb0 = (STAGE == 1) ? c0 / 128 : n0 / 128;
   const int sb1 = (STAGE == 1) ? (g.I + c0) / 128 : min(n0 / 128 + 1, g.H / 128 - 1);
-  const float* wsc = (WF == W_FP8) ? reinterpret_cast<const float*>(Sbase) + (size_t)e * (N / 128) * ksb : nullptr;
+  const bool wchan = WF == W_FP8 && g.wchan != 0;
+  const float* wsc = (WF == W_FP8) ? reinterpret_cast<const float*>(Sbase) +
+                                         (size_t)e * (wchan ? (size_t)N : (size_t)(N / 128) * ksb)
+                                   : nullptr;
 
   __syncthreads();                                 // LDS of the previous item is free
   if (tid < R) {
@@ -240,10 +246,16 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
       ROWW[tid] = (tid < m) ? g.topk_w[p] : 0.f;
     }
   }
-  // the item's two rows of FP8 weight block scales (K <= 16384: <= 128 blocks)
+  // the item's two rows of FP8 weight block scales (K <= 16384: <= 128
+  // blocks), or its columns' channel scales: SCW[c] for item column c
+  // (gate|up: gate channel c0 + c for c < 128, up channel I + c0 + c - 128;
+  // down: output column n0 + c, past H reading the last one)
   if (WF == W_FP8 && AF == ACT_FP8) {
     const int set = tid >> 7, kb = tid & 127;
-    if (kb < nsteps) SCW[tid] = wsc[(size_t)(set ? sb1 : sb0) * ksb + kb];
+    if (wchan)
+      SCW[tid] = wsc[(STAGE == 1) ? (set ? g.I : 0) + c0 + kb : min(n0 + tid, g.H - 1)];
+    else if (kb < nsteps)
+      SCW[tid] = wsc[(size_t)(set ? sb1 : sb0) * ksb + kb];
   }
   __syncthreads();
 
@@ -311,8 +323,8 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
   auto store_scale = [&](int s, int par, float sa) __attribute__((always_inline)) {   // par = s & 1
     if (AF != ACT_FP8) return;
     const int sc = min(s, nsteps - 1);             // steps past the end are never used
-    const float w0 = (WF == W_FP8) ? SCW[sc] : 1.f;
-    const float w1 = (WF == W_FP8) ? SCW[128 + sc] : 1.f;
+    const float w0 = (WF == W_FP8 && !wchan) ? SCW[sc] : 1.f;
+    const float w1 = (WF == W_FP8 && !wchan) ? SCW[128 + sc] : 1.f;
     // no branch here: a conditional block would let the compiler sink the
     // step's MFMAs below the step's closing barrier
     // spare threads write to the unused positions past 16 * kScStride
@@ -578,6 +590,22 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
   const rsrc_t saw = make_rsrc(g.sa, nrows * (uint32_t)(g.I / 128) * 4);
   const rsrc_t stw = make_rsrc(g.staging, nrows * (uint32_t)g.H * 2);
   if (STAGE == 1) {
+    if (WF == W_FP8 && AF == ACT_FP8 && wchan) {
+      // per-channel weight scales: lane holds channels 32w + 16q + 4gq + v
+      // of the item's gate (acc[rs][q]) and up (acc[rs][2 + q]) columns
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const v4f sg = lds_ld<v4f>(lds, L::kScw + (32 * w + 16 * q + 4 * gq) * 4);
+        const v4f su = lds_ld<v4f>(lds, L::kScw + (128 + 32 * w + 16 * q + 4 * gq) * 4);
+#pragma unroll
+        for (int rs = 0; rs < RS; ++rs)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            acc[rs][q][v] *= sg[v];
+            acc[rs][2 + q][v] *= su[v];
+          }
+      }
+    }
     // a = SiLU(g) * u, written over the gate accumulators: av[rs][q] = acc[rs][q]
 #pragma unroll
     for (int rs = 0; rs < RS; ++rs) {
@@ -657,6 +685,17 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
       });
     }
   } else if (AF == ACT_FP8) {
+    if (WF == W_FP8 && wchan) {
+      // per-channel weight scales of the lane's columns 64w + 16cs + 4gq + v
+#pragma unroll
+      for (int cs = 0; cs < 4; ++cs) {
+        const v4f sn = lds_ld<v4f>(lds, L::kScw + (64 * w + 16 * cs + 4 * gq) * 4);
+#pragma unroll
+        for (int rs = 0; rs < RS; ++rs)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[rs][cs][v] *= sn[v];
+      }
+    }
     // lane: row rs*16 + c16, columns 64w + 16cs + 4gq + v of the N block.
     // The whole tile (up to 128 rows x 256 columns of BF16 = 64 KB, the A
     // stages' space) is staged at once; chunk c (16 bytes) of staging row r

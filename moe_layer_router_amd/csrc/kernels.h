@@ -28,6 +28,7 @@ struct Plan {
   int act_fp8, wdt;            // ACT_*, W_* (act_fp8: the expert GEMMs read FP8 activations)
   int quant_in;                // BF16 input quantised in the layer: router reads xb, experts x
   int pow2;                    // power-of-two scales for the layer's own quantisations
+  int wchan;                   // FP8 weights with one scale per output channel
   int routing_given;
   int nblk;                    // 256-token blocks
   int nTR, nER;                // router tiles (kRouterTokens x kRouterExperts)
@@ -96,6 +97,7 @@ __host__ __device__ inline GemmArgs gemm_args(const Plan& p) {
   g.aq = p.aq; g.sa = p.sa; g.staging = p.staging; g.sxp = p.sxp;
   g.T = p.T; g.H = p.H; g.E = p.E; g.I = p.I; g.k = p.k;
   g.pow2 = p.pow2;
+  g.wchan = p.wchan;
   g.pow2_x = p.pow2 && p.quant_in;
   return g;
 }

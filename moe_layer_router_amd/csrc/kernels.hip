@@ -611,6 +611,10 @@ moe_status check_desc(const moe_desc* d) {
     return fail(MOE_ERR_INVALID_ARGUMENT, "unknown weight_layout %d", d->weight_layout);
   if (d->inter_scale != MOE_INTER_SCALE_F32 && d->inter_scale != MOE_INTER_SCALE_POW2)
     return fail(MOE_ERR_INVALID_ARGUMENT, "unknown inter_scale %d", d->inter_scale);
+  if (d->weight_scale != MOE_WSCALE_BLOCK && d->weight_scale != MOE_WSCALE_CHANNEL)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "unknown weight_scale %d", d->weight_scale);
+  if (d->weight_scale == MOE_WSCALE_CHANNEL && d->weight_dtype != MOE_DTYPE_FP8_E4M3)
+    return fail(MOE_ERR_UNSUPPORTED, "per-channel weight scales need FP8 weights (weight_dtype=%d)", d->weight_dtype);
   return MOE_OK;
 }
 
@@ -686,6 +690,7 @@ moe_status fill_plan(const moe_desc* d, const Layout& L, char* ws, Plan* P) {
   p.quant_in = d->act_dtype == MOE_DTYPE_BF16 && d->weight_dtype != MOE_DTYPE_BF16;
   p.act_fp8 = d->act_dtype == MOE_DTYPE_FP8_E4M3 || p.quant_in;
   p.pow2 = d->inter_scale == MOE_INTER_SCALE_POW2;
+  p.wchan = d->weight_scale == MOE_WSCALE_CHANNEL;
   p.wdt = d->weight_dtype == MOE_DTYPE_FP8_E4M3 ? W_FP8 : d->weight_dtype == MOE_DTYPE_FP4_E2M1 ? W_FP4 : W_BF16;
   p.routing_given = (d->flags & MOE_FLAG_ROUTING_GIVEN) != 0;
   p.nblk = L.nblk; p.nTR = L.nTR; p.nER = L.nER; p.nKS = L.nKS; p.max_tiles = L.max_tiles;

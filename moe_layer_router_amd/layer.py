@@ -45,7 +45,10 @@ def desc_from_inputs(inputs: dict, top_k: int, mode: str = "mega", flags: int = 
         weight = "fp4"
     if layout is None:
         layout = "tiled" if inputs.get("weights_packed") else "row_major"
-    return lib.make_desc(T, H, E, I, top_k, act, weight, mode, flags, layout, inter_scale)
+    # FP8 weight scales: [E][N/128][K/128] per block, [E][N] per output channel
+    sc = inputs.get("w_gate_up_scales")
+    wscale = "channel" if weight == "fp8" and sc is not None and sc.dim() == 2 else "block"
+    return lib.make_desc(T, H, E, I, top_k, act, weight, mode, flags, layout, inter_scale, wscale)
 
 
 class Workspace:

@@ -50,6 +50,9 @@ MOE_LAYOUT_TILED = 1
 # moe_inter_scale
 MOE_INTER_SCALE_F32 = 0
 MOE_INTER_SCALE_POW2 = 1
+# moe_weight_scale
+MOE_WSCALE_BLOCK = 0
+MOE_WSCALE_CHANNEL = 1
 # moe_peak_kind
 MOE_PEAK_KINDS = {"mfma16_fp8_fp8": 0, "mfma16_fp4_fp8": 1, "mfma16_fp4_fp4": 2, "mfma16_bf16": 3,
                   "mfma32_fp8_fp8": 4, "mfma32_fp4_fp8": 5}
@@ -65,7 +68,8 @@ class MoeDesc(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("E", ctypes.c_int32),
                 ("I", ctypes.c_int32), ("top_k", ctypes.c_int32), ("act_dtype", ctypes.c_int32),
                 ("weight_dtype", ctypes.c_int32), ("mode", ctypes.c_int32), ("flags", ctypes.c_int32),
-                ("weight_layout", ctypes.c_int32), ("inter_scale", ctypes.c_int32)]
+                ("weight_layout", ctypes.c_int32), ("inter_scale", ctypes.c_int32),
+                ("weight_scale", ctypes.c_int32)]
 
 
 class MoeWorkspaceRegions(ctypes.Structure):
@@ -118,12 +122,14 @@ _lib.moe_last_error.argtypes = []
 
 LAYOUTS = {"row_major": MOE_LAYOUT_ROW_MAJOR, "tiled": MOE_LAYOUT_TILED}
 INTER_SCALES = {"f32": MOE_INTER_SCALE_F32, "pow2": MOE_INTER_SCALE_POW2}
+WEIGHT_SCALES = {"block": MOE_WSCALE_BLOCK, "channel": MOE_WSCALE_CHANNEL}
 
 
 def make_desc(T, H, E, I, top_k, act="fp8", weight="fp8", mode="mega", flags=0, layout="tiled",
-              inter_scale="f32") -> MoeDesc:
+              inter_scale="f32", wscale="block") -> MoeDesc:
     return MoeDesc(T, H, E, I, top_k, DTYPES[act], DTYPES[weight], MODES.get(mode, mode), flags,
-                   LAYOUTS.get(layout, layout), INTER_SCALES.get(inter_scale, inter_scale))
+                   LAYOUTS.get(layout, layout), INTER_SCALES.get(inter_scale, inter_scale),
+                   WEIGHT_SCALES.get(wscale, wscale))
 
 
 def _ptr(t):

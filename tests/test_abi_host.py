@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert lib.moe_abi_version() == 3
+    assert lib.moe_abi_version() == 4
     assert lib.moe_status_string(lib.MOE_OK) == "MOE_OK"
     assert lib.moe_status_string(lib.MOE_ERR_WORKSPACE_TOO_SMALL) == "MOE_ERR_WORKSPACE_TOO_SMALL"
 
@@ -163,3 +163,14 @@ def test_quantize_input_rejects_bad_arguments_without_device():
     assert q(4, 256, lib.MOE_DTYPE_F32, 0, None, A, A, None) == lib.MOE_ERR_INVALID_ARGUMENT
     assert q(4, 256, lib.MOE_DTYPE_F32, 0, A, A + 4, A, None) == lib.MOE_ERR_INVALID_ARGUMENT
     assert q(1 << 20, 4096, lib.MOE_DTYPE_F32, 0, A, A, A, None) == lib.MOE_ERR_UNSUPPORTED
+
+
+def test_weight_scale_granularity():
+    # per-channel scales: FP8 weights only; unknown values are rejected
+    assert _validate(lib.make_desc(100, 512, 16, 256, 4, "fp8", "fp8", wscale="channel")) == lib.MOE_OK
+    assert _validate(lib.make_desc(100, 512, 16, 256, 4, "fp8", "fp4", wscale="channel")) == lib.MOE_ERR_UNSUPPORTED
+    assert _validate(lib.make_desc(64, 256, 8, 128, 2, "bf16", "bf16", wscale="channel"), x_scales=None,
+                     w_gate_up_scales=None, w_down_scales=None) == lib.MOE_ERR_UNSUPPORTED
+    assert _validate(lib.make_desc(100, 512, 16, 256, 4, "fp8", "fp8", wscale=7)) == lib.MOE_ERR_INVALID_ARGUMENT
+    assert lib.moe_workspace_size(lib.make_desc(100, 512, 16, 256, 4, "fp8", "fp8", wscale="channel")) == \
+        lib.moe_workspace_size(lib.make_desc(100, 512, 16, 256, 4, "fp8", "fp8"))

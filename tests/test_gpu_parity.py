@@ -127,6 +127,10 @@ SMALL = [
     gen.LayerConfig("s_fp8_pow2", 300, 512, 16, 4, 256, "fp8", "fp8", scales="pow2"),
     gen.LayerConfig("s_fp4_pow2", 600, 512, 16, 4, 384, "fp8", "fp4", scales="pow2"),
     gen.LayerConfig("s_bf16in_fp4_pow2", 300, 1024, 8, 2, 256, "bf16", "fp4", scales="pow2"),
+    # per-channel FP8 weight scales (one per output row), applied after the K sum
+    gen.LayerConfig("s_fp8_chan", 300, 512, 16, 4, 256, "fp8", "fp8", wscale="channel"),
+    gen.LayerConfig("s_chan_multitile", 600, 384, 4, 2, 384, "fp8", "fp8", wscale="channel"),   # H % 256 != 0
+    gen.LayerConfig("s_bf16in_fp8_chan", 300, 512, 16, 4, 256, "bf16", "fp8", wscale="channel", scales="pow2"),
 ]
 
 
@@ -173,6 +177,7 @@ EXACT = [
     gen.LayerConfig("x_fp8", 300, 1024, 16, 4, 256, "fp8", "fp8"),
     gen.LayerConfig("x_fp4", 300, 1024, 16, 4, 256, "fp8", "fp4"),
     gen.LayerConfig("x_bf16", 200, 512, 8, 2, 256, "bf16", "bf16"),
+    gen.LayerConfig("x_fp8_chan", 300, 1024, 16, 4, 256, "fp8", "fp8", wscale="channel"),
 ]
 
 
@@ -231,9 +236,10 @@ POW2_EXACT = gen.LayerConfig("x_fp8_pow2", 300, 1024, 16, 4, 256, "fp8", "fp8", 
 
 @pytest.mark.parametrize("cfg,exact", [(SMALL[0], False), (SMALL[1], False), (SMALL[4], False), (SMALL[2], False),
                                        (EXACT[0], True), (EXACT[1], True), (EXACT[2], True),
-                                       (SMALL[12], False), (POW2_EXACT, True)],
+                                       (SMALL[12], False), (POW2_EXACT, True), (SMALL[15], False), (SMALL[16], False),
+                                       (EXACT[3], True)],
                          ids=["s_fp8", "s_fp4", "s_multitile", "s_bf16", "x_fp8", "x_fp4", "x_bf16", "s_fp8_pow2",
-                              "x_fp8_pow2"])
+                              "x_fp8_pow2", "s_fp8_chan", "s_chan_multitile", "x_fp8_chan"])
 def test_intermediate_matches_oracle(L, cfg, exact):
     """Gate|up GEMM, SwiGLU and the per-128 FP8 re-quantisation, row by row.
     The device's scales lie in the oracle's derived scale window and its E4M3
