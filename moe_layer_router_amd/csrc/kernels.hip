@@ -225,17 +225,25 @@ DEV void signal_coherent(int32_t* c0, int32_t* c1 = nullptr) {
 // distinct descriptors and loops over plan sizes would run as divergent
 // loops.  Every argument is wave-uniform, so each phase starts by taking
 // them from the first lane.
-static_assert(sizeof(Plan) % 4 == 0, "plan words");
-DEV Plan uniform_plan(const Plan& in) {
-  uint32_t w[sizeof(Plan) / 4];
-  __builtin_memcpy(w, &in, sizeof(Plan));
-#pragma unroll
-  for (int i = 0; i < (int)(sizeof(Plan) / 4); ++i) w[i] = uni(w[i]);
+DEV int uni_i(int v) { return __builtin_amdgcn_readfirstlane(v); }
+// The phases get the plan as a pointer to the persistent kernel's own
+// argument in the kernarg segment (constant memory): taken from the first
+// lane, its fields come through the scalar cache.  A plan passed by value
+// would be copied through every lane's scratch memory on each call.
+typedef const __attribute__((address_space(4))) Plan KPlan;
+DEV Plan load_plan(KPlan* pv) {
+  const uint64_t a = reinterpret_cast<uint64_t>(pv);
+  const uint64_t u = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) << 32) |
+                     (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+  typedef const __attribute__((address_space(4))) uint32_t KWord;
+  KWord* src = (KWord*)u;
+  static_assert(sizeof(Plan) % 4 == 0, "plan words");
   Plan p;
-  __builtin_memcpy(&p, w, sizeof(Plan));
+  uint32_t* dst = reinterpret_cast<uint32_t*>(&p);
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(Plan) / 4); ++i) dst[i] = src[i];
   return p;
 }
-DEV int uni_i(int v) { return __builtin_amdgcn_readfirstlane(v); }
 // The GEMM items are inlined into the kernel: as a called function they
 // would save and restore the callee-saved VGPRs they use on every item.
 // Tiles as the GEMM phases read them: through the scalar cache, as k_gemm
@@ -263,9 +271,9 @@ __device__ __forceinline__ void mega_gemm_item(const Plan& p, Tile tl, int nb, i
   expert_gemm_item<AF, WF, STAGE, 1>(gemm_args(p), tl, nb, lds, signal_prev, at_loop_end);
 }
 template <int AF>
-__device__ __noinline__ void mega_router_item(Plan pv, int tt_, int et_, int ks_) {
+__device__ __noinline__ void mega_router_item(KPlan* pv, int tt_, int et_, int ks_) {
   MEGA_LDS;
-  const Plan p = uniform_plan(pv);
+  const Plan p = load_plan(pv);
   const int tt = uni_i(tt_), et = uni_i(et_), ks = uni_i(ks_);
   int s0, s1;
   router_slice(p.H, ks, p.nKS, &s0, &s1);
@@ -280,8 +288,8 @@ __device__ __noinline__ void mega_router_item(Plan pv, int tt_, int et_, int ks_
   }
 }
 constexpr int kQuantItemBlocks = 256;     // 128-channel blocks per quantisation item
-__device__ __noinline__ void mega_quant_item(Plan pv, int i_) {
-  const Plan p = uniform_plan(pv);
+__device__ __noinline__ void mega_quant_item(KPlan* pv, int i_) {
+  const Plan p = load_plan(pv);
   const int b0 = uni_i(i_) * kQuantItemBlocks;
   quant_blocks<QIN_BF16, kCoherent>(p.xb, p.T, p.H, b0, min(p.T * (p.H / 128), b0 + kQuantItemBlocks),
                                     p.pow2 != 0, const_cast<uint8_t*>(p.x), const_cast<float*>(p.x_scales),
@@ -290,8 +298,8 @@ __device__ __noinline__ void mega_quant_item(Plan pv, int i_) {
 // Part `part` of kReduceParts of the sum of router tile (tt, et)'s channel
 // slices (run once every slice of the tile is done).
 constexpr int kReduceParts = 8;
-__device__ __noinline__ void mega_reduce_item(Plan pv, int tt_, int et_, int part_) {
-  const Plan p = uniform_plan(pv);
+__device__ __noinline__ void mega_reduce_item(KPlan* pv, int tt_, int et_, int part_) {
+  const Plan p = load_plan(pv);
   const int tt = uni_i(tt_), et = uni_i(et_), part = uni_i(part_);
   RouterArgs ra{p.x, p.x_scales, p.wr, p.bias, p.logits, p.T, p.H, p.E, p.act_fp8};
   const int t0 = tt * kRouterTokens, e0 = et * kRouterExperts;
@@ -300,32 +308,32 @@ __device__ __noinline__ void mega_reduce_item(Plan pv, int tt_, int et_, int par
   router_sum_slices(ra, t0, e0, p.nKS, min(n, part * per), min(n, (part + 1) * per));
 }
 constexpr int kTopkItemTokens = 16;        // tokens per top-k item of the persistent kernel
-__device__ __noinline__ void mega_topk_item(Plan pv, int i) {
-  const Plan p = uniform_plan(pv);
+__device__ __noinline__ void mega_topk_item(KPlan* pv, int i) {
+  const Plan p = load_plan(pv);
   const int t0 = uni_i(i) * kTopkItemTokens;
   topk_tokens(p.logits, p.E, p.k, t0, min(kTopkItemTokens, p.T - t0), p.ids, p.wts);
 }
-__device__ __noinline__ void mega_count_item(Plan pv, int b_) {
+__device__ __noinline__ void mega_count_item(KPlan* pv, int b_) {
   MEGA_LDS;
-  const Plan p = uniform_plan(pv);
+  const Plan p = load_plan(pv);
   const int b = uni_i(b_);
   perm_count_block(p.ids, p.T, p.k, p.E, b, p.blockcnt, reinterpret_cast<int*>(lds));
 }
-__device__ __noinline__ void mega_scatter_item(Plan pv, int b_) {
+__device__ __noinline__ void mega_scatter_item(KPlan* pv, int b_) {
   MEGA_LDS;
-  const Plan p = uniform_plan(pv);
+  const Plan p = load_plan(pv);
   const int b = uni_i(b_);
   perm_scan_scatter_block(p.ids, p.T, p.k, p.E, b, p.nblk, p.blockcnt, p.tile_rows, p.offsets, p.tiles, p.meta,
                           p.perm, p.row_of, lds);
 }
 constexpr int kSxpRows = 256;             // permuted rows per activation-scale item
-__device__ __noinline__ void mega_sxp_item(Plan pv, int i_) {
-  const Plan p = uniform_plan(pv);
+__device__ __noinline__ void mega_sxp_item(KPlan* pv, int i_) {
+  const Plan p = load_plan(pv);
   const int r0 = uni_i(i_) * kSxpRows;
   permute_scales(p.perm, p.x_scales, p.T, p.k, p.H / 128, r0, min(p.T * p.k, r0 + kSxpRows), p.sxp);
 }
-__device__ __noinline__ void mega_combine_item(Plan pv, int nb_, int c) {
-  const Plan p = uniform_plan(pv);
+__device__ __noinline__ void mega_combine_item(KPlan* pv, int nb_, int c) {
+  const Plan p = load_plan(pv);
   const int nb = uni_i(nb_), t0 = uni_i(c) * kCombineTokens;
   combine_rows(p.staging, p.y, p.T, p.H, p.k, t0, min(p.T, t0 + kCombineTokens), nb * 256,
                   min(p.H, nb * 256 + 256));
@@ -336,6 +344,7 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_wav
 k_mega(Plan p) {
   __shared__ int s_q, s_ok, s_first[kXcds + 1];
   const int tid = threadIdx.x;
+  KPlan* const pk = (KPlan*)__builtin_amdgcn_kernarg_segment_ptr();   // p itself (the only argument)
   trace_stamp(p.trace, 0);
   const int nR = p.routing_given ? 0 : p.nTR * p.nER * p.nKS;
   // with the router's channels in slices, kReduceParts items per router tile
@@ -365,33 +374,33 @@ k_mega(Plan p) {
     __syncthreads();
     if (q >= q_end) break;
     if (q < q_rt) {
-      mega_quant_item(p, q);
+      mega_quant_item(pk, q);
       signal_coherent(&p.ctr[CTR_QUANT_DONE]);
     } else if (q < q_red) {
       const int r = q - q_rt;
       const int per_tt = p.nER * p.nKS;
       const int tt = r / per_tt, et = (r % per_tt) / p.nKS, ks = r % p.nKS;
-      mega_router_item<AF>(p, tt, et, ks);
+      mega_router_item<AF>(pk, tt, et, ks);
       signal_coherent(p.nKS == 1 ? &p.rdone[tt] : &p.rtile[tt * p.nER + et]);
     } else if (q < q_topk) {
       const int r = q - q_red, tile = r / kReduceParts;   // tile = tt * nER + et
       if (!wait_counter(&p.rtile[tile], p.nKS, p.err, &s_ok, false)) return;
-      mega_reduce_item(p, tile / p.nER, tile % p.nER, r % kReduceParts);
+      mega_reduce_item(pk, tile / p.nER, tile % p.nER, r % kReduceParts);
       signal_coherent(&p.rdone[tile / p.nER]);
     } else if (q < q_count) {
       const int i = q - q_topk;                          // tokens [16i, 16i+16)
       if (!wait_counter(&p.rdone[i / (kRouterTokens / kTopkItemTokens)], rdone_target, p.err, &s_ok, false)) return;
-      mega_topk_item(p, i);
+      mega_topk_item(pk, i);
       signal_coherent(&p.tkdone[i / (kPermBlock / kTopkItemTokens)]);
     } else if (q < q_scat) {
       const int b = q - q_count;
       if (!p.routing_given && !wait_counter(&p.tkdone[b], min(kPer, nK - kPer * b), p.err, &s_ok, false)) return;
-      mega_count_item(p, b);
+      mega_count_item(pk, b);
       signal_coherent(&p.ctr[CTR_COUNT_DONE]);
     } else if (q >= q_sxp) {
       if (!wait_counter(&p.ctr[CTR_SCATTER_DONE], p.nblk, p.err, &s_ok, false)) return;
       if (nQ > 0 && !wait_counter(&p.ctr[CTR_QUANT_DONE], nQ, p.err, &s_ok, false)) return;
-      mega_sxp_item(p, q - q_sxp);
+      mega_sxp_item(pk, q - q_sxp);
       signal_coherent(&p.ctr[CTR_SXP_DONE]);
     } else {
       // scan and scatter of one block, once every histogram is in (or, with
@@ -402,7 +411,7 @@ k_mega(Plan p) {
       } else if (!p.routing_given && !wait_counter(&p.tkdone[0], nK, p.err, &s_ok, false)) {
         return;
       }
-      mega_scatter_item(p, b);
+      mega_scatter_item(pk, b);
       signal_coherent(&p.ctr[CTR_SCATTER_DONE]);
     }
   }
@@ -480,7 +489,7 @@ k_mega(Plan p) {
     if (i >= p.nnb2 * p.nCT) break;
     const int nb = i / p.nCT, c = i % p.nCT;
     if (!wait_counter(&p.done2[nb], ntiles, p.err, &s_ok, false)) return;
-    mega_combine_item(p, nb, c);
+    mega_combine_item(pk, nb, c);
   }
   trace_stamp(p.trace, 5);
 }
