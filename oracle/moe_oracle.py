@@ -77,6 +77,15 @@ R13 Per-channel weight scales (the per-channel option of the quantisation
     E4M3(q[n, k]) * s[n].  Only FP8 weights take it (FP4 weights keep the
     E8M0-per-32 scaling of their format); activations keep their per-token
     per-128 scales.
+R14 The backward pass (the training workload of the pages: trainable
+    layers in the Tile Kernels section's model-layer bullet) is the exact
+    gradient of the layer with the routing held fixed (the selection is
+    piecewise constant) and every rounding of the forward pass (the
+    intermediate's re-quantisation or BF16 rounding) passed straight through
+    as the identity: y[t] = sum_j w[t, j] * SwiGLU(x[t] W_gu[e]^T) W_d[e]^T
+    with e = ids[t, j] and w the softmax of the selected logits
+    l = x_r W_r^T + b.  The router's gradient reaches x through the logits
+    (x_r is the router's input, R3).
 R9  The combine is the weighted sum over j of w[t, j] * expert_output.  The
     reference result is the unrounded fp64 sum; the device sums in fp32 in
     ascending j and rounds the result to BF16.
@@ -614,3 +623,90 @@ def layer(spec: Spec, inputs: dict, ids=None, tokens=None, inter=None, inter_sca
         y[out_row[toks]] += wt[:, None] * O
     return dict(y=y, logits=logits, ids=ids, weights=w, counts=counts,
                 offsets=offsets, perm=perm, row_of=row_of, xhat=xhat)
+
+
+# ------------------------------------------------------------------ backward
+def silu_grad(z: np.ndarray) -> np.ndarray:
+    """d/dz SiLU(z) = sigma(z) * (1 + z * (1 - sigma(z)))."""
+    sg = 1.0 / (1.0 + np.exp(-z))
+    return sg * (1.0 + z * (1.0 - sg))
+
+
+def forward_exact(xh, xr, wr, b, w_gu, w_d, ids, I: int) -> np.ndarray:
+    """The layer as a function of fp64 parameters, no rounding anywhere (R14):
+    xh [T, H] the experts' input, xr [T, H] the router's input, wr [E, H],
+    b [E], w_gu [E, 2I, H], w_d [E, H, I], ids [T, k] fixed."""
+    logits = xr @ wr.T + b[None, :]
+    w = topk_weights(logits, ids)
+    T, k = ids.shape
+    y = np.zeros((T, w_d.shape[1]))
+    for t in range(T):
+        for j in range(k):
+            e = ids[t, j]
+            gu = w_gu[e] @ xh[t]
+            y[t] += w[t, j] * (w_d[e] @ swiglu(gu[:I], gu[I:]))
+    return y
+
+
+def backward_exact(xh, xr, wr, b, w_gu, w_d, ids, dy, I: int) -> dict:
+    """Gradients of sum(dy * forward_exact(...)) (R14), token by token:
+
+    dw[t, j]  = <dy[t], o>,  o = SwiGLU(g, u) W_d[e]^T
+    dW_d[e]  += w[t, j] dy[t]^T a             (a = SwiGLU(g, u))
+    da        = w[t, j] dy[t] W_d[e]
+    dg        = da * u * SiLU'(g),  du = da * SiLU(g)
+    dW_gu[e] += [dg; du]^T xh[t],  dx[t] += [dg; du] W_gu[e]
+    dl[t, j]  = w[t, j] (dw[t, j] - sum_i w[t, i] dw[t, i])   (softmax over the selection)
+    dW_r[e]  += dl[t, j] xr[t],  db[e] += dl[t, j],  dxr[t] += dl[t, j] W_r[e]
+
+    dx is the gradient of the layer's input: the experts' and the router's
+    parts added (any quantisation between the input and either reader passes
+    straight through, R14)."""
+    logits = xr @ wr.T + b[None, :]
+    w = topk_weights(logits, ids)
+    T, k = ids.shape
+    H = xh.shape[1]
+    dx = np.zeros_like(xh)
+    dxr = np.zeros_like(xr)
+    dw_gu = np.zeros_like(w_gu)
+    dw_d = np.zeros_like(w_d)
+    dwr = np.zeros_like(wr)
+    db = np.zeros_like(b)
+    dws = np.zeros((T, k))
+    for t in range(T):
+        for j in range(k):
+            e = ids[t, j]
+            gu = w_gu[e] @ xh[t]
+            g, u = gu[:I], gu[I:]
+            a = swiglu(g, u)
+            dws[t, j] = dy[t] @ (w_d[e] @ a)
+            dw_d[e] += w[t, j] * np.outer(dy[t], a)
+            da = w[t, j] * (dy[t] @ w_d[e])
+            dgu = np.concatenate([da * u * silu_grad(g), da * silu(g)])
+            dw_gu[e] += np.outer(dgu, xh[t])
+            dx[t] += dgu @ w_gu[e]
+        dl = w[t] * (dws[t] - w[t] @ dws[t])
+        for j in range(k):
+            e = ids[t, j]
+            dwr[e] += dl[j] * xr[t]
+            db[e] += dl[j]
+            dxr[t] += dl[j] * wr[e]
+    return dict(dx=dx + dxr, dx_experts=dx, dx_router=dxr, dw_gate_up=dw_gu, dw_down=dw_d, dw_router=dwr, dbias=db, dweights=dws)
+
+
+def layer_backward(spec: Spec, inputs: dict, ids, dy) -> dict:
+    """The backward pass of the layer (R14) for routing ids [T, k] and the
+    output gradient dy [T, H]: gradients of x, W_gate_up, W_down, W_r and
+    the bias, in fp64, taken at the decoded values the forward pass reads
+    (BF16 layers: the values themselves)."""
+    xh = decode_activations(spec, inputs["x"], inputs.get("x_scales"))
+    xr = router_input(spec, inputs)
+    wr = F.bf16_decode(inputs["router_w"])
+    b = np.zeros(wr.shape[0]) if inputs.get("router_bias") is None else \
+        np.asarray(inputs["router_bias"], dtype=np.float32).astype(np.float64)
+    E = spec.E
+    sc = lambda key, e: None if inputs.get(key) is None else np.asarray(inputs[key][e])
+    w_gu = np.stack([decode_weight(spec, np.asarray(inputs["w_gate_up"][e]), sc("w_gate_up_scales", e)) for e in range(E)])
+    w_d = np.stack([decode_weight(spec, np.asarray(inputs["w_down"][e]), sc("w_down_scales", e)) for e in range(E)])
+    return backward_exact(xh, xr, wr, b, w_gu, w_d, np.asarray(ids, dtype=np.int64),
+                          np.asarray(dy, dtype=np.float64), spec.I)
