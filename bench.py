@@ -201,6 +201,8 @@ def main():
     ap.add_argument("--inter-scale", default="f32", choices=["f32", "pow2"],
                     help="scale rule of the layer's own FP8 quantisations (moe_desc.inter_scale)")
     ap.add_argument("--no-evict", action="store_true", help="skip the cache-evicted per-call timing")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward pass (moe_backward) of a BF16 layer instead (default workload dsv3_bf16)")
     ap.add_argument("--wscale", default=None, choices=["block", "channel"],
                     help="FP8 weight scale granularity (moe_desc.weight_scale; default: the workload's)")
     args = ap.parse_args()
@@ -213,6 +215,9 @@ def main():
     from moe_layer_router_amd import layer
     from workloads import gen
 
+    if args.backward:
+        bench_backward(args)
+        return
     cfg = gen.CONFIGS[args.workload]
     if args.wscale is not None:
         if cfg.weight != "fp8" and args.wscale == "channel":
@@ -352,6 +357,130 @@ def main():
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on a bounded sample (host cores)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(cfg, raw, args.cpu_experts)
+    print(json.dumps(result), flush=True)
+
+
+def backward_cost(cfg, active: int):
+    """Algorithmic FLOPs and HBM bytes of one backward pass: the gate|up
+    recompute, the unweighted intermediate gradient, the linear-1 input
+    gradient and the two weight gradients (16*T*k*H*I), the router's two
+    products (4*T*E*H); bytes: x, dy and the active experts' weights read,
+    dx and every gradient written in fp32."""
+    T, H, E, k, I = cfg.T, cfg.H, cfg.E, cfg.k, cfg.I
+    flops = 16.0 * T * k * H * I + 4.0 * T * E * H
+    nbytes = 2 * T * H * 2 + active * 3 * I * H * 2 + E * H * 2
+    nbytes += T * H * 4 + E * 3 * I * H * 4 + E * H * 4 + E * 4
+    return flops, nbytes
+
+
+def cpu_baseline_backward(cfg, raw, ids, dy, n_tokens=12, n_experts=4):
+    """The oracle's backward pass (backward_exact, fp64) on a bounded sample:
+    `n_tokens` tokens, each routed to all of the `n_experts` busiest experts
+    of the real routing (the oracle's cost per (token, expert) pair does not
+    depend on which pair it is), with those experts' weights.  The layer time
+    is extrapolated as T*k pairs x the time per pair (the router's products,
+    E*H per token, are under 3% of a pair's work and are not scaled up)."""
+    import torch
+    from threadpoolctl import threadpool_info
+    from oracle import moe_oracle as O
+    from oracle import formats as F
+    T, k = ids.shape
+    busy = np.argsort(-np.bincount(ids.ravel(), minlength=cfg.E), kind="stable")[:n_experts]
+    bf = lambda x: F.bf16_decode(x.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16))
+    idx = torch.as_tensor(busy)
+    xh = bf(raw["x"][:n_tokens])
+    wr = bf(raw["router_w"][idx.to(raw["router_w"].device)])
+    w_gu = bf(raw["w_gate_up"][idx.to(raw["w_gate_up"].device)])
+    w_d = bf(raw["w_down"][idx.to(raw["w_down"].device)])
+    dys = bf(dy[:n_tokens])
+    ids_s = np.tile(np.arange(n_experts, dtype=np.int64), (n_tokens, 1))
+    t0 = time.perf_counter()
+    O.backward_exact(xh, xh, wr, np.zeros(n_experts), w_gu, w_d, ids_s, dys, cfg.I)
+    dt = time.perf_counter() - t0
+    per_pair = dt / (n_tokens * n_experts)
+    t_layer = per_pair * T * k
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": round(T / t_layer, 3), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"fp64 numpy oracle backward_exact on {n_tokens} tokens x the {n_experts} busiest experts "
+                       f"({dt:.2f} s, {per_pair * 1e3:.1f} ms per token-expert pair); layer time extrapolated as "
+                       f"{T}*{k} pairs = {t_layer:.1f} s"),
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def bench_backward(args):
+    import torch
+    from moe_layer_router_amd import layer
+    from workloads import gen
+    name = args.workload if args.workload != "dsv3_fp8" else "dsv3_bf16"
+    cfg = gen.CONFIGS[name]
+    if cfg.act != "bf16" or cfg.weight != "bf16":
+        print("--backward needs a BF16 layer workload", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] backward: generating {cfg.name} inputs on {dev}", file=sys.stderr, flush=True)
+    raw = gen.make_inputs(cfg, seed=args.seed, device=dev)
+    fwd = layer.forward(layer.pack_weights(raw), cfg.k, mode="mega")
+    ids, wts = fwd["topk_ids"].clone(), fwd["topk_weights"].clone()
+    del fwd
+    g = torch.Generator(device="cpu").manual_seed(args.seed + 1)
+    dy = torch.randn(cfg.T, cfg.H, generator=g).to(torch.bfloat16).to(dev)
+    ws = layer.Workspace(dev)
+    stream = torch.cuda.current_stream()
+    out = layer.backward(raw, ids, wts, dy, workspace=ws)
+    torch.cuda.synchronize()
+    print(f"[bench] backward: warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        layer.backward(raw, ids, wts, dy, workspace=ws, out=out)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t_begin, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_begin.record(stream)
+    for i in range(args.steps):
+        starts[i].record(stream)
+        layer.backward(raw, ids, wts, dy, workspace=ws, out=out)
+        ends[i].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    print(f"[bench] backward: timed {args.steps} steps", file=sys.stderr, flush=True)
+    for key, v in out.items():
+        if v is not None and not torch.isfinite(v).all():
+            raise RuntimeError(f"non-finite {key}")
+    ms = t_begin.elapsed_time(t_end) / args.steps
+    per = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+    active = int((torch.bincount(ids.view(-1).long(), minlength=cfg.E) > 0).sum().item())
+    flops, nbytes = backward_cost(cfg, active)
+    t_call = float(per.mean()) / 1e3
+    t_mfma = flops / (PEAK_TFLOPS["bf16"] * 1e12)
+    t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
+    if t_hbm >= t_mfma:
+        roof = {"bound": "hbm", "achieved": round(nbytes / t_call / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(nbytes / t_call / 1e9 / PEAK_HBM_GBS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(flops / t_call / 1e12, 1), "peak": PEAK_TFLOPS["bf16"],
+                "unit": "TFLOP/s", "frac": round(flops / t_call / 1e12 / PEAK_TFLOPS["bf16"], 4)}
+    roof["kernel"] = "moe_backward (10 kernels)"
+    roof["traffic"] = None
+    result = {
+        "metric": "MoE-layer backward tokens/s (BF16 layer, routing given)",
+        "value": round(cfg.T / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16 operands, fp32 sums and gradients",
+        "data": "synthetic (seeded N(0,1) activations and output gradients, N(0,1/fan_in) weights)",
+        "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "E": cfg.E, "top_k": cfg.k, "I": cfg.I,
+                   "active_experts": active},
+        "tflops": round(flops / (ms / 1e3) / 1e12, 1),
+        "roofline": roof,
+        "roofline_model": {"algorithmic_tflop": round(flops / 1e12, 4), "algorithmic_gb": round(nbytes / 1e9, 4),
+                           "t_mfma_ms": round(t_mfma * 1e3, 4), "t_hbm_ms": round(t_hbm * 1e3, 4),
+                           "kernel_ms": round(t_call * 1e3, 4)},
+        "per_call_ms": {"median": round(float(np.median(per)), 4), "min": round(float(per.min()), 4),
+                        "mean": round(float(per.mean()), 4)},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] backward: timing the oracle on a bounded sample (host cores)", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline_backward(cfg, raw, ids.cpu().numpy().astype(np.int64), dy)
     print(json.dumps(result), flush=True)
 
 

@@ -330,6 +330,36 @@ moe_status moe_pack_weights(const moe_desc* d, int32_t which, const void* src, c
                             void* dst, void* dst_scales, moe_stream_t stream);
 
 /* Human-readable name of a status, and the calling thread's last error text. */
+/* Backward pass of the layer: the gradients of sum(dy * y) with the routing
+ * of the forward call (topk_ids, topk_weights) held fixed, the layer being a
+ * trainable layer as in the model-layer bullet of youleyou, "DeepSeek 模型更新
+ * 解读 Tile Kernels 与 DeepEP V2 新特性", section "Tile Kernels".  With
+ * e = topk_ids[t][j], w = topk_weights, g|u = x[t] W_gu[e]^T, a = SwiGLU(g, u):
+ *   dW_down[e]    += w[t][j] dy[t]^T a
+ *   dW_gate_up[e] += [dg | du]^T x[t],  dg = w dy[t] W_d[e] * u * SiLU'(g),
+ *                                       du = w dy[t] W_d[e] * SiLU(g)
+ *   dl[t][j]       = w[t][j] (dw[t][j] - sum_i w[t][i] dw[t][i]),  dw[t][j] = <dy[t], a W_d[e]^T>
+ *   dW_router[e]  += dl[t][j] x[t],  dbias[e] += dl[t][j]
+ *   dx[t]          = sum_j [dg | du] W_gu[e] + sum_j dl[t][j] W_router[e]
+ * (the forward pass's rounding of the intermediate is passed straight
+ * through).  BF16 layers only (act_dtype = weight_dtype = BF16, else
+ * MOE_ERR_UNSUPPORTED); weights in the row-major layout the forward call's
+ * caller loaded (weight_layout = ROW_MAJOR, else MOE_ERR_INVALID_ARGUMENT).
+ * Inputs: x [T][H], router_w [E][H], w_gate_up [E][2I][H], w_down [E][H][I],
+ * dy [T][H] (BF16); topk_ids [T][top_k] int32 and topk_weights fp32 as the
+ * forward call returned them.  Outputs (fp32, overwritten): dx [T][H],
+ * dw_gate_up [E][2I][H], dw_down [E][H][I], dw_router [E][H], dbias [E]
+ * (optional, NULL = not computed).  Sums are fp32; the inputs and weights
+ * enter the matrix cores as BF16 (exact), the fp32 intermediates (dg|du, w*a,
+ * the logit gradients) as two BF16 parts each (hi + lo, within 2^-17 of the
+ * fp32 value).  Asynchronous on `stream`; workspace of
+ * moe_backward_workspace_size(d) bytes (0 for an invalid descriptor). */
+size_t moe_backward_workspace_size(const moe_desc* d);
+moe_status moe_backward(const moe_desc* d, const void* x, const void* router_w, const void* w_gate_up,
+                        const void* w_down, const int32_t* topk_ids, const float* topk_weights, const void* dy,
+                        float* dx, float* dw_gate_up, float* dw_down, float* dw_router, float* dbias,
+                        void* workspace, size_t workspace_bytes, moe_stream_t stream);
+
 const char* moe_status_string(moe_status s);
 const char* moe_last_error(void);
 

@@ -8,6 +8,7 @@
 // combine are local permutations, and the overlap is between HBM weight
 // streaming and MFMA work of different work items running side by side.
 #include "kernels.h"
+#include "backward.h"
 
 namespace moe {
 
@@ -842,6 +843,55 @@ moe_status launch_layer(const Plan& p, const DevInfo& di, int mode, hipStream_t 
   return MOE_OK;
 }
 
+// ---------------------------------------------------------------- backward
+// Workspace of the backward pass: the permutation's regions of the forward
+// layout, then the backward's own buffers (P = T*k permuted rows).
+struct BwdLayout {
+  size_t gu, dau, dgu, aw, dws, dxr_rows, dl, dxr, total;
+};
+
+BwdLayout bwd_layout(const moe_desc* d) {
+  const Layout L = make_layout(d);
+  const size_t T = d->T, H = d->H, E = d->E, I = d->I, P = (size_t)d->T * d->top_k;
+  BwdLayout B{};
+  size_t o = align256(L.aq);                       // the forward layout up to the intermediate
+  B.gu = o; o = align256(o + P * 2 * I * 4);
+  B.dau = o; o = align256(o + P * I * 4);
+  B.dgu = o; o = align256(o + P * 2 * I * 4);
+  B.aw = o; o = align256(o + P * I * 4);
+  B.dws = o; o = align256(o + P * 4);
+  B.dxr_rows = o; o = align256(o + P * H * 4);
+  B.dl = o; o = align256(o + T * E * 4);
+  B.dxr = o; o = align256(o + T * H * 4);
+  B.total = o;
+  return B;
+}
+
+moe_status check_bwd_desc(const moe_desc* d) {
+  TRY(check_desc(d));
+  if (d->act_dtype != MOE_DTYPE_BF16 || d->weight_dtype != MOE_DTYPE_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "the backward pass supports BF16 layers only (act=%d weight=%d)", d->act_dtype,
+                d->weight_dtype);
+  if (d->weight_layout != MOE_LAYOUT_ROW_MAJOR)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "the backward pass reads row-major weights (weight_layout=%d)",
+                d->weight_layout);
+  return MOE_OK;
+}
+
+// a_f32: A is an fp32 intermediate (split into two BF16 parts in the tile)
+moe_status launch_bwd_gemm(const BwdGemm& g, dim3 grid, bool a_f32, hipStream_t st) {
+  if (a_f32)
+    hipLaunchKernelGGL(k_bwd_gemm<1>, grid, dim3(256), kBwdLds, st, g);
+  else
+    hipLaunchKernelGGL(k_bwd_gemm<0>, grid, dim3(256), kBwdLds, st, g);
+  HIP_TRY(hipGetLastError());
+  return MOE_OK;
+}
+
+BwdOperand bwd_op(const void* p, long ld, int trans, const int32_t* map = nullptr, int div = 1, long gstride = 0) {
+  return BwdOperand{p, ld, trans, map, div, gstride};
+}
+
 }  // namespace
 
 extern "C" {
@@ -1059,6 +1109,115 @@ moe_status moe_pack_weights(const moe_desc* d, int32_t which, const void* src, c
                        static_cast<uint8_t*>(dst_scales), rows, (int)N, K / 128);
     HIP_TRY(hipGetLastError());
   }
+  return MOE_OK;
+}
+
+size_t moe_backward_workspace_size(const moe_desc* d) {
+  if (check_bwd_desc(d) != MOE_OK) return 0;
+  return bwd_layout(d).total;
+}
+
+moe_status moe_backward(const moe_desc* d, const void* x, const void* router_w, const void* w_gate_up,
+                        const void* w_down, const int32_t* topk_ids, const float* topk_weights, const void* dy,
+                        float* dx, float* dw_gate_up, float* dw_down, float* dw_router, float* dbias,
+                        void* workspace, size_t workspace_bytes, moe_stream_t stream) {
+  TRY(check_bwd_desc(d));
+  TRY(check_ptr(x, "x"));
+  TRY(check_ptr(router_w, "router_w"));
+  TRY(check_ptr(w_gate_up, "w_gate_up"));
+  TRY(check_ptr(w_down, "w_down"));
+  TRY(check_ptr(topk_ids, "topk_ids"));
+  TRY(check_ptr(topk_weights, "topk_weights"));
+  TRY(check_ptr(dy, "dy"));
+  TRY(check_ptr(dx, "dx"));
+  TRY(check_ptr(dw_gate_up, "dw_gate_up"));
+  TRY(check_ptr(dw_down, "dw_down"));
+  TRY(check_ptr(dw_router, "dw_router"));
+  TRY(check_ptr(dbias, "dbias", false));
+  TRY(check_ptr(workspace, "workspace"));
+  const BwdLayout B = bwd_layout(d);
+  if (workspace_bytes < B.total)
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", workspace_bytes, B.total);
+  DevInfo di;
+  TRY(device_info(&di));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const Layout L = make_layout(d);
+  char* ws = static_cast<char*>(workspace);
+  Plan p;
+  TRY(fill_plan(d, L, ws, &p));
+  p.ids = const_cast<int32_t*>(topk_ids);
+  const int T = d->T, H = d->H, E = d->E, I = d->I, k = d->top_k, P = T * k;
+  float* GU = reinterpret_cast<float*>(ws + B.gu);
+  float* dAu = reinterpret_cast<float*>(ws + B.dau);
+  float* dGU = reinterpret_cast<float*>(ws + B.dgu);
+  float* Aw = reinterpret_cast<float*>(ws + B.aw);
+  float* dws = reinterpret_cast<float*>(ws + B.dws);
+  float* dXr = reinterpret_cast<float*>(ws + B.dxr_rows);
+  float* dl = reinterpret_cast<float*>(ws + B.dl);
+  float* dxr = reinterpret_cast<float*>(ws + B.dxr);
+
+  // counters, then the dense logit gradients (only the selected entries are written)
+  hipLaunchKernelGGL(k_zero, dim3(16), dim3(256), 0, st, p.err, (p.zero_bytes + 256) / 4);
+  HIP_TRY(hipGetLastError());
+  hipLaunchKernelGGL(k_bwd_zero, dim3(di.cus * 4), dim3(256), 0, st, reinterpret_cast<uint32_t*>(dl),
+                     (B.dxr - B.dl) / 4);
+  HIP_TRY(hipGetLastError());
+  TRY(launch_permute(p, p.row_of, st));          // perm, offsets, row_of, 64-row tiles
+
+  const auto up = [](long a, long b) { return (unsigned)((a + b - 1) / b); };
+  const long H2 = 2L * I;
+  BwdGemm g{};
+  g.tiles = p.tiles;
+  g.ntiles = p.meta;
+  g.offsets = p.offsets;
+  // GU = x[tok] W_gu[e]^T
+  g.a = bwd_op(x, H, 0, p.perm, k);
+  g.b = bwd_op(w_gate_up, H, 1, nullptr, 1, H2 * H);
+  g.c = GU; g.ldc = H2; g.N = (int)H2; g.K = H; g.group = BWD_GROUP_ROWS;
+  TRY(launch_bwd_gemm(g, dim3(p.max_tiles, up(H2, kBwdBN)), false, st));
+  // dAu = dy[tok] W_d[e]
+  g.a = bwd_op(dy, H, 0, p.perm, k);
+  g.b = bwd_op(w_down, I, 0, nullptr, 1, (long)H * I);
+  g.c = dAu; g.ldc = I; g.N = I; g.K = H;
+  TRY(launch_bwd_gemm(g, dim3(p.max_tiles, up(I, kBwdBN)), false, st));
+  // rows: dw, dG|dU, w a
+  hipLaunchKernelGGL(k_bwd_rows, dim3(P), dim3(256), 0, st, GU, dAu, p.perm, topk_weights, I, P, dGU, Aw, dws);
+  HIP_TRY(hipGetLastError());
+  // dXr = [dG|dU] W_gu[e]
+  g.a = bwd_op(dGU, H2, 0);
+  g.b = bwd_op(w_gate_up, H, 0, nullptr, 1, H2 * H);
+  g.c = dXr; g.ldc = H; g.N = H; g.K = (int)H2;
+  TRY(launch_bwd_gemm(g, dim3(p.max_tiles, up(H, kBwdBN)), true, st));
+  // dW_gu[e] = sum_p [dG|dU]_p^T x[tok(p)]
+  g.a = bwd_op(dGU, H2, 1);
+  g.b = bwd_op(x, H, 0, p.perm, k);
+  g.c = dw_gate_up; g.ldc = H; g.c_gstride = H2 * H; g.M = (int)H2; g.N = H; g.group = BWD_GROUP_K;
+  TRY(launch_bwd_gemm(g, dim3(up(H2, kBwdBM), up(H, kBwdBN), E), true, st));
+  // dW_d[e] = sum_p dy[tok(p)]^T (w a)_p, formed as its transpose
+  // sum_p (w a)_p^T dy[tok(p)] (the fp32 operand as A) and stored transposed
+  g.a = bwd_op(Aw, I, 1);
+  g.b = bwd_op(dy, H, 0, p.perm, k);
+  g.c = dw_down; g.ldc = I; g.c_trans = 1; g.c_gstride = (long)H * I; g.M = I; g.N = H;
+  TRY(launch_bwd_gemm(g, dim3(up(I, kBwdBM), up(H, kBwdBN), E), true, st));
+  g.c_trans = 0;
+  // router: logit gradients, bias, W_r and the router's share of dx
+  hipLaunchKernelGGL(k_bwd_router, dim3(up(T, 256)), dim3(256), 0, st, topk_ids, topk_weights, dws, T, E, k, dl);
+  HIP_TRY(hipGetLastError());
+  if (dbias) {
+    hipLaunchKernelGGL(k_bwd_dbias, dim3(up(E, 256)), dim3(256), 0, st, dl, T, E, dbias);
+    HIP_TRY(hipGetLastError());
+  }
+  g.a = bwd_op(dl, E, 1);
+  g.b = bwd_op(x, H, 0);
+  g.c = dw_router; g.ldc = H; g.c_gstride = 0; g.M = E; g.N = H; g.K = T; g.group = BWD_GROUP_NONE;
+  TRY(launch_bwd_gemm(g, dim3(up(E, kBwdBM), up(H, kBwdBN), 1), true, st));
+  g.a = bwd_op(dl, E, 0);
+  g.b = bwd_op(router_w, H, 0);
+  g.c = dxr; g.ldc = H; g.M = T; g.N = H; g.K = E;
+  TRY(launch_bwd_gemm(g, dim3(up(T, kBwdBM), up(H, kBwdBN), 1), true, st));
+  // dx = sum_j dXr[row(t, j)] + dxr
+  hipLaunchKernelGGL(k_bwd_dx, dim3(up((long)T * H, 256)), dim3(256), 0, st, dXr, p.row_of, dxr, T, H, k, dx);
+  HIP_TRY(hipGetLastError());
   return MOE_OK;
 }
 

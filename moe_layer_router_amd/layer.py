@@ -124,6 +124,32 @@ def quantize_input(x: torch.Tensor, scale_mode: str = "f32", stream=None):
     return xq, xs
 
 
+def backward(inputs: dict, topk_ids: torch.Tensor, topk_weights: torch.Tensor, dy: torch.Tensor,
+             workspace: Workspace = None, stream=None, want_dbias: bool = True, out: dict = None) -> dict:
+    """Gradients of a BF16 layer (moe_backward) for the routing a forward
+    call returned, from row-major weights (inputs as generated, not packed).
+    Returns dict(dx, dw_gate_up, dw_down, dw_router, dbias), fp32 (`out`, a
+    previous result, is reused)."""
+    if inputs.get("weights_packed"):
+        raise ValueError("backward() reads the row-major weights: pass the inputs before pack_weights()")
+    x = inputs["x"]
+    T, H = x.shape
+    k = topk_ids.shape[1]
+    desc = desc_from_inputs(inputs, k, layout="row_major")
+    E, I = desc.E, desc.I
+    dev = x.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    if out is None:
+        out = dict(dx=torch.empty(T, H, **f32), dw_gate_up=torch.empty(E, 2 * I, H, **f32),
+                   dw_down=torch.empty(E, H, I, **f32), dw_router=torch.empty(E, H, **f32),
+                   dbias=torch.empty(E, **f32) if want_dbias else None)
+    ws = (workspace or Workspace(dev)).get(lib.moe_backward_workspace_size(desc))
+    lib.moe_backward(desc, x, inputs["router_w"], inputs["w_gate_up"].contiguous(), inputs["w_down"].contiguous(),
+                     topk_ids.contiguous(), topk_weights.contiguous(), dy.contiguous(), out["dx"], out["dw_gate_up"],
+                     out["dw_down"], out["dw_router"], out["dbias"], ws, stream)
+    return out
+
+
 def trace_phases(out: dict) -> dict:
     """Phase timing of a finished forward(..., trace=True) call in the
     persistent kernel, from the per-workgroup stamps (100 MHz clock):

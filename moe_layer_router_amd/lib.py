@@ -100,6 +100,10 @@ _lib.moe_forward.restype = ctypes.c_int
 _lib.moe_forward.argtypes = [ctypes.POINTER(MoeDesc)] + [_P] * 13 + [_P, ctypes.c_size_t, _P]
 _lib.moe_quantize_input.restype = ctypes.c_int
 _lib.moe_quantize_input.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P]
+_lib.moe_backward_workspace_size.restype = ctypes.c_size_t
+_lib.moe_backward_workspace_size.argtypes = [ctypes.POINTER(MoeDesc)]
+_lib.moe_backward.restype = ctypes.c_int
+_lib.moe_backward.argtypes = [ctypes.POINTER(MoeDesc)] + [_P] * 13 + [ctypes.c_size_t, _P]
 _lib.moe_forward_static.restype = ctypes.c_int
 _lib.moe_forward_static.argtypes = [ctypes.POINTER(MoeDesc)] + [_P] * 13 + [_P]
 _lib.moe_route.restype = ctypes.c_int
@@ -220,6 +224,19 @@ def moe_forward_static(desc, x, x_scales, router_w, router_bias, w_gate_up, w_ga
 MOE_STATIC_WORKSPACE_BYTES = 64 << 20
 
 
+def moe_backward_workspace_size(desc) -> int:
+    return _lib.moe_backward_workspace_size(ctypes.byref(desc))
+
+
+def moe_backward(desc, x, router_w, w_gate_up, w_down, topk_ids, topk_weights, dy, dx, dw_gate_up, dw_down,
+                 dw_router, dbias, workspace, stream=None):
+    nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_lib.moe_backward(ctypes.byref(desc), _ptr(x), _ptr(router_w), _ptr(w_gate_up), _ptr(w_down),
+                             _ptr(topk_ids), _ptr(topk_weights), _ptr(dy), _ptr(dx), _ptr(dw_gate_up),
+                             _ptr(dw_down), _ptr(dw_router), _ptr(dbias), _ptr(workspace), nbytes,
+                             _stream(stream)), "moe_backward")
+
+
 def moe_quantize_input(x, xq, x_scales, scale_mode="f32", stream=None):
     """x: [T, H] bfloat16 or float32 tensor; xq [T, H] uint8; x_scales [T, H/128] float32."""
     import torch
@@ -267,4 +284,5 @@ def exported_symbols():
     return ["moe_abi_version", "moe_workspace_size", "moe_forward_static", "moe_quantize_input", "moe_route_workspace_size",
             "moe_permute_workspace_size", "moe_get_workspace_regions", "moe_validate", "moe_forward", "moe_route",
             "moe_permute", "moe_pack_weights", "moe_status_string", "moe_last_error",
-            "moe_peak_mfma_flops", "moe_peak_mfma", "moe_peak_hbm_read"]
+            "moe_peak_mfma_flops", "moe_peak_mfma", "moe_peak_hbm_read", "moe_backward_workspace_size",
+            "moe_backward"]

@@ -174,3 +174,16 @@ def test_weight_scale_granularity():
     assert _validate(lib.make_desc(100, 512, 16, 256, 4, "fp8", "fp8", wscale=7)) == lib.MOE_ERR_INVALID_ARGUMENT
     assert lib.moe_workspace_size(lib.make_desc(100, 512, 16, 256, 4, "fp8", "fp8", wscale="channel")) == \
         lib.moe_workspace_size(lib.make_desc(100, 512, 16, 256, 4, "fp8", "fp8"))
+
+
+def test_backward_descriptor_checks():
+    bf = lib.make_desc(64, 256, 8, 128, 2, "bf16", "bf16", layout="row_major")
+    assert lib.moe_backward_workspace_size(bf) > lib.moe_permute_workspace_size(bf)
+    # FP8 layers and tiled weights are rejected before any device work
+    assert lib.moe_backward_workspace_size(lib.make_desc(64, 256, 8, 128, 2, "fp8", "fp8", layout="row_major")) == 0
+    assert lib.moe_backward_workspace_size(lib.make_desc(64, 256, 8, 128, 2, "bf16", "bf16", layout="tiled")) == 0
+    for d, want in ((lib.make_desc(64, 256, 8, 128, 2, "fp8", "fp8", layout="row_major"), lib.MOE_ERR_UNSUPPORTED),
+                    (lib.make_desc(64, 256, 8, 128, 2, "bf16", "bf16", layout="tiled"), lib.MOE_ERR_INVALID_ARGUMENT)):
+        with pytest.raises(lib.MoeError) as ex:
+            lib.moe_backward(d, A, A, A, A, A, A, A, A, A, A, A, None, None, stream=0)
+        assert ex.value.status == want

@@ -58,6 +58,8 @@ CONFIGS = {
                                 note="DeepSeek-V3-shaped layer, FP8 x FP4 (E8M0 per 32)"),
     "decode_fp8_zipf": LayerConfig("decode_fp8_zipf", 256, 7168, 256, 8, 2048, "fp8", "fp8",
                                    zipf=1.1, note="decode-shaped, Zipf(1.1) expert popularity"),
+    "dsv3_bf16": LayerConfig("dsv3_bf16", 8192, 7168, 256, 8, 2048, "bf16", "bf16",
+                             note="DeepSeek-V3-shaped layer in BF16 (the backward pass's workload)"),
     "mega_e1024_fp4_zipf": LayerConfig("mega_e1024_fp4_zipf", 16384, 7168, 1024, 16, 1024, "fp8",
                                        "fp4", zipf=1.0,
                                        note="1024 experts, top-16, FP8 x FP4, Zipf(1.0)"),
