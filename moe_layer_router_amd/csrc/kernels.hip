@@ -847,7 +847,7 @@ moe_status launch_layer(const Plan& p, const DevInfo& di, int mode, hipStream_t 
 // Workspace of the backward pass: the permutation's regions of the forward
 // layout, then the backward's own buffers (P = T*k permuted rows).
 struct BwdLayout {
-  size_t gu, dau, dgu, aw, dws, dxr_rows, dl, dxr, total;
+  size_t gu, dau, dgu, dgu_lo, aw, aw_lo, dws, dxr_rows, dl, dl_lo, dxr, total;
 };
 
 BwdLayout bwd_layout(const moe_desc* d) {
@@ -857,11 +857,14 @@ BwdLayout bwd_layout(const moe_desc* d) {
   size_t o = align256(L.aq);                       // the forward layout up to the intermediate
   B.gu = o; o = align256(o + P * 2 * I * 4);
   B.dau = o; o = align256(o + P * I * 4);
-  B.dgu = o; o = align256(o + P * 2 * I * 4);
-  B.aw = o; o = align256(o + P * I * 4);
+  B.dgu = o; o = align256(o + P * 2 * I * 2);     // hi part, then the lo part
+  B.dgu_lo = o; o = align256(o + P * 2 * I * 2);
+  B.aw = o; o = align256(o + P * I * 2);
+  B.aw_lo = o; o = align256(o + P * I * 2);
   B.dws = o; o = align256(o + P * 4);
   B.dxr_rows = o; o = align256(o + P * H * 4);
-  B.dl = o; o = align256(o + T * E * 4);
+  B.dl = o; o = align256(o + T * E * 2);
+  B.dl_lo = o; o = align256(o + T * E * 2);
   B.dxr = o; o = align256(o + T * H * 4);
   B.total = o;
   return B;
@@ -879,17 +882,38 @@ moe_status check_bwd_desc(const moe_desc* d) {
 }
 
 // a_f32: A is an fp32 intermediate (split into two BF16 parts in the tile)
-moe_status launch_bwd_gemm(const BwdGemm& g, dim3 grid, bool a_f32, hipStream_t st) {
-  if (a_f32)
-    hipLaunchKernelGGL(k_bwd_gemm<1>, grid, dim3(256), kBwdLds, st, g);
+// grid: gx x gy x gz logical tiles (BwdGemm), launched as one dimension;
+// A split into hi / lo parts when g.a.p_lo is set
+moe_status launch_bwd_gemm(BwdGemm g, unsigned gx, unsigned gy, unsigned gz, hipStream_t st) {
+  g.gx = (int)gx;
+  g.gy = (int)gy;
+  g.gz = (int)gz;
+  size_t units = 1, gyb = gy;
+  if (g.group == BWD_GROUP_ROWS) g.gx = (int)(gx + 15) / 16 * 16;       // whole pairs, a multiple of 8 of them
+  if (g.group == BWD_GROUP_K) {
+    units = (gz + 7) / 8 * 8;
+    gyb = (gy + kBwdTpb - 1) / kBwdTpb;
+  }
+  const dim3 grid((unsigned)((size_t)g.gx * gyb * units));
+  const bool split = g.a.p_lo != nullptr;
+  if (split && g.c_trans)
+    hipLaunchKernelGGL((k_bwd_gemm<1, 1>), grid, dim3(256), bwd_lds_bytes<1>(), st, g);
+  else if (split)
+    hipLaunchKernelGGL((k_bwd_gemm<1, 0>), grid, dim3(256), bwd_lds_bytes<1>(), st, g);
+  else if (g.c_trans)
+    hipLaunchKernelGGL((k_bwd_gemm<0, 1>), grid, dim3(256), bwd_lds_bytes<0>(), st, g);
   else
-    hipLaunchKernelGGL(k_bwd_gemm<0>, grid, dim3(256), kBwdLds, st, g);
+    hipLaunchKernelGGL((k_bwd_gemm<0, 0>), grid, dim3(256), bwd_lds_bytes<0>(), st, g);
   HIP_TRY(hipGetLastError());
   return MOE_OK;
 }
 
 BwdOperand bwd_op(const void* p, long ld, int trans, const int32_t* map = nullptr, int div = 1, long gstride = 0) {
-  return BwdOperand{p, ld, trans, map, div, gstride};
+  return BwdOperand{p, nullptr, ld, trans, map, div, gstride};
+}
+// an fp32 operand held as hi / lo BF16 parts
+BwdOperand bwd_op2(const void* hi, const void* lo, long ld, int trans) {
+  return BwdOperand{hi, lo, ld, trans, nullptr, 1, 0};
 }
 
 }  // namespace
@@ -1149,22 +1173,27 @@ moe_status moe_backward(const moe_desc* d, const void* x, const void* router_w, 
   const int T = d->T, H = d->H, E = d->E, I = d->I, k = d->top_k, P = T * k;
   float* GU = reinterpret_cast<float*>(ws + B.gu);
   float* dAu = reinterpret_cast<float*>(ws + B.dau);
-  float* dGU = reinterpret_cast<float*>(ws + B.dgu);
-  float* Aw = reinterpret_cast<float*>(ws + B.aw);
+  uint16_t* dgu_hi = reinterpret_cast<uint16_t*>(ws + B.dgu);
+  uint16_t* dgu_lo = reinterpret_cast<uint16_t*>(ws + B.dgu_lo);
+  uint16_t* aw_hi = reinterpret_cast<uint16_t*>(ws + B.aw);
+  uint16_t* aw_lo = reinterpret_cast<uint16_t*>(ws + B.aw_lo);
   float* dws = reinterpret_cast<float*>(ws + B.dws);
   float* dXr = reinterpret_cast<float*>(ws + B.dxr_rows);
-  float* dl = reinterpret_cast<float*>(ws + B.dl);
+  uint16_t* dl_hi = reinterpret_cast<uint16_t*>(ws + B.dl);
+  uint16_t* dl_lo = reinterpret_cast<uint16_t*>(ws + B.dl_lo);
   float* dxr = reinterpret_cast<float*>(ws + B.dxr);
 
   // counters, then the dense logit gradients (only the selected entries are written)
   hipLaunchKernelGGL(k_zero, dim3(16), dim3(256), 0, st, p.err, (p.zero_bytes + 256) / 4);
   HIP_TRY(hipGetLastError());
-  hipLaunchKernelGGL(k_bwd_zero, dim3(di.cus * 4), dim3(256), 0, st, reinterpret_cast<uint32_t*>(dl),
-                     (B.dxr - B.dl) / 4);
+  hipLaunchKernelGGL(k_bwd_zero, dim3(di.cus * 4), dim3(256), 0, st, reinterpret_cast<uint32_t*>(dl_hi),
+                     (B.dxr - B.dl) / 4);        // both parts
   HIP_TRY(hipGetLastError());
-  TRY(launch_permute(p, p.row_of, st));          // perm, offsets, row_of, 64-row tiles
+  p.tile_rows = kBwdBM;
+  TRY(launch_permute(p, p.row_of, st));          // perm, offsets, row_of, row tiles of at most kBwdBM
 
   const auto up = [](long a, long b) { return (unsigned)((a + b - 1) / b); };
+  const unsigned pairs = (unsigned)p.max_tiles;     // row-tile slots (launch_bwd_gemm pads them)
   const long H2 = 2L * I;
   BwdGemm g{};
   g.tiles = p.tiles;
@@ -1174,49 +1203,51 @@ moe_status moe_backward(const moe_desc* d, const void* x, const void* router_w, 
   g.a = bwd_op(x, H, 0, p.perm, k);
   g.b = bwd_op(w_gate_up, H, 1, nullptr, 1, H2 * H);
   g.c = GU; g.ldc = H2; g.N = (int)H2; g.K = H; g.group = BWD_GROUP_ROWS;
-  TRY(launch_bwd_gemm(g, dim3(p.max_tiles, up(H2, kBwdBN)), false, st));
+  TRY(launch_bwd_gemm(g, pairs, up(H2, kBwdBN), 1, st));
   // dAu = dy[tok] W_d[e]
   g.a = bwd_op(dy, H, 0, p.perm, k);
   g.b = bwd_op(w_down, I, 0, nullptr, 1, (long)H * I);
   g.c = dAu; g.ldc = I; g.N = I; g.K = H;
-  TRY(launch_bwd_gemm(g, dim3(p.max_tiles, up(I, kBwdBN)), false, st));
+  TRY(launch_bwd_gemm(g, pairs, up(I, kBwdBN), 1, st));
   // rows: dw, dG|dU, w a
-  hipLaunchKernelGGL(k_bwd_rows, dim3(P), dim3(256), 0, st, GU, dAu, p.perm, topk_weights, I, P, dGU, Aw, dws);
+  hipLaunchKernelGGL(k_bwd_rows, dim3(P), dim3(256), 0, st, GU, dAu, p.perm, topk_weights, I, P, dgu_hi, dgu_lo,
+                     aw_hi, aw_lo, dws);
   HIP_TRY(hipGetLastError());
   // dXr = [dG|dU] W_gu[e]
-  g.a = bwd_op(dGU, H2, 0);
+  g.a = bwd_op2(dgu_hi, dgu_lo, H2, 0);
   g.b = bwd_op(w_gate_up, H, 0, nullptr, 1, H2 * H);
   g.c = dXr; g.ldc = H; g.N = H; g.K = (int)H2;
-  TRY(launch_bwd_gemm(g, dim3(p.max_tiles, up(H, kBwdBN)), true, st));
+  TRY(launch_bwd_gemm(g, pairs, up(H, kBwdBN), 1, st));
   // dW_gu[e] = sum_p [dG|dU]_p^T x[tok(p)]
-  g.a = bwd_op(dGU, H2, 1);
+  g.a = bwd_op2(dgu_hi, dgu_lo, H2, 1);
   g.b = bwd_op(x, H, 0, p.perm, k);
   g.c = dw_gate_up; g.ldc = H; g.c_gstride = H2 * H; g.M = (int)H2; g.N = H; g.group = BWD_GROUP_K;
-  TRY(launch_bwd_gemm(g, dim3(up(H2, kBwdBM), up(H, kBwdBN), E), true, st));
+  TRY(launch_bwd_gemm(g, up(H2, kBwdBM), up(H, kBwdBN), E, st));
   // dW_d[e] = sum_p dy[tok(p)]^T (w a)_p, formed as its transpose
   // sum_p (w a)_p^T dy[tok(p)] (the fp32 operand as A) and stored transposed
-  g.a = bwd_op(Aw, I, 1);
+  g.a = bwd_op2(aw_hi, aw_lo, I, 1);
   g.b = bwd_op(dy, H, 0, p.perm, k);
   g.c = dw_down; g.ldc = I; g.c_trans = 1; g.c_gstride = (long)H * I; g.M = I; g.N = H;
-  TRY(launch_bwd_gemm(g, dim3(up(I, kBwdBM), up(H, kBwdBN), E), true, st));
+  TRY(launch_bwd_gemm(g, up(I, kBwdBM), up(H, kBwdBN), E, st));
   g.c_trans = 0;
   // router: logit gradients, bias, W_r and the router's share of dx
-  hipLaunchKernelGGL(k_bwd_router, dim3(up(T, 256)), dim3(256), 0, st, topk_ids, topk_weights, dws, T, E, k, dl);
+  hipLaunchKernelGGL(k_bwd_router, dim3(up(T, 256)), dim3(256), 0, st, topk_ids, topk_weights, dws, T, E, k, dl_hi,
+                     dl_lo);
   HIP_TRY(hipGetLastError());
   if (dbias) {
-    hipLaunchKernelGGL(k_bwd_dbias, dim3(up(E, 256)), dim3(256), 0, st, dl, T, E, dbias);
+    hipLaunchKernelGGL(k_bwd_dbias, dim3(E), dim3(256), 0, st, dl_hi, dl_lo, T, E, dbias);
     HIP_TRY(hipGetLastError());
   }
-  g.a = bwd_op(dl, E, 1);
+  g.a = bwd_op2(dl_hi, dl_lo, E, 1);
   g.b = bwd_op(x, H, 0);
   g.c = dw_router; g.ldc = H; g.c_gstride = 0; g.M = E; g.N = H; g.K = T; g.group = BWD_GROUP_NONE;
-  TRY(launch_bwd_gemm(g, dim3(up(E, kBwdBM), up(H, kBwdBN), 1), true, st));
-  g.a = bwd_op(dl, E, 0);
+  TRY(launch_bwd_gemm(g, up(E, kBwdBM), up(H, kBwdBN), 1, st));
+  g.a = bwd_op2(dl_hi, dl_lo, E, 0);
   g.b = bwd_op(router_w, H, 0);
   g.c = dxr; g.ldc = H; g.M = T; g.N = H; g.K = E;
-  TRY(launch_bwd_gemm(g, dim3(up(T, kBwdBM), up(H, kBwdBN), 1), true, st));
+  TRY(launch_bwd_gemm(g, up(T, kBwdBM), up(H, kBwdBN), 1, st));
   // dx = sum_j dXr[row(t, j)] + dxr
-  hipLaunchKernelGGL(k_bwd_dx, dim3(up((long)T * H, 256)), dim3(256), 0, st, dXr, p.row_of, dxr, T, H, k, dx);
+  hipLaunchKernelGGL(k_bwd_dx, dim3(up((long)T * (H / 4), 256)), dim3(256), 0, st, dXr, p.row_of, dxr, T, H, k, dx);
   HIP_TRY(hipGetLastError());
   return MOE_OK;
 }
