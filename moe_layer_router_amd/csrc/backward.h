@@ -77,6 +77,7 @@ struct BwdGemm {
   const Tile* tiles;       // BWD_GROUP_ROWS: row tiles (e, r0, rows), count at *ntiles
   const int32_t* ntiles;
   const int32_t* offsets;  // BWD_GROUP_K: [E+1] K range of group e
+  long a_bytes, b_bytes;   // operand buffer sizes (A: each part; B: per group), for the direct-load kernel
   int gx, gy, gz;          // grouped rows: row-tile slots (a multiple of 16), column blocks;
                            // grouped K: row blocks, column blocks, groups (the grid holds
                            // gx * ceil(gy / kBwdTpb) * (gz rounded up to 8) workgroups);
@@ -367,6 +368,97 @@ __global__ void __launch_bounds__(256) k_bwd_gemm(BwdGemm g) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// The product with both operands K-contiguous and BF16 (the recomputed
+// gate|up GEMM: gathered input rows times the expert's weight rows) with
+// both operands loaded straight into LDS (buffer loads to LDS, no staging
+// registers), kBwdNs stages deep, one barrier per 64-K step.  The tiles are
+// [128 rows][64 K] with the chunk swizzle above, read with 16-byte loads.
+// Rows past a tile's end read the tile's first row (their results are never
+// stored).  Requires N a multiple of 128, K a multiple of 64, and buffers
+// below 2 GiB (32-bit buffer offsets); grouped rows only.
+constexpr int kBwdNs = 3;                                // LDS stages
+constexpr int kBwdDmaLds = kBwdNs * 2 * kBwdTile * 2;    // bytes: A and B tiles per stage
+
+__global__ void __launch_bounds__(256) k_bwd_gemm_dma(BwdGemm g) {
+  constexpr int LA = 8;                                  // DMA instructions per wave per step
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int c16 = lane & 15, gq = lane >> 4, wm = w & 1, wn = w >> 1;
+
+  long pair, inner;
+  bwd_unit(2L * g.gy, pair, inner);
+  const int t = (int)(2 * pair + (inner & 1));
+  const long n0 = (inner >> 1) * kBwdBN;
+  if (t >= *g.ntiles) return;
+  const Tile tl = g.tiles[t];
+  const long m0 = tl.r0, M = (long)tl.r0 + tl.rows, N = g.N, K = g.K;
+  const uint16_t* bbase = static_cast<const uint16_t*>(g.b.p) + (long)tl.e * g.b.gstride;
+
+  // DMA instruction q of wave w fills 1 KB u = 4q + w of a tile: rows
+  // 8u + l/8, physical chunk l % 8, i.e. logical chunk (l % 8) ^ swz(row)
+  const rsrc_t ars = make_rsrc(g.a.p, (uint32_t)g.a_bytes);
+  const rsrc_t brs = make_rsrc(bbase, (uint32_t)g.b_bytes);
+  uint32_t aoff[4], boff[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r = 8 * (4 * q + w) + (lane >> 3), c = (lane & 7) ^ ((r ^ (r >> 3)) & 7);
+    const long ar = m0 + r < M ? m0 + r : m0;
+    const long sr = g.a.map ? (long)(g.a.map[ar] / g.a.div) : ar;
+    aoff[q] = (uint32_t)(sr * g.a.ld * 2 + 16 * c);
+    boff[q] = (uint32_t)((n0 + r) * g.b.ld * 2 + 16 * c);
+  }
+  const long nsteps = K / kBwdBK;
+  auto dma = [&](long s) {                       // step s (clamped) into stage s % kBwdNs
+    const uint32_t k0b = (uint32_t)((s < nsteps ? s : nsteps - 1) * kBwdBK * 2);
+    char* st = lds + (int)(s % kBwdNs) * 2 * kBwdTile * 2;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      char* dst = st + (4 * q + w) * 1024;
+      buf_ld16_lds<0>(ars, dst, aoff[q], k0b);
+      buf_ld16_lds<0>(brs, dst + kBwdTile * 2, boff[q], k0b);
+    }
+  };
+
+  v4f acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < kBwdNs - 1; ++s) dma(s);
+  for (long s = 0; s < nsteps; ++s) {
+    // this wave's DMAs of step s are done (later steps' may still be in
+    // flight), and every wave is past step s - 1
+    barrier_vmcnt<(kBwdNs - 2) * LA>();
+    dma(s + kBwdNs - 1);                         // into the stage step s - 1 used
+    const uint16_t* At = reinterpret_cast<const uint16_t*>(lds + (int)(s % kBwdNs) * 2 * kBwdTile * 2);
+    const uint16_t* Bt = At + kBwdTile;
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      v8bf bf[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        bf[j] = as_v8bf(*reinterpret_cast<const v4i*>(Bt + bwd_off(64 * wn + 16 * j + c16, 4 * kh + gq)));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const v8bf ah = as_v8bf(*reinterpret_cast<const v4i*>(At + bwd_off(64 * wm + 16 * i + c16, 4 * kh + gq)));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_bf16(bf[j], ah, acc[i][j]);
+      }
+    }
+  }
+  wait_vmcnt<0>();                               // no DMA into LDS outlives the workgroup
+  // lane holds rows m = 64wm + 16i + c16, columns n = 64wn + 16j + 4gq + v
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const long m = m0 + 64 * wm + 16 * i + c16, n = n0 + 64 * wn + 16 * j + 4 * gq;
+      if (m < M) *reinterpret_cast<v4f*>(g.c + m * g.ldc + n) = acc[i][j];
+    }
+}
+
 // Store v as its hi = bf16(v) and lo = bf16(v - hi) parts.
 DEV void bwd_split_store(uint16_t* hi, uint16_t* lo, size_t i, float v) {
   const uint32_t h = f32_to_bf16_rne(v);
@@ -460,6 +552,19 @@ __global__ void __launch_bounds__(256) k_bwd_dx(const float* dXr, const int32_t*
   v4f s = v4f{0.f, 0.f, 0.f, 0.f};
   for (int j = 0; j < k; ++j) s += *reinterpret_cast<const v4f*>(dXr + (size_t)row_of[(size_t)t * k + j] * H + h);
   *reinterpret_cast<v4f*>(dx + (size_t)t * H + h) = s + *reinterpret_cast<const v4f*>(dxr + (size_t)t * H + h);
+}
+
+// out[p] = in[perm[p] / k] for the P permuted rows (BF16 rows of H, H a
+// multiple of 8): the input and output gradient in permuted row order for
+// the weight-gradient products.
+__global__ void __launch_bounds__(256) k_bwd_gather(const uint16_t* in, const int32_t* perm, int k, int H, long P,
+                                                    uint16_t* out) {
+  const long H8 = H / 8;
+  for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < P * H8; i += (long)gridDim.x * blockDim.x) {
+    const long p = i / H8, c = i % H8;
+    *reinterpret_cast<v4i*>(out + p * H + 8 * c) =
+        *reinterpret_cast<const v4i*>(in + (long)(perm[p] / k) * H + 8 * c);
+  }
 }
 
 // Fill n 32-bit words with zero.

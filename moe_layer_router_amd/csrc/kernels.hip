@@ -847,7 +847,7 @@ moe_status launch_layer(const Plan& p, const DevInfo& di, int mode, hipStream_t 
 // Workspace of the backward pass: the permutation's regions of the forward
 // layout, then the backward's own buffers (P = T*k permuted rows).
 struct BwdLayout {
-  size_t gu, dau, dgu, dgu_lo, aw, aw_lo, dws, dxr_rows, dl, dl_lo, dxr, total;
+  size_t gu, dau, dgu, dgu_lo, aw, aw_lo, dws, dxr_rows, dl, dl_lo, dxr, xp, dyp, total;
 };
 
 BwdLayout bwd_layout(const moe_desc* d) {
@@ -866,6 +866,8 @@ BwdLayout bwd_layout(const moe_desc* d) {
   B.dl = o; o = align256(o + T * E * 2);
   B.dl_lo = o; o = align256(o + T * E * 2);
   B.dxr = o; o = align256(o + T * H * 4);
+  B.xp = o; o = align256(o + P * H * 2);
+  B.dyp = o; o = align256(o + P * H * 2);
   B.total = o;
   return B;
 }
@@ -883,7 +885,10 @@ moe_status check_bwd_desc(const moe_desc* d) {
 
 // a_f32: A is an fp32 intermediate (split into two BF16 parts in the tile)
 // grid: gx x gy x gz logical tiles (BwdGemm), launched as one dimension;
-// A split into hi / lo parts when g.a.p_lo is set
+// A split into hi / lo parts when g.a.p_lo is set.  The grouped-row product
+// of two K-contiguous BF16 operands with whole column tiles runs the
+// direct-load kernel (when its buffers fit 32-bit offsets); the others run
+// the register-staged kernel.
 moe_status launch_bwd_gemm(BwdGemm g, unsigned gx, unsigned gy, unsigned gz, hipStream_t st) {
   g.gx = (int)gx;
   g.gy = (int)gy;
@@ -896,6 +901,14 @@ moe_status launch_bwd_gemm(BwdGemm g, unsigned gx, unsigned gy, unsigned gz, hip
   }
   const dim3 grid((unsigned)((size_t)g.gx * gyb * units));
   const bool split = g.a.p_lo != nullptr;
+  const long lim = 1L << 31;
+  if (g.group == BWD_GROUP_ROWS && !split && !g.c_trans && !g.a.trans && g.b.trans && g.N % kBwdBN == 0 &&
+      g.K % kBwdBK == 0 && g.a.ld % 8 == 0 && g.b.ld % 8 == 0 && g.a_bytes < lim && g.b_bytes < lim) {
+    TRY(set_lds_limit(k_bwd_gemm_dma, kBwdDmaLds));
+    hipLaunchKernelGGL(k_bwd_gemm_dma, grid, dim3(256), kBwdDmaLds, st, g);
+    HIP_TRY(hipGetLastError());
+    return MOE_OK;
+  }
   if (split && g.c_trans)
     hipLaunchKernelGGL((k_bwd_gemm<1, 1>), grid, dim3(256), bwd_lds_bytes<1>(), st, g);
   else if (split)
@@ -1199,14 +1212,26 @@ moe_status moe_backward(const moe_desc* d, const void* x, const void* router_w, 
   g.tiles = p.tiles;
   g.ntiles = p.meta;
   g.offsets = p.offsets;
+  const long Pl = P;
+  // x and dy in permuted row order (the weight-gradient products' B)
+  uint16_t* xp = reinterpret_cast<uint16_t*>(ws + B.xp);
+  uint16_t* dyp = reinterpret_cast<uint16_t*>(ws + B.dyp);
+  hipLaunchKernelGGL(k_bwd_gather, dim3(di.cus * 8), dim3(256), 0, st, static_cast<const uint16_t*>(x), p.perm, k, H,
+                     Pl, xp);
+  HIP_TRY(hipGetLastError());
+  hipLaunchKernelGGL(k_bwd_gather, dim3(di.cus * 8), dim3(256), 0, st, static_cast<const uint16_t*>(dy), p.perm, k,
+                     H, Pl, dyp);
+  HIP_TRY(hipGetLastError());
   // GU = x[tok] W_gu[e]^T
   g.a = bwd_op(x, H, 0, p.perm, k);
   g.b = bwd_op(w_gate_up, H, 1, nullptr, 1, H2 * H);
+  g.a_bytes = (long)T * H * 2; g.b_bytes = H2 * H * 2;
   g.c = GU; g.ldc = H2; g.N = (int)H2; g.K = H; g.group = BWD_GROUP_ROWS;
   TRY(launch_bwd_gemm(g, pairs, up(H2, kBwdBN), 1, st));
   // dAu = dy[tok] W_d[e]
   g.a = bwd_op(dy, H, 0, p.perm, k);
   g.b = bwd_op(w_down, I, 0, nullptr, 1, (long)H * I);
+  g.a_bytes = (long)T * H * 2; g.b_bytes = (long)H * I * 2;
   g.c = dAu; g.ldc = I; g.N = I; g.K = H;
   TRY(launch_bwd_gemm(g, pairs, up(I, kBwdBN), 1, st));
   // rows: dw, dG|dU, w a
@@ -1216,17 +1241,20 @@ moe_status moe_backward(const moe_desc* d, const void* x, const void* router_w, 
   // dXr = [dG|dU] W_gu[e]
   g.a = bwd_op2(dgu_hi, dgu_lo, H2, 0);
   g.b = bwd_op(w_gate_up, H, 0, nullptr, 1, H2 * H);
+  g.a_bytes = Pl * H2 * 2; g.b_bytes = H2 * H * 2;
   g.c = dXr; g.ldc = H; g.N = H; g.K = (int)H2;
   TRY(launch_bwd_gemm(g, pairs, up(H, kBwdBN), 1, st));
-  // dW_gu[e] = sum_p [dG|dU]_p^T x[tok(p)]
+  // dW_gu[e] = sum_p [dG|dU]_p^T x[tok(p)] (x in permuted order)
   g.a = bwd_op2(dgu_hi, dgu_lo, H2, 1);
-  g.b = bwd_op(x, H, 0, p.perm, k);
+  g.b = bwd_op(xp, H, 0);
+  g.a_bytes = Pl * H2 * 2; g.b_bytes = Pl * H * 2;
   g.c = dw_gate_up; g.ldc = H; g.c_gstride = H2 * H; g.M = (int)H2; g.N = H; g.group = BWD_GROUP_K;
   TRY(launch_bwd_gemm(g, up(H2, kBwdBM), up(H, kBwdBN), E, st));
   // dW_d[e] = sum_p dy[tok(p)]^T (w a)_p, formed as its transpose
-  // sum_p (w a)_p^T dy[tok(p)] (the fp32 operand as A) and stored transposed
+  // sum_p (w a)_p^T dy[tok(p)] (the split operand as A) and stored transposed
   g.a = bwd_op2(aw_hi, aw_lo, I, 1);
-  g.b = bwd_op(dy, H, 0, p.perm, k);
+  g.b = bwd_op(dyp, H, 0);
+  g.a_bytes = Pl * I * 2; g.b_bytes = Pl * H * 2;
   g.c = dw_down; g.ldc = I; g.c_trans = 1; g.c_gstride = (long)H * I; g.M = I; g.N = H;
   TRY(launch_bwd_gemm(g, up(I, kBwdBM), up(H, kBwdBN), E, st));
   g.c_trans = 0;
