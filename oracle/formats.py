@@ -14,6 +14,15 @@ formats (E2M1: bias 1, values 0, 0.5, 1, 1.5, 2, 3, 4, 6 with a sign bit;
 E8M0: 2**(code - 127), code 255 is NaN).  BF16 is the top half of an IEEE
 binary32.
 
+E5M6, the third format of the quantisation bullet, is not defined on the pages
+either; it is read (R15) as the IEEE-754-style binary format with 1 sign, 5
+exponent (bias 15) and 6 fraction bits: subnormals at exponent 0, exponent 31
+reserved for infinities and NaN (as in binary16), largest finite
+(2 - 2**-6) * 2**15 = 65024.  Codes are 12 bits (sign in bit 11), stored two
+to three bytes, little-endian: byte 0 = low 8 bits of the first code, byte 1
+= its high 4 bits and the low 4 bits of the second, byte 2 = the second's high
+8 bits.
+
 Every table here is built from those definitions with integer arithmetic, not
 from any library cast; ``tests/test_formats.py`` pins them exhaustively against
 the closed forms and against PyTorch's own float8 casts.
@@ -104,6 +113,66 @@ def e4m3_encode(values) -> np.ndarray:
     code = np.where(mag == _E4M3_POS[hi], hi, code)             # exact hits
     sign = np.signbit(v).astype(np.uint8) << 7
     return (code.astype(np.uint8) | sign).astype(np.uint8)
+
+
+E5M6_MAX = 65024.0
+
+
+def _e5m6_value(code: int) -> float:
+    """Value of one 12-bit E5M6 code: sign (bit 11), 5 exponent bits (bias 15), 6 fraction bits."""
+    sign = -1.0 if (code >> 11) & 1 else 1.0
+    exp = (code >> 6) & 0x1F
+    man = code & 0x3F
+    if exp == 0x1F:
+        return sign * float("inf") if man == 0 else float("nan")
+    if exp == 0:                       # subnormal: 0.m * 2**(1 - bias)
+        return sign * (man / 64.0) * 2.0 ** (1 - 15)
+    return sign * (1.0 + man / 64.0) * 2.0 ** (exp - 15)
+
+
+E5M6_TABLE = np.array([_e5m6_value(c) for c in range(4096)], dtype=np.float64)
+_E5M6_POS = E5M6_TABLE[:0x7C0]         # +0 .. +65024, increasing in code order
+
+
+def e5m6_decode(codes) -> np.ndarray:
+    """12-bit E5M6 codes -> float64 values."""
+    return E5M6_TABLE[np.asarray(codes, dtype=np.int64) & 0xFFF]
+
+
+def e5m6_encode(values) -> np.ndarray:
+    """Round float64 values to E5M6 codes: round to nearest, ties to the even
+    code (fraction LSB 0), saturating to +-65024.  The sign bit follows the
+    input's sign."""
+    v = np.asarray(values, dtype=np.float64)
+    if not np.all(np.isfinite(v)):
+        raise ValueError("non-finite value passed to e5m6_encode")
+    mag = np.minimum(np.abs(v), E5M6_MAX)
+    hi = np.searchsorted(_E5M6_POS, mag, side="left")          # first code >= mag
+    hi = np.minimum(hi, 0x7BF)
+    lo = np.maximum(hi - 1, 0)
+    d_lo = mag - _E5M6_POS[lo]
+    d_hi = _E5M6_POS[hi] - mag
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo)
+    code = np.where(mag == _E5M6_POS[hi], hi, code)             # exact hits
+    sign = np.signbit(v).astype(np.uint16) << 11
+    return (code.astype(np.uint16) | sign).astype(np.uint16)
+
+
+def e5m6_pack(codes) -> np.ndarray:
+    """[..., 2n] 12-bit codes -> [..., 3n] bytes (two codes to three bytes)."""
+    c = np.asarray(codes, dtype=np.uint32)
+    a, b = c[..., 0::2], c[..., 1::2]
+    out = np.stack([a & 0xFF, (a >> 8) | ((b & 0xF) << 4), b >> 4], axis=-1)
+    return out.reshape(*c.shape[:-1], -1).astype(np.uint8)
+
+
+def e5m6_unpack(packed) -> np.ndarray:
+    """[..., 3n] bytes -> [..., 2n] 12-bit codes."""
+    p = np.asarray(packed, dtype=np.uint32).reshape(*np.shape(packed)[:-1], -1, 3)
+    a = p[..., 0] | ((p[..., 1] & 0xF) << 8)
+    b = (p[..., 1] >> 4) | (p[..., 2] << 4)
+    return np.stack([a, b], axis=-1).reshape(*np.shape(packed)[:-1], -1).astype(np.uint16)
 
 
 def bf16_round(values) -> np.ndarray:

@@ -86,6 +86,14 @@ R14 The backward pass (the training workload of the pages: trainable
     with e = ids[t, j] and w the softmax of the selected logits
     l = x_r W_r^T + b.  The router's gradient reaches x through the logits
     (x_r is the router's input, R3).
+R15 E5M6 quantisation (the third format of the quantisation bullet, a
+    conversion target: no matrix-core instruction takes it, and every E5M6
+    value is exactly a BF16 and an fp32 number): the format of
+    formats.py; per token and 128 channels as R12 with 65024 in place of
+    448: s = fl32(amax / 65024) (a zero block gets s = 1), codes =
+    E5M6_RNE_sat(fl32(x * fl32(1 / s))); or s = 2**e with e the smallest
+    integer such that 65024 * 2**e >= amax (clamped to [-127, 127]) and codes
+    of the exact x / s.  Dequantisation gives fl32(value(code) * s).
 R9  The combine is the weighted sum over j of w[t, j] * expert_output.  The
     reference result is the unrounded fp64 sum; the device sums in fp32 in
     ascending j and rounds the result to BF16.
@@ -221,15 +229,16 @@ def swiglu(g: np.ndarray, u: np.ndarray) -> np.ndarray:
 
 
 # --------------------------------------------------- input quantisation (R12)
-def pow2_scale_exponent(amax: np.ndarray) -> np.ndarray:
-    """Smallest integer e with 448 * 2**e >= amax (amax > 0), clamped to
-    [-127, 127]; 0 where amax == 0 (scale 1).  Exact: 448 * 2**e is exact in
-    fp64 for every e in range."""
+def pow2_scale_exponent(amax: np.ndarray, fmax: float = F.E4M3_MAX) -> np.ndarray:
+    """Smallest integer e with fmax * 2**e >= amax (amax > 0; fmax the
+    format's largest finite value, 448 for E4M3), clamped to [-127, 127]; 0
+    where amax == 0 (scale 1).  Exact: fmax * 2**e is exact in fp64 for every
+    e in range."""
     amax = np.asarray(amax, dtype=np.float64)
-    e = np.ceil(np.log2(np.where(amax > 0, amax, 1.0) / F.E4M3_MAX)).astype(np.int64)
+    e = np.ceil(np.log2(np.where(amax > 0, amax, 1.0) / fmax)).astype(np.int64)
     # correct the floating-point log2 by one step either way, exactly
-    e = np.where(np.ldexp(F.E4M3_MAX, e - 1) >= amax, e - 1, e)
-    e = np.where(np.ldexp(F.E4M3_MAX, e) < amax, e + 1, e)
+    e = np.where(np.ldexp(fmax, e - 1) >= amax, e - 1, e)
+    e = np.where(np.ldexp(fmax, e) < amax, e + 1, e)
     e = np.clip(e, -127, 127)
     return np.where(amax > 0, e, 0)
 
@@ -261,6 +270,42 @@ def quantise_tokens_fp8(x: np.ndarray, pow2: bool = False):
         s = s32.astype(np.float64)
     codes = F.e4m3_encode(v)
     return codes.reshape(T, H), s
+
+
+# ---------------------------------------------------- E5M6 quantisation (R15)
+def quantise_tokens_e5m6(x: np.ndarray, pow2: bool = False):
+    """Per-token, per-128-channel E5M6 quantisation (reading R15).  x: [T, H]
+    values exactly representable in fp32.  Returns (codes uint16 [T, H] of
+    12 bits, scales float64 [T, H/128] (fp32 values)).  The same steps as
+    quantise_tokens_fp8 with the E5M6 maximum: s = fl32(amax / 65024),
+    inv = fl32(1 / s), v = fl32(x * inv), E5M6 round-to-nearest-even with
+    saturation; with pow2, s = 2**e and v = x / s exactly."""
+    x = np.asarray(x, dtype=np.float64)
+    T, H = x.shape
+    b = x.reshape(T, H // 128, 128)
+    if not np.all(np.isfinite(b)) or not np.array_equal(b, b.astype(np.float32).astype(np.float64)):
+        raise ValueError("quantise_tokens_e5m6 takes finite values representable in fp32")
+    amax = np.abs(b).max(axis=2)
+    if pow2:
+        s = np.ldexp(1.0, pow2_scale_exponent(amax, F.E5M6_MAX))
+        v = b / s[:, :, None]                                   # exact (power-of-two scaling)
+    else:
+        a32 = amax.astype(np.float32)
+        s32 = np.where(a32 > 0, a32 / np.float32(F.E5M6_MAX), np.float32(1.0)).astype(np.float32)
+        inv = (np.float32(1.0) / s32).astype(np.float32)
+        v = (b.astype(np.float32) * inv[:, :, None]).astype(np.float32).astype(np.float64)
+        s = s32.astype(np.float64)
+    return F.e5m6_encode(v).reshape(T, H), s
+
+
+def dequantise_e5m6(codes: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """fl32(value(code) * s) per element (reading R15): codes [T, H], scales
+    [T, H/128] -> fp32 values as float64."""
+    codes = np.asarray(codes)
+    T, H = codes.shape
+    v = F.e5m6_decode(codes).reshape(T, H // 128, 128)
+    out = (v.astype(np.float32) * np.asarray(s, dtype=np.float32)[:, :, None]).astype(np.float32)
+    return out.reshape(T, H).astype(np.float64)
 
 
 # --------------------------------------------- device deviation bounds (R10)

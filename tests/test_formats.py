@@ -113,3 +113,66 @@ def test_bf16_round_matches_torch_rne():
 def test_f32_round():
     assert F.f32_round(np.array([1.0 + 2.0 ** -30]))[0] == 1.0
     assert F.f32_round(np.array([1.0 + 2.0 ** -23]))[0] == 1.0 + 2.0 ** -23
+
+
+# ------------------------------------------------------------- E5M6 (R15)
+def _fp16_from_e5m6_fields(code: int) -> float:
+    # E5M6 has binary16's sign and exponent fields and the top 6 of its 10
+    # fraction bits: the same value as the binary16 number with the low four
+    # fraction bits zero (numpy's float16 decodes it independently)
+    bits = ((code >> 11) & 1) << 15 | ((code >> 6) & 0x1F) << 10 | (code & 0x3F) << 4
+    return float(np.array([bits], dtype=np.uint16).view(np.float16)[0])
+
+
+def test_e5m6_table_matches_binary16_subset_exhaustively():
+    ref = np.array([_fp16_from_e5m6_fields(c) for c in range(4096)])
+    nan = np.isnan(ref)
+    assert np.array_equal(nan, np.isnan(F.E5M6_TABLE))
+    assert np.array_equal(ref[~nan], F.E5M6_TABLE[~nan])
+    assert nan.sum() == 2 * 63                                   # exponent 31, fraction != 0
+
+
+def test_e5m6_closed_form_landmarks():
+    assert F.E5M6_TABLE[0x7BF] == F.E5M6_MAX == (2 - 2.0 ** -6) * 2.0 ** 15
+    assert F.E5M6_TABLE[0x001] == 2.0 ** -20                    # smallest subnormal
+    assert F.E5M6_TABLE[0x040] == 2.0 ** -14                    # smallest normal
+    assert F.E5M6_TABLE[0x3C0] == 1.0 and F.E5M6_TABLE[0xBC0] == -1.0
+    assert np.isinf(F.E5M6_TABLE[0x7C0]) and np.signbit(F.E5M6_TABLE[0x800])
+    assert np.all(np.diff(F.E5M6_TABLE[:0x7C0]) > 0)
+
+
+def test_e5m6_encode_ties_even_and_saturates():
+    pos = F.E5M6_TABLE[:0x7C0]
+    mids = (pos[:-1] + pos[1:]) / 2
+    lo = np.arange(0x7BF)
+    even = np.where(lo % 2 == 0, lo, lo + 1)
+    assert np.array_equal(F.e5m6_encode(mids), even)
+    assert np.array_equal(F.e5m6_encode(np.nextafter(mids, 0)), lo)
+    assert np.array_equal(F.e5m6_encode(np.nextafter(mids, np.inf)), lo + 1)
+    assert np.array_equal(F.e5m6_encode(pos), np.arange(0x7C0))
+    assert np.array_equal(F.e5m6_encode(-pos[1:]), np.arange(1, 0x7C0) | 0x800)
+    assert F.e5m6_encode([65024.0 + 300, 1e30, -1e30]).tolist() == [0x7BF, 0x7BF, 0xFBF]
+    assert F.e5m6_encode([-0.0])[0] == 0x800
+
+
+def test_e5m6_encode_matches_arithmetic_rounding():
+    # the same rounding written as arithmetic: the value's unit in the last
+    # of 6 fraction bits (2**-20 below the normal range), np.rint (ties to
+    # even) of the quotient, then saturation
+    rng = np.random.default_rng(5)
+    v = rng.standard_normal(200000) * np.exp2(rng.uniform(-24, 18, 200000))
+    a = np.abs(v)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    ulp = np.exp2(np.maximum(e, -14) - 6)
+    ref = np.minimum(np.rint(a / ulp) * ulp, F.E5M6_MAX) * np.sign(v)
+    got = F.e5m6_decode(F.e5m6_encode(v))
+    assert np.array_equal(got, ref)
+
+
+def test_e5m6_pack_layout_and_round_trip():
+    assert F.e5m6_pack([0x123, 0xABC]).tolist() == [0x23, 0xC1, 0xAB]
+    rng = np.random.default_rng(6)
+    c = rng.integers(0, 4096, size=(3, 256)).astype(np.uint16)
+    p = F.e5m6_pack(c)
+    assert p.shape == (3, 384)
+    assert np.array_equal(F.e5m6_unpack(p), c)

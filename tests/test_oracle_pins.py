@@ -510,3 +510,42 @@ def test_layer_with_channel_scales_equals_dense_bruteforce():
     r = O.layer(spec, inp)
     ref = _dense_bruteforce(spec, inp)
     assert np.allclose(r["y"], ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+
+
+# ------------------------------------------------ E5M6 quantisation (R15)
+def test_e5m6_quantisation_block_max_and_error_bound():
+    rng = np.random.default_rng(21)
+    x = (rng.standard_normal((6, 384)) * np.exp2(rng.integers(-10, 10, (6, 1)))).astype(np.float32).astype(np.float64)
+    x[2, 128:256] = 0.0                                          # a zero block
+    for pow2 in (False, True):
+        codes, s = O.quantise_tokens_e5m6(x, pow2=pow2)
+        b = x.reshape(6, 3, 128)
+        amax = np.abs(b).max(axis=2)
+        assert s[2, 1] == 1.0 and np.all(codes[2, 128:256] == 0)
+        if pow2:
+            assert O.powers_of_two(s)
+            nz = amax > 0
+            assert np.all(F.E5M6_MAX * s[nz] >= amax[nz]) and np.all(F.E5M6_MAX * s[nz] / 2 < amax[nz])
+            assert np.array_equal(codes.reshape(6, 3, 128), F.e5m6_encode(b / s[:, :, None]))
+        else:
+            # the block maximum lands on the largest code
+            arg = np.abs(b).argmax(axis=2)
+            top = np.take_along_axis(codes.reshape(6, 3, 128), arg[:, :, None], 2)[:, :, 0] & 0x7FF
+            assert np.all(top[amax > 0] == 0x7BF)
+        deq = O.dequantise_e5m6(codes, s)
+        # half a unit in the 6th fraction bit, the subnormal step, and the fp32 roundings
+        bound = np.abs(x) * (2.0 ** -7 + 2.0 ** -22) + np.repeat(s, 128, axis=1) * 2.0 ** -21
+        assert np.all(np.abs(deq - x) <= bound)
+
+
+def test_e5m6_quantisation_uses_the_e5m6_maximum():
+    # a block whose maximum is 448 would keep its values unscaled under the
+    # E4M3 rule; under the E5M6 rule the maximum maps to 65024
+    x = np.zeros((1, 128))
+    x[0, 0] = 448.0
+    x[0, 1] = 3.0
+    codes, s = O.quantise_tokens_e5m6(x)
+    assert F.e5m6_decode(codes[0, 0]) == F.E5M6_MAX
+    assert np.float32(s[0, 0]) == np.float32(448.0) / np.float32(F.E5M6_MAX)
+    _, s2 = O.quantise_tokens_e5m6(x, pow2=True)
+    assert s2[0, 0] == 2.0 ** -7                                # 65024 / 128 = 508 >= 448 > 254
