@@ -203,6 +203,8 @@ def main():
     ap.add_argument("--no-evict", action="store_true", help="skip the cache-evicted per-call timing")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (moe_backward) of a BF16 layer instead (default workload dsv3_bf16)")
+    ap.add_argument("--e5m6", action="store_true",
+                    help="time the E5M6 quantisation and dequantisation of the workload's activations instead")
     ap.add_argument("--wscale", default=None, choices=["block", "channel"],
                     help="FP8 weight scale granularity (moe_desc.weight_scale; default: the workload's)")
     args = ap.parse_args()
@@ -217,6 +219,9 @@ def main():
 
     if args.backward:
         bench_backward(args)
+        return
+    if args.e5m6:
+        bench_e5m6(args)
         return
     cfg = gen.CONFIGS[args.workload]
     if args.wscale is not None:
@@ -481,6 +486,69 @@ def bench_backward(args):
     if not args.no_cpu_baseline:
         print("[bench] backward: timing the oracle on a bounded sample (host cores)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline_backward(cfg, raw, ids.cpu().numpy().astype(np.int64), dy)
+    print(json.dumps(result), flush=True)
+
+
+def bench_e5m6(args):
+    """E5M6 conversion of the workload's activations x [T][H] (BF16): the
+    quantisation (2 bytes read, 1.5 written per element, plus a 4-byte scale
+    per 128) and the dequantisation to fp32 (1.5 + 4/128 read, 4 written),
+    each HBM-bound; timed with HIP events over `steps` launches each."""
+    import torch
+    from moe_layer_router_amd import layer
+    from workloads import gen
+    cfg = gen.CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    g = torch.Generator(device="cpu").manual_seed(args.seed)
+    x = torch.randn(cfg.T, cfg.H, generator=g).to(torch.bfloat16).to(dev)
+    stream = torch.cuda.current_stream()
+    xq, xs = layer.quantize_e5m6(x)
+    out = layer.dequantize_e5m6(xq, xs)
+    torch.cuda.synchronize()
+    n = cfg.T * cfg.H
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(args.steps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / args.steps / 1e3
+
+    from moe_layer_router_amd import lib
+    t_q = timed(lambda: lib.moe_quantize_e5m6(x, xq, xs, "f32"))
+    t_d = timed(lambda: lib.moe_dequantize_e5m6(xq, xs, out))
+    bq = n * 2 + n * 1.5 + n / 128 * 4
+    bd = n * 1.5 + n / 128 * 4 + n * 4
+    roof = {"bound": "hbm", "achieved": round(bq / t_q / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(bq / t_q / 1e9 / PEAK_HBM_GBS, 4), "kernel": "k_quant_e5m6", "traffic": None}
+    result = {
+        "metric": "E5M6 per-token quantisation tokens/s (BF16 activations)", "value": round(cfg.T / t_q, 1),
+        "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(t_q * 1e3, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 in, 12-bit E5M6 codes + fp32 scales out", "data": "synthetic (seeded N(0,1) activations)",
+        "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H},
+        "roofline": roof,
+        "dequantise": {"ms": round(t_d * 1e3, 5), "achieved_GBs": round(bd / t_d / 1e9, 1),
+                       "frac": round(bd / t_d / 1e9 / PEAK_HBM_GBS, 4)},
+    }
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_info
+        from oracle import moe_oracle as O
+        rows = min(cfg.T, 512)
+        xv = x[:rows].float().cpu().double().numpy()
+        t0 = time.perf_counter()
+        O.quantise_tokens_e5m6(xv)
+        dt = time.perf_counter() - t0
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        result["cpu_baseline"] = {"value": round(rows / dt, 1), "unit": "tokens/s", "cores": int(threads),
+                                  "kind": "oracle", "sample": f"fp64 numpy oracle quantise_tokens_e5m6 on the first "
+                                                              f"{rows} tokens ({dt:.2f} s)"}
     print(json.dumps(result), flush=True)
 
 

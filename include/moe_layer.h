@@ -101,8 +101,9 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 4   /* 3: moe_desc.weight_layout and moe_desc.inter_scale;
-                               4: moe_desc.weight_scale */
+#define MOE_ABI_VERSION 5   /* 3: moe_desc.weight_layout and moe_desc.inter_scale;
+                               4: moe_desc.weight_scale;
+                               5: moe_quantize_e5m6, moe_dequantize_e5m6 */
 
 typedef enum moe_status {
   MOE_OK = 0,
@@ -261,6 +262,35 @@ moe_status moe_forward(const moe_desc* d,
  * on `stream`; errors as moe_forward. */
 moe_status moe_quantize_input(int32_t T, int32_t H, int32_t in_dtype, int32_t scale_mode, const void* x,
                               uint8_t* xq, float* x_scales, moe_stream_t stream);
+
+/* Per-token E5M6 quantisation, the third format of the same quantisation
+ * bullet (youleyou, "DeepSeek 模型更新解读 Tile Kernels 与 DeepEP V2 新特性",
+ * section "Tile Kernels": per-token / per-block / per-channel FP8 / FP4 /
+ * E5M6 quantisation).  The pages do not define E5M6; it is read as the
+ * IEEE-754-style binary format with 1 sign, 5 exponent (bias 15) and 6
+ * fraction bits: subnormals at exponent 0, exponent 31 reserved for
+ * infinities and NaN, largest finite 65024.  No matrix-core instruction
+ * takes it; it is a storage format (each value is exactly a BF16 number).
+ * For each token t and 128-channel block c of x [T][H] (in_dtype
+ * MOE_DTYPE_BF16 or MOE_DTYPE_F32, finite values): amax = max |x|;
+ * scale_mode MOE_INTER_SCALE_F32: s = fl32(amax / 65024), codes = E5M6
+ * round-to-nearest-even, saturating to +-65024, of fl32(x * fl32(1 / s));
+ * MOE_INTER_SCALE_POW2: s = the smallest power of two with 65024 s >= amax
+ * (clamped to 2^-127 .. 2^127) and codes of x / s; a block of zeros gets
+ * s = 1.  Outputs xq [T][3H/2] bytes: the 12-bit codes (sign in bit 11) of
+ * a row, two to three bytes, little-endian (byte 0 = the first code's low 8
+ * bits, byte 1 = its high 4 bits | the second code's low 4 bits << 4, byte
+ * 2 = the second code's high 8 bits), and x_scales [T][H/128] fp32.  1 <= T,
+ * H a multiple of 128, T * H < 2^31; pointers 16-byte aligned.  Enqueued on
+ * `stream`; errors as moe_quantize_input. */
+moe_status moe_quantize_e5m6(int32_t T, int32_t H, int32_t in_dtype, int32_t scale_mode, const void* x,
+                             uint8_t* xq, float* x_scales, moe_stream_t stream);
+
+/* Inverse of moe_quantize_e5m6: out [T][H] fp32 = fl32(value(code) * s)
+ * for the codes xq [T][3H/2] and scales x_scales [T][H/128] (same layout
+ * and limits).  Enqueued on `stream`. */
+moe_status moe_dequantize_e5m6(int32_t T, int32_t H, const uint8_t* xq, const float* x_scales, float* out,
+                               moe_stream_t stream);
 
 /* Bytes of the library's own device workspace used by moe_forward_static. */
 #define MOE_STATIC_WORKSPACE_BYTES ((size_t)64 << 20)

@@ -69,6 +69,18 @@ __global__ void __launch_bounds__(256) k_quant(const void* x, int T, int H, int 
   quant_blocks<IN>(x, T, H, b0, min(nblk, b0 + per), pow2 != 0, xq, xs, threadIdx.x, 256);
 }
 
+// E5M6 quantisation and dequantisation (same block-to-workgroup mapping).
+template <int IN>
+__global__ void __launch_bounds__(256) k_quant_e5m6(const void* x, int T, int H, int pow2, uint8_t* xq, float* xs) {
+  const int nblk = T * (H / 128);
+  const int per = 16 * 4;
+  const int b0 = blockIdx.x * per;
+  quant_blocks_e5m6<IN>(x, T, H, b0, min(nblk, b0 + per), pow2 != 0, xq, xs, threadIdx.x, 256);
+}
+__global__ void __launch_bounds__(256) k_dequant_e5m6(const uint8_t* xq, const float* xs, int T, int H, float* out) {
+  dequant_e5m6(xq, xs, T, H, (size_t)blockIdx.x * blockDim.x + threadIdx.x, out);
+}
+
 // Activation scales in permuted row order (FP8 layers): 256 rows per block.
 __global__ void __launch_bounds__(256) k_permute_scales(const int32_t* perm, const float* x_scales, int T, int k,
                                                         int ns, float* sxp) {
@@ -1048,6 +1060,44 @@ moe_status moe_quantize_input(int32_t T, int32_t H, int32_t in_dtype, int32_t sc
     hipLaunchKernelGGL(k_quant<QIN_BF16>, dim3((nb + 63) / 64), dim3(256), 0, st, x, T, H, pow2, xq, x_scales);
   else
     hipLaunchKernelGGL(k_quant<QIN_F32>, dim3((nb + 63) / 64), dim3(256), 0, st, x, T, H, pow2, xq, x_scales);
+  HIP_TRY(hipGetLastError());
+  return MOE_OK;
+}
+
+moe_status moe_quantize_e5m6(int32_t T, int32_t H, int32_t in_dtype, int32_t scale_mode, const void* x, uint8_t* xq,
+                             float* x_scales, moe_stream_t stream) {
+  if (T < 1) return fail(MOE_ERR_INVALID_ARGUMENT, "T must be >= 1 (got %d)", T);
+  if (H < 128 || H % 128) return fail(MOE_ERR_INVALID_ARGUMENT, "H must be a positive multiple of 128 (got %d)", H);
+  if ((long long)T * H >= (1LL << 31)) return fail(MOE_ERR_UNSUPPORTED, "T * H must be below 2^31");
+  if (in_dtype != MOE_DTYPE_BF16 && in_dtype != MOE_DTYPE_F32)
+    return fail(MOE_ERR_UNSUPPORTED, "in_dtype must be MOE_DTYPE_BF16 or MOE_DTYPE_F32 (got %d)", in_dtype);
+  if (scale_mode != MOE_INTER_SCALE_F32 && scale_mode != MOE_INTER_SCALE_POW2)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "unknown scale_mode %d", scale_mode);
+  TRY(check_ptr(x, "x"));
+  TRY(check_ptr(xq, "xq"));
+  TRY(check_ptr(x_scales, "x_scales"));
+  const int nb = T * (H / 128);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int pow2 = scale_mode == MOE_INTER_SCALE_POW2;
+  if (in_dtype == MOE_DTYPE_BF16)
+    hipLaunchKernelGGL(k_quant_e5m6<QIN_BF16>, dim3((nb + 63) / 64), dim3(256), 0, st, x, T, H, pow2, xq, x_scales);
+  else
+    hipLaunchKernelGGL(k_quant_e5m6<QIN_F32>, dim3((nb + 63) / 64), dim3(256), 0, st, x, T, H, pow2, xq, x_scales);
+  HIP_TRY(hipGetLastError());
+  return MOE_OK;
+}
+
+moe_status moe_dequantize_e5m6(int32_t T, int32_t H, const uint8_t* xq, const float* x_scales, float* out,
+                               moe_stream_t stream) {
+  if (T < 1) return fail(MOE_ERR_INVALID_ARGUMENT, "T must be >= 1 (got %d)", T);
+  if (H < 128 || H % 128) return fail(MOE_ERR_INVALID_ARGUMENT, "H must be a positive multiple of 128 (got %d)", H);
+  if ((long long)T * H >= (1LL << 31)) return fail(MOE_ERR_UNSUPPORTED, "T * H must be below 2^31");
+  TRY(check_ptr(xq, "xq"));
+  TRY(check_ptr(x_scales, "x_scales"));
+  TRY(check_ptr(out, "out"));
+  const long n8 = (long)T * H / 8;
+  hipLaunchKernelGGL(k_dequant_e5m6, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     xq, x_scales, T, H, out);
   HIP_TRY(hipGetLastError());
   return MOE_OK;
 }

@@ -124,6 +124,25 @@ def quantize_input(x: torch.Tensor, scale_mode: str = "f32", stream=None):
     return xq, xs
 
 
+def quantize_e5m6(x: torch.Tensor, scale_mode: str = "f32", stream=None):
+    """Per-token, per-128-channel E5M6 quantisation (moe_quantize_e5m6) of a
+    [T, H] bfloat16 / float32 tensor: (codes [T, 3H/2] uint8, scales
+    [T, H/128] float32)."""
+    T, H = x.shape
+    xq = torch.empty(T, H // 2 * 3, dtype=torch.uint8, device=x.device)
+    xs = torch.empty(T, H // 128, dtype=torch.float32, device=x.device)
+    lib.moe_quantize_e5m6(x.contiguous(), xq, xs, scale_mode, stream)
+    return xq, xs
+
+
+def dequantize_e5m6(xq: torch.Tensor, xs: torch.Tensor, stream=None) -> torch.Tensor:
+    """float32 [T, H] values of E5M6 codes and their scales (moe_dequantize_e5m6)."""
+    T, H = xq.shape[0], xq.shape[1] // 3 * 2
+    out = torch.empty(T, H, dtype=torch.float32, device=xq.device)
+    lib.moe_dequantize_e5m6(xq.contiguous(), xs.contiguous(), out, stream)
+    return out
+
+
 def backward(inputs: dict, topk_ids: torch.Tensor, topk_weights: torch.Tensor, dy: torch.Tensor,
              workspace: Workspace = None, stream=None, want_dbias: bool = True, out: dict = None) -> dict:
     """Gradients of a BF16 layer (moe_backward) for the routing a forward

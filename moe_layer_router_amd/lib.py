@@ -100,6 +100,10 @@ _lib.moe_forward.restype = ctypes.c_int
 _lib.moe_forward.argtypes = [ctypes.POINTER(MoeDesc)] + [_P] * 13 + [_P, ctypes.c_size_t, _P]
 _lib.moe_quantize_input.restype = ctypes.c_int
 _lib.moe_quantize_input.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P]
+_lib.moe_quantize_e5m6.restype = ctypes.c_int
+_lib.moe_quantize_e5m6.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P]
+_lib.moe_dequantize_e5m6.restype = ctypes.c_int
+_lib.moe_dequantize_e5m6.argtypes = [ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P]
 _lib.moe_backward_workspace_size.restype = ctypes.c_size_t
 _lib.moe_backward_workspace_size.argtypes = [ctypes.POINTER(MoeDesc)]
 _lib.moe_backward.restype = ctypes.c_int
@@ -246,6 +250,22 @@ def moe_quantize_input(x, xq, x_scales, scale_mode="f32", stream=None):
                                    _ptr(x_scales), _stream(stream)), "moe_quantize_input")
 
 
+def moe_quantize_e5m6(x, xq, x_scales, scale_mode="f32", stream=None):
+    """x: [T, H] bfloat16 or float32 tensor; xq [T, 3H/2] uint8; x_scales [T, H/128] float32."""
+    import torch
+    T, H = x.shape
+    in_dtype = MOE_DTYPE_BF16 if x.dtype == torch.bfloat16 else MOE_DTYPE_F32
+    _check(_lib.moe_quantize_e5m6(T, H, in_dtype, INTER_SCALES.get(scale_mode, scale_mode), _ptr(x), _ptr(xq),
+                                  _ptr(x_scales), _stream(stream)), "moe_quantize_e5m6")
+
+
+def moe_dequantize_e5m6(xq, x_scales, out, stream=None):
+    """xq [T, 3H/2] uint8, x_scales [T, H/128] float32 -> out [T, H] float32."""
+    T, H = out.shape
+    _check(_lib.moe_dequantize_e5m6(T, H, _ptr(xq), _ptr(x_scales), _ptr(out), _stream(stream)),
+           "moe_dequantize_e5m6")
+
+
 def moe_route(desc, x, x_scales, router_w, router_bias, logits, topk_ids, topk_weights, workspace,
               stream=None):
     st = _lib.moe_route(ctypes.byref(desc), _ptr(x), _ptr(x_scales), _ptr(router_w), _ptr(router_bias),
@@ -285,4 +305,4 @@ def exported_symbols():
             "moe_permute_workspace_size", "moe_get_workspace_regions", "moe_validate", "moe_forward", "moe_route",
             "moe_permute", "moe_pack_weights", "moe_status_string", "moe_last_error",
             "moe_peak_mfma_flops", "moe_peak_mfma", "moe_peak_hbm_read", "moe_backward_workspace_size",
-            "moe_backward"]
+            "moe_backward", "moe_quantize_e5m6", "moe_dequantize_e5m6"]

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert lib.moe_abi_version() == 4
+    assert lib.moe_abi_version() == 5
     assert lib.moe_status_string(lib.MOE_OK) == "MOE_OK"
     assert lib.moe_status_string(lib.MOE_ERR_WORKSPACE_TOO_SMALL) == "MOE_ERR_WORKSPACE_TOO_SMALL"
 
@@ -187,3 +187,18 @@ def test_backward_descriptor_checks():
         with pytest.raises(lib.MoeError) as ex:
             lib.moe_backward(d, A, A, A, A, A, A, A, A, A, A, A, None, None, stream=0)
         assert ex.value.status == want
+
+
+def test_e5m6_entry_points_reject_bad_arguments_without_device():
+    q, d = lib._lib.moe_quantize_e5m6, lib._lib.moe_dequantize_e5m6
+    A = 0x100000
+    assert q(0, 256, lib.MOE_DTYPE_BF16, 0, A, A, A, None) == lib.MOE_ERR_INVALID_ARGUMENT
+    assert q(4, 200, lib.MOE_DTYPE_BF16, 0, A, A, A, None) == lib.MOE_ERR_INVALID_ARGUMENT
+    assert q(4, 256, lib.MOE_DTYPE_FP8_E4M3, 0, A, A, A, None) == lib.MOE_ERR_UNSUPPORTED
+    assert q(4, 256, lib.MOE_DTYPE_F32, 7, A, A, A, None) == lib.MOE_ERR_INVALID_ARGUMENT
+    assert q(4, 256, lib.MOE_DTYPE_F32, 0, A, None, A, None) == lib.MOE_ERR_INVALID_ARGUMENT
+    assert q(1 << 20, 4096, lib.MOE_DTYPE_F32, 0, A, A, A, None) == lib.MOE_ERR_UNSUPPORTED
+    assert d(0, 256, A, A, A, None) == lib.MOE_ERR_INVALID_ARGUMENT
+    assert d(4, 100, A, A, A, None) == lib.MOE_ERR_INVALID_ARGUMENT
+    assert d(4, 256, A, A + 8, A, None) == lib.MOE_ERR_INVALID_ARGUMENT
+    assert d(4, 256, A, A, None, None) == lib.MOE_ERR_INVALID_ARGUMENT
