@@ -30,6 +30,8 @@ struct Plan {
   int pow2;                    // power-of-two scales for the layer's own quantisations
   int wchan;                   // FP8 weights with one scale per output channel
   int routing_given;
+  int head_given;              // persistent kernel: routing and permutation already done by the
+                               // separate kernels in the same stream (its head queue is empty)
   int nblk;                    // 256-token blocks
   int nTR, nER;                // router tiles (kRouterTokens x kRouterExperts)
   int nKS;                     // router K slices (partial logits summed by the top-k)

@@ -340,6 +340,7 @@ __device__ __noinline__ void mega_scatter_item(KPlan* pv, int b_) {
                           p.perm, p.row_of, lds);
 }
 constexpr int kSxpRows = 256;             // permuted rows per activation-scale item
+constexpr int kMegaHeadSplitBlocks = 8;   // 256-token blocks from which the head runs as separate kernels
 __device__ __noinline__ void mega_sxp_item(KPlan* pv, int i_) {
   const Plan p = load_plan(pv);
   const int r0 = uni_i(i_) * kSxpRows;
@@ -359,22 +360,25 @@ k_mega(Plan p) {
   const int tid = threadIdx.x;
   KPlan* const pk = (KPlan*)__builtin_amdgcn_kernarg_segment_ptr();   // p itself (the only argument)
   trace_stamp(p.trace, 0);
-  const int nR = p.routing_given ? 0 : p.nTR * p.nER * p.nKS;
+  // (with head_given the separate kernels have done the whole head: no items)
+  const bool head = !p.head_given;
+  const int nR = (p.routing_given || !head) ? 0 : p.nTR * p.nER * p.nKS;
   // with the router's channels in slices, kReduceParts items per router tile
   // sum the slices once all of them are done
-  const int nRd = (p.routing_given || p.nKS == 1) ? 0 : p.nTR * p.nER * kReduceParts;
-  const int nK = p.routing_given ? 0 : (p.T + kTopkItemTokens - 1) / kTopkItemTokens;
+  const int nRd = (p.routing_given || !head || p.nKS == 1) ? 0 : p.nTR * p.nER * kReduceParts;
+  const int nK = (p.routing_given || !head) ? 0 : (p.T + kTopkItemTokens - 1) / kTopkItemTokens;
   // histogram items only when there are several 256-token blocks (a single
   // block counts itself in its scatter item)
-  const int nC = (p.nblk > 1) ? p.nblk : 0;
+  const int nC = (head && p.nblk > 1) ? p.nblk : 0;
+  const int nS = head ? p.nblk : 0;
   // FP8 layers: the activation scales in permuted row order, after the scatter
-  const int nX = p.sxp ? (p.T * p.k + kSxpRows - 1) / kSxpRows : 0;
+  const int nX = (head && p.sxp) ? (p.T * p.k + kSxpRows - 1) / kSxpRows : 0;
   // BF16 input quantised in the layer: quantisation items come first (they
   // depend on nothing; the activation-scale items and the GEMMs wait for them)
-  const int nQ = p.quant_in ? (p.T * (p.H / 128) + kQuantItemBlocks - 1) / kQuantItemBlocks : 0;
+  const int nQ = (head && p.quant_in) ? (p.T * (p.H / 128) + kQuantItemBlocks - 1) / kQuantItemBlocks : 0;
   const int q_rt = nQ;
   const int q_red = q_rt + nR, q_topk = q_red + nRd, q_count = q_topk + nK, q_scat = q_count + nC,
-            q_sxp = q_scat + p.nblk;
+            q_sxp = q_scat + nS;
   const int q_end = q_sxp + nX;
   constexpr int kPer = kPermBlock / kTopkItemTokens;   // top-k items per 256-token block
   const int rdone_target = p.nER * ((p.nKS == 1) ? 1 : kReduceParts);   // per token tile
@@ -438,7 +442,7 @@ k_mega(Plan p) {
   if (nQ > 0 && !wait_counter(&p.ctr[CTR_QUANT_DONE], nQ, p.err, &s_ok, false)) return;
   if (nX > 0) {
     if (!wait_counter(&p.ctr[CTR_SXP_DONE], nX, p.err, &s_ok)) return;     // (after every scatter item)
-  } else if (!wait_counter(&p.ctr[CTR_SCATTER_DONE], p.nblk, p.err, &s_ok)) {
+  } else if (head && !wait_counter(&p.ctr[CTR_SCATTER_DONE], p.nblk, p.err, &s_ok)) {
     return;
   }
   if (tid <= kXcds) s_first[tid] = __hip_atomic_load(&p.meta[1 + tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -816,7 +820,12 @@ moe_status launch_layer(const Plan& p, const DevInfo& di, int mode, hipStream_t 
   const size_t zero_ints = (p.zero_bytes + 256) / 4;   // error word region + counters
   hipLaunchKernelGGL(k_zero, dim3(16), dim3(256), 0, st, p.err, zero_ints);
   HIP_TRY(hipGetLastError());
-  if (mode == MOE_MODE_SEPARATE) {
+  // The persistent kernel's head (routing and permutation) runs at one
+  // workgroup per CU; from kMegaHeadSplitBlocks 256-token blocks on, the
+  // separate kernels (several workgroups per CU) do it faster, and the
+  // persistent kernel then starts at the GEMM items.
+  const bool split_head = mode != MOE_MODE_SEPARATE && p.nblk >= kMegaHeadSplitBlocks;
+  if (mode == MOE_MODE_SEPARATE || split_head) {
     if (p.quant_in) {
       const int nb = p.T * (p.H / 128);
       hipLaunchKernelGGL(k_quant<QIN_BF16>, dim3((nb + 63) / 64), dim3(256), 0, st, (const void*)p.xb, p.T, p.H,
@@ -830,6 +839,8 @@ moe_status launch_layer(const Plan& p, const DevInfo& di, int mode, hipStream_t 
                          p.k, p.H / 128, p.sxp);
       HIP_TRY(hipGetLastError());
     }
+  }
+  if (mode == MOE_MODE_SEPARATE) {
     const GemmArgs g = gemm_args(p);
     const int lds = gemm_lds(AF == ACT_FP8);
     TRY(set_lds_limit(k_gemm<AF, WF, 1>, lds));
@@ -849,7 +860,9 @@ moe_status launch_layer(const Plan& p, const DevInfo& di, int mode, hipStream_t 
     int occ = 0;
     HIP_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_mega<AF, WF>, 256, lds));
     if (occ < 1) occ = 1;
-    hipLaunchKernelGGL((k_mega<AF, WF>), dim3(di.cus * occ), dim3(256), lds, st, p);
+    Plan pm = p;
+    pm.head_given = split_head ? 1 : 0;
+    hipLaunchKernelGGL((k_mega<AF, WF>), dim3(di.cus * occ), dim3(256), lds, st, pm);
     HIP_TRY(hipGetLastError());
   }
   return MOE_OK;
