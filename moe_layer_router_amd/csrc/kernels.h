@@ -39,6 +39,7 @@ struct Plan {
   int tile_rows;               // rows of a full GEMM tile
   int nnb1, nnb2;              // N blocks of gate|up (128 channels) and down (256 columns)
   int nCT;                     // combine token chunks per N block
+  int comb_tokens;             // tokens per combine item (kCombineTokens, fewer for small T)
   // caller buffers
   const uint8_t* x; const float* x_scales; const uint16_t* wr; const float* bias;
   const uint16_t* xb;          // BF16 input (quant_in), the router's input

@@ -348,8 +348,9 @@ __device__ __noinline__ void mega_sxp_item(KPlan* pv, int i_) {
 }
 __device__ __noinline__ void mega_combine_item(KPlan* pv, int nb_, int c) {
   const Plan p = load_plan(pv);
-  const int nb = uni_i(nb_), t0 = uni_i(c) * kCombineTokens;
-  combine_rows(p.staging, p.y, p.T, p.H, p.k, t0, min(p.T, t0 + kCombineTokens), nb * 256,
+  const int ct = uni_i(p.comb_tokens);
+  const int nb = uni_i(nb_), t0 = uni_i(c) * ct;
+  combine_rows(p.staging, p.y, p.T, p.H, p.k, t0, min(p.T, t0 + ct), nb * 256,
                   min(p.H, nb * 256 + 256));
 }
 
@@ -496,7 +497,7 @@ k_mega(Plan p) {
   trace_stamp(p.trace, 4);
   trace_count(p.trace, 7, n_items);
 
-  // 4. combine items (N block, 256 tokens) once every down item of the N
+  // 4. combine items (N block, comb_tokens tokens) once every down item of the N
   // block is done (all down items have been claimed)
   for (;;) {
     __syncthreads();
@@ -722,6 +723,7 @@ moe_status fill_plan(const moe_desc* d, const Layout& L, char* ws, Plan* P) {
   p.nblk = L.nblk; p.nTR = L.nTR; p.nER = L.nER; p.nKS = L.nKS; p.max_tiles = L.max_tiles;
   p.tile_rows = p.act_fp8 ? GemmLds<ACT_FP8>::kRows : GemmLds<ACT_BF16>::kRows;
   p.nnb1 = L.nnb1; p.nnb2 = L.nnb2;
+  p.comb_tokens = kCombineTokens;
   p.nCT = (d->T + kCombineTokens - 1) / kCombineTokens;
   p.err = reinterpret_cast<int32_t*>(ws + L.err);
   p.ctr = reinterpret_cast<int32_t*>(ws + L.ctr);
@@ -862,6 +864,13 @@ moe_status launch_layer(const Plan& p, const DevInfo& di, int mode, hipStream_t 
     if (occ < 1) occ = 1;
     Plan pm = p;
     pm.head_given = split_head ? 1 : 0;
+    // combine items: at least two per workgroup where the token count allows
+    // (a decode batch has one 256-token chunk per N block: too few items for
+    // the grid, and the combine tail is then latency-bound)
+    const int nnb = (p.H + 255) / 256;
+    while (pm.comb_tokens > 16 && (long)((p.T + pm.comb_tokens - 1) / pm.comb_tokens) * nnb < 2L * di.cus * occ)
+      pm.comb_tokens /= 2;
+    pm.nCT = (p.T + pm.comb_tokens - 1) / pm.comb_tokens;
     hipLaunchKernelGGL((k_mega<AF, WF>), dim3(di.cus * occ), dim3(256), lds, st, pm);
     HIP_TRY(hipGetLastError());
   }
