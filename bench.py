@@ -306,6 +306,10 @@ def main():
     roof, t_mfma, t_hbm = roofline(cfg, f_exp, f_router, nbytes, t_launch)
     kernel = "k_mega" if args.mode == "mega" else "layer_separate"
     roof["kernel"] = kernel
+    # what the timed interval holds (the per-call HIP event pair)
+    roof["covers"] = ("one moe_forward call: the counter clear, the routing and permutation kernels (from 2048 "
+                      "tokens on; below that they run inside k_mega) and k_mega" if args.mode == "mega" else
+                      "one moe_forward call: every kernel of the separate pipeline")
     # (the committed counter summaries are of the workloads' own weight scales)
     roof["traffic"] = measured_traffic(kernel, cfg.name) if cfg == gen.CONFIGS[cfg.name] else None
     tflops = (f_exp + f_router) / (ms / 1e3) / 1e12
