@@ -739,6 +739,40 @@ def backward_exact(xh, xr, wr, b, w_gu, w_d, ids, dy, I: int) -> dict:
     return dict(dx=dx + dxr, dx_experts=dx, dx_router=dxr, dw_gate_up=dw_gu, dw_down=dw_d, dw_router=dwr, dbias=db, dweights=dws)
 
 
+def weight_grad_elements(xh, xr, wr, b, w_gu_e, w_d_e, e: int, ids, dy, I: int, chans, cols) -> dict:
+    """Elements of one expert's weight gradients (R14) from their
+    definition, for the channels `chans` (indices into 0..I-1) and the model
+    columns `cols`: dW_gate_up[e][i][h] (gate rows i, up rows I + i) and
+    dW_down[e][h][i], summed over the (token, slot) pairs routed to e:
+
+    dG = dA_i u_i SiLU'(g_i),  dU = dA_i SiLU(g_i),  dA_i = w <dy, W_d[e][:, i]>
+    dW_gate[i][h] += dG x[h],  dW_up[i][h] += dU x[h],
+    dW_down[h][i] += w dy[h] SiLU(g_i) u_i
+
+    with g_i = <W_gu[e][i], x>, u_i = <W_gu[e][I + i], x> and w the pair's
+    routing weight (softmax over the token's selected logits).  Only rows i
+    and I + i of W_gu[e] and column i of W_d[e] are read, so the cost is
+    three dot products of length H per pair and channel."""
+    ids = np.asarray(ids, dtype=np.int64)
+    chans = np.asarray(chans, dtype=np.int64)
+    cols = np.asarray(cols, dtype=np.int64)
+    gate = np.zeros((chans.size, cols.size))
+    up = np.zeros((chans.size, cols.size))
+    down = np.zeros((cols.size, chans.size))
+    toks, slots = np.nonzero(ids == e)
+    for t, j in zip(toks, slots):
+        logits = xr[t] @ wr.T + b
+        w = topk_weights(logits[None, :], ids[t][None, :])[0, j]
+        for c, i in enumerate(chans):
+            g = w_gu_e[i] @ xh[t]
+            u = w_gu_e[I + i] @ xh[t]
+            da = w * (dy[t] @ w_d_e[:, i])
+            gate[c] += da * u * silu_grad(np.array(g)) * xh[t, cols]
+            up[c] += da * silu(np.array(g)) * xh[t, cols]
+            down[:, c] += w * dy[t, cols] * silu(np.array(g)) * u
+    return dict(dw_gate=gate, dw_up=up, dw_down=down)
+
+
 def layer_backward(spec: Spec, inputs: dict, ids, dy) -> dict:
     """The backward pass of the layer (R14) for routing ids [T, k] and the
     output gradient dy [T, H]: gradients of x, W_gate_up, W_down, W_r and

@@ -101,3 +101,43 @@ def test_layer_backward_decodes_the_inputs():
     ref = O.backward_exact(xh, xh, F.bf16_decode(inp["router_w"]), np.zeros(cfg.E), w_gu, w_d, ids, dy, cfg.I)
     for key in ("dx", "dw_gate_up", "dw_down", "dw_router", "dbias"):
         assert np.array_equal(r[key], ref[key]), key
+
+
+def test_weight_grad_elements_match_backward_exact():
+    # the per-element definition used for full-size sampling against the
+    # whole-layer backward on a small problem, for a busy and a sparse expert
+    rng = np.random.default_rng(77)
+    T, H, E, k, I = 40, 24, 6, 3, 8
+    xh = rng.standard_normal((T, H))
+    wr = rng.standard_normal((E, H)) / 5
+    b = rng.standard_normal(E) / 10
+    w_gu = rng.standard_normal((E, 2 * I, H)) / 5
+    w_d = rng.standard_normal((E, H, I)) / 3
+    dy = rng.standard_normal((T, H))
+    ids = O.topk_select(xh @ wr.T + b, k)
+    ref = O.backward_exact(xh, xh, wr, b, w_gu, w_d, ids, dy, I)
+    counts = np.bincount(ids.ravel(), minlength=E)
+    chans = np.array([0, 3, I - 1])
+    cols = np.array([1, 5, H - 1, 7])
+    for e in (int(counts.argmax()), int(counts.argmin())):
+        got = O.weight_grad_elements(xh, xh, wr, b, w_gu[e], w_d[e], e, ids, dy, I, chans, cols)
+        np.testing.assert_allclose(got["dw_gate"], ref["dw_gate_up"][e][np.ix_(chans, cols)], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(got["dw_up"], ref["dw_gate_up"][e][np.ix_(I + chans, cols)], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(got["dw_down"], ref["dw_down"][e][np.ix_(cols, chans)], rtol=1e-12, atol=1e-12)
+
+
+def test_router_and_bias_gradients_sum_to_zero_over_experts():
+    # the routing weights of a token sum to one, so the logit gradients of a
+    # token sum to zero: sum_e dbias[e] = 0 and sum_e dW_r[e] = 0 exactly
+    rng = np.random.default_rng(78)
+    T, H, E, k, I = 30, 16, 8, 4, 8
+    xh = rng.standard_normal((T, H))
+    wr = rng.standard_normal((E, H)) / 4
+    b = rng.standard_normal(E) / 10
+    w_gu = rng.standard_normal((E, 2 * I, H)) / 4
+    w_d = rng.standard_normal((E, H, I)) / 3
+    dy = rng.standard_normal((T, H))
+    ids = O.topk_select(xh @ wr.T + b, k)
+    ref = O.backward_exact(xh, xh, wr, b, w_gu, w_d, ids, dy, I)
+    assert abs(ref["dbias"].sum()) < 1e-12 * np.abs(ref["dbias"]).sum()
+    assert np.all(np.abs(ref["dw_router"].sum(axis=0)) < 1e-12 * np.abs(ref["dw_router"]).sum(axis=0))
