@@ -85,3 +85,74 @@ def test_backward_is_deterministic(gpu_lib):
     torch.cuda.synchronize()
     for key in a:
         assert torch.equal(a[key], b[key]), key
+
+
+def test_backward_full_size_sampled(gpu_lib):
+    """dsv3_bf16 (T=8192, H=7168, E=256, top-8, I=2048), the configuration
+    `bench.py --backward` times, in the same launch configuration:
+    - dx of sampled tokens against the oracle's backward on the token alone
+      (its k experts; the softmax over the selection needs only the
+      selected logits);
+    - elements of the busiest and the sparsest expert's dW_gate_up and
+      dW_down against their definition (weight_grad_elements), scaled by
+      the rms of the device's whole matrix;
+    - the router and bias gradients summed over experts are zero (the
+      routing weights of a token sum to one), to fp32 accumulation;
+    - every gradient finite."""
+    from moe_layer_router_amd import layer as L
+    cfg = gen.CONFIGS["dsv3_bf16"]
+    T, H, E, k, I = cfg.T, cfg.H, cfg.E, cfg.k, cfg.I
+    print(f"[full-size backward] {cfg.name}", flush=True)
+    raw = gen.make_inputs(cfg, seed=5, device="cuda")
+    fwd = L.forward(L.pack_weights(raw), k, mode="mega")
+    ids, wts = fwd["topk_ids"].clone(), fwd["topk_weights"].clone()
+    del fwd
+    torch.cuda.empty_cache()
+    g = torch.Generator(device="cpu").manual_seed(6)
+    dy = torch.randn(T, H, generator=g).to(torch.bfloat16)
+    out = L.backward(raw, ids, wts, dy.cuda())
+    torch.cuda.synchronize()
+    for key, v in out.items():
+        assert bool(torch.isfinite(v).all()), f"non-finite {key}"
+
+    bf = lambda t: F.bf16_decode(t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16))
+    ids_np = ids.cpu().numpy().astype(np.int64)
+    xh = bf(raw["x"])
+    dyh = bf(dy)
+    wr = bf(raw["router_w"])
+    b = np.zeros(E)
+    # dx of sampled tokens
+    dx = out["dx"]
+    for t in (0, 4097, T - 1):
+        es = ids_np[t]
+        w_gu = np.stack([bf(raw["w_gate_up"][int(e)]) for e in es])
+        w_d = np.stack([bf(raw["w_down"][int(e)]) for e in es])
+        sub = O.backward_exact(xh[t:t + 1], xh[t:t + 1], wr[es], b[es], w_gu, w_d, np.arange(k)[None, :],
+                               dyh[t:t + 1], I)
+        err = _check(f"dx[{t}]", dx[t:t + 1].cpu().numpy().astype(np.float64), sub["dx"], (1,))
+        print(f"dx[{t}] max relative error {err:.2e}", flush=True)
+    # weight-gradient elements of the busiest and the sparsest used expert
+    counts = np.bincount(ids_np.ravel(), minlength=E)
+    used = np.flatnonzero(counts)
+    chans = np.array([0, 777, I - 1])
+    cols = np.array([0, 1, 1000, 3333, 5000, H - 1])
+    for e in (int(used[counts[used].argmax()]), int(used[counts[used].argmin()])):
+        ref = O.weight_grad_elements(xh, xh, wr, b, bf(raw["w_gate_up"][e]), bf(raw["w_down"][e]), e, ids_np, dyh,
+                                     I, chans, cols)
+        dgu = out["dw_gate_up"][e].cpu().numpy().astype(np.float64)
+        dwd = out["dw_down"][e].cpu().numpy().astype(np.float64)
+        for name, got, r, blk in (("gate", dgu[np.ix_(chans, cols)], ref["dw_gate"], dgu),
+                                  ("up", dgu[np.ix_(I + chans, cols)], ref["dw_up"], dgu),
+                                  ("down", dwd[np.ix_(cols, chans)], ref["dw_down"], dwd)):
+            floor = np.sqrt((blk ** 2).mean())
+            err = np.abs(got - r) / np.maximum(np.abs(r), floor)
+            assert err.max() <= BWD_TOL, f"expert {e} ({counts[e]} rows) dW_{name}: max relative error {err.max():.3e}"
+            print(f"expert {e} ({counts[e]} rows) dW_{name} max relative error {err.max():.2e}", flush=True)
+    # router and bias gradients: zero sums over experts
+    db = out["dbias"].cpu().numpy().astype(np.float64)
+    assert abs(db.sum()) <= 1e-3 * np.abs(db).sum()
+    dwr = out["dw_router"].cpu().numpy().astype(np.float64)
+    ratio = np.abs(dwr.sum(axis=0)) / np.abs(dwr).sum(axis=0)
+    assert ratio.max() <= 1e-3, f"sum over experts of dW_router / sum of magnitudes up to {ratio.max():.2e}"
+    print(f"sum of dbias / sum |dbias| {abs(db.sum()) / np.abs(db).sum():.2e}; dW_router column ratio max "
+          f"{ratio.max():.2e}", flush=True)
