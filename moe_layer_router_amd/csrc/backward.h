@@ -7,7 +7,9 @@
 //
 // With P = T*k permuted rows (row p holding flat index perm[p] = t*k + j of
 // token t = tok(p) and expert e), the backward pass is seven grouped GEMMs
-// with fp32 accumulation, and three small kernels:
+// with fp32 accumulation, and small kernels (x and dy gathered into
+// permuted row order for the weight-gradient products, the row and router
+// steps, the sums):
 //   GU   [P][2I] = x[tok(p)] W_gu[e]^T                   (recomputed linear 1)
 //   dAu  [P][I]  = dy[tok(p)] W_d[e]                     (unweighted d intermediate)
 //   rows:         a = SwiGLU(g, u), dw_p = <dAu_p, a>, dA = w_p dAu,
@@ -23,12 +25,13 @@
 // 128 x 128 tile of C, each wave 64 x 64 (4 x 4 tiles of 16 x 16, the
 // 16x16x32 BF16 MFMA), in steps of 64 K.  Operands are described as stored
 // matrices S[r][c] with a leading dimension, optionally transposed, and with
-// an optional map of the stored row (row' = map[row] / div: the permuted row
-// to its token).  Each step's tiles go to LDS as [128 rows][64 K] BF16 with
-// no padding; the 16-byte chunk c (K 8c..8c+7) of row r sits at chunk
-// c ^ ((r ^ r/8) mod 8), so that the MFMA operand reads (16 B, 8 rows at a
-// time), the K-contiguous stores (8 chunks of one row) and the transposed
-// stores (8 B, 8 rows apart) all fall in distinct banks.  A K-contiguous
+// an optional map of the stored row of a K-contiguous operand (row' =
+// map[row] / div: the permuted row to its token).  Each step's tiles go to
+// LDS as [128 rows][64 K] BF16 with no padding; the 16-byte chunk c
+// (K 8c..8c+7) of row r sits at chunk c ^ ((r ^ r/8) mod 8), so that the
+// MFMA operand reads (16 B, 8 rows at a time), the K-contiguous stores (8
+// chunks of one row) and the transposed stores (8 B, 8 rows apart) all fall
+// in distinct banks.  A K-contiguous
 // operand is staged as pieces of 8 K of one row; a transposed one (stored
 // [K][rows]: the weight-gradient products and the weights used as their
 // stored transpose) as 4 K x 8 rows per thread, loaded as four 16-byte runs
@@ -117,14 +120,12 @@ DEV BwdPos bwd_pos(int tid) {
 
 // Where this thread's pieces of an operand come from, fixed for the whole
 // K loop.  K-contiguous: the (mapped) stored row of each piece, -1 outside
-// the tile's logical rows.  Transposed: the first stored column of the row
-// octet and how many of its 8 columns lie inside (0..8); with a stored-row
-// map, the mapped rows of the next step's 4 K are fetched a step ahead.
+// the tile's logical rows.  Transposed (never mapped): the first stored
+// column of the row octet and how many of its 8 columns lie inside (0..8).
 struct BwdSrc {
   long row[4];
   long col;
   int ncol;
-  int32_t mrow[4];
 };
 
 DEV void bwd_src_init(const BwdOperand& o, bool kc, const BwdPos& ps, long row0, long nrows, BwdSrc& s) {
@@ -140,14 +141,6 @@ DEV void bwd_src_init(const BwdOperand& o, bool kc, const BwdPos& ps, long row0,
   }
 }
 
-// Mapped stored rows of the transposed operand's K 4kq..4kq+3 of the step at k0.
-DEV void bwd_src_map(const BwdOperand& o, const BwdPos& ps, long k0, long nk, long kb, BwdSrc& s) {
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const long gk = k0 + 4 * ps.kq + q;
-    s.mrow[q] = gk < nk ? o.map[kb + gk] / o.div : 0;
-  }
-}
 
 // Eight consecutive BF16 elements from `src`, those at i >= n read as zero
 // (n <= 0: all zero); `vec`: src is 16-byte aligned and n >= 8.
@@ -160,7 +153,7 @@ DEV v4i bwd_fetch(const uint16_t* src, int n, bool vec) {
 }
 
 // This thread's loads of the step at k0 of one 128 x 64 tile: K [k0, nk)
-// (zero outside); a transposed operand's stored row is kb + K (mapped).
+// (zero outside); a transposed operand's stored row is kb + K.
 // `ald`: the leading dimension keeps every piece 16-byte aligned.
 DEV void bwd_load_tile(const BwdOperand& o, const uint16_t* base, bool kc, bool ald, const BwdPos& ps,
                        const BwdSrc& s, long k0, long nk, long kb, v4i (&raw)[4]) {
@@ -175,8 +168,7 @@ DEV void bwd_load_tile(const BwdOperand& o, const uint16_t* base, bool kc, bool 
     for (int q = 0; q < 4; ++q) {
       const long gk = k0 + 4 * ps.kq + q;
       const bool in = gk < nk;
-      const long rr = o.map ? (long)s.mrow[q] : kb + gk;
-      raw[q] = bwd_fetch(base + rr * o.ld + s.col, in ? s.ncol : 0, ald && in && s.ncol == 8);
+      raw[q] = bwd_fetch(base + (kb + gk) * o.ld + s.col, in ? s.ncol : 0, ald && in && s.ncol == 8);
     }
   }
 }
@@ -271,7 +263,6 @@ __global__ void __launch_bounds__(256) k_bwd_gemm(BwdGemm g) {
   BwdSrc sa, sb;
   bwd_src_init(g.a, a_kc, ps, m0, M, sa);
   bwd_src_init(g.b, b_kc, ps, n_first, N, sb);
-  const bool a_map = !a_kc && g.a.map, b_map = !b_kc && g.b.map;
 
   v4f acc[4][4];
 #pragma unroll
@@ -316,13 +307,7 @@ __global__ void __launch_bounds__(256) k_bwd_gemm(BwdGemm g) {
     if (AF32) bwd_load_tile(g.a, abase_lo, a_kc, a_ald, ps, sa, k0, K, k_base, ral);
     bwd_load_tile(g.b, bbase, b_kc, b_ald, ps, sb, k0, K, k_base, rb);
   };
-  auto maps = [&](long k0) {                     // mapped stored rows of the step at k0
-    if (a_map) bwd_src_map(g.a, ps, k0, K, k_base, sa);
-    if (b_map) bwd_src_map(g.b, ps, k0, K, k_base, sb);
-  };
-  maps(0);
   load(0);
-  maps(nsteps > 1 ? kBwdBK : 0);
   // steps of all nt tiles in one loop: s = step of the tile at column n0
   const long total = nsteps * nt;
   long s = 0, n0 = n_first;
@@ -339,7 +324,6 @@ __global__ void __launch_bounds__(256) k_bwd_gemm(BwdGemm g) {
         bwd_src_init(g.b, b_kc, ps, n0 + kBwdBN, N, sb);
       }
       load(s1 * kBwdBK);
-      maps(s1 + 1 < nsteps ? (s1 + 1) * kBwdBK : 0);   // the step after, a step ahead
     }
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {

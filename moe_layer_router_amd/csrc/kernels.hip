@@ -917,7 +917,6 @@ moe_status check_bwd_desc(const moe_desc* d) {
   return MOE_OK;
 }
 
-// a_f32: A is an fp32 intermediate (split into two BF16 parts in the tile)
 // grid: gx x gy x gz logical tiles (BwdGemm), launched as one dimension;
 // A split into hi / lo parts when g.a.p_lo is set.  The grouped-row product
 // of two K-contiguous BF16 operands with whole column tiles runs the
@@ -936,6 +935,8 @@ moe_status launch_bwd_gemm(BwdGemm g, unsigned gx, unsigned gy, unsigned gz, hip
   const dim3 grid((unsigned)((size_t)g.gx * gyb * units));
   const bool split = g.a.p_lo != nullptr;
   const long lim = 1L << 31;
+  if ((g.a.trans && g.a.map) || (!g.b.trans && g.b.map))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "internal: a transposed backward operand has a row map");
   if (g.group == BWD_GROUP_ROWS && !split && !g.c_trans && !g.a.trans && g.b.trans && g.N % kBwdBN == 0 &&
       g.K % kBwdBK == 0 && g.a.ld % 8 == 0 && g.b.ld % 8 == 0 && g.a_bytes < lim && g.b_bytes < lim) {
     TRY(set_lds_limit(k_bwd_gemm_dma, kBwdDmaLds));
