@@ -376,7 +376,7 @@ __global__ void __launch_bounds__(256) k_bwd_gemm_dma(BwdGemm g) {
   const long n0 = (inner >> 1) * kBwdBN;
   if (t >= *g.ntiles) return;
   const Tile tl = g.tiles[t];
-  const long m0 = tl.r0, M = (long)tl.r0 + tl.rows, N = g.N, K = g.K;
+  const long m0 = tl.r0, M = (long)tl.r0 + tl.rows, K = g.K;
   const uint16_t* bbase = static_cast<const uint16_t*>(g.b.p) + (long)tl.e * g.b.gstride;
 
   // DMA instruction q of wave w fills 1 KB u = 4q + w of a tile: rows

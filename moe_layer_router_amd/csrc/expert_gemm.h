@@ -90,7 +90,11 @@ struct GemmLds {
   static constexpr int kScStride = (kMaxRs + 3) / 4 * 4;
   static_assert(16 * kScStride + 64 <= kScRows, "scale positions and the spare slots fit");
   static constexpr int kSaRows = (kRows + 63) / 64 * 64;         // rows of an activation-scale slot
-  static constexpr int kPd = (AF == ACT_FP8) ? 3 : 2;            // prefetch distance (steps)
+  // Prefetch distance (steps) of gate|up, which sets the LDS stages.  The
+  // down GEMM (K = I, 8 to 16 steps at DeepSeek-V3-like shapes) runs two
+  // steps ahead: measured 0.5-2.6% faster than three on every workload.
+  static constexpr int kPd = (AF == ACT_FP8) ? 3 : 2;
+  static constexpr int kPdDown = 2;                               // <= kPd
   static constexpr int kAStages = kPd + 1;
   static constexpr int kSC = kA + kAStages * kASlot;             // [2][2][kScRows] fp32 row scales
   static constexpr int kRowI = kSC + 2 * 2 * kScRows * 4;        // [kRows] int
@@ -183,7 +187,9 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
   constexpr int NDMA = (R * AB + 4095) / 4096;    // DMA instructions per thread per step
   constexpr int ESZ = (AF == ACT_FP8) ? 1 : 2;    // activation element size
   constexpr int NB = (WF == W_BF16) ? 16 : 8;     // B load instructions per lane per step
-  constexpr int PD = L::kPd;                       // A and scales: loaded PD (+1) steps ahead
+  constexpr int PD = (STAGE == 2) ? L::kPdDown : L::kPd;   // A and scales: loaded PD (+1) steps ahead
+  constexpr int AST = PD + 1;                      // A stages and activation-scale slots in use
+  static_assert(PD <= L::kPd, "stages fit the LDS layout");
   constexpr int NBUF = (WF == W_BF16) ? 2 : PD + 1; // B register buffers (B distance NBUF - 1)
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int gq = lane >> 4, c16 = lane & 15;
@@ -277,7 +283,7 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
     const uint32_t rbase = (STAGE == 1) ? (uint32_t)ROWI[rowc] * g.H : (uint32_t)(r0 + rowc) * g.I;
     aoff[j] = rbase * ESZ + c * 16;
   }
-  // stage `slot` (= s % kAStages) receives A(s).  Steps past the last
+  // stage `slot` (= s % AST) receives A(s).  Steps past the last
   // (issued so that the step stays branch-free) load the last step again:
   // an unclamped offset would reach into the next permuted row, which in
   // the persistent kernel may belong to a tile whose gate|up item has not
@@ -291,7 +297,7 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
   };
 
   // ---- per-row scales (FP8 activations).  The activation scales of step s
-  // are loaded straight into LDS slot s % kSaSlots, PD + 1 steps ahead: wave w
+  // are loaded straight into LDS slot s % AST, PD + 1 steps ahead: wave w
   // loads rows 64*(w % NSW) + lane (NSW waves cover the tile; the others
   // write the same values as wave w % NSW), so that thread tid < kRows finds
   // the scale of row tid.  SC[par][set] holds sA[row] * sB[set] for the
@@ -313,7 +319,7 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
                                      : make_rsrc(g.x_scales, (uint32_t)g.T * (g.H / 128) * 4);
   const uint32_t saoff = permuted ? (uint32_t)(r0 + srow) * 4 : (uint32_t)ROWI[srow] * (uint32_t)(g.H / 128) * 4;
   const uint32_t sastep = permuted ? nrows_all * 4 : 4u;
-  auto dma_sa = [&](int s, int slot) __attribute__((always_inline)) {   // slot = s % kSaSlots
+  auto dma_sa = [&](int s, int slot) __attribute__((always_inline)) {   // slot = s % AST
     buf_ld4_lds<STAGE == 2 ? CP : 0>(sars, lds + L::kSA + slot * (L::kSaRows * 4) + (w % NSW) * 256, saoff,
                                      (uint32_t)min(s, nsteps - 1) * sastep);
   };
@@ -523,7 +529,7 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
   BFrag bb[NBUF];
   auto issue_a = [&](int s) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < NDMA; ++j) dma_a(s, s % L::kAStages, j);
+    for (int j = 0; j < NDMA; ++j) dma_a(s, s % AST, j);
   };
   auto load_b = [&](int s, BFrag& b) __attribute__((always_inline)) {
 #pragma unroll
@@ -536,7 +542,7 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
   if (NSA) dma_sa(0, 0);
 #pragma unroll
   for (int v = 0; v < PD; ++v) {
-    if (NSA) dma_sa(v + 1, (v + 1) % L::kSaSlots);
+    if (NSA) dma_sa(v + 1, (v + 1) % AST);
     issue_a(v);
     __builtin_amdgcn_sched_barrier(0);
     if (v < NBUF - 1) load_b(v, bb[v]);
@@ -553,21 +559,20 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
   barrier_vmcnt<AFTER_A0>();                       // A(0) is in LDS for every wave
   if (signal_prev && tid == 0) __hip_atomic_fetch_add(signal_prev, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   // The loop body is UNR steps, a multiple of NBUF (B buffer rotation), of
-  // 2 (scale parity), of kAStages (A stage rotation) and of kSaSlots, so
+  // 2 (scale parity) and of AST (A stage and scale slot rotation), so
   // every buffer and LDS slot index in it is a compile-time constant; a long
   // body also makes the loop head, where the compiler's wait counts are
   // merged from two paths and come out conservative, rarer.  Step s reads
   // the scales of step s+1 into a register within the step: no loaded value
   // is carried across the loop's back edge, where the compiler would drain
   // every load in flight.
-  constexpr int UNR = (AF == ACT_FP8) ? 16 : 6;
-  static_assert(UNR % NBUF == 0 && UNR % 2 == 0 && UNR % L::kAStages == 0 && UNR % L::kSaSlots == 0,
-                "loop unroll");
+  constexpr int UNR = (AF == ACT_FP8) ? (AST == 4 ? 16 : 12) : 6;
+  static_assert(UNR % NBUF == 0 && UNR % 2 == 0 && UNR % AST == 0, "loop unroll");
   auto step = [&](int s, int u) __attribute__((always_inline)) {
-    const float sa_next = read_sa((u + 1) % L::kSaSlots);
-    compute(u % L::kAStages, u & 1, bb[u % NBUF], NLOAD, [&](int j) __attribute__((always_inline)) {
-      if (j < NSA) dma_sa(s + PD + 1, (u + PD + 1) % L::kSaSlots);
-      else if (j < NSA + NDMA) dma_a(s + PD, (u + PD) % L::kAStages, j - NSA);
+    const float sa_next = read_sa((u + 1) % AST);
+    compute(u % AST, u & 1, bb[u % NBUF], NLOAD, [&](int j) __attribute__((always_inline)) {
+      if (j < NSA) dma_sa(s + PD + 1, (u + PD + 1) % AST);
+      else if (j < NSA + NDMA) dma_a(s + PD, (u + PD) % AST, j - NSA);
       else load_b_piece(s + NBUF - 1, bb[(u + NBUF - 1) % NBUF], j - NSA - NDMA);
     });
     store_scale(s + 1, (u + 1) & 1, sa_next);

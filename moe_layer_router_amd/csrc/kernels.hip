@@ -38,9 +38,12 @@ __global__ void __launch_bounds__(256) k_router(RouterArgs a, int nks, int32_t* 
 }
 
 constexpr int kTopkTokens = 32;   // tokens per top-k workgroup (separate mode)
-__global__ void __launch_bounds__(256) k_topk(const float* logits, int T, int E, int k, int32_t* ids, float* wts) {
-  const int t0 = blockIdx.x * kTopkTokens;
-  topk_tokens(logits, E, k, t0, min(kTopkTokens, T - t0), ids, wts);
+// `tpb` tokens per workgroup: kTopkTokens (16-lane rows) for E <= 256, one
+// token per wave above (more workgroups in flight for the longer rows).
+__global__ void __launch_bounds__(256) k_topk(const float* logits, int T, int E, int k, int32_t* ids, float* wts,
+                                              int tpb) {
+  const int t0 = blockIdx.x * tpb;
+  topk_tokens(logits, E, k, t0, min(tpb, T - t0), ids, wts);
 }
 
 __global__ void __launch_bounds__(256) k_count(const int32_t* ids, int T, int k, int E, int32_t* blockcnt) {
@@ -48,8 +51,9 @@ __global__ void __launch_bounds__(256) k_count(const int32_t* ids, int T, int k,
   perm_count_block(ids, T, k, E, blockIdx.x, blockcnt, reinterpret_cast<int*>(lds));
 }
 
-__global__ void __launch_bounds__(256) k_scan(const int32_t* blockcnt, int nblk, int E, int tile_rows, int32_t* base,
-                                              int32_t* offsets, Tile* tiles, int32_t* meta) {
+// One workgroup of up to 1024 threads (one expert per thread up to E = 1024).
+__global__ void __launch_bounds__(1024) k_scan(const int32_t* blockcnt, int nblk, int E, int tile_rows, int32_t* base,
+                                               int32_t* offsets, Tile* tiles, int32_t* meta) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   perm_scan(blockcnt, nblk, E, tile_rows, base, offsets, tiles, meta, reinterpret_cast<int*>(lds));
 }
@@ -515,6 +519,7 @@ k_mega(Plan p) {
 }  // namespace moe
 
 // ===================================================================== host
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -800,8 +805,8 @@ moe_status launch_route(const Plan& p, float* logits, int nks, hipStream_t st) {
     hipLaunchKernelGGL(k_router<ACT_BF16>, dim3(p.nER, p.nTR, nks), dim3(256), kRouterLds, st, ra, nks, p.rtile);
   }
   HIP_TRY(hipGetLastError());
-  hipLaunchKernelGGL(k_topk, dim3((p.T + kTopkTokens - 1) / kTopkTokens), dim3(256), 0, st, logits, p.T, p.E, p.k,
-                     p.ids, p.wts);
+  const int tpb = p.E <= 256 ? kTopkTokens : 4;
+  hipLaunchKernelGGL(k_topk, dim3((p.T + tpb - 1) / tpb), dim3(256), 0, st, logits, p.T, p.E, p.k, p.ids, p.wts, tpb);
   HIP_TRY(hipGetLastError());
   return MOE_OK;
 }
@@ -809,8 +814,9 @@ moe_status launch_route(const Plan& p, float* logits, int nks, hipStream_t st) {
 moe_status launch_permute(const Plan& p, int32_t* row_of, hipStream_t st) {
   hipLaunchKernelGGL(k_count, dim3(p.nblk), dim3(256), p.E * 4, st, p.ids, p.T, p.k, p.E, p.blockcnt);
   HIP_TRY(hipGetLastError());
-  hipLaunchKernelGGL(k_scan, dim3(1), dim3(256), (2 * p.E + 72) * 4, st, p.blockcnt, p.nblk, p.E, p.tile_rows, p.base,
-                     p.offsets, p.tiles, p.meta);
+  const int scan_threads = std::min(1024, std::max(256, (p.E + 63) / 64 * 64));
+  hipLaunchKernelGGL(k_scan, dim3(1), dim3(scan_threads), (2 * p.E + 72) * 4, st, p.blockcnt, p.nblk, p.E,
+                     p.tile_rows, p.base, p.offsets, p.tiles, p.meta);
   HIP_TRY(hipGetLastError());
   hipLaunchKernelGGL(k_scatter, dim3(p.nblk), dim3(256), 4 * p.E * 8, st, p.ids, p.T, p.k, p.E, p.base, p.perm, row_of);
   HIP_TRY(hipGetLastError());
