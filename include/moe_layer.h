@@ -70,8 +70,9 @@
  * workspace) for the expert GEMMs, while the router reads the BF16 input;
  * x_scales must then be NULL.
  * Limits: T >= 1; H and I multiples of 128 (H <= 16384, I <= 16384);
- * 1 <= top_k <= E; E <= 1024; top_k <= 16; T * top_k * max(H, I) * 2 < 4 GiB
- * (the staging and intermediate rows are addressed with 32-bit offsets).
+ * 1 <= top_k <= E; E <= 1024; top_k <= 16; T * top_k * max(Hp, I) * 2 < 4 GiB
+ * with Hp = H rounded up to a multiple of 256 (the staging and intermediate
+ * rows are addressed with 32-bit offsets).
  * Pointers must be 16-byte aligned.
  *
  * Ownership and asynchrony.  The library never allocates device memory in
@@ -199,7 +200,9 @@ size_t moe_permute_workspace_size(const moe_desc* d);
  *                 order: E4M3 codes (FP8 layers) or BF16 (BF16 layers)
  *   inter_scales  [I/128][T*top_k] fp32 re-quantisation scales (FP8 layers),
  *                 K block major: block c of permuted row r at c*T*top_k + r
- *   staging       [T*top_k][H] BF16 weighted expert outputs, row t*top_k+j
+ *   staging       [Hp/256][T*top_k][256] BF16 weighted expert outputs:
+ *                 columns 256b .. 256b+255 of row t*top_k+j at
+ *                 (b*T*top_k + t*top_k + j)*256 (Hp = H rounded up to 256)
  *   trace         with MOE_FLAG_TRACE (persistent kernel): [1024][8] uint64,
  *                 row b for workgroup b < 1024: the device's constant 100 MHz
  *                 clock at 0 kernel entry, 1 the end of its routing phase

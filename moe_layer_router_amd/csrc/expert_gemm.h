@@ -58,7 +58,7 @@ struct GemmArgs {
   uint8_t* aq;               // [T*k][I] E4M3 (or BF16 for BF16 layers)
   float* sa;                 // [I/128][T*k] (K block major, permuted rows)
   const float* sxp;          // [H/128][T*k] x_scales in permuted row order, or NULL
-  uint16_t* staging;         // [T*k][H] BF16, indexed by flat index p
+  uint16_t* staging;         // [H/256][T*k][256] BF16: N block, then flat index p, then column
   int T, H, E, I, k;
   int pow2;                  // re-quantise the intermediate with power-of-two scales
   int pow2_x;                // the activation scales are powers of two (the layer's own quantisation)
@@ -593,7 +593,7 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
   const uint32_t nrows = (uint32_t)(g.T * g.k);
   const rsrc_t aqw = make_rsrc(g.aq, nrows * (uint32_t)g.I * ESZ);
   const rsrc_t saw = make_rsrc(g.sa, nrows * (uint32_t)(g.I / 128) * 4);
-  const rsrc_t stw = make_rsrc(g.staging, nrows * (uint32_t)g.H * 2);
+  const rsrc_t stw = make_rsrc(g.staging, nrows * (uint32_t)((g.H + 255) / 256) * 512u);
   if (STAGE == 1) {
     if (WF == W_FP8 && AF == ACT_FP8 && wchan) {
       // per-channel weight scales: lane holds channels 32w + 16q + 4gq + v
@@ -728,7 +728,7 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
         const int rl = q >> 5, c = q & 31;
         const int row = CH * 16 * h + rl, col = n0 + c * 8;
         *lo = L::kA + rl * 512 + ((c ^ (rl & 15)) << 4);
-        *go = ((uint32_t)ROWI[row] * g.H + col) * 2;
+        *go = (((uint32_t)nb * nrows + (uint32_t)ROWI[row]) * 256u + (uint32_t)(c * 8)) * 2;
         return row < m && col < g.H;
       });
     }
@@ -761,7 +761,7 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
         const int rl = q >> 5, c = q & 31;
         const int row = CH * 16 * h + rl, col = n0 + c * 8;
         *lo = L::kA + rl * 512 + (c ^ (((rl >> 2) & 3) << 1)) * 16;
-        *go = ((uint32_t)ROWI[row] * g.H + col) * 2;
+        *go = (((uint32_t)nb * nrows + (uint32_t)ROWI[row]) * 256u + (uint32_t)(c * 8)) * 2;
         return row < m && col < g.H;
       });
     }
@@ -797,11 +797,15 @@ DEV void expert_gemm_item(const GemmArgs& g, const Tile& t, int nb, char* lds, i
 
 // y[t, n0:n1] = BF16( sum_j staging[t*k + j, n0:n1] ) for tokens [t0, t1),
 // fp32 sums in ascending j; 8 channels (16 bytes) per thread and step.
+// Staging is N-block major ([H/256][T*k][256]), so the k rows of a token in
+// one N block, and the rows of consecutive tokens, are adjacent: a combine
+// item reads one contiguous run per N block.
 // Ordinary loads also in the persistent kernel: a 128-byte line of staging
 // lies in one (row, 256-column block), written once per launch, write-through,
 // before the block's counter that the caller waits for.
 DEV void combine_rows(const uint16_t* staging, uint16_t* y, int T, int H, int k, int t0, int t1, int n0, int n1) {
-  const rsrc_t srs = make_rsrc_u(staging, (uint32_t)T * (uint32_t)k * (uint32_t)H * 2);
+  const uint32_t P = (uint32_t)T * (uint32_t)k;
+  const rsrc_t srs = make_rsrc_u(staging, P * (uint32_t)((H + 255) / 256) * 512u);
   const int cpt = (n1 - n0) / 8;
   const int total = (t1 - t0) * cpt;
   // U (token, 8-channel) pairs per thread and pass, rows read four j at a
@@ -816,7 +820,7 @@ DEV void combine_rows(const uint16_t* staging, uint16_t* y, int T, int H, int k,
       const int idx = min(i0 + u * nthr, total - 1);
       tt[u] = t0 + idx / cpt;
       cc[u] = n0 + (idx % cpt) * 8;
-      off[u] = ((uint32_t)tt[u] * (uint32_t)k * (uint32_t)H + (uint32_t)cc[u]) * 2;
+      off[u] = (((uint32_t)(cc[u] >> 8) * P + (uint32_t)tt[u] * (uint32_t)k) * 256u + (uint32_t)(cc[u] & 255)) * 2;
     }
     float s[U][8];
 #pragma unroll
@@ -830,7 +834,7 @@ DEV void combine_rows(const uint16_t* staging, uint16_t* y, int T, int H, int k,
         s[u][2 * i + 1] += bf16_to_f32((uint32_t)v[i] >> 16);
       }
     };
-    const uint32_t row = (uint32_t)H * 2;
+    const uint32_t row = 512u;                     // staging rows of one N block are adjacent
     int j = 0;
     for (; j + 4 <= k; j += 4) {
       v4i v[4][U];

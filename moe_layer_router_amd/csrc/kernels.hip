@@ -158,9 +158,12 @@ __global__ void __launch_bounds__(256) k_pack_e8m0(const uint8_t* src, uint8_t* 
   }
 }
 
+// Workgroup (x, nb): tokens [64x, 64x + 64) of N block nb, whose staging
+// rows are one contiguous run.
+constexpr int kCombineKernelTokens = 64;
 __global__ void __launch_bounds__(256) k_combine(const uint16_t* staging, uint16_t* y, int T, int H, int k) {
-  const int t0 = blockIdx.x * 16;
-  combine_rows(staging, y, T, H, k, t0, min(T, t0 + 16), 0, H);
+  const int t0 = blockIdx.x * kCombineKernelTokens, nb = blockIdx.y;
+  combine_rows(staging, y, T, H, k, t0, min(T, t0 + kCombineKernelTokens), nb * 256, min(H, nb * 256 + 256));
 }
 
 // ------------------------------------------------------- persistent kernel
@@ -602,7 +605,7 @@ Layout make_layout(const moe_desc* d) {
   L.sxp = o; if (fp8_experts && L.nblk > 1) o = align256(o + T * k * (H / 128) * 4);
   L.xq = o; if (quant_in) o = align256(o + T * H);
   L.xs = o; if (quant_in) o = align256(o + T * (H / 128) * 4);
-  L.staging = o; o = align256(o + T * k * H * 2);
+  L.staging = o; o = align256(o + T * k * (size_t)L.nnb2 * 256 * 2);
   L.trace = o; if (d->flags & MOE_FLAG_TRACE) o = align256(o + (size_t)kTraceGroups * kTraceFields * 8);
   L.total = o;
   return L;
@@ -623,10 +626,12 @@ moe_status check_desc(const moe_desc* d) {
   if (d->I > 16384) return fail(MOE_ERR_UNSUPPORTED, "I > 16384 is not supported (got %d)", d->I);
   if ((long long)d->T * d->top_k > (1LL << 30)) return fail(MOE_ERR_UNSUPPORTED, "T * top_k too large");
   // whole-array buffers are addressed with 32-bit byte offsets; the staging
-  // rows (T*top_k*H BF16) and the intermediate rows (T*top_k*I, at most
-  // 2 bytes each) are the largest of them
-  if ((long long)d->T * d->top_k * (d->H > d->I ? d->H : d->I) * 2 > 0xFFFFFFFFLL)
-    return fail(MOE_ERR_UNSUPPORTED, "T * top_k * max(H, I) * 2 must be below 4 GiB (got T=%d, top_k=%d, H=%d, I=%d)",
+  // rows (T*top_k rows of H rounded up to 256, BF16) and the intermediate
+  // rows (T*top_k*I, at most 2 bytes each) are the largest of them
+  const long long hpad = (d->H + 255LL) / 256 * 256;
+  if ((long long)d->T * d->top_k * (hpad > d->I ? hpad : d->I) * 2 > 0xFFFFFFFFLL)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "T * top_k * max(H rounded up to 256, I) * 2 must be below 4 GiB (got T=%d, top_k=%d, H=%d, I=%d)",
                 d->T, d->top_k, d->H, d->I);
   const bool wq = d->weight_dtype == MOE_DTYPE_FP8_E4M3 || d->weight_dtype == MOE_DTYPE_FP4_E2M1;
   const bool pair_ok = (d->act_dtype == MOE_DTYPE_BF16 && (d->weight_dtype == MOE_DTYPE_BF16 || wq)) ||
@@ -860,7 +865,8 @@ moe_status launch_layer(const Plan& p, const DevInfo& di, int mode, hipStream_t 
     hipLaunchKernelGGL((k_gemm<AF, WF, 2>), dim3(grid), dim3(256), lds, st, g, p.tiles, p.meta, p.nnb2,
                        p.ctr + CTR_Q2);
     HIP_TRY(hipGetLastError());
-    hipLaunchKernelGGL(k_combine, dim3((p.T + 15) / 16), dim3(256), 0, st, p.staging, p.y, p.T, p.H, p.k);
+    hipLaunchKernelGGL(k_combine, dim3((p.T + kCombineKernelTokens - 1) / kCombineKernelTokens, p.nnb2), dim3(256), 0,
+                       st, p.staging, p.y, p.T, p.H, p.k);
     HIP_TRY(hipGetLastError());
   } else {
     const int lds = mega_lds(p);
