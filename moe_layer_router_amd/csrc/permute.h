@@ -30,17 +30,27 @@ struct Tile {
 static_assert(sizeof(Tile) == 6 * sizeof(int32_t), "tile fields are stored one by one");
 
 // Work item i of a GEMM over (tile, N block) pairs with nnb N blocks.  Items
-// are ordered expert by expert, then by N block, then by the expert's tiles,
-// so that the items reading the same weight slab are adjacent in the queue
-// and run at the same time (the later reads hit the caches).
+// are ordered expert by expert; an expert's tiles in groups of up to
+// kTileGroup, and within a group by N block, then tile.  The items reading
+// the same weight slab (one N block of the group's tiles) and those reading
+// the same rows (one tile's N blocks) are then all close in the queue and
+// run at about the same time, so the later reads hit the caches.  Without
+// the groups, an expert with hundreds of tiles (a popular expert under a
+// skewed routing) would read each tile's rows once per N block, hundreds of
+// items apart, long after the L2 dropped them.  An expert with at most
+// kTileGroup tiles is one group: N block, then tile.
 // (`tiles` is any pointer to Tile, also one into another address space.)
+constexpr int kTileGroup = 4;
 template <typename TilePtr>
 DEV void gemm_item_of(TilePtr tiles, int nnb, int i, int* t, int* nb) {
   const int j = i / nnb;
   const int g0 = tiles[j].g0, gn = tiles[j].gn;
   const int local = i - g0 * nnb;
-  *nb = local / gn;
-  *t = g0 + local % gn;
+  const int q = local / (kTileGroup * nnb);          // group (all before it are full)
+  const int r = local - q * kTileGroup * nnb;
+  const int sz = min(kTileGroup, gn - q * kTileGroup);
+  *nb = r / sz;
+  *t = g0 + q * kTileGroup + r % sz;
 }
 
 // Variant (16-row subtiles computed) of a tile of `rows` rows whose full size
