@@ -49,7 +49,7 @@ struct Plan {
   int32_t* err;                // device error word (byte offset 0)
   int32_t* ctr;                // [CTR_NUM]
   int32_t* rdone;              // [nTR]    router items finished per token tile
-  int32_t* rtile;              // [nTR*nER] K slices finished per router tile
+  int32_t* rtile;              // [nTR*nER] K slices finished per router tile (separate router kernel)
   int32_t* tkdone;             // [nblk]   top-k items finished per 256-token block
   int32_t* done1;              // [max_tiles] gate|up items finished per tile
   int32_t* done2;              // [nnb2]   down items finished per N block

@@ -223,10 +223,9 @@ DEV void signal_coherent(int32_t* c0, int32_t* c1 = nullptr) {
 // workgroup moves to the next queue only once every item of the current one
 // has been claimed by a running workgroup, so no wait can deadlock whatever
 // the grid size:
-//   head queue:   router tiles (128 tokens x 64 experts) -> rdone[token tile]
-//                   (with channel slices: -> rtile[tile], then 8 items
-//                   per tile sum the slices -> rdone[token tile])
-//                 top-k of 16 tokens                     -> tkdone[256-token block]
+//   head queue:   router tiles (128 tokens x 64 experts, or one channel
+//                   slice of one)                        -> rdone[token tile]
+//                 top-k of 16 tokens (summing the slices) -> tkdone[256-token block]
 //                 expert histogram of 256 tokens        -> COUNT_DONE
 //                   (only with more than one 256-token block)
 //                 scan and stable scatter of 256 tokens -> SCATTER_DONE
@@ -315,23 +314,12 @@ __device__ __noinline__ void mega_quant_item(KPlan* pv, int i_) {
                                     p.pow2 != 0, const_cast<uint8_t*>(p.x), const_cast<float*>(p.x_scales),
                                     threadIdx.x, blockDim.x);
 }
-// Part `part` of kReduceParts of the sum of router tile (tt, et)'s channel
-// slices (run once every slice of the tile is done).
-constexpr int kReduceParts = 8;
-__device__ __noinline__ void mega_reduce_item(KPlan* pv, int tt_, int et_, int part_) {
-  const Plan p = load_plan(pv);
-  const int tt = uni_i(tt_), et = uni_i(et_), part = uni_i(part_);
-  RouterArgs ra{p.x, p.x_scales, p.wr, p.bias, p.logits, p.T, p.H, p.E, p.act_fp8};
-  const int t0 = tt * kRouterTokens, e0 = et * kRouterExperts;
-  const int n = router_tile_elems(ra, t0, e0);
-  const int per = (n + kReduceParts - 1) / kReduceParts;
-  router_sum_slices(ra, t0, e0, p.nKS, min(n, part * per), min(n, (part + 1) * per));
-}
 constexpr int kTopkItemTokens = 16;        // tokens per top-k item of the persistent kernel
 __device__ __noinline__ void mega_topk_item(KPlan* pv, int i) {
   const Plan p = load_plan(pv);
   const int t0 = uni_i(i) * kTopkItemTokens;
-  topk_tokens(p.logits, p.E, p.k, t0, min(kTopkItemTokens, p.T - t0), p.ids, p.wts);
+  // (with channel slices the partials of slice s are at logits + s*T*E)
+  topk_tokens(p.logits, p.E, p.k, t0, min(kTopkItemTokens, p.T - t0), p.ids, p.wts, p.nKS, (size_t)p.T * p.E);
 }
 __device__ __noinline__ void mega_count_item(KPlan* pv, int b_) {
   MEGA_LDS;
@@ -371,9 +359,6 @@ k_mega(Plan p) {
   // (with head_given the separate kernels have done the whole head: no items)
   const bool head = !p.head_given;
   const int nR = (p.routing_given || !head) ? 0 : p.nTR * p.nER * p.nKS;
-  // with the router's channels in slices, kReduceParts items per router tile
-  // sum the slices once all of them are done
-  const int nRd = (p.routing_given || !head || p.nKS == 1) ? 0 : p.nTR * p.nER * kReduceParts;
   const int nK = (p.routing_given || !head) ? 0 : (p.T + kTopkItemTokens - 1) / kTopkItemTokens;
   // histogram items only when there are several 256-token blocks (a single
   // block counts itself in its scatter item)
@@ -385,11 +370,11 @@ k_mega(Plan p) {
   // depend on nothing; the activation-scale items and the GEMMs wait for them)
   const int nQ = (head && p.quant_in) ? (p.T * (p.H / 128) + kQuantItemBlocks - 1) / kQuantItemBlocks : 0;
   const int q_rt = nQ;
-  const int q_red = q_rt + nR, q_topk = q_red + nRd, q_count = q_topk + nK, q_scat = q_count + nC,
+  const int q_topk = q_rt + nR, q_count = q_topk + nK, q_scat = q_count + nC,
             q_sxp = q_scat + nS;
   const int q_end = q_sxp + nX;
   constexpr int kPer = kPermBlock / kTopkItemTokens;   // top-k items per 256-token block
-  const int rdone_target = p.nER * ((p.nKS == 1) ? 1 : kReduceParts);   // per token tile
+  const int rdone_target = p.nER * p.nKS;          // router items per token tile
 
   // 1. routing and permutation items from the head queue
   for (;;) {
@@ -401,17 +386,12 @@ k_mega(Plan p) {
     if (q < q_rt) {
       mega_quant_item(pk, q);
       signal_coherent(&p.ctr[CTR_QUANT_DONE]);
-    } else if (q < q_red) {
+    } else if (q < q_topk) {
       const int r = q - q_rt;
       const int per_tt = p.nER * p.nKS;
       const int tt = r / per_tt, et = (r % per_tt) / p.nKS, ks = r % p.nKS;
       mega_router_item<AF>(pk, tt, et, ks);
-      signal_coherent(p.nKS == 1 ? &p.rdone[tt] : &p.rtile[tt * p.nER + et]);
-    } else if (q < q_topk) {
-      const int r = q - q_red, tile = r / kReduceParts;   // tile = tt * nER + et
-      if (!wait_counter(&p.rtile[tile], p.nKS, p.err, &s_ok, false)) return;
-      mega_reduce_item(pk, tile / p.nER, tile % p.nER, r % kReduceParts);
-      signal_coherent(&p.rdone[tile / p.nER]);
+      signal_coherent(&p.rdone[tt]);
     } else if (q < q_count) {
       const int i = q - q_topk;                          // tokens [16i, 16i+16)
       if (!wait_counter(&p.rdone[i / (kRouterTokens / kTopkItemTokens)], rdone_target, p.err, &s_ok, false)) return;

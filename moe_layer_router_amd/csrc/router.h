@@ -292,18 +292,45 @@ DEV uint64_t wave_max64(uint64_t v) {
   return a > b ? a : b;
 }
 
+// The 16 logits a lane works on, lrow[idx(j)] for j < 16 (every index in
+// range), as the sum of the S channel-slice partials at lrow + s*sstride in
+// slice order, the same fp32 sum as router_sum_slices (S = 1: the logits
+// themselves).  All loads are issued before any is used: coherent loads
+// stay in program order with the arithmetic between them, so a sum between
+// loads would make each wait for the one before.
+template <typename IdxF>
+DEV void load_logits16(const float* lrow, int S, size_t sstride, const IdxF& idx, float* v) {
+  constexpr int kMaxS = 8;
+  float p[kMaxS][16];
+#pragma unroll
+  for (int s = 0; s < kMaxS; ++s)
+    if (s < S)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) p[s][j] = ld_coh(lrow + s * sstride + idx(j));
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    float x = p[0][j];
+#pragma unroll
+    for (int s = 1; s < kMaxS; ++s)
+      if (s < S) x += p[s][j];
+    v[j] = x;
+  }
+}
+
 // Top-k of one token's logits by one wave.  Keys pack the order-preserving
 // image of the logit in the high word and (E-1-e) in the low word, so the
 // largest key is the largest logit with the lowest index.  E <= 1024, k <= 16.
-DEV void topk_token(const float* lrow, int E, int k, int32_t* ids, float* wts) {
+DEV void topk_token(const float* lrow, int E, int k, int32_t* ids, float* wts, int S, size_t sstride) {
   const int lane = threadIdx.x & 63;
-  // All 16 loads first, each from an in-range address, the unused keys
+  // All loads first, each from an in-range address, the unused keys
   // cleared afterwards: a load under a condition is a branch that waits for
-  // it, and coherent loads stay in program order with the arithmetic between
-  // them, so either way each load would wait for the one before.
+  // it (see load_logits16).  Lanes whose indices were clamped store nothing.
   float v[16];
+  load_logits16(lrow, S, sstride, [&](int i) { return min(lane + 64 * i, E - 1); }, v);
+  if (S > 1)
 #pragma unroll
-  for (int i = 0; i < 16; ++i) v[i] = ld_coh(lrow + min(lane + 64 * i, E - 1));
+    for (int i = 0; i < 16; ++i)
+      if (lane + 64 * i < E) st_coh(const_cast<float*>(lrow) + lane + 64 * i, v[i]);
   uint64_t key[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
@@ -339,11 +366,15 @@ DEV void topk_token(const float* lrow, int E, int k, int32_t* ids, float* wts) {
 
 // Top-k of one token per DPP row (16 lanes), E <= 256, k <= 16: lane i of
 // the row holds experts i + 16j.  Same keys and order as topk_token.
-DEV void topk_token16(const float* lrow, bool valid, int E, int k, int32_t* ids, float* wts) {
+DEV void topk_token16(const float* lrow, bool valid, int E, int k, int32_t* ids, float* wts, int S,
+                      size_t sstride) {
   const int li = threadIdx.x & 15;
   float v[16];                                     // (loads first: see topk_token)
+  load_logits16(lrow, S, sstride, [&](int j) { return min(li + 16 * j, E - 1); }, v);
+  if (S > 1 && valid)
 #pragma unroll
-  for (int j = 0; j < 16; ++j) v[j] = ld_coh(lrow + min(li + 16 * j, E - 1));
+    for (int j = 0; j < 16; ++j)
+      if (li + 16 * j < E) st_coh(const_cast<float*>(lrow) + li + 16 * j, v[j]);
   uint64_t key[16];
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
@@ -377,8 +408,12 @@ DEV void topk_token16(const float* lrow, bool valid, int E, int k, int32_t* ids,
 }
 
 // Top-k for `count` consecutive tokens starting at t0: one token per DPP row
-// (16 per workgroup pass) when E <= 256, else one wave per token.
-DEV void topk_tokens(const float* logits, int E, int k, int t0, int count, int32_t* ids, float* wts) {
+// (16 per workgroup pass) when E <= 256, else one wave per token.  With
+// S > 1 the logits are the sums of S channel-slice partials ([S][T][E] from
+// `logits`, slice stride sstride = T*E elements, summed in slice order), and
+// the sums are stored over slice 0.
+DEV void topk_tokens(const float* logits, int E, int k, int t0, int count, int32_t* ids, float* wts, int S = 1,
+                     size_t sstride = 0) {
 
   if (E <= 256) {
     const int rowid = threadIdx.x >> 4, nrows = blockDim.x >> 4;
@@ -386,14 +421,14 @@ DEV void topk_tokens(const float* logits, int E, int k, int t0, int count, int32
       const int i = i0 + rowid;
       const bool valid = i < count;
       const int t = t0 + (valid ? i : 0);
-      topk_token16(logits + (size_t)t * E, valid, E, k, ids + (size_t)t * k, wts + (size_t)t * k);
+      topk_token16(logits + (size_t)t * E, valid, E, k, ids + (size_t)t * k, wts + (size_t)t * k, S, sstride);
     }
     return;
   }
   const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
   for (int i = w; i < count; i += nw) {
     const int t = t0 + i;
-    topk_token(logits + (size_t)t * E, E, k, ids + (size_t)t * k, wts + (size_t)t * k);
+    topk_token(logits + (size_t)t * E, E, k, ids + (size_t)t * k, wts + (size_t)t * k, S, sstride);
   }
 }
 
