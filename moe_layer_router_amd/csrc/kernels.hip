@@ -27,14 +27,16 @@ DEV void router_slice(int H, int ks, int nks, int* s0, int* s1) {
 // Router tiles (blockIdx.x: 64 experts, .y: 128 tokens, .z: K slice); slice
 // ks writes its partial logits to a.logits + ks*T*E, and the last slice of a
 // tile to finish sums them into slice 0 (tile_cnt: one counter per tile).
-template <int AF>
+// NE experts per tile; the wide tiles (NE = kRouterExpertsWide) run with
+// one slice only.
+template <int AF, int NE = kRouterExperts>
 __global__ void __launch_bounds__(256) k_router(RouterArgs a, int nks, int32_t* tile_cnt) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   int s0, s1;
   router_slice(a.H, blockIdx.z, nks, &s0, &s1);
-  const int t0 = blockIdx.y * kRouterTokens, e0 = blockIdx.x * kRouterExperts;
-  router_tile<AF>(a, t0, e0, lds, s0, s1, a.logits + (size_t)blockIdx.z * a.T * a.E, blockIdx.z == 0);
-  if (nks > 1) router_reduce(a, t0, e0, nks, &tile_cnt[blockIdx.y * gridDim.x + blockIdx.x]);
+  const int t0 = blockIdx.y * kRouterTokens, e0 = blockIdx.x * NE;
+  router_tile<AF, NE>(a, t0, e0, lds, s0, s1, a.logits + (size_t)blockIdx.z * a.T * a.E, blockIdx.z == 0);
+  if (NE == kRouterExperts && nks > 1) router_reduce(a, t0, e0, nks, &tile_cnt[blockIdx.y * gridDim.x + blockIdx.x]);
 }
 
 constexpr int kTopkTokens = 32;   // tokens per top-k workgroup (separate mode)
@@ -782,7 +784,15 @@ moe_status launch_route(const Plan& p, float* logits, int nks, hipStream_t st) {
   RouterArgs ra{p.x, p.x_scales, p.wr, p.bias, logits, p.T, p.H, p.E, p.act_fp8};
   if (p.quant_in) ra = RouterArgs{reinterpret_cast<const uint8_t*>(p.xb), nullptr, p.wr, p.bias, logits, p.T, p.H,
                                   p.E, 0};
-  if (ra.act_fp8) {
+  const int wide_tiles = p.nTR * ((p.E + kRouterExpertsWide - 1) / kRouterExpertsWide);
+  if (ra.act_fp8 && nks == 1 && p.E >= 512 && wide_tiles >= 1024) {
+    // wide tiles (128 experts): half the router weight bytes per flop, where
+    // they are still several per CU
+    TRY(set_lds_limit(k_router<ACT_FP8, kRouterExpertsWide>, kRouterLds));
+    hipLaunchKernelGGL((k_router<ACT_FP8, kRouterExpertsWide>),
+                       dim3((p.E + kRouterExpertsWide - 1) / kRouterExpertsWide, p.nTR, 1), dim3(256), kRouterLds, st, ra,
+                       1, p.rtile);
+  } else if (ra.act_fp8) {
     TRY(set_lds_limit(k_router<ACT_FP8>, kRouterLds));
     hipLaunchKernelGGL(k_router<ACT_FP8>, dim3(p.nER, p.nTR, nks), dim3(256), kRouterLds, st, ra, nks, p.rtile);
   } else {

@@ -31,8 +31,20 @@ constexpr int kRouterX = kRouterW + 64 * 256;
 constexpr int kRouterSc = kRouterX + 128 * 256;
 constexpr int kRouterStage = kRouterSc + 4 * 256;
 constexpr int kRouterLds = kRouterStages * kRouterStage;
+// The wide tile (128 experts, E4M3 activations only): weights [128][256 B],
+// activations [128][128 B], scales; the same LDS total.
+constexpr int kRouterExpertsWide = 128;
+template <int AF, int NE>
+struct RouterLds {
+  static_assert(NE == kRouterExperts || (NE == kRouterExpertsWide && AF == ACT_FP8), "router tile widths");
+  static constexpr int kW = 0;
+  static constexpr int kX = kW + NE * 256;
+  static constexpr int kSc = kX + 128 * ((NE == kRouterExperts) ? 256 : 128);
+  static constexpr int kStage = kSc + 4 * 256;
+};
+static_assert(kRouterStages * RouterLds<ACT_FP8, kRouterExpertsWide>::kStage <= kRouterLds, "wide tile fits");
 
-// Logits of tokens [t0, t0+128) x experts [e0, e0+64) on 256 threads, over
+// Logits of tokens [t0, t0+128) x experts [e0, e0+NE) on 256 threads, over
 // the K steps [s0, s1) (128 channels each), written to `out` ([T][E]); the
 // bias is added when add_bias (the K slice that starts at channel 0).
 //
@@ -43,15 +55,19 @@ constexpr int kRouterLds = kRouterStages * kRouterStage;
 // ahead; each row of 16-byte chunks is stored with chunk c at c ^ (row & 15)
 // (c ^ (row & 7) for 128-byte activation rows) so that the 16 rows read by one
 // operand fetch fall in distinct banks.  Wave w owns tokens 32w..32w+31 (it
-// loads exactly those activation rows and scales itself) and all 64 experts:
-// 2 x 4 accumulator tiles.  Within a step, lane group g holds K elements
+// loads exactly those activation rows and scales itself) and all NE experts:
+// 2 x NE/16 accumulator tiles.  The wide tile (NE = 128) halves the router
+// weight bytes per flop; it is used where there are enough tiles to fill the
+// GPU anyway (E >= 512).  Within a step, lane group g holds K elements
 // 32g + 8i .. +7 in MFMA i (the same permutation of K for both operands), so a
 // lane reads contiguous bytes.  E4M3: each step's partial sum is scaled by the
 // token's scale of that 128-channel block and added to the fp32 logits.
-template <int AF>
+template <int AF, int NE = kRouterExperts>
 DEV void router_tile(const RouterArgs& a, int t0, int e0, char* lds, int s0, int s1, float* out, bool add_bias) {
+  using L = RouterLds<AF, NE>;
+  constexpr int NC = NE / 16;                                // expert subtiles
   constexpr int XB = (AF == ACT_FP8) ? 128 : 256;          // activation bytes per token per step
-  constexpr int NW = 4;                                      // weight loads per wave per step (1 KB each)
+  constexpr int NW = NE / 16;                                // weight loads per wave per step (1 KB each)
   constexpr int NX = XB * 128 / 1024 / 4;                    // activation loads per wave per step
   constexpr int NS = (AF == ACT_FP8) ? 1 : 0;                // scale loads per wave per step
   constexpr int NLOAD = NW + NX + NS;
@@ -65,7 +81,7 @@ DEV void router_tile(const RouterArgs& a, int t0, int e0, char* lds, int s0, int
   uint32_t woff[NW], xoff[NX];
 #pragma unroll
   for (int j = 0; j < NW; ++j) {
-    const int r = 16 * w + 4 * j + lane / 16;                 // expert row of the tile
+    const int r = (NE / 4) * w + 4 * j + lane / 16;           // expert row of the tile
     const int c = (lane & 15) ^ (r & 15);                     // logical chunk of physical chunk lane & 15
     woff[j] = (uint32_t)(e0 + r) * (uint32_t)a.H * 2 + c * 16;
   }
@@ -83,23 +99,23 @@ DEV void router_tile(const RouterArgs& a, int t0, int e0, char* lds, int s0, int
   }
   const uint32_t soff = (uint32_t)(t0 + 32 * w + (lane & 31)) * (uint32_t)(a.H / 128) * 4;
   auto issue = [&](int s, int j) __attribute__((always_inline)) {   // load j of step s
-    char* st = lds + (s % kRouterStages) * kRouterStage;
+    char* st = lds + (s % kRouterStages) * L::kStage;
     if (j < NW) {
-      buf_ld16_lds(wrs, st + kRouterW + (16 * w + 4 * j) * 256, woff[j], uni((uint32_t)s * 256));
+      buf_ld16_lds(wrs, st + L::kW + ((NE / 4) * w + 4 * j) * 256, woff[j], uni((uint32_t)s * 256));
     } else if (j < NW + NX) {
       const int jx = j - NW;
       const int rows = (AF == ACT_FP8) ? 8 : 4;
-      buf_ld16_lds(xrs, st + kRouterX + (32 * w + rows * jx) * XB, xoff[jx], uni((uint32_t)s * 128 * (XB / 128)));
+      buf_ld16_lds(xrs, st + L::kX + (32 * w + rows * jx) * XB, xoff[jx], uni((uint32_t)s * 128 * (XB / 128)));
     } else {
-      buf_ld4_lds(srs, st + kRouterSc + w * 256, soff, uni((uint32_t)s * 4));
+      buf_ld4_lds(srs, st + L::kSc + w * 256, soff, uni((uint32_t)s * 4));
     }
   };
 
-  v4f acc[2][4];
+  v4f acc[2][NC];
 #pragma unroll
   for (int st = 0; st < 2; ++st)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) acc[st][c] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < NC; ++c) acc[st][c] = v4f{0.f, 0.f, 0.f, 0.f};
 
 #pragma unroll
   for (int j = 0; j < NLOAD; ++j) issue(s0, j);
@@ -108,15 +124,15 @@ DEV void router_tile(const RouterArgs& a, int t0, int e0, char* lds, int s0, int
   barrier_vmcnt<NLOAD>();
 
   for (int s = s0; s < s1; ++s) {
-    const char* st = lds + (s % kRouterStages) * kRouterStage;
+    const char* st = lds + (s % kRouterStages) * L::kStage;
     // A operands of both token subtiles
     v8bf av[2][4];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       const int row = 32 * w + 16 * sub + c16;
       if (AF == ACT_FP8) {
-        const v4i q0 = ld16(st + kRouterX + row * 128 + (((2 * g) ^ (row & 7)) << 4));
-        const v4i q1 = ld16(st + kRouterX + row * 128 + (((2 * g + 1) ^ (row & 7)) << 4));
+        const v4i q0 = ld16(st + L::kX + row * 128 + (((2 * g) ^ (row & 7)) << 4));
+        const v4i q1 = ld16(st + L::kX + row * 128 + (((2 * g + 1) ^ (row & 7)) << 4));
         const int qs[8] = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -129,17 +145,18 @@ DEV void router_tile(const RouterArgs& a, int t0, int e0, char* lds, int s0, int
       } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          av[sub][i] = as_v8bf(ld16(st + kRouterX + row * 256 + (((4 * g + i) ^ (row & 15)) << 4)));
+          av[sub][i] = as_v8bf(ld16(st + L::kX + row * 256 + (((4 * g + i) ^ (row & 15)) << 4)));
       }
     }
-    v4f part[2][4];
+    v4f part[2][NC];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      issue(s + 2, i);                                        // weights of step s+2
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
+      for (int j = i * NW / 4; j < (i + 1) * NW / 4; ++j) issue(s + 2, j);   // weights of step s+2
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
         const int row = 16 * c + c16;
-        const v8bf bv = as_v8bf(ld16(st + kRouterW + row * 256 + (((4 * g + i) ^ (row & 15)) << 4)));
+        const v8bf bv = as_v8bf(ld16(st + L::kW + row * 256 + (((4 * g + i) ^ (row & 15)) << 4)));
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub) {
           if (AF == ACT_FP8)
@@ -154,9 +171,9 @@ DEV void router_tile(const RouterArgs& a, int t0, int e0, char* lds, int s0, int
     if (AF == ACT_FP8) {
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub) {
-        const v4f sc = *reinterpret_cast<const v4f*>(st + kRouterSc + w * 256 + (16 * sub + 4 * g) * 4);
+        const v4f sc = *reinterpret_cast<const v4f*>(st + L::kSc + w * 256 + (16 * sub + 4 * g) * 4);
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
+        for (int c = 0; c < NC; ++c)
 #pragma unroll
           for (int v = 0; v < 4; ++v) acc[sub][c][v] = __builtin_fmaf(part[sub][c][v], sc[v], acc[sub][c][v]);
       }
@@ -172,11 +189,11 @@ DEV void router_tile(const RouterArgs& a, int t0, int e0, char* lds, int s0, int
   // a condition would each be a branch with a wait.
   // (the biases are loaded before the first store, which could alias them)
   const rsrc_t ors = make_rsrc_u(out, (uint32_t)a.T * (uint32_t)a.E * 4u);
-  float bias[4];
+  float bias[NC];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) bias[c] = (add_bias && a.bias) ? a.bias[min(e0 + 16 * c + c16, a.E - 1)] : 0.f;
+  for (int c = 0; c < NC; ++c) bias[c] = (add_bias && a.bias) ? a.bias[min(e0 + 16 * c + c16, a.E - 1)] : 0.f;
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
+  for (int c = 0; c < NC; ++c) {
     const int e = e0 + 16 * c + c16;
     const float b = bias[c];
 #pragma unroll
