@@ -59,9 +59,14 @@
  * 16*l + j of piece p (l = 0..63, j = 0..15) is byte BS*s + 64*p + 16*(l/16)
  * + j of row 16*t + l%16 of the row-major matrix.  (K step major, so that
  * the blocks one K step of a GEMM item reads are adjacent and spread over
- * the memory channels.)  FP4 E8M0 scales: block (s, t) is 64 bytes at
- * (s*(N/16) + t)*64, byte l holding the scale of row 16*t + l%16 for K group
- * 4*s + l/16.  FP8 fp32 block scales stay row-major.
+ * the memory channels.)  FP4 E8M0 scales: per K step s and quad q (q =
+ * 0 .. N/64-1) 256 bytes at (s*(N/64) + q)*256; byte 4*l + c (l = 0..63,
+ * c = 0..3) holds the scale of row 16*t + l%16 for K group 4*s + l/16, where
+ * t is the quad's c-th 16-row tile: for the gate|up matrix t = 2q + c (c < 2,
+ * gate rows) or N/32 + 2q + c - 2 (c >= 2, the matching up rows), for the
+ * down matrix t = 4q + c.  (The four column tiles a wave of a GEMM item
+ * multiplies are one quad: their scales are one 4-byte load per lane.)
+ * FP8 fp32 block scales stay row-major.
  * moe_pack_weights converts row-major weights into this layout.
  *
  * Supported dtype pairs (act x weight): BF16 x BF16, FP8 x FP8, FP8 x FP4,

@@ -210,9 +210,6 @@ template <int AUX = 0>
 DEV void buf_stf(rsrc_t r, uint32_t voff, float v) {
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, v), r, (int)voff, 0, AUX);
 }
-DEV uint32_t buf_ldu8(rsrc_t r, uint32_t voff, uint32_t soff) {
-  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, (int)voff, (int)soff, 0);
-}
 // 16 bytes per lane from the buffer straight into LDS: lane l's bytes land
 // at lds_base + 16*l (lds_base is wave-uniform).
 template <int AUX = 0>

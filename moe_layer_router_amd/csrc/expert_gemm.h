@@ -109,10 +109,11 @@ struct GemmLds {
 };
 
 // One step's B fragments: d[cs][i] are 16-byte pieces of column tile cs
-// (FP8 uses i = 0..1, FP4 i = 0, BF16 i = 0..3); sc[cs] is the FP4 E8M0 scale.
+// (FP8 uses i = 0..1, FP4 i = 0, BF16 i = 0..3); with FP4, byte cs of sc is
+// the E8M0 scale of column tile cs (one load for the wave's four tiles).
 struct BFrag {
   v4i d[4][4];
-  int sc[4];
+  uint32_t sc;
 };
 
 // 16-byte chunk position of logical chunk c of A row `row` in LDS.  FP8 rows
@@ -186,7 +187,7 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
   constexpr int R = RS * 16;                      // rows computed
   constexpr int NDMA = (R * AB + 4095) / 4096;    // DMA instructions per thread per step
   constexpr int ESZ = (AF == ACT_FP8) ? 1 : 2;    // activation element size
-  constexpr int NB = (WF == W_BF16) ? 16 : 8;     // B load instructions per lane per step
+  constexpr int NB = (WF == W_BF16) ? 16 : (WF == W_FP8) ? 8 : 5;   // B load instructions per lane per step
   constexpr int PD = (STAGE == 2) ? L::kPdDown : L::kPd;   // A and scales: loaded PD (+1) steps ahead
   constexpr int AST = PD + 1;                      // A stages and activation-scale slots in use
   static_assert(PD <= L::kPd, "stages fit the LDS layout");
@@ -223,14 +224,18 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
   // the row-major matrix.  One piece is exactly one B operand load of a
   // wave: 1 KB contiguous; the blocks of one step are adjacent.
   constexpr uint32_t BS = (WF == W_FP8) ? 128 : (WF == W_BF16) ? 256 : 64;   // bytes per row per K step
-  uint32_t boff[4], bsoff[4];                      // this lane's piece offsets (and E8M0 offsets)
+  uint32_t boff[4];                                // this lane's piece offsets
 #pragma unroll
   for (int cs = 0; cs < 4; ++cs) {
     const int nt = ((STAGE == 1) ? ((cs < 2) ? c0 : g.I + c0) + 32 * w + 16 * (cs & 1) : n0 + 64 * w + 16 * cs) / 16;
     const int ntc = wave_ok ? nt : 0;
     boff[cs] = (uint32_t)ntc * 16u * BS + 16u * lane;
-    bsoff[cs] = (uint32_t)ntc * 64u + lane;
   }
+  // FP4 E8M0 scales (see moe_pack_weights): per K step, quads of 256 bytes,
+  // 4 bytes per lane, byte c the scale of the quad's tile c: for gate|up the
+  // gate tiles 2q, 2q+1 and up tiles 2q, 2q+1, for down the tiles 4q..4q+3.
+  // A wave's four column tiles are exactly one quad.
+  const uint32_t bsoff = (uint32_t)(wave_ok ? ((STAGE == 1) ? c0 / 32 + w : n0 / 64 + w) : 0) * 256u + 4u * lane;
   // fp32 weight-scale rows (FP8): two 128-blocks of N per item; or, with
   // per-channel scales, the scales of the item's 256 B-columns (applied in
   // the epilogue, after the K sum)
@@ -349,8 +354,8 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
     if (WF == W_FP8) {
       b.d[q >> 1][q & 1] = buf_ld16(wrs, boff[q >> 1] + 1024 * (q & 1), bstep(s));
     } else if (WF == W_FP4) {
-      if ((q & 1) == 0) b.d[q >> 1][0] = buf_ld16(wrs, boff[q >> 1], bstep(s));
-      else b.sc[q >> 1] = (int)buf_ldu8(srs, bsoff[q >> 1], (uint32_t)min(s, nsteps - 1) * (uint32_t)N * 4u);
+      if (q < 4) b.d[q][0] = buf_ld16(wrs, boff[q], bstep(s));
+      else b.sc = __float_as_uint(buf_ldf(srs, bsoff, (uint32_t)min(s, nsteps - 1) * (uint32_t)N * 4u));
     } else {
       b.d[q >> 2][q & 3] = buf_ld16(wrs, boff[q >> 2] + 1024 * (q & 3), bstep(s));
     }
@@ -454,10 +459,11 @@ DEV void expert_gemm_tile(const GemmArgs& g, int e, int r0, int m, int nb, char*
               p[rs & 1][cs] = mfma_fp8_fp8(bv, av, zero);
             } else if (E8) {
               const v8i bv = {b.d[cs][0][0], b.d[cs][0][1], b.d[cs][0][2], b.d[cs][0][3], 0, 0, 0, 0};
-              acc[rs][cs] = mfma_fp4_fp8(bv, av, acc[rs][cs], b.sc[cs], e8m0_of_pow2(scv[0][rs >> 2][rs & 3]));
+              acc[rs][cs] = mfma_fp4_fp8(bv, av, acc[rs][cs], (int)((b.sc >> (8 * cs)) & 0xFFu),
+                                         e8m0_of_pow2(scv[0][rs >> 2][rs & 3]));
             } else {
               const v8i bv = {b.d[cs][0][0], b.d[cs][0][1], b.d[cs][0][2], b.d[cs][0][3], 0, 0, 0, 0};
-              p[rs & 1][cs] = mfma_fp4_fp8(bv, av, zero, b.sc[cs]);
+              p[rs & 1][cs] = mfma_fp4_fp8(bv, av, zero, (int)((b.sc >> (8 * cs)) & 0xFFu));
             }
           }
         }

@@ -145,17 +145,22 @@ __global__ void __launch_bounds__(256) k_pack_weights(const uint8_t* src, uint8_
   }
 }
 
-// E8M0 scales [E*N][K/32] -> 64-byte blocks per (K step, 16-row tile).
-__global__ void __launch_bounds__(256) k_pack_e8m0(const uint8_t* src, uint8_t* dst, size_t rows, int n, int nsteps) {
-  const int nt = n / 16;
+// E8M0 scales [E*N][K/32] -> per (K step s, quad q) 256 bytes, byte
+// 4*l + c the scale of row 16*tile + l%16, K group 4*s + l/16, where tile is
+// the quad's c-th 16-row tile: gate|up (gu) 2q + c for c < 2 and
+// N/32 + 2q + c - 2 (the up rows) for c >= 2; down 4q + c.
+__global__ void __launch_bounds__(256) k_pack_e8m0(const uint8_t* src, uint8_t* dst, size_t rows, int n, int nsteps,
+                                                   int gu) {
+  const int nq = n / 64;
   const size_t total = rows * (size_t)nsteps * 4;
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
-    const int l = (int)(i & 63);
-    size_t r = i >> 6;                               // (e, s, t)
-    const int t = (int)(r % nt);
-    r /= nt;
+    const int c = (int)(i & 3), l = (int)((i >> 2) & 63);
+    size_t r = i >> 8;                               // (e, s, q)
+    const int q = (int)(r % nq);
+    r /= nq;
     const int s = (int)(r % nsteps);
-    const size_t row = (r / nsteps) * n + (size_t)t * 16 + (l & 15);
+    const int tile = gu ? ((c < 2) ? 2 * q + c : n / 32 + 2 * q + c - 2) : 4 * q + c;
+    const size_t row = (r / nsteps) * n + (size_t)tile * 16 + (l & 15);
     dst[i] = src[row * ((size_t)nsteps * 4) + 4 * s + (l >> 4)];
   }
 }
@@ -1218,7 +1223,7 @@ moe_status moe_pack_weights(const moe_desc* d, int32_t which, const void* src, c
   HIP_TRY(hipGetLastError());
   if (fp4) {
     hipLaunchKernelGGL(k_pack_e8m0, dim3(grid), dim3(256), 0, st, static_cast<const uint8_t*>(src_scales),
-                       static_cast<uint8_t*>(dst_scales), rows, (int)N, K / 128);
+                       static_cast<uint8_t*>(dst_scales), rows, (int)N, K / 128, which == MOE_WEIGHTS_GATE_UP ? 1 : 0);
     HIP_TRY(hipGetLastError());
   }
   return MOE_OK;

@@ -303,12 +303,22 @@ def _tiled_reference(w: np.ndarray, bs: int) -> np.ndarray:
     return np.ascontiguousarray(v).reshape(E, N, KB)
 
 
-def _tiled_scales_reference(sc: np.ndarray) -> np.ndarray:
-    """E8M0 scales [E][N][K/32] -> per (s, t), K step major, 64 bytes, byte
-    l = row 16t + l%16, group 4s + l//16."""
+def _tiled_scales_reference(sc: np.ndarray, gate_up: bool) -> np.ndarray:
+    """E8M0 scales [E][N][K/32] -> per (K step s, quad q) 256 bytes, byte
+    4l + c = row 16t + l%16, group 4s + l//16, with t the quad's c-th tile:
+    gate|up 2q + c (c < 2) or N/32 + 2q + c - 2, down 4q + c."""
     E, N, G = sc.shape
-    v = sc.reshape(E, N // 16, 16, G // 4, 4).transpose(0, 3, 1, 4, 2)   # e, s, t, l//16, row%16
-    return np.ascontiguousarray(v).reshape(E, N, G)
+    S, nq = G // 4, N // 64
+    q, c, l = np.arange(nq)[:, None, None], np.arange(4)[None, None, :], np.arange(64)[None, :, None]
+    if gate_up:
+        t = np.where(c < 2, 2 * q + c, N // 32 + 2 * q + c - 2)
+    else:
+        t = 4 * q + c
+    rows = (t * 16 + l % 16)                                            # [q][l][c]
+    out = np.empty((E, S, nq, 64, 4), dtype=sc.dtype)
+    for s in range(S):
+        out[:, s] = sc[:, rows, 4 * s + l // 16]
+    return out.reshape(E, N, G)
 
 
 @pytest.mark.parametrize("weight", ["fp8", "fp4", "bf16"])
@@ -325,6 +335,6 @@ def test_pack_weights_layout_bit_exact(L, weight):
         assert np.array_equal(got, _tiled_reference(src, bs)), w
         if weight == "fp4":
             s_src = inp[sc].cpu().numpy()
-            assert np.array_equal(packed[sc].cpu().numpy(), _tiled_scales_reference(s_src)), sc
+            assert np.array_equal(packed[sc].cpu().numpy(), _tiled_scales_reference(s_src, w == "w_gate_up")), sc
         elif weight == "fp8":
             assert packed[sc] is inp[sc]
