@@ -107,9 +107,12 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 5   /* 3: moe_desc.weight_layout and moe_desc.inter_scale;
+#define MOE_ABI_VERSION 6   /* 3: moe_desc.weight_layout and moe_desc.inter_scale;
                                4: moe_desc.weight_scale;
-                               5: moe_quantize_e5m6, moe_dequantize_e5m6 */
+                               5: moe_quantize_e5m6, moe_dequantize_e5m6;
+                               6: FP4 E8M0 scales packed in quads (weights packed
+                                  by an earlier version must be packed again),
+                                  staging region N-block major */
 
 typedef enum moe_status {
   MOE_OK = 0,
